@@ -1,0 +1,193 @@
+/*
+ * csa2.h -- C ABI of the gfx950 (MI355X) library for CSA2 sparse attention
+ * over an FP4 KV cache (E2M1 elements, one E4M3 scale per 16 channels).
+ *
+ * Three calls cover the three statically assigned layer modes described in
+ * the course brief "DeepSeek-V4.1-Flash" (section "CSA2: most layers don't
+ * keep their own cache", mode table) and in the metallab.ai article on the
+ * V4.1-Flash KV cache (paragraph on the three modes):
+ *
+ *   Full    : csa2_quantize_kv_fp4 (write own main KV)
+ *             -> csa2_index_topk(CSA2_FULL, ..., pool_size)   own indexer
+ *             -> csa2_sparse_attn
+ *   Reindex : csa2_index_topk(CSA2_REINDEX, pool = last Full's pool)
+ *             -> csa2_sparse_attn
+ *   Reuse   : csa2_sparse_attn(idx = last Full/Reindex selection)
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *     every buffer (inputs, outputs, workspace); the library never allocates,
+ *     frees, synchronizes or copies to the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Work is enqueued on it and the call returns without waiting.
+ *   - Inputs are read-only.  Outputs are overwritten in full, padding too.
+ *   - Return value: CSA2_OK (0) or a negative status.  Only host-visible
+ *     arguments are checked; device data are never read by the host.
+ *     Data-dependent conditions are defined behaviour, not errors: an index
+ *     < 0 or >= the row's visible count is skipped, an empty selection
+ *     gives output 0 and lse = -inf.
+ *   - csa2_last_error() returns a thread-local message for the last failing
+ *     call of the calling thread.
+ *   - Calls that share a workspace must be ordered on one stream.
+ *
+ * Packed variable-length batches work like cu_seqlens: every row r owns a
+ * segment of the cache starting at row_kv_start[r]; entry (token position)
+ * j of that row lives at cache row row_kv_start[r] + j.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define CSA2_OK 0
+#define CSA2_E_INVALID (-1)     /* null pointer, bad dtype, shape or alignment */
+#define CSA2_E_UNSUPPORTED (-2) /* valid request this build does not implement */
+#define CSA2_E_WORKSPACE (-3)   /* workspace missing or smaller than required  */
+#define CSA2_E_HIP (-4)         /* a HIP launch failed; message has the reason */
+
+/* element types */
+#define CSA2_F32 0
+#define CSA2_BF16 1
+
+/* indexer modes */
+#define CSA2_FULL 0
+#define CSA2_REINDEX 1
+
+/* geometry of one cache entry ("FP4 cache entries, and why they're safe":
+ * 512 values x 4 bits + 512/16 scales x 1 byte = 256 + 32 = 288 bytes) */
+#define CSA2_HEAD_DIM 512
+#define CSA2_CODE_BYTES 256
+#define CSA2_SCALE_BYTES 32
+#define CSA2_MAX_TOP_K 4096
+
+/*
+ * Quantize-on-write ("FP4 cache entries, and why they're safe", course
+ * brief "DeepSeek-V4.1-Flash": E2M1 elements with one E4M3 scale per group
+ * of 16 channels, no second-level global scale).  Per group g:
+ *   amax = max|x_c|; s = E4M3(amax / 6) (fp32 division, round to nearest
+ *   even, saturating at 448); code_c = E2M1(x_c / s) (fp32 division, round
+ *   to nearest even, saturating at 6, sign kept); a group with s = 0 gets
+ *   all-zero codes.
+ *
+ * x            [n_tokens, x_row_stride] elements of x_dtype (CSA2_F32 or
+ *              CSA2_BF16); the first 512 of each row are quantized.  Must be
+ *              16-byte aligned with x_row_stride * element size a multiple
+ *              of 16.  Values must be finite.
+ * dst_rows     [n_tokens] int64 cache row of each token, or NULL for rows
+ *              0..n_tokens-1 (then n_tokens <= cap_rows is required).  A
+ *              destination outside [0, cap_rows) is skipped.
+ * kv_codes     [cap_rows, 256] uint8: byte i = code of channel 2i (low
+ *              nibble) | code of channel 2i+1 (high nibble).
+ * kv_scales    [cap_rows, 32] uint8: E4M3 scale byte of group g.
+ * Errors: CSA2_E_INVALID for null buffers, n_tokens < 0, bad dtype,
+ * misalignment, x_row_stride < 512, or (dst_rows NULL and n_tokens > cap_rows).
+ */
+int32_t csa2_quantize_kv_fp4(const void* x, int32_t x_dtype, int64_t n_tokens, int64_t x_row_stride,
+                             const int64_t* dst_rows, uint8_t* kv_codes, uint8_t* kv_scales,
+                             int64_t cap_rows, void* stream);
+
+/*
+ * Indexer + top-K ("The global branch: compress, index, select" and "The
+ * hierarchical indexer" in the course brief; "The Paper" in the talk
+ * write-up "DeepSeek V4.1 Flash: pushing the limits").
+ *
+ * Score of entry j for row r (fp32, fixed operation order, bit-reproducible):
+ *   acc_h = fmaf chain over c = 0..63 of idx_q[r,h,c] * idx_k[j,c] from +0;
+ *   score = sum over h = 0..H-1, left to right, of max(acc_h, +0).
+ * Selection: the top_k entries by (score desc, position asc); out_idx[r] holds
+ * their positions ascending, padded with -1.
+ *
+ * mode = CSA2_FULL: candidates are positions 0..row_visible[r]-1.  With
+ *   pool_size > 0 (block_size must be 8) it also emits the hierarchical
+ *   candidate pool: blocks of 8 positions scored by their best member, the
+ *   top pool_size/8 blocks by (block score desc, block asc), their member
+ *   positions ascending in out_pool[r] (padded with -1), the count in
+ *   out_pool_len[r].
+ * mode = CSA2_REINDEX: candidates are pool[r, i] for i < pool_len[r] (or
+ *   i < pool_stride if pool_len is NULL); entries < 0 or >= row_visible[r]
+ *   are skipped.  Valid entries must be unique and ascending (as
+ *   CSA2_FULL emits them); ties are broken by pool order.
+ *
+ * idx_q        [n_rows, n_heads, head_dim] of q_dtype.
+ * idx_k        [cache rows, head_dim] of k_dtype; row_kv_start[r] + j.
+ * row_kv_start [n_rows] int64;  row_visible [n_rows] int32.
+ * max_visible  host-side upper bound of row_visible (sizes grids and
+ *              workspace); larger row_visible values are clamped to it.
+ * head_dim must be 64; n_heads in 1..32; 1 <= top_k <= CSA2_MAX_TOP_K.
+ * out_idx      [n_rows, top_k] int32.
+ * workspace    device scratch of csa2_index_topk_workspace_size(...) bytes,
+ *              256-byte aligned.
+ */
+int32_t csa2_index_topk(int32_t mode, int32_t n_rows,
+                        const void* idx_q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                        const void* idx_k, int32_t k_dtype,
+                        const int64_t* row_kv_start, const int32_t* row_visible, int32_t max_visible,
+                        const int32_t* pool, const int32_t* pool_len, int32_t pool_stride,
+                        int32_t top_k, int32_t* out_idx,
+                        int32_t pool_size, int32_t block_size, int32_t* out_pool, int32_t* out_pool_len,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+size_t csa2_index_topk_workspace_size(int32_t mode, int32_t n_rows, int32_t n_heads, int32_t max_visible,
+                                      int32_t pool_stride, int32_t top_k, int32_t pool_size);
+
+/*
+ * Sparse attention over the selected entries ("The Paper" in the talk
+ * write-up: K and V are the same Main KV entry, the selected entries are
+ * attended with the normal attention operation; "The global branch" in the
+ * course brief: one 512-dim latent per entry shared by every query head).
+ * For row r, head h, over S = {idx[r,i] : 0 <= idx[r,i] < row_visible[r]}:
+ *   x_j = E2M1(code) * E4M3(scale) dequantized entry j;
+ *   z_j = softmax_scale * q[r,h] . x_j;  p = softmax(z) over S;
+ *   out[r,h] = sum_j p_j x_j;  lse[r,h] = ln sum_j exp(z_j).
+ * S empty: out = 0, lse = -inf.  Duplicate indices count as often as listed.
+ *
+ * q            [n_rows, n_heads, 512] of q_dtype (CSA2_F32 or CSA2_BF16);
+ *              16-byte aligned.  bf16 values are used exactly; fp32 values
+ *              are split into two fp16 halves (about 22 significant bits).
+ *              |q| must stay below 65504.
+ * n_heads      a multiple of 16, at most 128; head_dim must be 512.
+ * kv_codes/kv_scales  the cache written by csa2_quantize_kv_fp4.
+ * idx          [n_rows, top_k] int32 positions (e.g. out_idx of the indexer).
+ * row_visible  [n_rows] int32 or NULL (NULL: every idx >= 0 is valid).
+ * out          [n_rows, n_heads, 512] of out_dtype (CSA2_F32 or CSA2_BF16).
+ * lse          [n_rows, n_heads] fp32 or NULL.
+ * workspace    csa2_sparse_attn_workspace_size(...) bytes (may be 0 when
+ *              that function returns 0), 256-byte aligned.
+ * Results are deterministic: the same inputs give the same bits.
+ */
+int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                         const uint8_t* kv_codes, const uint8_t* kv_scales, const int64_t* row_kv_start,
+                         const int32_t* idx, int32_t top_k, const int32_t* row_visible,
+                         float softmax_scale, void* out, int32_t out_dtype, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+size_t csa2_sparse_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t q_dtype, int32_t top_k);
+
+/* Thread-local description of the last non-zero status of this thread. */
+const char* csa2_last_error(void);
+
+/*
+ * Measurement hook.  When `start_event`/`stop_event` (hipEvent_t as void*)
+ * are non-NULL, later calls record them on the launch stream immediately
+ * before and after every launch of kernel `kernel_id`; NULL pointers stop
+ * the recording.  Process-wide; not thread-safe.  Returns CSA2_E_INVALID
+ * for an unknown id.
+ */
+#define CSA2_KERNEL_QUANT 1
+#define CSA2_KERNEL_INDEX_SCAN 2
+#define CSA2_KERNEL_REINDEX_SCORE 3
+#define CSA2_KERNEL_ATTN 4
+#define CSA2_KERNEL_ATTN_COMBINE 5
+int32_t csa2_profile_kernel_events(int32_t kernel_id, void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,154 @@
+"""ctypes binding of libcsa2.so (the C ABI in include/csa2.h).
+
+Argument marshalling only: torch tensors supply device pointers, the
+current HIP stream is passed through, and every non-zero status raises
+``CSA2Error`` with the library's message.  All arithmetic runs in the HIP
+kernels of libcsa2.so; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcsa2.so")
+
+F32, BF16 = 0, 1
+FULL, REINDEX = 0, 1
+MAX_TOP_K = 4096
+KERNEL_QUANT, KERNEL_INDEX_SCAN, KERNEL_REINDEX_SCORE, KERNEL_ATTN, KERNEL_ATTN_COMBINE = 1, 2, 3, 4, 5
+EXPORTED = (
+    "csa2_quantize_kv_fp4",
+    "csa2_index_topk",
+    "csa2_index_topk_workspace_size",
+    "csa2_sparse_attn",
+    "csa2_sparse_attn_workspace_size",
+    "csa2_last_error",
+    "csa2_profile_kernel_events",
+)
+
+_LIB = None
+
+
+class CSA2Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("csa2 status %d: %s" % (code, msg))
+        self.code = code
+
+
+def lib():
+    """Load libcsa2.so; raises if it has not been built (no fallback exists)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libcsa2.so is not built; run __graft_entry__.build() or "
+                              "python sparse_attention_fp4_e4m3_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.csa2_quantize_kv_fp4.argtypes = [P, i32, i64, i64, P, P, P, i64, P]
+        L.csa2_quantize_kv_fp4.restype = i32
+        L.csa2_index_topk.argtypes = [i32, i32, P, i32, i32, i32, P, i32, P, P, i32, P, P, i32, i32, P, i32, i32,
+                                      P, P, P, sz, P]
+        L.csa2_index_topk.restype = i32
+        L.csa2_index_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.csa2_index_topk_workspace_size.restype = sz
+        L.csa2_sparse_attn.argtypes = [i32, P, i32, i32, i32, P, P, P, P, i32, P, ctypes.c_float, P, i32, P, P, sz, P]
+        L.csa2_sparse_attn.restype = i32
+        L.csa2_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.csa2_sparse_attn_workspace_size.restype = sz
+        L.csa2_last_error.argtypes = []
+        L.csa2_last_error.restype = ctypes.c_char_p
+        L.csa2_profile_kernel_events.argtypes = [i32, P, P]
+        L.csa2_profile_kernel_events.restype = i32
+        _LIB = L
+    return _LIB
+
+
+def _check(code: int):
+    if code != 0:
+        raise CSA2Error(code, lib().csa2_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def quantize_kv_fp4(x: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor,
+                    dst_rows: Optional[torch.Tensor] = None, stream=None) -> None:
+    """x [n, 512(+)] fp32/bf16 -> FP4 rows of kv_codes [cap, 256] u8 / kv_scales [cap, 32] u8."""
+    _contig(kv_codes, kv_scales, dst_rows)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [n, C] with unit channel stride")
+    _check(lib().csa2_quantize_kv_fp4(_ptr(x), _dt(x), x.shape[0], x.stride(0), _ptr(dst_rows),
+                                      _ptr(kv_codes), _ptr(kv_scales), kv_codes.shape[0], _stream(stream)))
+
+
+def index_topk_workspace_size(mode: int, n_rows: int, n_heads: int, max_visible: int, pool_stride: int,
+                              top_k: int, pool_size: int) -> int:
+    return int(lib().csa2_index_topk_workspace_size(mode, n_rows, n_heads, max_visible, pool_stride, top_k,
+                                                    pool_size))
+
+
+def index_topk(mode: int, idx_q: torch.Tensor, idx_k: torch.Tensor, row_kv_start: torch.Tensor,
+               row_visible: torch.Tensor, max_visible: int, top_k: int, out_idx: torch.Tensor,
+               workspace: torch.Tensor, pool: Optional[torch.Tensor] = None,
+               pool_len: Optional[torch.Tensor] = None, pool_size: int = 0,
+               out_pool: Optional[torch.Tensor] = None, out_pool_len: Optional[torch.Tensor] = None,
+               stream=None) -> None:
+    """Indexer scores + exact top-K (and the HSI pool in Full mode)."""
+    _contig(idx_q, idx_k, row_kv_start, row_visible, out_idx, workspace, pool, pool_len, out_pool, out_pool_len)
+    R, H, Dk = idx_q.shape
+    pool_stride = pool.shape[1] if pool is not None else 0
+    _check(lib().csa2_index_topk(
+        mode, R, _ptr(idx_q), _dt(idx_q), H, Dk, _ptr(idx_k), _dt(idx_k), _ptr(row_kv_start), _ptr(row_visible),
+        int(max_visible), _ptr(pool), _ptr(pool_len), pool_stride, top_k, _ptr(out_idx), pool_size,
+        8 if pool_size else 0, _ptr(out_pool), _ptr(out_pool_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sparse_attn_workspace_size(n_rows: int, n_heads: int, q_dtype: int, top_k: int) -> int:
+    return int(lib().csa2_sparse_attn_workspace_size(n_rows, n_heads, q_dtype, top_k))
+
+
+def sparse_attn(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor, row_kv_start: torch.Tensor,
+                idx: torch.Tensor, out: torch.Tensor, softmax_scale: float,
+                row_visible: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Gather + dequant + softmax attention over the selected entries."""
+    _contig(q, kv_codes, kv_scales, row_kv_start, idx, out, row_visible, lse, workspace)
+    R, Hq, D = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().csa2_sparse_attn(
+        R, _ptr(q), _dt(q), Hq, D, _ptr(kv_codes), _ptr(kv_scales), _ptr(row_kv_start), _ptr(idx),
+        idx.shape[1], _ptr(row_visible), float(softmax_scale), _ptr(out), _dt(out), _ptr(lse), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+
+
+def profile_kernel_events(kernel_id: int, start=None, stop=None) -> None:
+    """Record torch.cuda.Event pairs around every launch of one kernel (None stops)."""
+    s = None if start is None else ctypes.c_void_p(start.cuda_event)
+    e = None if stop is None else ctypes.c_void_p(stop.cuda_event)
+    _check(lib().csa2_profile_kernel_events(kernel_id, s, e))

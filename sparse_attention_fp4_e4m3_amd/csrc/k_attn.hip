@@ -1,0 +1,615 @@
+// k_attn.hip -- gather + FP4 dequant + online-softmax sparse attention on
+// gfx950 MFMA, with a deterministic split-K combine.
+//
+// What it computes ("The Paper" in the talk write-up "DeepSeek V4.1 Flash:
+// pushing the limits": K and V are the same Main KV entry; "The global
+// branch" in the course brief "DeepSeek-V4.1-Flash": one 512-dim latent per
+// entry shared by all query heads): for a row r and head h, softmax over the
+// selected entries of softmax_scale * q . x_hat, then the weighted sum of the
+// x_hat.  x_hat = E2M1 code * E4M3 scale is exact in fp16, so both products
+// run on fp16 MFMA (v_mfma_f32_16x16x32_f16, fp32 accumulate): bf16 queries
+// convert to fp16 exactly; fp32 queries are split into hi + lo fp16 halves.
+// Probabilities are rounded to fp16 for the PV product and the row sums add
+// up those same rounded values.
+//
+// Work split.  A workgroup (4 waves) owns one (row, head group of up to 64
+// heads, key split) and walks its keys in steps of 128:
+//  * QK^T, keys split across waves: wave w takes keys [32w, 32w+32) of the
+//    step and all heads; it loads its keys' 288-byte rows straight from HBM
+//    into registers (prefetched one step ahead) and dequantizes them into
+//    the A operand (key rows); queries sit in LDS as the B operand.  The
+//    result S^T has each lane holding 8 keys of one head, so the running max
+//    and sums need only two cross-lane steps.
+//  * softmax: per-wave maxima and sums meet in LDS; probabilities go to LDS
+//    as fp16 [head][key].
+//  * PV, output channels split across waves: wave w produces channels
+//    [128w, 128w+128) of every head, reading the raw codes of all 128 keys
+//    from LDS and re-pairing nibbles of neighbouring keys so that each
+//    packed fp16 pair holds two keys of one channel (the K-contiguous layout
+//    the B operand needs).
+// Each FP4 element is dequantized once per workgroup for QK^T and once for
+// PV; every dequantized value feeds all heads of the group.
+#include "csa2_common.h"
+
+#ifndef CSA2_HW_CVT
+#define CSA2_HW_CVT 1
+#endif
+
+namespace csa2 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kStep = 128;           // keys per step (32 per wave)
+constexpr int kCsStride = 272;       // bytes per staged code row (256 + 16 pad)
+constexpr int kScStride = 136;       // fp16 per staged scale row (128 keys + 8 pad)
+constexpr int kPStride = 136;        // fp16 per probability row
+constexpr int kQStride = 520;        // fp16 per query row (512 + 8 pad)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ half2v bits_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+
+// two E2M1 codes (byte SEL of w: low nibble first) -> two fp16 values
+template <int SEL>
+__device__ __forceinline__ half2v fp4x2_to_h2(uint32_t w) {
+#if CSA2_HW_CVT
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+#else
+  const uint32_t b = (w >> (8 * SEL)) & 0xFFu;
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t c = (b >> (4 * k)) & 15u, mag = c & 7u;
+    uint32_t bits = mag < 2u ? (mag ? 0x3800u : 0u) : ((((mag >> 1) + 14u) << 10) | ((mag & 1u) << 9));
+    bits |= (c & 8u) << 12;
+    out |= bits << (16 * k);
+  }
+  return bits_h2(out);
+#endif
+}
+
+// two E4M3 bytes (half SEL of w) -> two fp16 values
+template <bool SEL>
+__device__ __forceinline__ half2v e4m3x2_to_h2(uint32_t w) {
+#if CSA2_HW_CVT
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL);
+#else
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t b = (w >> (16 * (SEL ? 1 : 0) + 8 * k)) & 0xFFu;
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    out |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v) << (16 * k);
+  }
+  return bits_h2(out);
+#endif
+}
+
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
+
+__device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8 cat4(half2v a, half2v b, half2v c, half2v d) {
+  return __builtin_bit_cast(half8, u32x4{h2_bits(a), h2_bits(b), h2_bits(c), h2_bits(d)});
+}
+
+struct AttnArgs {
+  const void* q;
+  int Hq;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const int64_t* row_start;
+  const int32_t* idx;
+  int top_k;
+  const int32_t* row_visible;
+  float c2;              // softmax_scale * log2(e)
+  void* out;
+  int out_dtype;
+  float* lse;
+  int splits;
+  int keys_per_split;    // multiple of kStep
+  float* ws_o;           // [R, Hq, splits, 512]
+  float* ws_m;           // [R, Hq, splits]
+  float* ws_l;           // [R, Hq, splits]
+};
+
+template <int NHT, bool SPLITQ>
+struct Smem {
+  static constexpr int kQRows = 16 * NHT * (SPLITQ ? 2 : 1);
+  _Float16 q[kQRows * kQStride];
+  uint8_t cs[kStep * kCsStride];
+  _Float16 sct[kGroups * kScStride];
+  _Float16 p[16 * NHT * kPStride];
+  float red_max[4][64];
+  float red_sum[4][64];
+  float alpha[64];
+  float lfin[64];
+  float mfin[64];
+};
+
+struct Raw {
+  u32x4 c[2][4];  // [key tile][16-byte piece]: code bytes [64*q4, 64*q4+64) of the lane's key
+  u32x2 s[2];     // scale bytes [8*q4, 8*q4+8)
+};
+
+__device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int r, int64_t rs, int vis, int kpos0, int kend,
+                                         const int32_t (&j)[2], uint32_t (&valid)[2], int lane) {
+  const int m = lane & 15, q4 = lane >> 4;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int i = kpos0 + 16 * kt + m;
+    const bool ok = i < kend && j[kt] >= 0 && j[kt] < vis;
+    valid[kt] = ok;
+    if (ok) {
+      const int64_t row = rs + j[kt];
+      const u32x4* pc = reinterpret_cast<const u32x4*>(a.codes + row * kCodeBytes + 64 * q4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) R.c[kt][c] = __builtin_nontemporal_load(pc + c);
+      R.s[kt] = *reinterpret_cast<const u32x2*>(a.scales + row * kGroups + 8 * q4);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) R.c[kt][c] = u32x4{0u, 0u, 0u, 0u};
+      R.s[kt] = u32x2{0u, 0u};
+    }
+  }
+}
+
+__device__ __forceinline__ void load_idx(int32_t (&j)[2], const AttnArgs& a, int r, int kpos0, int kend, int lane) {
+  const int m = lane & 15;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int i = kpos0 + 16 * kt + m;
+    j[kt] = (i < kend) ? a.idx[(int64_t)r * a.top_k + i] : -1;
+  }
+}
+
+template <int NHT, bool SPLITQ, int QDT>
+__global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  Smem<NHT, SPLITQ>& sm = *reinterpret_cast<Smem<NHT, SPLITQ>*>(smem_raw);
+  constexpr int HG = 16 * NHT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
+  const int h0 = hg * HG;
+  const int kbeg = split * a.keys_per_split;
+  const int kend = min(a.top_k, kbeg + a.keys_per_split);
+  const int nsteps = kend > kbeg ? (kend - kbeg + kStep - 1) / kStep : 0;
+  const int vis = a.row_visible ? a.row_visible[r] : 0x7FFFFFFF;
+  const int64_t rs = a.row_start[r];
+
+  // ---- prologue: first step's keys in flight, queries to LDS
+  int32_t jcur[2], jnext[2];
+  uint32_t vcur[2], vnext[2];
+  Raw cur, nxt;
+  if (nsteps > 0) {
+    load_idx(jcur, a, r, kbeg + 32 * w, kend, lane);
+    load_raw(cur, a, r, rs, vis, kbeg + 32 * w, kend, jcur, vcur, lane);
+  }
+  if (nsteps > 1) load_idx(jnext, a, r, kbeg + kStep + 32 * w, kend, lane);
+  {
+    // HG heads x 512 channels; 16-byte pieces
+    if (QDT == CSA2_BF16) {
+      const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
+      for (int p = tid; p < HG * kDim / 8; p += kThreads) {
+        const int h = p / (kDim / 8), c8 = (p % (kDim / 8)) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qb + (int64_t)h * kDim + c8);
+        half8 hv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          hv[2 * k] = (_Float16)__uint_as_float(v[k] << 16);
+          hv[2 * k + 1] = (_Float16)__uint_as_float(v[k] & 0xFFFF0000u);
+        }
+        *reinterpret_cast<half8*>(&sm.q[h * kQStride + c8]) = hv;
+      }
+    } else {
+      const float* qf = static_cast<const float*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
+      for (int p = tid; p < HG * kDim / 4; p += kThreads) {
+        const int h = p / (kDim / 4), c4 = (p % (kDim / 4)) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(qf + (int64_t)h * kDim + c4);
+        const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const _Float16 hi = (_Float16)f[k];
+          sm.q[h * kQStride + c4 + k] = hi;
+          if (SPLITQ) sm.q[(HG + h) * kQStride + c4 + k] = (_Float16)(f[k] - (float)hi);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  floatx4 O[NHT][8];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mrun[NHT], lrun[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    mrun[ht] = -INFINITY;
+    lrun[ht] = 0.0f;
+  }
+
+  for (int st = 0; st < nsteps; ++st) {
+    const int kstep0 = kbeg + st * kStep;
+    // scale bytes of this lane's two keys -> fp16 (groups 8*q4 .. 8*q4+7)
+    half2v sc[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sc[kt][0] = e4m3x2_to_h2<false>(cur.s[kt][0]);
+      sc[kt][1] = e4m3x2_to_h2<true>(cur.s[kt][0]);
+      sc[kt][2] = e4m3x2_to_h2<false>(cur.s[kt][1]);
+      sc[kt][3] = e4m3x2_to_h2<true>(cur.s[kt][1]);
+    }
+
+    // ---- QK^T: S^T[key][head] for this wave's 32 keys
+    floatx4 S[2][NHT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      // K-step ks covers channels 128*q4 + 8*ks .. +7 (the same mapping on both operands)
+      half8 bq[NHT * (SPLITQ ? 2 : 1)];
+#pragma unroll
+      for (int ht = 0; ht < NHT * (SPLITQ ? 2 : 1); ++ht)
+        bq[ht] = *reinterpret_cast<const half8*>(&sm.q[(16 * ht + n16) * kQStride + 128 * q4 + 8 * ks]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint32_t word = cur.c[kt][ks >> 2][ks & 3];
+        const half2v s1 = sc[kt][ks >> 2];
+        const half2v ss = (ks & 2) ? half2v{s1[1], s1[1]} : half2v{s1[0], s1[0]};
+        const half8 av = cat4(fp4x2_to_h2<0>(word) * ss, fp4x2_to_h2<1>(word) * ss, fp4x2_to_h2<2>(word) * ss,
+                              fp4x2_to_h2<3>(word) * ss);
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          S[kt][ht] = mfma(av, bq[ht], S[kt][ht]);
+          if (SPLITQ) S[kt][ht] = mfma(av, bq[NHT + ht], S[kt][ht]);
+        }
+      }
+    }
+
+    // ---- prefetch the next step (registers), its indices one step further
+    if (st + 1 < nsteps) {
+      load_raw(nxt, a, r, rs, vis, kstep0 + kStep + 32 * w, kend, jnext, vnext, lane);
+      if (st + 2 < nsteps) load_idx(jnext, a, r, kstep0 + 2 * kStep + 32 * w, kend, lane);
+    }
+
+    // ---- softmax, part 1: scaled logits, masked, per-wave max per head
+    const unsigned long long vm0 = __ballot(vcur[0]), vm1 = __ballot(vcur[1]);
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const unsigned long long vm = kt ? vm1 : vm0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (vm >> (4 * q4 + i)) & 1ull;
+          const float z = ok ? S[kt][ht][i] * a.c2 : -INFINITY;
+          S[kt][ht][i] = z;
+          mx = fmaxf(mx, z);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (q4 == 0) sm.red_max[w][16 * ht + n16] = mx;
+    }
+    __syncthreads();  // B1: maxima visible; every wave is past the previous PV
+
+    // ---- stage this step's raw codes and fp16 scales for PV
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = 32 * w + 16 * kt + n16;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&sm.cs[key * kCsStride + 64 * q4 + 16 * c]) = cur.c[kt][c];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        sm.sct[(8 * q4 + 2 * g) * kScStride + key] = sc[kt][g][0];
+        sm.sct[(8 * q4 + 2 * g + 1) * kScStride + key] = sc[kt][g][1];
+      }
+    }
+
+    // ---- softmax, part 2: running max, probabilities (fp16), sums
+    float alpha[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      const float mstep = fmaxf(fmaxf(sm.red_max[0][h], sm.red_max[1][h]), fmaxf(sm.red_max[2][h], sm.red_max[3][h]));
+      const float mnew = fmaxf(mrun[ht], mstep);
+      const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+      alpha[ht] = __builtin_amdgcn_exp2f(mrun[ht] - muse);
+      mrun[ht] = mnew;
+      float sum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        _Float16 p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = (_Float16)__builtin_amdgcn_exp2f(S[kt][ht][i] - muse);
+          sum += (float)p[i];
+        }
+        *reinterpret_cast<u32x2*>(&sm.p[h * kPStride + 32 * w + 16 * kt + 4 * q4]) =
+            u32x2{h2_bits(half2v{p[0], p[1]}), h2_bits(half2v{p[2], p[3]})};
+      }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      if (q4 == 0) {
+        sm.red_sum[w][h] = sum;
+        if (w == 0) sm.alpha[h] = alpha[ht];
+      }
+    }
+    __syncthreads();  // B2: probabilities, sums, alpha and staged codes visible
+
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      lrun[ht] = lrun[ht] * alpha[ht] + (((sm.red_sum[0][h] + sm.red_sum[1][h]) + sm.red_sum[2][h]) + sm.red_sum[3][h]);
+    }
+
+    // ---- PV: channels [128w, 128w+128) of every head
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = sm.alpha[16 * ht + 4 * q4 + i];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) O[ht][t][i] *= al;
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int key0 = 32 * kc + 8 * q4;  // this lane's 8 keys (slots 0..7)
+      uint32_t W[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        W[k] = *reinterpret_cast<const uint32_t*>(&sm.cs[(key0 + k) * kCsStride + 64 * w + 4 * n16]);
+      const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[(8 * w + (n16 >> 1)) * kScStride + key0]);
+      uint32_t Bw[8][4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // E: byte b = channel 2b of keys (2p, 2p+1); D: channel 2b+1 of the same keys
+        const uint32_t E = bfi(0x0F0F0F0Fu, W[2 * p], W[2 * p + 1] << 4);
+        const uint32_t D = bfi(0x0F0F0F0Fu, W[2 * p] >> 4, W[2 * p + 1]);
+        const half2v sp = bits_h2(spw[p]);
+        Bw[0][p] = h2_bits(fp4x2_to_h2<0>(E) * sp);
+        Bw[2][p] = h2_bits(fp4x2_to_h2<1>(E) * sp);
+        Bw[4][p] = h2_bits(fp4x2_to_h2<2>(E) * sp);
+        Bw[6][p] = h2_bits(fp4x2_to_h2<3>(E) * sp);
+        Bw[1][p] = h2_bits(fp4x2_to_h2<0>(D) * sp);
+        Bw[3][p] = h2_bits(fp4x2_to_h2<1>(D) * sp);
+        Bw[5][p] = h2_bits(fp4x2_to_h2<2>(D) * sp);
+        Bw[7][p] = h2_bits(fp4x2_to_h2<3>(D) * sp);
+      }
+      half8 B[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) B[t] = __builtin_bit_cast(half8, u32x4{Bw[t][0], Bw[t][1], Bw[t][2], Bw[t][3]});
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        const half8 av = *reinterpret_cast<const half8*>(&sm.p[(16 * ht + n16) * kPStride + key0]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) O[ht][t] = mfma(av, B[t], O[ht][t]);
+      }
+    }
+
+    // rotate the prefetch registers
+    if (st + 1 < nsteps) {
+      cur = nxt;
+      vcur[0] = vnext[0];
+      vcur[1] = vnext[1];
+    }
+  }
+
+  // ---- epilogue
+  if (w == 0 && q4 == 0) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      sm.lfin[16 * ht + n16] = lrun[ht];
+      sm.mfin[16 * ht + n16] = mrun[ht];
+    }
+  }
+  __syncthreads();
+  const int64_t rowh = (int64_t)r * a.Hq + h0;
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * ht + 4 * q4 + i;
+      const int ch = 128 * w + 8 * n16;
+      const float L = sm.lfin[h];
+      if (a.splits == 1) {
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = O[ht][t][i] * inv;
+        if (a.out_dtype == CSA2_F32) {
+          float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch);
+          o[0] = make_float4(v[0], v[1], v[2], v[3]);
+          o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          uint32_t pk[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+            lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+            hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+            pk[k] = lo | (hi << 16);
+          }
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + ch) =
+              make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+      } else {
+        float4* o = reinterpret_cast<float4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch);
+        o[0] = make_float4(O[ht][0][i], O[ht][1][i], O[ht][2][i], O[ht][3][i]);
+        o[1] = make_float4(O[ht][4][i], O[ht][5][i], O[ht][6][i], O[ht][7][i]);
+      }
+    }
+  }
+  if (w == 0 && q4 == 0) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      if (a.splits == 1) {
+        if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mrun[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
+      } else {
+        a.ws_m[(rowh + h) * a.splits + split] = mrun[ht];
+        a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+      }
+    }
+  }
+}
+
+// one (row, head) per workgroup of 128 threads, 4 channels per thread;
+// splits merged in fixed order
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_m,
+                                                      const float* __restrict__ ws_l, int splits, void* out,
+                                                      int out_dtype, float* lse) {
+  const int64_t rh = blockIdx.x;
+  const float* m = ws_m + rh * splits;
+  const float* l = ws_l + rh * splits;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, m[s]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float wgt = __builtin_amdgcn_exp2f(m[s] - M);
+      L += wgt * l[s];
+      const float4 v = reinterpret_cast<const float4*>(ws_o + (rh * splits + s) * kDim)[threadIdx.x];
+      acc.x += wgt * v.x;
+      acc.y += wgt * v.y;
+      acc.z += wgt * v.z;
+      acc.w += wgt * v.w;
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  if (out_dtype == CSA2_F32) {
+    reinterpret_cast<float4*>(static_cast<float*>(out) + rh * kDim)[threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint32_t pk[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+      lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+      hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+      pk[k] = lo | (hi << 16);
+    }
+    reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + rh * kDim)[threadIdx.x] = make_uint2(pk[0], pk[1]);
+  }
+  if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+struct Plan {
+  int nht, head_groups, splits, keys_per_split;
+  bool splitq;
+};
+
+Plan plan(int R, int Hq, int q_dtype, int top_k) {
+  Plan p{};
+  p.splitq = q_dtype == CSA2_F32;
+  const int max_splits = (int)std::max<int64_t>(1, ceil_div(top_k, kStep));
+  const int cand[4] = {4, 3, 2, 1};
+  p.nht = 1;
+  for (int c : cand) {
+    if (p.splitq && c > 2) continue;
+    if ((Hq / 16) % c) continue;
+    p.nht = c;
+    const int64_t wgs = (int64_t)R * (Hq / (16 * c)) * max_splits;
+    if (wgs >= 256) break;
+  }
+  p.head_groups = Hq / (16 * p.nht);
+  const int64_t base = (int64_t)R * p.head_groups;
+  int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(256, base)));
+  p.keys_per_split = (int)round_up(ceil_div(top_k, splits), kStep);
+  p.splits = (int)ceil_div(top_k, p.keys_per_split);
+  return p;
+}
+
+template <int NHT, bool SPLITQ, int QDT>
+hipError_t go(const Plan& p, int R, const AttnArgs& a, hipStream_t s) {
+  auto kern = k_sparse_attn<NHT, SPLITQ, QDT>;
+  const size_t lds = sizeof(Smem<NHT, SPLITQ>);
+  static bool configured = false;
+  if (!configured) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    configured = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(p.splits, R, p.head_groups), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k) {
+  const Plan p = plan(R, Hq, q_dtype, top_k);
+  if (p.splits <= 1) return 0;
+  const size_t n = (size_t)R * Hq * p.splits;
+  return ((n * kDim * 4 + 255) & ~size_t(255)) + 2 * ((n * 4 + 255) & ~size_t(255));
+}
+
+hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
+                              const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
+                              float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  const Plan p = plan(R, Hq, q_dtype, top_k);
+  AttnArgs a{};
+  a.q = q;
+  a.Hq = Hq;
+  a.codes = codes;
+  a.scales = scales;
+  a.row_start = row_start;
+  a.idx = idx;
+  a.top_k = top_k;
+  a.row_visible = row_visible;
+  a.c2 = softmax_scale * kLog2e;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.lse = lse;
+  a.splits = p.splits;
+  a.keys_per_split = p.keys_per_split;
+  if (p.splits > 1) {
+    const size_t n = (size_t)R * Hq * p.splits;
+    char* b = static_cast<char*>(ws);
+    a.ws_o = reinterpret_cast<float*>(b);
+    b += (n * kDim * 4 + 255) & ~size_t(255);
+    a.ws_m = reinterpret_cast<float*>(b);
+    b += (n * 4 + 255) & ~size_t(255);
+    a.ws_l = reinterpret_cast<float*>(b);
+  }
+  auto& ev = profile_events(CSA2_KERNEL_ATTN);
+  if (ev.start) hipEventRecord(ev.start, s);
+  hipError_t e;
+  if (q_dtype == CSA2_BF16) {
+    switch (p.nht) {
+      case 4: e = go<4, false, CSA2_BF16>(p, R, a, s); break;
+      case 3: e = go<3, false, CSA2_BF16>(p, R, a, s); break;
+      case 2: e = go<2, false, CSA2_BF16>(p, R, a, s); break;
+      default: e = go<1, false, CSA2_BF16>(p, R, a, s); break;
+    }
+  } else {
+    switch (p.nht) {
+      case 2: e = go<2, true, CSA2_F32>(p, R, a, s); break;
+      default: e = go<1, true, CSA2_F32>(p, R, a, s); break;
+    }
+  }
+  if (ev.stop) hipEventRecord(ev.stop, s);
+  if (e != hipSuccess) return e;
+  if (p.splits > 1) {
+    auto& ec = profile_events(CSA2_KERNEL_ATTN_COMBINE);
+    if (ec.start) hipEventRecord(ec.start, s);
+    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((int64_t)R * Hq)), dim3(128), 0, s, a.ws_o, a.ws_m, a.ws_l,
+                       p.splits, out, out_dtype, lse);
+    if (ec.stop) hipEventRecord(ec.stop, s);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace csa2

@@ -1,0 +1,112 @@
+// k_quant.hip -- quantize-on-write of 512-channel KV latents to FP4.
+//
+// Cache format of "FP4 cache entries, and why they're safe" (course brief
+// "DeepSeek-V4.1-Flash"): E2M1 elements, one E4M3 scale per 16 channels, no
+// second-level global scale, 256 + 32 = 288 bytes per entry.  Scale choice
+// and rounding are the plainest reading of that section: s = E4M3(amax/6)
+// round-to-nearest-even (6 = largest E2M1 value), elements E2M1(x/s)
+// round-to-nearest-even.
+//
+// Layout: 32 lanes per token, lane g owns group g (16 channels = 64 B of
+// fp32 input or 32 B of bf16), so a wave covers two tokens with fully
+// coalesced loads; each lane writes 8 code bytes and 1 scale byte.
+// HBM-bound: 2 KiB (fp32) or 1 KiB (bf16) read + 288 B written per token.
+#include "csa2_common.h"
+
+namespace csa2 {
+namespace {
+
+// nearest E4M3 (E4M3FN) code of v >= 0, ties to even, saturating at 448
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  if (!(v > 0.0f)) return 0u;
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9 (scaling by 512 is exact)
+    return (uint32_t)__float2int_rn(v * 512.0f);
+  }
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t e = (u >> 23) - 120u;  // rebias 127 -> 7
+  const uint32_t man = u & 0x7FFFFFu;
+  const uint32_t keep = man >> 20, rest = man & 0xFFFFFu;
+  uint32_t code = (e << 3) | keep;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) code += 1u;  // carries into the exponent
+  return code;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// nearest E2M1 code, ties to even code, |q| > 6 -> 6, sign kept.
+// Thresholds: midpoints .25 .75 1.25 1.75 2.5 3.5 5; at a midpoint the even
+// code wins, hence '>' above an even neighbour and '>=' below one.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  const float a = fabsf(q);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant_fp4(const void* __restrict__ x, int64_t n, int64_t stride,
+                                                   const int64_t* __restrict__ dst_rows, uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales, int64_t cap) {
+  const int64_t tok = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int g = threadIdx.x & 31;
+  if (tok >= n) return;
+  const int64_t dst = dst_rows ? dst_rows[tok] : tok;
+  if (dst < 0 || dst >= cap) return;
+  float v[16];
+  if (DT == CSA2_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + tok * stride + g * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 t = p[i];
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + tok * stride + g * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 t = p[i];
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+        v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sb = e4m3_code(__fdiv_rn(amax, 6.0f));
+  const float s = e4m3_value(sb);
+  uint32_t lo = 0, hi = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo |= e2m1_code(__fdiv_rn(v[i], s)) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi |= e2m1_code(__fdiv_rn(v[8 + i], s)) << (4 * i);
+  }
+  *reinterpret_cast<uint2*>(codes + dst * kCodeBytes + g * 8) = make_uint2(lo, hi);
+  scales[dst * kGroups + g] = (uint8_t)sb;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
+                           uint8_t* codes, uint8_t* scales, int64_t cap, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(n, 8)), block(256);
+  auto& ev = profile_events(CSA2_KERNEL_QUANT);
+  if (ev.start) hipEventRecord(ev.start, s);
+  if (x_dtype == CSA2_F32)
+    hipLaunchKernelGGL(k_quant_fp4<CSA2_F32>, grid, block, 0, s, x, n, stride, dst_rows, codes, scales, cap);
+  else
+    hipLaunchKernelGGL(k_quant_fp4<CSA2_BF16>, grid, block, 0, s, x, n, stride, dst_rows, codes, scales, cap);
+  if (ev.stop) hipEventRecord(ev.stop, s);
+  return hipGetLastError();
+}
+
+}  // namespace csa2
