@@ -1,0 +1,342 @@
+"""CSA2 decode benchmark on one MI355X.
+
+Default workload: the six-layer chain at 128K context, batch 16 (Full with
+an 8,192-entry candidate pool, two Reindex layers, three Reuse layers), one
+decode step per timed step: the first Full layer quantizes each sequence's
+newest token into the FP4 cache, every selecting layer runs the indexer and
+exact top-K, every layer runs sparse attention with its own query.  Inputs
+are seeded synthetic data (gen/) resident in HBM before timing starts.
+
+Prints one JSON line: tokens/s over the timed steps, the roofline of the
+dominant kernel (HIP events on the launch stream via the library's
+measurement hook), and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload c3|c2|c5] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import gen  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "CSA2 decode tokens/s + achieved HBM GB/s (FP4 KV) at 128K ctx, 1 GPU"
+KV_ROW_BYTES = 288
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ setup
+
+def build_cache(w, lens, device, chunk=65536):
+    """Quantize every sequence's KV into one packed FP4 cache on the GPU."""
+    import torch
+
+    from sparse_attention_fp4_e4m3_amd import Cache, csa2
+
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    rows = int(lens.sum())
+    codes = torch.empty(rows, 256, dtype=torch.uint8, device=device)
+    scales = torch.empty(rows, 32, dtype=torch.uint8, device=device)
+    kdt = torch.bfloat16 if w.idx_dtype == "bf16" else torch.float32
+    idx_k = torch.empty(rows, 64, dtype=kdt, device=device)
+    for b in range(len(lens)):
+        for t0 in range(0, int(lens[b]), chunk):
+            t1 = min(int(lens[b]), t0 + chunk)
+            x = torch.from_numpy(gen.kv_rows(w, b, t0, t1)).to(device)
+            r0 = int(starts[b]) + t0
+            csa2.quantize_kv_fp4(x, codes[r0:r0 + (t1 - t0)], scales[r0:r0 + (t1 - t0)])
+            ik = gen.idx_k_rows(w, b, t0, t1)
+            if kdt == torch.bfloat16:
+                ik = torch.from_numpy(gen.bf16_bits(ik).view(np.int16)).view(torch.bfloat16)
+            else:
+                ik = torch.from_numpy(ik)
+            idx_k[r0:r0 + (t1 - t0)] = ik.to(device)
+        torch.cuda.synchronize()
+    return Cache(codes, scales, idx_k, torch.from_numpy(starts).to(device),
+                 torch.from_numpy(lens.astype(np.int32)).to(device), int(lens.max())), starts
+
+
+def to_dev(a, kind, device):
+    import torch
+
+    if kind == "bf16":
+        return torch.from_numpy(gen.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def layer_inputs(w, device):
+    qs, iqs = [], []
+    for li, L in enumerate(w.layers):
+        qs.append(to_dev(gen.attn_q(w, li), w.q_dtype, device))
+        iqs.append(to_dev(gen.index_q(w, li), w.idx_dtype, device) if L.mode != "reuse" else None)
+    return qs, iqs
+
+
+# ------------------------------------------------------------------ accounting
+
+def algorithmic_bytes(w, lens):
+    """Bytes the method must move per decode step, by kernel family."""
+    R, K = w.B, w.K
+    qb = 2 if w.q_dtype == "bf16" else 4
+    kb = 2 if w.idx_dtype == "bf16" else 4
+    out = {"quantize": R * (512 * 4 + KV_ROW_BYTES)}
+    out["index_scan"] = int(lens.sum()) * 64 * kb
+    pool = 0
+    reindex = 0
+    for L in w.layers:
+        if L.mode == "full":
+            pool = L.pool_size
+        elif L.mode == "reindex":
+            reindex += R * pool * 64 * kb
+    out["reindex_score"] = reindex
+    per_attn = R * (K * KV_ROW_BYTES + K * 4 + w.Hq * 512 * qb + w.Hq * 512 * 4)
+    out["attention_per_layer"] = per_attn
+    out["attention"] = per_attn * len(w.layers)
+    out["total"] = out["quantize"] + out["index_scan"] + out["reindex_score"] + out["attention"]
+    return out
+
+
+def attention_flops(w):
+    return 4.0 * w.B * w.Hq * w.K * 512
+
+
+def traffic_from_profiles(kernel_file):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = os.path.join(ROOT, "sparse_attention_fp4_e4m3_amd", "csrc", kernel_file)
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        ent = rec.get(kernel_file)
+        if ent and ent.get("source_sha256_16") == h:
+            return ent.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(w, lens, sample_rows):
+    """One decode step of the same chain for `sample_rows` sequences, run by the CPU oracle."""
+    import oracle
+
+    rows = list(range(min(sample_rows, w.B)))
+    log("cpu baseline: preparing oracle cache for %d sequences" % len(rows))
+    caches = {}
+    for b in rows:
+        x = gen.kv_rows(w, b, 0, int(lens[b]))
+        caches[b] = (oracle.quantize(x), gen.idx_k_rows(w, b, 0, int(lens[b])))
+        del x
+    qs = [gen.attn_q(w, li, 0, len(rows)) for li in range(len(w.layers))]
+    iqs = [gen.index_q(w, li, 0, len(rows)) if L.mode != "reuse" else None for li, L in enumerate(w.layers)]
+    new_kv = [gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b])) for b in rows]
+    t0 = time.perf_counter()
+    for b in rows:
+        (codes, scales), ik = caches[b]
+        n = int(lens[b])
+        c1, s1 = oracle.quantize(new_kv[b])  # the newest token, written by the first Full layer
+        codes[n - 1], scales[n - 1] = c1[0], s1[0]
+        pool = None
+        sel = None
+        for li, L in enumerate(w.layers):
+            if L.mode == "full":
+                sel, pool, _ = oracle.full_select(iqs[li][b], ik, n, w.K, L.pool_size)
+            elif L.mode == "reindex":
+                sel = oracle.reindex_select(iqs[li][b], ik, pool, n, w.K)
+            oracle.attention(qs[li][b], codes, scales, sel, n, w.softmax_scale)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d sequences, one full decode step of the %d-layer chain (quantize newest token, "
+                      "indexer scan over %d tokens, top-K, pool, Reindex, attention per layer); %.1f s wall"
+                      % (len(rows), w.B, len(w.layers), int(lens[0]), dt)}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5"])
+    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU per process and box; --gpus %d is not supported "
+              "(multi-GPU sharding is a design note only)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_fp4_e4m3_amd import LayerChain, LayerSpec, csa2
+
+    device = torch.device("cuda:0")
+    w = gen.get(args.workload)
+    lens = gen.seq_lens(w)
+    log("workload %s: %s" % (w.name, w.description))
+    t = time.time()
+    cache, _ = build_cache(w, lens, device)
+    log("cache built in %.1f s (%d rows)" % (time.time() - t, int(lens.sum())))
+    qs, iqs = layer_inputs(w, device)
+    new_rows = np.concatenate([[0], np.cumsum(lens)[:-1]]) + lens - 1
+    new_kv = torch.from_numpy(np.concatenate([gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b]))
+                                              for b in range(w.B)])).to(device)
+    new_rows_t = torch.from_numpy(new_rows.astype(np.int64)).to(device)
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, cache.max_visible,
+                       qs[0].dtype, device)
+
+    def step():
+        chain.step(cache, qs, iqs, w.softmax_scale, new_kv=new_kv, new_kv_rows=new_rows_t)
+
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=device)
+        b_ = torch.empty_like(a)
+        b_.copy_(a)
+        torch.cuda.synchronize()
+
+    # eager warm-up (also configures the kernels), then capture one decode step as a HIP graph
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            step()
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    run = graph.replay if graph is not None else step
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+
+    # per-kernel durations: HIP events recorded by the library on the launch stream around
+    # each kernel, over an eager pass of the same number of steps (a kernel launched several
+    # times per step is timed on its last launch of the step)
+    kernels = {"index_scan": csa2.KERNEL_INDEX_SCAN, "reindex_score": csa2.KERNEL_REINDEX_SCORE,
+               "attention": csa2.KERNEL_ATTN, "attention_combine": csa2.KERNEL_ATTN_COMBINE,
+               "quantize": csa2.KERNEL_QUANT}
+    n_launch = {"index_scan": 1, "quantize": 1,
+                "reindex_score": sum(L.mode == "reindex" for L in w.layers),
+                "attention": len(w.layers), "attention_combine": len(w.layers)}
+
+    def arm(kid):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        e.record()  # materialize the handles
+        csa2.profile_kernel_events(kid, s, e)
+        return s, e
+
+    pairs = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        armed = {k: arm(kid) for k, kid in kernels.items()}
+        step()
+        pairs.append(armed)
+    torch.cuda.synchronize()
+    for kid in kernels.values():
+        csa2.profile_kernel_events(kid, None, None)
+    per_kernel_us = {}
+    for k in kernels:
+        vals = [p[k][0].elapsed_time(p[k][1]) * 1e3 for p in pairs]
+        per_kernel_us[k] = float(np.mean(vals))
+
+    byt = algorithmic_bytes(w, lens)
+    attn_flops = attention_flops(w)
+    kern = {
+        "index_scan": {"avg_us": per_kernel_us["index_scan"], "bytes": byt["index_scan"]},
+        "reindex_score": {"avg_us": per_kernel_us["reindex_score"], "bytes": byt["reindex_score"] //
+                          max(1, n_launch["reindex_score"])},
+        "attention": {"avg_us": per_kernel_us["attention"], "bytes": byt["attention_per_layer"],
+                      "flops": attn_flops},
+        "attention_combine": {"avg_us": per_kernel_us["attention_combine"]},
+        "quantize": {"avg_us": per_kernel_us["quantize"], "bytes": byt["quantize"]},
+    }
+    for k, v in kern.items():
+        if "bytes" in v and v["avg_us"] > 0:
+            v["GBps"] = v["bytes"] / (v["avg_us"] * 1e3)
+            v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
+        if "flops" in v and v["avg_us"] > 0:
+            v["TFLOPs"] = v["flops"] / (v["avg_us"] * 1e6)
+            v["mfma_frac"] = v["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+        v["per_step_us"] = v["avg_us"] * n_launch.get(k, 1)
+    dominant = max(["index_scan", "attention", "reindex_score"], key=lambda k: kern[k]["per_step_us"])
+    dk = kern[dominant]
+    if dominant == "attention":
+        roof = {"kernel": "k_sparse_attn", "bound": "mfma", "achieved": dk["TFLOPs"],
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": dk["mfma_frac"],
+                "traffic": traffic_from_profiles("k_attn.hip")}
+    else:
+        roof = {"kernel": "k_scan_full" if dominant == "index_scan" else "k_score_pool", "bound": "hbm",
+                "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["hbm_frac"],
+                "traffic": traffic_from_profiles("k_index.hip")}
+
+    tokens_s = w.B / (ms_step * 1e-3)
+    res = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s: %s" % (w.name, w.description), "batch": w.B, "ctx": int(lens.max()),
+                   "layers": [L.mode for L in w.layers], "top_k": w.K, "q_heads": w.Hq, "indexer_heads": w.H,
+                   "kv": "fp4 e2m1 + e4m3 scale per 16 ch (288 B/entry)",
+                   "compute": "indexer fp32 fmaf; attention f16 MFMA, f32 accumulate", "parallelism": "single GPU",
+                   "launch": "eager" if graph is None else "hip graph replay of one decode step"},
+        "roofline": roof,
+        "kernels": kern,
+    }
+    res["chain_hbm_GBps"] = byt["total"] / (ms_step * 1e-3) / 1e9
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -93,6 +93,10 @@ int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t
   if (top_k < 1 || top_k > CSA2_MAX_TOP_K) return fail(CSA2_E_INVALID, "%s: top_k %d outside 1..%d", fn, top_k,
                                                        CSA2_MAX_TOP_K);
   if (max_visible < 0) return fail(CSA2_E_INVALID, "%s: max_visible < 0", fn);
+  if (max_visible > topk_max_visible())
+    return fail(CSA2_E_UNSUPPORTED, "%s: max_visible %d above the built limit %d", fn, max_visible, topk_max_visible());
+  if (mode == CSA2_REINDEX && pool_stride > 65536)
+    return fail(CSA2_E_UNSUPPORTED, "%s: pool_stride %d above 65536", fn, pool_stride);
   if (n_rows == 0) return CSA2_OK;
   if (!idx_q || !idx_k || !row_kv_start || !row_visible || !out_idx)
     return fail(CSA2_E_INVALID, "%s: null buffer", fn);

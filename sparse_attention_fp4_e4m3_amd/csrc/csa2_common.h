@@ -16,10 +16,6 @@ constexpr int kCodeBytes = 256; // E2M1 bytes per entry
 constexpr int kIdxDim = 64;     // indexer head dim
 constexpr int kBlock = 8;       // hierarchical pool block
 
-// radix digits over the 31 value bits of a non-negative fp32 score
-constexpr int kBins1 = 2048, kBins2 = 2048, kBins3 = 512;
-constexpr int kShift1 = 20, kShift2 = 9;
-
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -38,18 +34,8 @@ ProfileEvents& profile_events(int kernel_id);
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
                            uint8_t* codes, uint8_t* scales, int64_t cap, hipStream_t s);
 
-struct TopkWorkspace {
-  // carved from the caller's workspace
-  float* qf;             // [R, H, 64] fp32 copy of the indexer queries
-  float* scores;         // [R, n_pad] fp32 (Full: positions; Reindex: pool slots)
-  float* bmax;           // [R, nb_pad] fp32 block maxima (Full with pool)
-  uint32_t* hist;        // [2 series][R][kBins1 + kBins2 + kBins3]
-  uint32_t* counts;      // [2 series][R][chunks][2]
-  int64_t n_pad, nb_pad;
-  int chunks, bchunks;
-};
-
 size_t topk_workspace_bytes(int mode, int R, int H, int max_visible, int pool_stride, int pool_size);
+int topk_max_visible();
 
 hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k, int k_dtype,
                              const int64_t* row_start, const int32_t* row_visible, int max_visible,
@@ -64,11 +50,16 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
 
 // ------------------------------------------------------------ device helpers
-#if defined(__HIP_DEVICE_COMPILE__)
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-#endif
+// Workgroup barrier for LDS traffic only.  HIP's __syncthreads() also waits
+// for every outstanding global load (s_waitcnt vmcnt(0)), which would drain
+// register prefetches issued ahead of the barrier; this one waits for this
+// wave's LDS operations only, so global loads stay in flight across it.
+// Use it only where the data exchanged through the barrier lives in LDS.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 }  // namespace csa2

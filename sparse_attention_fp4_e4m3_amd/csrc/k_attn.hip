@@ -136,7 +136,10 @@ struct Raw {
   u32x2 s[2];     // scale bytes [8*q4, 8*q4+8)
 };
 
-__device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int r, int64_t rs, int vis, int kpos0, int kend,
+// Branch-free gather: an invalid key loads row 0 of the cache (always
+// present) and is zeroed afterwards, so every load is issued unconditionally
+// and the compiler can keep them all in flight.
+__device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int64_t rs, int vis, int kpos0, int kend,
                                          const int32_t (&j)[2], uint32_t (&valid)[2], int lane) {
   const int m = lane & 15, q4 = lane >> 4;
 #pragma unroll
@@ -144,17 +147,23 @@ __device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int r, int64
     const int i = kpos0 + 16 * kt + m;
     const bool ok = i < kend && j[kt] >= 0 && j[kt] < vis;
     valid[kt] = ok;
-    if (ok) {
-      const int64_t row = rs + j[kt];
-      const u32x4* pc = reinterpret_cast<const u32x4*>(a.codes + row * kCodeBytes + 64 * q4);
+    const int64_t row = ok ? rs + j[kt] : 0;
+    const u32x4* pc = reinterpret_cast<const u32x4*>(a.codes + row * kCodeBytes + 64 * q4);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) R.c[kt][c] = __builtin_nontemporal_load(pc + c);
-      R.s[kt] = *reinterpret_cast<const u32x2*>(a.scales + row * kGroups + 8 * q4);
-    } else {
+    for (int c = 0; c < 4; ++c) R.c[kt][c] = __builtin_nontemporal_load(pc + c);
+    R.s[kt] = *reinterpret_cast<const u32x2*>(a.scales + row * kGroups + 8 * q4);
+  }
+}
+
+__device__ __forceinline__ void mask_raw(Raw& R, const uint32_t (&valid)[2]) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) R.c[kt][c] = u32x4{0u, 0u, 0u, 0u};
-      R.s[kt] = u32x2{0u, 0u};
-    }
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) R.c[kt][c][e] = valid[kt] ? R.c[kt][c][e] : 0u;
+    R.s[kt][0] = valid[kt] ? R.s[kt][0] : 0u;
+    R.s[kt][1] = valid[kt] ? R.s[kt][1] : 0u;
   }
 }
 
@@ -163,7 +172,9 @@ __device__ __forceinline__ void load_idx(int32_t (&j)[2], const AttnArgs& a, int
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int i = kpos0 + 16 * kt + m;
-    j[kt] = (i < kend) ? a.idx[(int64_t)r * a.top_k + i] : -1;
+    const int ic = i < kend ? i : kend - 1;  // kend > kpos0 >= 0 whenever this is called
+    const int32_t v = a.idx[(int64_t)r * a.top_k + ic];
+    j[kt] = (i < kend) ? v : -1;
   }
 }
 
@@ -187,36 +198,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   uint32_t vcur[2], vnext[2];
   Raw cur, nxt;
   if (nsteps > 0) {
-    load_idx(jcur, a, r, kbeg + 32 * w, kend, lane);
-    load_raw(cur, a, r, rs, vis, kbeg + 32 * w, kend, jcur, vcur, lane);
+    load_idx(jcur, a, r, min(kbeg + 32 * w, kend - 1), kend, lane);
+    if (kbeg + 32 * w >= kend) jcur[0] = jcur[1] = -1;
+    load_raw(cur, a, rs, vis, kbeg + 32 * w, kend, jcur, vcur, lane);
   }
-  if (nsteps > 1) load_idx(jnext, a, r, kbeg + kStep + 32 * w, kend, lane);
+  if (nsteps > 1) {
+    load_idx(jnext, a, r, min(kbeg + kStep + 32 * w, kend - 1), kend, lane);
+    if (kbeg + kStep + 32 * w >= kend) jnext[0] = jnext[1] = -1;
+  }
   {
-    // HG heads x 512 channels; 16-byte pieces
+    // HG heads x 512 channels in 16-byte pieces; all loads issued before any conversion
     if (QDT == CSA2_BF16) {
+      constexpr int NP = HG * kDim / 8 / kThreads;  // pieces per thread
       const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
-      for (int p = tid; p < HG * kDim / 8; p += kThreads) {
-        const int h = p / (kDim / 8), c8 = (p % (kDim / 8)) * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qb + (int64_t)h * kDim + c8);
+      u32x4 v[NP];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int p = tid + kThreads * i;
+        v[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)(p / (kDim / 8)) * kDim + (p % (kDim / 8)) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int p = tid + kThreads * i;
         half8 hv;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          hv[2 * k] = (_Float16)__uint_as_float(v[k] << 16);
-          hv[2 * k + 1] = (_Float16)__uint_as_float(v[k] & 0xFFFF0000u);
+          hv[2 * k] = (_Float16)__uint_as_float(v[i][k] << 16);
+          hv[2 * k + 1] = (_Float16)__uint_as_float(v[i][k] & 0xFFFF0000u);
         }
-        *reinterpret_cast<half8*>(&sm.q[h * kQStride + c8]) = hv;
+        *reinterpret_cast<half8*>(&sm.q[(p / (kDim / 8)) * kQStride + (p % (kDim / 8)) * 8]) = hv;
       }
     } else {
+      constexpr int NP = HG * kDim / 4 / kThreads;
       const float* qf = static_cast<const float*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
-      for (int p = tid; p < HG * kDim / 4; p += kThreads) {
+      floatx4 v[NP];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int p = tid + kThreads * i;
+        v[i] = *reinterpret_cast<const floatx4*>(qf + (int64_t)(p / (kDim / 4)) * kDim + (p % (kDim / 4)) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int p = tid + kThreads * i;
         const int h = p / (kDim / 4), c4 = (p % (kDim / 4)) * 4;
-        const float4 v = *reinterpret_cast<const float4*>(qf + (int64_t)h * kDim + c4);
-        const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const _Float16 hi = (_Float16)f[k];
+          const _Float16 hi = (_Float16)v[i][k];
           sm.q[h * kQStride + c4 + k] = hi;
-          if (SPLITQ) sm.q[(HG + h) * kQStride + c4 + k] = (_Float16)(f[k] - (float)hi);
+          if (SPLITQ) sm.q[(HG + h) * kQStride + c4 + k] = (_Float16)(v[i][k] - (float)hi);
         }
       }
     }
@@ -237,6 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 
   for (int st = 0; st < nsteps; ++st) {
     const int kstep0 = kbeg + st * kStep;
+    mask_raw(cur, vcur);
     // scale bytes of this lane's two keys -> fp16 (groups 8*q4 .. 8*q4+7)
     half2v sc[2][4];
 #pragma unroll
@@ -273,12 +303,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
           if (SPLITQ) S[kt][ht] = mfma(av, bq[NHT + ht], S[kt][ht]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep dequant of later K-steps from piling up registers
     }
 
     // ---- prefetch the next step (registers), its indices one step further
     if (st + 1 < nsteps) {
-      load_raw(nxt, a, r, rs, vis, kstep0 + kStep + 32 * w, kend, jnext, vnext, lane);
-      if (st + 2 < nsteps) load_idx(jnext, a, r, kstep0 + 2 * kStep + 32 * w, kend, lane);
+      load_raw(nxt, a, rs, vis, kstep0 + kStep + 32 * w, kend, jnext, vnext, lane);
+      if (st + 2 < nsteps) {
+        load_idx(jnext, a, r, min(kstep0 + 2 * kStep + 32 * w, kend - 1), kend, lane);
+        if (kstep0 + 2 * kStep + 32 * w >= kend) jnext[0] = jnext[1] = -1;
+      }
     }
 
     // ---- softmax, part 1: scaled logits, masked, per-wave max per head
@@ -301,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       if (q4 == 0) sm.red_max[w][16 * ht + n16] = mx;
     }
-    __syncthreads();  // B1: maxima visible; every wave is past the previous PV
+    lds_barrier();  // B1: maxima visible; every wave is past the previous PV
 
     // ---- stage this step's raw codes and fp16 scales for PV
 #pragma unroll
@@ -345,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
         if (w == 0) sm.alpha[h] = alpha[ht];
       }
     }
-    __syncthreads();  // B2: probabilities, sums, alpha and staged codes visible
+    lds_barrier();  // B2: probabilities, sums, alpha and staged codes visible
 
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -353,14 +387,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       lrun[ht] = lrun[ht] * alpha[ht] + (((sm.red_sum[0][h] + sm.red_sum[1][h]) + sm.red_sum[2][h]) + sm.red_sum[3][h]);
     }
 
-    // ---- PV: channels [128w, 128w+128) of every head
+    // ---- PV: channels [128w, 128w+128) of every head.  Rescale the running
+    // output only when some head's maximum moved (O is still zero on step 0).
+    if (st > 0) {
+      float al[NHT][4];
+      bool moved = false;
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
+      for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float al = sm.alpha[16 * ht + 4 * q4 + i];
+        for (int i = 0; i < 4; ++i) {
+          al[ht][i] = sm.alpha[16 * ht + 4 * q4 + i];
+          moved |= al[ht][i] != 1.0f;
+        }
+      if (__ballot(moved)) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) O[ht][t][i] *= al;
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) O[ht][t][i] *= al[ht][i];
       }
     }
 #pragma unroll
@@ -396,6 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) O[ht][t] = mfma(av, B[t], O[ht][t]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // rotate the prefetch registers
@@ -478,14 +524,26 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float wgt = __builtin_amdgcn_exp2f(m[s] - M);
-      L += wgt * l[s];
-      const float4 v = reinterpret_cast<const float4*>(ws_o + (rh * splits + s) * kDim)[threadIdx.x];
-      acc.x += wgt * v.x;
-      acc.y += wgt * v.y;
-      acc.z += wgt * v.z;
-      acc.w += wgt * v.w;
+    // fixed split order; loads batched 8 at a time
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      float4 v[8];
+      float wgt[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int s = s0 + k < splits ? s0 + k : splits - 1;
+        v[k] = reinterpret_cast<const float4*>(ws_o + (rh * splits + s) * kDim)[threadIdx.x];
+        wgt[k] = __builtin_amdgcn_exp2f(m[s] - M);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (s0 + k < splits) {
+          L += wgt[k] * l[s0 + k];
+          acc.x += wgt[k] * v[k].x;
+          acc.y += wgt[k] * v[k].y;
+          acc.z += wgt[k] * v[k].z;
+          acc.w += wgt[k] * v[k].w;
+        }
+      }
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -538,7 +596,8 @@ hipError_t go(const Plan& p, int R, const AttnArgs& a, hipStream_t s) {
   const size_t lds = sizeof(Smem<NHT, SPLITQ>);
   static bool configured = false;
   if (!configured) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
     configured = true;
   }
   hipLaunchKernelGGL(kern, dim3(p.splits, R, p.head_groups), dim3(kThreads), lds, s, a);
@@ -584,7 +643,7 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
     a.ws_l = reinterpret_cast<float*>(b);
   }
   auto& ev = profile_events(CSA2_KERNEL_ATTN);
-  if (ev.start) hipEventRecord(ev.start, s);
+  if (ev.start) (void)hipEventRecord(ev.start, s);
   hipError_t e;
   if (q_dtype == CSA2_BF16) {
     switch (p.nht) {
@@ -599,14 +658,14 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
       default: e = go<1, true, CSA2_F32>(p, R, a, s); break;
     }
   }
-  if (ev.stop) hipEventRecord(ev.stop, s);
+  if (ev.stop) (void)hipEventRecord(ev.stop, s);
   if (e != hipSuccess) return e;
   if (p.splits > 1) {
     auto& ec = profile_events(CSA2_KERNEL_ATTN_COMBINE);
-    if (ec.start) hipEventRecord(ec.start, s);
+    if (ec.start) (void)hipEventRecord(ec.start, s);
     hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((int64_t)R * Hq)), dim3(128), 0, s, a.ws_o, a.ws_m, a.ws_l,
                        p.splits, out, out_dtype, lse);
-    if (ec.stop) hipEventRecord(ec.stop, s);
+    if (ec.stop) (void)hipEventRecord(ec.stop, s);
     e = hipGetLastError();
   }
   return e;

@@ -10,17 +10,22 @@
 // head sum) so that selection is reproducible bit for bit.
 //
 // Pipeline of one csa2_index_topk call (one stream, no host sync):
-//   k_prep           indexer queries -> fp32, zero the radix histograms
-//   k_scan_full      (Full)    every visible entry: score, block max, and the
-//                              first radix histogram, fused; HBM-bound on the
-//                              128 B (bf16) key rows
-//   k_score_pool     (Reindex) pool entries only, same score
-//   k_radix_pass<2>  second 11-bit digit histogram inside the threshold bin
-//   k_radix_pass<3>  last 9-bit digit histogram
-//   k_select_count   exact threshold T; per-chunk counts of > T and == T
-//   k_select_write   ordered compaction: positions ascending, ties to the
-//                    lower position, -1 padding; expands selected blocks
-//                    into the pool
+//   k_prep      indexer queries -> fp32 ([channel quad][head][4] order);
+//               zero the first-digit histograms
+//   k_score     Full: every visible entry; Reindex: the pool entries.  Key
+//               rows are staged through LDS with fully coalesced 16-byte
+//               loads (the next tile prefetched into registers), queries
+//               are broadcast from LDS, each thread runs the H fmaf chains of
+//               one key.  Full also writes the 8-entry block maxima and
+//               builds the first radix histogram (12 bits) of scores and
+//               block maxima in the same pass.  HBM-bound on the key rows.
+//   k_collect   (Full) every wave compacts, in position order, the entries
+//               whose first digit reaches the threshold bin into its own
+//               slice of a candidate list (no block-wide syncs)
+//   k_finalize  one workgroup per row and series: exact threshold with two
+//               more radix digits over the candidates, then an ordered
+//               compaction: positions ascending, ties to the lower position,
+//               -1 padding; selected blocks expand into the pool
 // Scores are non-negative fp32, so their bit patterns order like uint32;
 // invalid slots carry -1.0 (sign bit set) and are never counted.
 #include <algorithm>
@@ -31,52 +36,31 @@
 namespace csa2 {
 namespace {
 
-constexpr int kScanThreads = 256;
-constexpr int kScanKeysPerThread = 2;
-constexpr int kScanIters = 4;
-constexpr int kScanChunk = kScanThreads * kScanKeysPerThread * kScanIters;  // 2048 positions
-constexpr int kSelChunk = 8192;                                            // radix pass chunk
-constexpr int kHistWords = kBins1 + kBins2 + kBins3;
+constexpr int kThreads = 256;
+constexpr int kFinThreads = 1024;
+constexpr int kSub = 2048;  // elements per collect wave (one candidate slice)
+// radix digits over the 31 value bits: 12 / 11 / 8
+constexpr int kD1 = 4096, kD2 = 2048, kD3 = 256;
+constexpr int kS1 = 19, kS2 = 8;
+constexpr int kFullTilesPerWG = 8;
+constexpr int kMaxHeads = 32;
 
-struct Series {
-  const float* arr;      // [R, stride] scores (sign bit set = invalid)
-  int64_t stride;
-  uint32_t* hist;        // [R, kHistWords]
-  uint32_t* counts;      // [R, chunks, 2]
-  uint32_t* state;       // [R, 4]: T, need_ties, all_flag, nsel
-  int chunks;
-  int K;
+template <int KDT>
+struct KeyTile {
+  static constexpr int kBytes = KDT == CSA2_BF16 ? 128 : 256;   // one indexer key row
+  static constexpr int kKeys = 256;                             // one key per thread
+  static constexpr int kStride = kBytes + 16;                   // padded LDS row
+  static constexpr int kPieces = kBytes / 16;                   // 16-byte pieces per row
+  static constexpr int kPerThread = kKeys * kPieces / kThreads;  // 8 (bf16) or 16 (fp32)
 };
 
-struct SelArgs {
-  Series s[2];
-  int nseries;
-  int mode;                 // CSA2_FULL / CSA2_REINDEX
-  const int32_t* row_visible;
-  int max_visible;
-  int pool_stride;
-  const int32_t* pool;      // Reindex: slot -> position
-  int32_t* out_idx;         // [R, K]
-  int32_t* out_pool;        // [R, pool_size]
-  int32_t* out_pool_len;    // [R]
-  int pool_size;
-};
+__device__ __forceinline__ int clampv(int v, int maxv) { return v < 0 ? 0 : (v > maxv ? maxv : v); }
 
-__device__ __forceinline__ int row_len(const SelArgs& a, int series, int r) {
-  if (a.mode == CSA2_REINDEX) return a.pool_stride;
-  int v = a.row_visible[r];
-  v = v < 0 ? 0 : (v > a.max_visible ? a.max_visible : v);
-  return series == 0 ? v : (v + kBlock - 1) / kBlock;
-}
+// ------------------------------------------------------------ block helpers
 
-__device__ __forceinline__ int visible_of(const int32_t* rv, int r, int maxv) {
-  int v = rv[r];
-  return v < 0 ? 0 : (v > maxv ? maxv : v);
-}
-
-// ------------------------------------------------------------ block scans
-// 256 threads = 4 waves of 64.
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* lds, uint32_t* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -88,7 +72,7 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* lds, ui
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t t = lds[w];
     before += (w < wave) ? t : 0u;
     tot += t;
@@ -98,173 +82,38 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* lds, ui
   return before + x - v;
 }
 
-__device__ __forceinline__ uint32_t block_flag_prefix(bool f, uint32_t* lds, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(f);
-  const uint32_t lp = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) lds[wave] = (uint32_t)__popcll(m);
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t t = lds[w];
-    before += (w < wave) ? t : 0u;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + lp;
-}
-
-// Bin holding the K-th largest element of a histogram (bins scanned from
-// the top).  Returns -1 when the histogram holds fewer than K elements.
-// *above = elements in higher bins, *total = all elements.
-__device__ int find_bin(const uint32_t* __restrict__ h, int nbins, uint32_t K, uint32_t* above, uint32_t* total,
-                        uint32_t* lds) {
-  const int per = nbins / 256;
-  const int hi = nbins - threadIdx.x * per;  // this thread: bins [hi-per, hi), descending
+// Bin holding the K-th largest element of a histogram in global or shared
+// memory (bins scanned from the top); -1 when it holds fewer than K.
+// *above = elements in higher bins, *total = all elements.  lds >= 20 words.
+template <int NT>
+__device__ int find_bin(const uint32_t* h, int nbins, uint32_t K, uint32_t* above, uint32_t* total, uint32_t* lds) {
+  const int per = (nbins + NT - 1) / NT;
+  const int hi = nbins - (int)threadIdx.x * per;  // this thread: bins [max(hi-per,0), hi), descending
+  const int lo = hi - per < 0 ? 0 : hi - per;
   uint32_t local = 0;
-  for (int b = hi - 1; b >= hi - per; --b) local += h[b];
+  for (int b = hi - 1; b >= lo; --b) local += h[b];
   uint32_t tot;
-  const uint32_t before = block_excl_sum(local, lds, &tot);
-  if (threadIdx.x == 0) lds[8] = 0xFFFFFFFFu;
+  const uint32_t before = block_excl_sum<NT>(local, lds, &tot);
+  if (threadIdx.x == 0) lds[16] = 0xFFFFFFFFu;
   __syncthreads();
-  if (before < K && K <= before + local) {
+  if (hi > 0 && before < K && K <= before + local) {
     uint32_t c = before;
-    for (int b = hi - 1; b >= hi - per; --b) {
+    for (int b = hi - 1; b >= lo; --b) {
       const uint32_t n = h[b];
       if (K <= c + n) {
-        lds[8] = (uint32_t)b;
-        lds[9] = c;
+        lds[16] = (uint32_t)b;
+        lds[17] = c;
         break;
       }
       c += n;
     }
   }
   __syncthreads();
-  const uint32_t bin = lds[8], ab = lds[9];
+  const uint32_t bin = lds[16], ab = lds[17];
   __syncthreads();
   *total = tot;
   *above = (bin == 0xFFFFFFFFu) ? tot : ab;
   return (bin == 0xFFFFFFFFu) ? -1 : (int)bin;
-}
-
-struct Threshold {
-  uint32_t T;       // exact 31-bit key of the K-th largest element
-  uint32_t need;    // ties at T to take (>= 1) unless all
-  uint32_t nsel;    // elements selected = min(K, valid)
-  bool all;         // fewer than K valid elements: select every valid one
-};
-
-// levels: how many digits are resolved (1..3); returns partial info for the
-// radix passes and the full threshold at level 3.
-__device__ Threshold resolve(const uint32_t* __restrict__ hist, uint32_t K, int levels, uint32_t* lds, int* b1o,
-                             int* b2o) {
-  Threshold t{0u, 0u, 0u, false};
-  uint32_t above1, total;
-  const int b1 = find_bin(hist, kBins1, K, &above1, &total, lds);
-  *b1o = b1;
-  if (b1 < 0) {
-    t.all = true;
-    t.nsel = total;
-    return t;
-  }
-  t.nsel = K;
-  if (levels < 2) return t;
-  uint32_t above2, tot2;
-  const int b2 = find_bin(hist + kBins1, kBins2, K - above1, &above2, &tot2, lds);
-  *b2o = b2;
-  if (levels < 3) return t;
-  uint32_t above3, tot3;
-  const int b3 = find_bin(hist + kBins1 + kBins2, kBins3, K - above1 - above2, &above3, &tot3, lds);
-  t.T = ((uint32_t)b1 << kShift1) | ((uint32_t)b2 << kShift2) | (uint32_t)b3;
-  t.need = K - above1 - above2 - above3;
-  return t;
-}
-
-// ------------------------------------------------------------ the score
-// fmaf chain over channels from +0, ReLU, heads summed left to right.
-template <int KDT>
-__device__ __forceinline__ void load_key(const void* __restrict__ k, int64_t row, float (&kv)[kIdxDim]) {
-  if (KDT == CSA2_BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(k) + row * kIdxDim);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 t = __builtin_nontemporal_load(p + i);
-      const uint32_t w[4] = {t[0], t[1], t[2], t[3]};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kv[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-        kv[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(k) + row * kIdxDim);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32x4 t = __builtin_nontemporal_load(p + i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kv[4 * i + j] = __uint_as_float(t[j]);
-    }
-  }
-}
-
-// scores of NK keys against H heads (H a template constant, or 0 = runtime hr)
-template <int H, int NK>
-__device__ __forceinline__ void score_keys(const float* __restrict__ q, int hr, const float (&kv)[NK][kIdxDim],
-                                           float (&out)[NK]) {
-  if constexpr (H > 0) {
-    float acc[NK][H];
-#pragma unroll
-    for (int n = 0; n < NK; ++n)
-#pragma unroll
-      for (int h = 0; h < H; ++h) acc[n][h] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kIdxDim; ++c)
-#pragma unroll
-      for (int h = 0; h < H; ++h) {
-        const float qv = q[h * kIdxDim + c];
-#pragma unroll
-        for (int n = 0; n < NK; ++n) acc[n][h] = __builtin_fmaf(qv, kv[n][c], acc[n][h]);
-      }
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-      float s = acc[n][0] > 0.0f ? acc[n][0] : 0.0f;
-#pragma unroll
-      for (int h = 1; h < H; ++h) s = __fadd_rn(s, acc[n][h] > 0.0f ? acc[n][h] : 0.0f);
-      out[n] = s;
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < NK; ++n) out[n] = 0.0f;
-    for (int h = 0; h < hr; ++h) {
-      float acc[NK];
-#pragma unroll
-      for (int n = 0; n < NK; ++n) acc[n] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < kIdxDim; ++c) {
-        const float qv = q[h * kIdxDim + c];
-#pragma unroll
-        for (int n = 0; n < NK; ++n) acc[n] = __builtin_fmaf(qv, kv[n][c], acc[n]);
-      }
-#pragma unroll
-      for (int n = 0; n < NK; ++n) {
-        const float rel = acc[n] > 0.0f ? acc[n] : 0.0f;
-        out[n] = (h == 0) ? rel : __fadd_rn(out[n], rel);
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------ kernels
-
-__global__ __launch_bounds__(256) void k_prep(const void* __restrict__ idx_q, int q_dtype, int64_t nq,
-                                              float* __restrict__ qf, uint32_t* __restrict__ hist, int64_t nhist) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nq; i += stride)
-    qf[i] = (q_dtype == CSA2_BF16) ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(idx_q)[i] << 16)
-                                   : static_cast<const float*>(idx_q)[i];
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nhist; i += stride) hist[i] = 0u;
 }
 
 __device__ __forceinline__ void flush_hist(uint32_t* __restrict__ g, const uint32_t* __restrict__ l, int n) {
@@ -274,295 +123,402 @@ __device__ __forceinline__ void flush_hist(uint32_t* __restrict__ g, const uint3
   }
 }
 
-template <int KDT, int H, bool POOL>
-__global__ __launch_bounds__(kScanThreads) void k_scan_full(
-    const float* __restrict__ qf, int hr, const void* __restrict__ idx_k, const int64_t* __restrict__ row_start,
-    const int32_t* __restrict__ row_visible, int max_vis, float* __restrict__ scores, int64_t n_pad,
-    float* __restrict__ bmax, int64_t nb_pad, uint32_t* __restrict__ hist_s, uint32_t* __restrict__ hist_b) {
-  __shared__ uint32_t h1[kBins1];
-  __shared__ uint32_t hb[POOL ? kBins1 : 1];
+// ------------------------------------------------------------ kernels
+
+__global__ __launch_bounds__(256) void k_prep(const void* __restrict__ idx_q, int q_dtype, int R, int H,
+                                              float* __restrict__ qf, uint32_t* __restrict__ hist, int64_t nhist) {
+  const int64_t nq = (int64_t)R * H * kIdxDim;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nq; i += stride) {
+    const int64_t r = i / (H * kIdxDim);
+    const int rem = (int)(i % (H * kIdxDim));
+    const int h = rem / kIdxDim, c = rem % kIdxDim;
+    const float v = (q_dtype == CSA2_BF16) ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(idx_q)[i] << 16)
+                                           : static_cast<const float*>(idx_q)[i];
+    qf[r * H * kIdxDim + ((c >> 2) * H + h) * 4 + (c & 3)] = v;
+  }
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nhist; i += stride) hist[i] = 0u;
+}
+
+struct ScoreArgs {
+  int H;
+  const void* idx_k;
+  const int64_t* row_start;
+  const int32_t* row_visible;
+  int max_visible;
+  const int32_t* pool;        // Reindex
+  const int32_t* pool_len;
+  int pool_stride;
+  float* scores;              // [R][n_pad]
+  int64_t n_pad;
+  float* bmax;                // [R][nb_pad]
+  int64_t nb_pad;
+  uint32_t* hist_s;           // [R][kD1]
+  uint32_t* hist_b;           // [R][kD1]
+  int tiles_per_wg;
+};
+
+template <int KDT>
+struct Staged {
+  u32x4 v[KeyTile<KDT>::kPerThread];
+};
+
+// HC: compile-time head count (0 = runtime a.H, at most 32)
+template <int KDT, int HC, bool REINDEX, bool POOL>
+__global__ __launch_bounds__(kThreads, 2) void k_score(ScoreArgs a, const float* __restrict__ qf) {
+  using T = KeyTile<KDT>;
+  constexpr int NACC = HC > 0 ? HC : kMaxHeads;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* tile = smem;                                                   // kKeys * kStride
+  uint32_t* h1 = reinterpret_cast<uint32_t*>(smem + T::kKeys * T::kStride);  // kD1
+  uint32_t* hb = h1 + kD1;                                                // kD1 (POOL)
+  int32_t* posb = reinterpret_cast<int32_t*>(hb + (POOL ? kD1 : 0));     // kKeys (Reindex)
+
+  const int H = HC > 0 ? HC : a.H;
   const int r = blockIdx.y;
-  const int vis = visible_of(row_visible, r, max_vis);
-  const int base = blockIdx.x * kScanChunk;
-  if (base >= vis) return;
-  for (int b = threadIdx.x; b < kBins1; b += kScanThreads) {
+  const int vis = clampv(a.row_visible[r], a.max_visible);
+  const int n = REINDEX ? a.pool_stride : vis;
+  const int64_t base0 = (int64_t)blockIdx.x * a.tiles_per_wg * T::kKeys;
+  if (base0 >= n) return;
+  const int ntiles = (int)std::min<int64_t>(a.tiles_per_wg, ceil_div(n - base0, T::kKeys));
+  int plen = 0;
+  if (REINDEX) plen = a.pool_len ? clampv(a.pool_len[r], a.pool_stride) : a.pool_stride;
+  for (int b = threadIdx.x; b < kD1; b += kThreads) {
     h1[b] = 0u;
     if (POOL) hb[b] = 0u;
   }
-  __syncthreads();
-  const float* q = qf + (int64_t)r * (H > 0 ? H : hr) * kIdxDim;
-  const int64_t rs = row_start[r];
-  float* srow = scores + (int64_t)r * n_pad;
-  for (int it = 0; it < kScanIters; ++it) {
-    int j[kScanKeysPerThread];
-    float kv[kScanKeysPerThread][kIdxDim];
-#pragma unroll
-    for (int n = 0; n < kScanKeysPerThread; ++n) {
-      j[n] = base + (it * kScanKeysPerThread + n) * kScanThreads + threadIdx.x;
-      const int jj = j[n] < vis ? j[n] : vis - 1;  // tail lanes reload a valid row, result dropped
-      load_key<KDT>(idx_k, rs + jj, kv[n]);
+  if (REINDEX) {
+    for (int k = threadIdx.x; k < T::kKeys; k += kThreads) {
+      const int64_t i = base0 + k;
+      const int p = (i < plen) ? a.pool[(int64_t)r * a.pool_stride + i] : -1;
+      posb[k] = (p >= 0 && p < vis) ? p : -1;
     }
-    float s[kScanKeysPerThread];
-    score_keys<H, kScanKeysPerThread>(q, hr, kv, s);
+    __syncthreads();
+  }
+  const int64_t rs = a.row_start[r];
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.idx_k);
+  float* srow = a.scores + (int64_t)r * a.n_pad;
+
+  // piece id = tid + 256*i -> key id / kPieces, piece id % kPieces (16 consecutive bytes of the tile)
+  auto load_tile = [&](int64_t base, Staged<KDT>& st) {
 #pragma unroll
-    for (int n = 0; n < kScanKeysPerThread; ++n) {
-      const bool ok = j[n] < vis;
-      if (ok) {
-        srow[j[n]] = s[n];
-        atomicAdd(&h1[__float_as_uint(s[n]) >> kShift1], 1u);
+    for (int i = 0; i < T::kPerThread; ++i) {
+      const int id = threadIdx.x + kThreads * i;
+      const int k = id / T::kPieces, piece = id % T::kPieces;
+      int64_t pos;
+      bool ok;
+      if (REINDEX) {
+        pos = posb[k];
+        ok = pos >= 0;
+      } else {
+        pos = base + k;
+        ok = pos < vis;
       }
-      if (POOL) {
-        // block of 8 consecutive positions = 8 consecutive lanes
-        float m = ok ? s[n] : -1.0f;
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        m = fmaxf(m, __shfl_xor(m, 4, 64));
-        if (ok && (threadIdx.x & 7) == 0) {
-          bmax[(int64_t)r * nb_pad + j[n] / kBlock] = m;
-          atomicAdd(&hb[__float_as_uint(m) >> kShift1], 1u);
+      // invalid keys read row 0 of the key array (always present) and are zeroed: no branch around the load
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (ok ? rs + pos : 0) * T::kBytes) +
+                                                 piece);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.v[i][e] = ok ? v[e] : 0u;
+    }
+  };
+
+  Staged<KDT> st;
+  load_tile(base0, st);
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t base = base0 + (int64_t)t * T::kKeys;
+    __syncthreads();  // the previous tile is consumed
+#pragma unroll
+    for (int i = 0; i < T::kPerThread; ++i) {
+      const int id = threadIdx.x + kThreads * i;
+      *reinterpret_cast<u32x4*>(tile + (id / T::kPieces) * T::kStride + (id % T::kPieces) * 16) = st.v[i];
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(base + T::kKeys, st);
+
+    // the H fmaf chains of key tid, channels in order
+    float acc[NACC];
+#pragma unroll
+    for (int h = 0; h < NACC; ++h) acc[h] = 0.0f;
+    const uint8_t* row = tile + threadIdx.x * T::kStride;
+#pragma unroll 2
+    for (int c4 = 0; c4 < 16; ++c4) {
+      float kv[4];
+      if (KDT == CSA2_BF16) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(row + c4 * 8);
+        kv[0] = __uint_as_float(w[0] << 16);
+        kv[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+        kv[2] = __uint_as_float(w[1] << 16);
+        kv[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+      } else {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(row + c4 * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[j] = __uint_as_float(w[j]);
+      }
+      // the H x 4 query values of this channel quad are wave-uniform: scalar loads
+      const float* qrow = qf + (int64_t)r * H * kIdxDim + c4 * H * 4;
+      if constexpr (HC > 0) {
+#pragma unroll
+        for (int h = 0; h < HC; ++h) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[h] = __builtin_fmaf(qrow[h * 4 + j], kv[j], acc[h]);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < kMaxHeads; ++h) {
+          if (h < H) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[h] = __builtin_fmaf(qrow[h * 4 + j], kv[j], acc[h]);
+          }
         }
       }
     }
-  }
-  __syncthreads();
-  flush_hist(hist_s + (int64_t)r * kHistWords, h1, kBins1);
-  if (POOL) flush_hist(hist_b + (int64_t)r * kHistWords, hb, kBins1);
-}
-
-template <int KDT, int H>
-__global__ __launch_bounds__(kScanThreads) void k_score_pool(
-    const float* __restrict__ qf, int hr, const void* __restrict__ idx_k, const int64_t* __restrict__ row_start,
-    const int32_t* __restrict__ row_visible, int max_vis, const int32_t* __restrict__ pool,
-    const int32_t* __restrict__ pool_len, int pool_stride, float* __restrict__ scores, int64_t n_pad,
-    uint32_t* __restrict__ hist_s) {
-  __shared__ uint32_t h1[kBins1];
-  const int r = blockIdx.y;
-  const int base = blockIdx.x * kScanChunk;
-  if (base >= pool_stride) return;
-  for (int b = threadIdx.x; b < kBins1; b += kScanThreads) h1[b] = 0u;
-  __syncthreads();
-  const int vis = visible_of(row_visible, r, max_vis);
-  int plen = pool_len ? pool_len[r] : pool_stride;
-  plen = plen < 0 ? 0 : (plen > pool_stride ? pool_stride : plen);
-  const float* q = qf + (int64_t)r * (H > 0 ? H : hr) * kIdxDim;
-  const int64_t rs = row_start[r];
-  const int32_t* prow = pool + (int64_t)r * pool_stride;
-  float* srow = scores + (int64_t)r * n_pad;
-  for (int it = 0; it < kScanIters; ++it) {
-    int i[kScanKeysPerThread];
-    bool ok[kScanKeysPerThread];
-    float kv[kScanKeysPerThread][kIdxDim];
+    float s = acc[0] > 0.0f ? acc[0] : 0.0f;
 #pragma unroll
-    for (int n = 0; n < kScanKeysPerThread; ++n) {
-      i[n] = base + (it * kScanKeysPerThread + n) * kScanThreads + threadIdx.x;
-      const int p = (i[n] < plen) ? prow[i[n]] : -1;
-      ok[n] = p >= 0 && p < vis;
-      if (ok[n]) {
-        load_key<KDT>(idx_k, rs + p, kv[n]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < kIdxDim; ++c) kv[n][c] = 0.0f;
+    for (int h = 1; h < NACC; ++h)
+      if (HC > 0 || h < H) s = __fadd_rn(s, acc[h] > 0.0f ? acc[h] : 0.0f);
+    const int k = threadIdx.x;
+    const int64_t i = base + k;
+    bool ok;
+    if (REINDEX) ok = posb[k] >= 0;
+    else ok = i < vis;
+    if (i < n) srow[i] = ok ? s : -1.0f;
+    if (!REINDEX && ok) atomicAdd(&h1[__float_as_uint(s) >> kS1], 1u);
+    if (POOL) {
+      // a block of 8 consecutive positions = 8 consecutive lanes
+      float m = ok ? s : -1.0f;
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      m = fmaxf(m, __shfl_xor(m, 4, 64));
+      if (ok && (threadIdx.x & 7) == 0) {
+        a.bmax[(int64_t)r * a.nb_pad + i / kBlock] = m;
+        atomicAdd(&hb[__float_as_uint(m) >> kS1], 1u);
       }
     }
-    float s[kScanKeysPerThread];
-    score_keys<H, kScanKeysPerThread>(q, hr, kv, s);
+  }
+  __syncthreads();
+  if (!REINDEX) {
+    flush_hist(a.hist_s + (int64_t)r * kD1, h1, kD1);
+    if (POOL) flush_hist(a.hist_b + (int64_t)r * kD1, hb, kD1);
+  }
+}
+
+struct Series {
+  const float* arr;      // [R, stride] keys (sign bit set = invalid)
+  int64_t stride;
+  const uint32_t* hist;  // [R, kD1] first-digit histogram (Full)
+  float* cand_key;       // [R, 2*stride] candidate keys (Full): per-slice lists, then the packed list
+  int32_t* cand_pos;     // [R, 2*stride] candidate positions (Full)
+  uint32_t* counts;      // [R, nsub] candidates per slice (Full)
+  int nsub;              // slices of kSub elements
+  int K;
+};
+
+struct SelArgs {
+  Series s[2];
+  int nseries;
+  int mode;
+  const int32_t* row_visible;
+  int max_visible;
+  int pool_stride;
+  const int32_t* pool;
+  int32_t* out_idx;      // [R, K]
+  int32_t* out_pool;     // [R, pool_size]
+  int32_t* out_pool_len; // [R]
+  int pool_size;
+};
+
+__device__ __forceinline__ int series_len(const SelArgs& a, int series, int r) {
+  if (a.mode == CSA2_REINDEX) return a.pool_stride;
+  const int v = clampv(a.row_visible[r], a.max_visible);
+  return series == 0 ? v : (v + kBlock - 1) / kBlock;
+}
+
+// Full mode: each wave compacts its slice of kSub elements, keeping those
+// whose first digit is at least the threshold bin (all valid ones when the
+// row holds fewer than K).
+__global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
+  __shared__ uint32_t red[32];
+  const int series = blockIdx.z, r = blockIdx.y;
+  if (series >= a.nseries) return;
+  const Series& S = a.s[series];
+  const int n = series_len(a, series, r);
+  const int64_t wg_base = (int64_t)blockIdx.x * 4 * kSub;
+  if (wg_base >= n) return;
+  uint32_t above, total;
+  const int b1 = find_bin<kThreads>(S.hist + (int64_t)r * kD1, kD1, (uint32_t)S.K, &above, &total, red);
+  const uint32_t thr = b1 < 0 ? 0u : (uint32_t)b1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = wg_base + (int64_t)wave * kSub;
+  if (base >= n) return;
+  const int sub = (int)(base / kSub);
+  const int end = (int)std::min<int64_t>(n, base + kSub);
+  const float* arr = S.arr + (int64_t)r * S.stride;
+  float* ck = S.cand_key + (int64_t)r * 2 * S.stride + base;
+  int32_t* cp = S.cand_pos + (int64_t)r * 2 * S.stride + base;
+  uint32_t cnt = 0;
+  constexpr int kPer = kSub / 64;  // 32 elements per lane, all loads in flight at once
+  float v[kPer];
 #pragma unroll
-    for (int n = 0; n < kScanKeysPerThread; ++n) {
-      if (i[n] < pool_stride) srow[i[n]] = ok[n] ? s[n] : -1.0f;
-      if (ok[n]) atomicAdd(&h1[__float_as_uint(s[n]) >> kShift1], 1u);
-    }
+  for (int k = 0; k < kPer; ++k) {
+    const int i = (int)base + 64 * k + lane;
+    v[k] = arr[i < end ? i : end - 1];
   }
-  __syncthreads();
-  flush_hist(hist_s + (int64_t)r * kHistWords, h1, kBins1);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = (int)base + 64 * k + lane;
+    const uint32_t key = __float_as_uint(v[k]);
+    const bool take = i < end && !(key >> 31) && (key >> kS1) >= thr;
+    const unsigned long long m = __ballot(take);
+    if (take) {
+      const uint32_t at = cnt + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+      ck[at] = v[k];
+      cp[at] = i;
+    }
+    cnt += (uint32_t)__popcll(m);
+  }
+  if (lane == 0) S.counts[(int64_t)r * S.nsub + sub] = cnt;
 }
 
-// Histogram of the next digit over elements that match the resolved prefix.
-template <int LEVEL>
-__global__ __launch_bounds__(256) void k_radix_pass(SelArgs a) {
-  __shared__ uint32_t lh[LEVEL == 2 ? kBins2 : kBins3];
-  __shared__ uint32_t red[16];
-  const int series = blockIdx.z, r = blockIdx.y, c = blockIdx.x;
+// One workgroup per (row, series): gather the candidates into one contiguous
+// list (Full), find the exact threshold with three radix digits, then the
+// ordered compaction into the outputs.
+__global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
+  __shared__ uint32_t hist[kD1];
+  __shared__ uint32_t pre[1024 + 1];
+  __shared__ uint32_t red[32];
+  const int series = blockIdx.y, r = blockIdx.x;
   if (series >= a.nseries) return;
   const Series& S = a.s[series];
-  const int n = row_len(a, series, r);
-  const int base = c * kSelChunk;
-  if (base >= n) return;
-  const uint32_t* hist = S.hist + (int64_t)r * kHistWords;
-  int b1 = -1, b2 = -1;
-  const Threshold t = resolve(hist, (uint32_t)S.K, LEVEL - 1, red, &b1, &b2);
-  if (t.all) return;
-  constexpr int NB = LEVEL == 2 ? kBins2 : kBins3;
-  for (int b = threadIdx.x; b < NB; b += 256) lh[b] = 0u;
-  __syncthreads();
-  const float* arr = S.arr + (int64_t)r * S.stride;
-  const int end = min(n, base + kSelChunk);
-  for (int i = base + threadIdx.x; i < end; i += 256) {
-    const uint32_t key = __float_as_uint(arr[i]);
-    if (key >> 31) continue;
-    if ((int)(key >> kShift1) != b1) continue;
-    if (LEVEL == 2) {
-      atomicAdd(&lh[(key >> kShift2) & (kBins2 - 1)], 1u);
-    } else {
-      if ((int)((key >> kShift2) & (kBins2 - 1)) != b2) continue;
-      atomicAdd(&lh[key & (kBins3 - 1)], 1u);
+  const int n = series_len(a, series, r);
+  const bool full = a.mode == CSA2_FULL;
+  const int vis = clampv(a.row_visible[r], a.max_visible);
+  const float* keys;
+  const int32_t* posr;
+  uint32_t M;
+  if (full) {
+    // slice s holds counts[s] candidates at [s*kSub, ...); pack them into the
+    // second half of the candidate arrays (rows are 2 * stride long)
+    const int nsub = (n + kSub - 1) / kSub;
+    uint32_t carry = 0;
+    for (int s0 = 0; s0 < nsub; s0 += kFinThreads) {
+      const int s = s0 + threadIdx.x;
+      const uint32_t c = (s < nsub) ? S.counts[(int64_t)r * S.nsub + s] : 0u;
+      uint32_t tot;
+      const uint32_t ex = block_excl_sum<kFinThreads>(c, red, &tot);
+      if (s < nsub) pre[s] = carry + ex;
+      carry += tot;
     }
+    if (threadIdx.x == 0) pre[nsub] = carry;
+    __syncthreads();
+    M = pre[nsub];
+    const float* sk = S.cand_key + (int64_t)r * 2 * S.stride;
+    const int32_t* sp = S.cand_pos + (int64_t)r * 2 * S.stride;
+    float* dk = S.cand_key + (int64_t)r * 2 * S.stride + S.stride;
+    int32_t* dp = S.cand_pos + (int64_t)r * 2 * S.stride + S.stride;
+#pragma unroll 4
+    for (uint32_t c = threadIdx.x; c < M; c += kFinThreads) {
+      int lo = 0, hi = nsub;  // largest s with pre[s] <= c
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= c) lo = mid;
+        else hi = mid;
+      }
+      const int64_t at = (int64_t)lo * kSub + (c - pre[lo]);
+      dk[c] = sk[at];
+      dp[c] = sp[at];
+    }
+    __syncthreads();
+    keys = dk;
+    posr = dp;
+  } else {
+    keys = S.arr + (int64_t)r * S.stride;
+    posr = a.pool + (int64_t)r * a.pool_stride;
+    M = (uint32_t)n;
   }
-  __syncthreads();
-  flush_hist(S.hist + (int64_t)r * kHistWords + (LEVEL == 2 ? kBins1 : kBins1 + kBins2), lh, NB);
-}
 
-__global__ __launch_bounds__(256) void k_select_count(SelArgs a) {
-  __shared__ uint32_t red[16];
-  const int series = blockIdx.z, r = blockIdx.y, c = blockIdx.x;
-  if (series >= a.nseries) return;
-  const Series& S = a.s[series];
-  const int n = row_len(a, series, r);
-  const int base = c * kSelChunk;
-  if (base >= n && c != 0) return;
-  int b1, b2;
-  const Threshold t = resolve(S.hist + (int64_t)r * kHistWords, (uint32_t)S.K, 3, red, &b1, &b2);
-  if (c == 0 && threadIdx.x == 0) {
-    uint32_t* st = S.state + (int64_t)r * 4;
-    st[0] = t.T;
-    st[1] = t.need;
-    st[2] = t.all ? 1u : 0u;
-    st[3] = t.nsel;
+  // ---- exact threshold: three digits over the candidates
+  uint32_t K = (uint32_t)S.K;
+  uint32_t prefix = 0;  // resolved high bits
+  int shift_hi = 31;
+  bool all = false;
+  uint32_t need = 0;
+#pragma unroll 1
+  for (int lev = 0; lev < 3; ++lev) {
+    const int sh = lev == 0 ? kS1 : (lev == 1 ? kS2 : 0);
+    const int nb = lev == 0 ? kD1 : (lev == 1 ? kD2 : kD3);
+    for (int b = threadIdx.x; b < nb; b += kFinThreads) hist[b] = 0u;
+    __syncthreads();
+#pragma unroll 4
+    for (uint32_t i = threadIdx.x; i < M; i += kFinThreads) {
+      const uint32_t key = __float_as_uint(keys[i]);
+      if (!(key >> 31) && (lev == 0 || (key >> shift_hi) == prefix)) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t above, total;
+    const int b = find_bin<kFinThreads>(hist, nb, K, &above, &total, red);
+    if (b < 0) {  // only at the first level: fewer than K valid candidates
+      all = true;
+      break;
+    }
+    prefix = (prefix << (shift_hi - sh)) | (uint32_t)b;
+    shift_hi = sh;
+    K -= above;
+    need = K;
   }
-  if (base >= n) return;
-  const float* arr = S.arr + (int64_t)r * S.stride;
-  const int end = min(n, base + kSelChunk);
+  const uint32_t T = prefix;  // the full 31-bit key of the K-th largest
+
+  // ---- ordered compaction: thread t owns candidates [t*per, (t+1)*per)
+  const uint32_t per = (M + kFinThreads - 1) / kFinThreads;
+  const uint32_t c0 = min(M, threadIdx.x * per), c1 = min(M, c0 + per);
   uint32_t gt = 0, eq = 0;
-  for (int i = base + threadIdx.x; i < end; i += 256) {
-    const uint32_t key = __float_as_uint(arr[i]);
+#pragma unroll 4
+  for (uint32_t c = c0; c < c1; ++c) {
+    const uint32_t key = __float_as_uint(keys[c]);
+    gt += (!(key >> 31) && (all || key > T)) ? 1u : 0u;
+    eq += (!(key >> 31) && !all && key == T) ? 1u : 0u;
+  }
+  uint32_t tot_gt, tot_eq;
+  const uint32_t gt_before = block_excl_sum<kFinThreads>(gt, red, &tot_gt);
+  const uint32_t eq_before = block_excl_sum<kFinThreads>(eq, red, &tot_eq);
+  const uint32_t nsel = all ? tot_gt : (uint32_t)S.K;
+  uint32_t out = gt_before + (all ? 0u : min(eq_before, need));
+  uint32_t ties = eq_before;
+  bool last_block_kept = false;
+  for (uint32_t c = c0; c < c1; ++c) {
+    const uint32_t key = __float_as_uint(keys[c]);
     if (key >> 31) continue;
-    if (t.all || key > t.T) ++gt;
-    else if (key == t.T) ++eq;
-  }
-  uint32_t tg, te;
-  block_excl_sum(gt, red, &tg);
-  block_excl_sum(eq, red, &te);
-  if (threadIdx.x == 0) {
-    uint32_t* cnt = S.counts + ((int64_t)r * S.chunks + c) * 2;
-    cnt[0] = tg;
-    cnt[1] = te;
-  }
-}
-
-__global__ __launch_bounds__(256) void k_select_write(SelArgs a) {
-  __shared__ uint32_t red[16];
-  __shared__ uint32_t pre[2];
-  const int series = blockIdx.z, r = blockIdx.y, c = blockIdx.x;
-  if (series >= a.nseries) return;
-  const Series& S = a.s[series];
-  const int n = row_len(a, series, r);
-  const int base = c * kSelChunk;
-  const uint32_t* st = S.state + (int64_t)r * 4;
-  const uint32_t T = st[0], need = st[1], nsel = st[3];
-  const bool all = st[2] != 0u;
-  const int vis = (a.mode == CSA2_FULL) ? visible_of(a.row_visible, r, a.max_visible) : 0;
-  // padding and the pool length (chunk 0)
-  if (c == 0) {
+    bool sel;
+    if (all || key > T) sel = true;
+    else if (key == T) sel = (ties++ < need);
+    else sel = false;
+    if (!sel || out >= nsel) continue;
+    const int32_t pos = posr[c];
     if (series == 0) {
-      int32_t* o = a.out_idx + (int64_t)r * S.K;
-      for (int i = (int)nsel + threadIdx.x; i < S.K; i += 256) o[i] = -1;
+      a.out_idx[(int64_t)r * S.K + out] = pos;
     } else {
-      // pool length: full blocks except a partial last block if it was kept
-      const int nb = n;  // blocks of this row
-      int plen = (int)nsel * kBlock;
-      if (nsel > 0 && (vis % kBlock) != 0) {
-        const uint32_t lastkey = __float_as_uint(S.arr[(int64_t)r * S.stride + nb - 1]);
-        bool kept;
-        if (all) kept = true;
-        else if (lastkey > T) kept = true;
-        else if (lastkey == T) {
-          // the last block is the highest-index tie: kept iff every tie is taken
-          uint32_t ties = 0;
-          const uint32_t* cnt = S.counts + (int64_t)r * S.chunks * 2;
-          const int nch = (nb + kSelChunk - 1) / kSelChunk;
-          for (int k = 0; k < nch; ++k) ties += cnt[2 * k + 1];
-          kept = need >= ties;
-        } else kept = false;
-        if (kept) plen -= kBlock - (vis % kBlock);
-      }
-      int32_t* o = a.out_pool + (int64_t)r * a.pool_size;
-      for (int i = plen + threadIdx.x; i < a.pool_size; i += 256) o[i] = -1;
-      if (threadIdx.x == 0) a.out_pool_len[r] = plen;
-    }
-  }
-  if (base >= n) return;
-  // selections and ties in earlier chunks
-  if (threadIdx.x == 0) {
-    uint32_t gtb = 0, eqb = 0;
-    const uint32_t* cnt = S.counts + (int64_t)r * S.chunks * 2;
-    for (int k = 0; k < c; ++k) {
-      gtb += cnt[2 * k];
-      eqb += cnt[2 * k + 1];
-    }
-    pre[0] = gtb + (all ? 0u : min(eqb, need));
-    pre[1] = eqb;
-  }
-  __syncthreads();
-  uint32_t out_pos = pre[0];
-  uint32_t ties_seen = pre[1];
-  __syncthreads();
-  const float* arr = S.arr + (int64_t)r * S.stride;
-  const int end = min(n, base + kSelChunk);
-  for (int i0 = base; i0 < end; i0 += 256) {
-    const int i = i0 + threadIdx.x;
-    const uint32_t key = (i < end) ? __float_as_uint(arr[i]) : 0x80000000u;
-    const bool valid = !(key >> 31);
-    const bool tie = valid && !all && key == T;
-    uint32_t ntie;
-    const uint32_t tr = block_flag_prefix(tie, red, &ntie);
-    const bool sel = valid && (all || key > T || (tie && ties_seen + tr < need));
-    uint32_t nsel_it;
-    const uint32_t sr = block_flag_prefix(sel, red, &nsel_it);
-    if (sel) {
-      const uint32_t p = out_pos + sr;
-      if (p >= nsel) {
-        // unreachable when the threshold is consistent; keeps every store in bounds
-      } else if (series == 0) {
-        const int32_t pos = (a.mode == CSA2_FULL) ? i : a.pool[(int64_t)r * a.pool_stride + i];
-        a.out_idx[(int64_t)r * S.K + p] = pos;
-      } else {
-        int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)p * kBlock;
+      int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)out * kBlock;
 #pragma unroll
-        for (int m = 0; m < kBlock; ++m) {
-          const int pos = i * kBlock + m;
-          if (pos < vis) o[m] = pos;
-        }
-      }
+      for (int m = 0; m < kBlock; ++m) o[m] = (pos * kBlock + m < vis) ? pos * kBlock + m : -1;
+      if (pos == n - 1) last_block_kept = true;
     }
-    out_pos += nsel_it;
-    ties_seen += ntie;
+    ++out;
   }
-}
-
-template <int KDT, int H, bool POOL>
-void launch_scoring(int mode, dim3 grid, hipStream_t s, const float* qf, int hr, const void* idx_k,
-                    const int64_t* row_start, const int32_t* row_visible, int max_vis, const int32_t* pool,
-                    const int32_t* pool_len, int pool_stride, const TopkWorkspace& w, uint32_t* hist_b) {
-  if (mode == CSA2_FULL)
-    hipLaunchKernelGGL((k_scan_full<KDT, H, POOL>), grid, dim3(kScanThreads), 0, s, qf, hr, idx_k, row_start,
-                       row_visible, max_vis, w.scores, w.n_pad, w.bmax, w.nb_pad, w.hist, hist_b);
-  else
-    hipLaunchKernelGGL((k_score_pool<KDT, H>), grid, dim3(kScanThreads), 0, s, qf, hr, idx_k, row_start,
-                       row_visible, max_vis, pool, pool_len, pool_stride, w.scores, w.n_pad, w.hist);
-}
-
-template <int KDT, bool POOL>
-void dispatch_heads(int H, int mode, dim3 grid, hipStream_t s, const float* qf, const void* idx_k,
-                    const int64_t* row_start, const int32_t* row_visible, int max_vis, const int32_t* pool,
-                    const int32_t* pool_len, int pool_stride, const TopkWorkspace& w, uint32_t* hist_b) {
-  if (H == 8)
-    launch_scoring<KDT, 8, POOL>(mode, grid, s, qf, H, idx_k, row_start, row_visible, max_vis, pool, pool_len,
-                                 pool_stride, w, hist_b);
-  else if (H == 4)
-    launch_scoring<KDT, 4, POOL>(mode, grid, s, qf, H, idx_k, row_start, row_visible, max_vis, pool, pool_len,
-                                 pool_stride, w, hist_b);
-  else
-    launch_scoring<KDT, 0, POOL>(mode, grid, s, qf, H, idx_k, row_start, row_visible, max_vis, pool, pool_len,
-                                 pool_stride, w, hist_b);
+  // ---- padding and pool length
+  if (series == 0) {
+    int32_t* o = a.out_idx + (int64_t)r * S.K;
+    for (int i = (int)nsel + threadIdx.x; i < S.K; i += kFinThreads) o[i] = -1;
+  } else {
+    if (threadIdx.x == 0) red[20] = 0u;
+    __syncthreads();
+    if (last_block_kept) red[20] = 1u;
+    __syncthreads();
+    // the partial last block is the highest block, hence the last one written
+    int plen = (int)nsel * kBlock;
+    if (red[20] && (vis % kBlock) != 0) plen -= kBlock - (vis % kBlock);
+    int32_t* o = a.out_pool + (int64_t)r * a.pool_size;
+    for (int i = (int)nsel * kBlock + threadIdx.x; i < a.pool_size; i += kFinThreads) o[i] = -1;
+    if (threadIdx.x == 0) a.out_pool_len[r] = plen;
+  }
 }
 
 struct Carve {
@@ -577,33 +533,67 @@ struct Carve {
 };
 
 struct Layout {
-  TopkWorkspace w;
-  uint32_t* hist_b;
-  uint32_t* counts_b;
-  uint32_t* state;
+  float* qf;
+  uint32_t* hist;  // [2][R][kD1]
+  float* scores;
+  float* bmax;
+  float* cand_key[2];
+  int32_t* cand_pos[2];
+  uint32_t* counts[2];
+  int64_t n_pad, nb_pad;
+  int nsub, nbsub;
   size_t bytes;
 };
 
 Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stride, int pool_size) {
   Layout L{};
   Carve c{static_cast<char*>(base)};
-  const int64_t n = (mode == CSA2_FULL) ? max_visible : pool_stride;
-  L.w.n_pad = round_up(n > 0 ? n : 1, 64);
-  L.w.chunks = (int)ceil_div(n > 0 ? n : 1, kSelChunk);
-  const bool pool_on = mode == CSA2_FULL && pool_size > 0;
+  const bool full = mode == CSA2_FULL;
+  const int64_t n = full ? max_visible : pool_stride;
+  const bool pool_on = full && pool_size > 0;
   const int64_t nb = pool_on ? ceil_div(max_visible, kBlock) : 0;
-  L.w.nb_pad = round_up(nb > 0 ? nb : 1, 64);
-  L.w.bchunks = (int)ceil_div(nb > 0 ? nb : 1, kSelChunk);
-  L.w.qf = c.take<float>((size_t)R * H * kIdxDim);
-  L.w.hist = c.take<uint32_t>((size_t)R * kHistWords * (pool_on ? 2 : 1));
-  L.hist_b = pool_on ? L.w.hist + (size_t)R * kHistWords : nullptr;
-  L.w.counts = c.take<uint32_t>((size_t)R * L.w.chunks * 2);
-  L.counts_b = pool_on ? c.take<uint32_t>((size_t)R * L.w.bchunks * 2) : nullptr;
-  L.state = c.take<uint32_t>((size_t)R * 8);
-  L.w.scores = c.take<float>((size_t)R * L.w.n_pad);
-  L.w.bmax = pool_on ? c.take<float>((size_t)R * L.w.nb_pad) : nullptr;
+  L.n_pad = round_up(std::max<int64_t>(n, 1), kSub);
+  L.nb_pad = round_up(std::max<int64_t>(nb, 1), kSub);
+  L.nsub = (int)(L.n_pad / kSub);
+  L.nbsub = (int)(L.nb_pad / kSub);
+  L.qf = c.take<float>((size_t)R * H * kIdxDim);
+  L.hist = c.take<uint32_t>((size_t)R * kD1 * 2);
+  L.scores = c.take<float>((size_t)R * L.n_pad);
+  L.bmax = pool_on ? c.take<float>((size_t)R * L.nb_pad) : nullptr;
+  if (full) {
+    L.cand_key[0] = c.take<float>((size_t)R * 2 * L.n_pad);
+    L.cand_pos[0] = c.take<int32_t>((size_t)R * 2 * L.n_pad);
+    L.counts[0] = c.take<uint32_t>((size_t)R * L.nsub);
+  }
+  if (pool_on) {
+    L.cand_key[1] = c.take<float>((size_t)R * 2 * L.nb_pad);
+    L.cand_pos[1] = c.take<int32_t>((size_t)R * 2 * L.nb_pad);
+    L.counts[1] = c.take<uint32_t>((size_t)R * L.nbsub);
+  }
   L.bytes = c.off;
   return L;
+}
+
+template <int KDT, int HC, bool REINDEX, bool POOL>
+void launch_score(const ScoreArgs& sa, const float* qf, dim3 grid, hipStream_t s) {
+  using T = KeyTile<KDT>;
+  const size_t lds = (size_t)T::kKeys * T::kStride + (size_t)kD1 * 4 * (POOL ? 2 : 1) +
+                     (REINDEX ? (size_t)T::kKeys * 4 : 0);
+  auto kern = k_score<KDT, HC, REINDEX, POOL>;
+  static bool configured = false;
+  if (!configured) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)((size_t)T::kKeys * T::kStride + (size_t)kD1 * 8 + T::kKeys * 4));
+    configured = true;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, sa, qf);
+}
+
+template <int KDT, bool REINDEX, bool POOL>
+void dispatch_heads(int H, const ScoreArgs& sa, const float* qf, dim3 grid, hipStream_t s) {
+  if (H == 8) launch_score<KDT, 8, REINDEX, POOL>(sa, qf, grid, s);
+  else if (H == 4) launch_score<KDT, 4, REINDEX, POOL>(sa, qf, grid, s);
+  else launch_score<KDT, 0, REINDEX, POOL>(sa, qf, grid, s);
 }
 
 }  // namespace
@@ -612,44 +602,54 @@ size_t topk_workspace_bytes(int mode, int R, int H, int max_visible, int pool_st
   return layout(nullptr, mode, R, H, max_visible, pool_stride, pool_size).bytes;
 }
 
+int topk_max_visible() { return 1024 * kSub; }
+
 hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k, int k_dtype,
                              const int64_t* row_start, const int32_t* row_visible, int max_visible,
                              const int32_t* pool, const int32_t* pool_len, int pool_stride, int top_k,
                              int32_t* out_idx, int pool_size, int32_t* out_pool, int32_t* out_pool_len, void* ws,
                              hipStream_t s) {
-  const bool pool_on = mode == CSA2_FULL && pool_size > 0;
+  const bool full = mode == CSA2_FULL;
+  const bool pool_on = full && pool_size > 0;
   Layout L = layout(ws, mode, R, H, max_visible, pool_stride, pool_size);
   const int64_t nq = (int64_t)R * H * kIdxDim;
-  const int64_t nhist = (int64_t)R * kHistWords * (pool_on ? 2 : 1);
+  const int64_t nhist = full ? (int64_t)R * kD1 * 2 : 0;
   hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(std::max(nq, nhist), 256))), dim3(256),
-                     0, s, idx_q, q_dtype, nq, L.w.qf, L.w.hist, nhist);
+                     0, s, idx_q, q_dtype, R, H, L.qf, L.hist, nhist);
 
-  // scoring
-  const int64_t n = (mode == CSA2_FULL) ? max_visible : pool_stride;
+  const int64_t n = full ? max_visible : pool_stride;
   if (n > 0) {
-    const dim3 grid((unsigned)ceil_div(n, kScanChunk), (unsigned)R);
-    auto& ev = profile_events(mode == CSA2_FULL ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
-    if (ev.start) hipEventRecord(ev.start, s);
-    const TopkWorkspace& w = L.w;
+    ScoreArgs sa{};
+    sa.H = H;
+    sa.idx_k = idx_k;
+    sa.row_start = row_start;
+    sa.row_visible = row_visible;
+    sa.max_visible = max_visible;
+    sa.pool = pool;
+    sa.pool_len = pool_len;
+    sa.pool_stride = pool_stride;
+    sa.scores = L.scores;
+    sa.n_pad = L.n_pad;
+    sa.bmax = L.bmax;
+    sa.nb_pad = L.nb_pad;
+    sa.hist_s = L.hist;
+    sa.hist_b = L.hist + (size_t)R * kD1;
+    sa.tiles_per_wg = full ? kFullTilesPerWG : 1;
+    const dim3 grid((unsigned)ceil_div(n, (int64_t)256 * sa.tiles_per_wg), (unsigned)R);
+    auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
+    if (ev.start) (void)hipEventRecord(ev.start, s);
     if (k_dtype == CSA2_BF16) {
-      if (pool_on)
-        dispatch_heads<CSA2_BF16, true>(H, mode, grid, s, w.qf, idx_k, row_start, row_visible, max_visible, pool,
-                                        pool_len, pool_stride, w, L.hist_b);
-      else
-        dispatch_heads<CSA2_BF16, false>(H, mode, grid, s, w.qf, idx_k, row_start, row_visible, max_visible, pool,
-                                         pool_len, pool_stride, w, L.hist_b);
+      if (!full) dispatch_heads<CSA2_BF16, true, false>(H, sa, L.qf, grid, s);
+      else if (pool_on) dispatch_heads<CSA2_BF16, false, true>(H, sa, L.qf, grid, s);
+      else dispatch_heads<CSA2_BF16, false, false>(H, sa, L.qf, grid, s);
     } else {
-      if (pool_on)
-        dispatch_heads<CSA2_F32, true>(H, mode, grid, s, w.qf, idx_k, row_start, row_visible, max_visible, pool,
-                                       pool_len, pool_stride, w, L.hist_b);
-      else
-        dispatch_heads<CSA2_F32, false>(H, mode, grid, s, w.qf, idx_k, row_start, row_visible, max_visible, pool,
-                                        pool_len, pool_stride, w, L.hist_b);
+      if (!full) dispatch_heads<CSA2_F32, true, false>(H, sa, L.qf, grid, s);
+      else if (pool_on) dispatch_heads<CSA2_F32, false, true>(H, sa, L.qf, grid, s);
+      else dispatch_heads<CSA2_F32, false, false>(H, sa, L.qf, grid, s);
     }
-    if (ev.stop) hipEventRecord(ev.stop, s);
+    if (ev.stop) (void)hipEventRecord(ev.stop, s);
   }
 
-  // selection
   SelArgs a{};
   a.mode = mode;
   a.row_visible = row_visible;
@@ -661,15 +661,15 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   a.out_pool_len = out_pool_len;
   a.pool_size = pool_size;
   a.nseries = pool_on ? 2 : 1;
-  a.s[0] = Series{L.w.scores, L.w.n_pad, L.w.hist, L.w.counts, L.state, L.w.chunks, top_k};
-  if (pool_on) a.s[1] = Series{L.w.bmax, L.w.nb_pad, L.hist_b, L.counts_b, L.state + (size_t)R * 4, L.w.bchunks,
-                               pool_size / kBlock};
-  const int gx = std::max(L.w.chunks, pool_on ? L.w.bchunks : 1);
-  const dim3 grid((unsigned)gx, (unsigned)R, (unsigned)a.nseries);
-  hipLaunchKernelGGL(k_radix_pass<2>, grid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_radix_pass<3>, grid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_select_count, grid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_select_write, grid, dim3(256), 0, s, a);
+  a.s[0] = Series{L.scores, L.n_pad, L.hist, L.cand_key[0], L.cand_pos[0], L.counts[0], L.nsub, top_k};
+  if (pool_on)
+    a.s[1] = Series{L.bmax, L.nb_pad, L.hist + (size_t)R * kD1, L.cand_key[1], L.cand_pos[1], L.counts[1], L.nbsub,
+                    pool_size / kBlock};
+  if (full) {
+    const int gx = (int)ceil_div(std::max(L.nsub, pool_on ? L.nbsub : 1), 4);
+    hipLaunchKernelGGL(k_collect, dim3((unsigned)gx, (unsigned)R, (unsigned)a.nseries), dim3(kThreads), 0, s, a);
+  }
+  hipLaunchKernelGGL(k_finalize, dim3((unsigned)R, (unsigned)a.nseries), dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -100,12 +100,12 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t n, int64_t stride
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)ceil_div(n, 8)), block(256);
   auto& ev = profile_events(CSA2_KERNEL_QUANT);
-  if (ev.start) hipEventRecord(ev.start, s);
+  if (ev.start) (void)hipEventRecord(ev.start, s);
   if (x_dtype == CSA2_F32)
     hipLaunchKernelGGL(k_quant_fp4<CSA2_F32>, grid, block, 0, s, x, n, stride, dst_rows, codes, scales, cap);
   else
     hipLaunchKernelGGL(k_quant_fp4<CSA2_BF16>, grid, block, 0, s, x, n, stride, dst_rows, codes, scales, cap);
-  if (ev.stop) hipEventRecord(ev.stop, s);
+  if (ev.stop) (void)hipEventRecord(ev.stop, s);
   return hipGetLastError();
 }
 

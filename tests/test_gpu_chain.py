@@ -1,0 +1,138 @@
+"""GPU parity of whole layer-mode chains (Full -> Reindex -> Reuse) against the
+CPU oracle at oracle-sized shapes drawn from the workload generators, and
+HIP-graph replay of a chain step against eager execution."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gpu_util import DEV, check_attention, dev, say
+from sparse_attention_fp4_e4m3_amd import Cache, LayerChain, LayerSpec, csa2
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_dev(a, kind):
+    if kind == "bf16":
+        return torch.from_numpy(gen.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
+
+
+def _setup(w):
+    lens = gen.seq_lens(w)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    raw = [gen.kv_rows(w, b, 0, int(lens[b])) for b in range(w.B)]
+    ik = [gen.idx_k_rows(w, b, 0, int(lens[b])) for b in range(w.B)]
+    x = np.concatenate(raw)
+    codes = torch.empty(len(x), 256, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(len(x), 32, dtype=torch.uint8, device=DEV)
+    csa2.quantize_kv_fp4(torch.from_numpy(x).to(DEV), codes, scales)
+    cache = Cache(codes, scales, _to_dev(np.concatenate(ik), w.idx_dtype), dev(starts),
+                  dev(lens.astype(np.int32)), int(lens.max()))
+    qs = [_to_dev(gen.attn_q(w, li), w.q_dtype) for li in range(len(w.layers))]
+    iqs = [_to_dev(gen.index_q(w, li), w.idx_dtype) if L.mode != "reuse" else None for li, L in enumerate(w.layers)]
+    return lens, starts, raw, ik, cache, qs, iqs
+
+
+def _oracle_chain(w, lens, raw, ik, b):
+    """The oracle's own quantization, selections and attention for sequence b."""
+    oc, os_ = oracle.quantize(raw[b])
+    n = int(lens[b])
+    res = []
+    pool = sel = None
+    for li, L in enumerate(w.layers):
+        q = gen.attn_q(w, li, b, b + 1)[0]
+        if L.mode == "full":
+            sel, pool, plen = oracle.full_select(gen.index_q(w, li, b, b + 1)[0], ik[b], n, w.K, L.pool_size)
+        elif L.mode == "reindex":
+            sel = oracle.reindex_select(gen.index_q(w, li, b, b + 1)[0], ik[b], pool, n, w.K)
+        o, lse = oracle.attention(q, oc, os_, sel, n, w.softmax_scale)
+        res.append((sel.copy(), None if pool is None else pool.copy(), o, lse))
+    return oc, os_, res
+
+
+def _run_and_compare(w, rows=None):
+    lens, starts, raw, ik, cache, qs, iqs = _setup(w)
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, cache.max_visible,
+                       qs[0].dtype, DEV)
+    chain.step(cache, qs, iqs, w.softmax_scale)
+    torch.cuda.synchronize()
+    gcodes, gscales = cache.kv_codes.cpu().numpy(), cache.kv_scales.cpu().numpy()
+    rows = range(w.B) if rows is None else rows
+    worst = 0.0
+    for b in rows:
+        oc, os_, ref = _oracle_chain(w, lens, raw, ik, b)
+        s0, n = int(starts[b]), int(lens[b])
+        assert np.array_equal(gcodes[s0:s0 + n], oc) and np.array_equal(gscales[s0:s0 + n], os_), "codes, seq %d" % b
+        for li, (sel, pool, o, lse) in enumerate(ref):
+            L = w.layers[li]
+            if L.mode != "reuse":
+                assert np.array_equal(chain.idx[li][b].cpu().numpy(), sel), "indices, layer %d seq %d" % (li, b)
+            if L.mode == "full" and L.pool_size:
+                gp, gl = chain.pool[li]
+                assert np.array_equal(gp[b].cpu().numpy(), pool), "pool, seq %d" % b
+            worst = max(worst, check_attention(chain.out[li][b:b + 1], chain.lse[li][b:b + 1], o[None], lse[None],
+                                               "%s layer %d (%s) seq %d" % (w.name, li, L.mode, b)))
+    return worst
+
+
+def test_tiny_decode_full_at_workload_size():
+    """The tiny decode workload at its own size: B=1, n=4096, fp32, K=256."""
+    say("max err %.3e" % _run_and_compare(gen.get("c1")))
+
+
+def test_layer_chain_128k_structure_scaled():
+    """Full (pool) -> 2 x Reindex -> 3 x Reuse, the 128K chain's structure at oracle size."""
+    w = gen.get("c3").scaled(B=3, n=24001, K=512, layers=(gen.Layer("full", 2048), gen.Layer("reindex"),
+                                                         gen.Layer("reindex"), gen.Layer("reuse"),
+                                                         gen.Layer("reuse"), gen.Layer("reuse")))
+    say("max err %.3e" % _run_and_compare(w))
+
+
+def test_decode_ragged_outliers_scaled():
+    """Variable lengths and x20 outlier channels, Full mode, at oracle size."""
+    w = gen.get("c2").scaled(B=6, n=20000, len_range=(7000, 20000), K=1024)
+    say("max err %.3e" % _run_and_compare(w))
+
+
+def test_long_decode_drift_scaled():
+    """Drifting keys, Full (pool) -> Reindex -> Reuse, at oracle size."""
+    w = gen.get("c5").scaled(B=2, n=65536, K=1024, layers=(gen.Layer("full", 4096), gen.Layer("reindex"),
+                                                          gen.Layer("reuse")))
+    say("max err %.3e" % _run_and_compare(w))
+
+
+def test_graph_replay_matches_eager():
+    w = gen.get("c3").scaled(B=4, n=30000, K=512, layers=(gen.Layer("full", 2048), gen.Layer("reindex"),
+                                                         gen.Layer("reuse")))
+    lens, starts, raw, ik, cache, qs, iqs = _setup(w)
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, cache.max_visible,
+                       qs[0].dtype, DEV)
+    new_rows = dev((starts + lens - 1).astype(np.int64))
+    new_kv = torch.from_numpy(np.stack([r[-1] for r in raw])).to(DEV)
+
+    def step():
+        chain.step(cache, qs, iqs, w.softmax_scale, new_kv=new_kv, new_kv_rows=new_rows)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in chain.out + chain.lse + [i for i in chain.idx if i is not None]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in chain.out + chain.lse:
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = chain.out + chain.lse + [i for i in chain.idx if i is not None]
+        for a, b in zip(got, eager):
+            assert torch.equal(a, b), "replay %d differs from eager" % rep
