@@ -12,23 +12,24 @@
 // Probabilities are rounded to fp16 for the PV product and the row sums add
 // up those same rounded values.
 //
-// Work split.  A workgroup (4 waves) owns one (row, head group of up to 64
-// heads, key split) and walks its keys in steps of 128:
-//  * QK^T, keys split across waves: wave w takes keys [32w, 32w+32) of the
-//    step and all heads; it loads its keys' 288-byte rows straight from HBM
-//    into registers (prefetched one step ahead) and dequantizes them into
-//    the A operand (key rows); queries sit in LDS as the B operand.  The
-//    result S^T has each lane holding 8 keys of one head, so the running max
-//    and sums need only two cross-lane steps.
-//  * softmax: per-wave maxima and sums meet in LDS; probabilities go to LDS
-//    as fp16 [head][key].
+// Work split.  A workgroup (8 waves, two per SIMD so that one wave's memory
+// and LDS latency overlaps the other's math) owns one (row, head group of up
+// to 64 heads, key split) and walks its keys in steps of 128:
+//  * QK^T, keys split across waves: wave w takes keys [16w, 16w+16) of the
+//    step and every head of the group.  Its lanes load their keys' 288-byte
+//    rows straight from HBM into registers (prefetched one step ahead) and
+//    dequantize them into the A operand (key rows); queries sit in LDS as
+//    the B operand.  The result S^T gives each lane 4 keys of one head.
+//  * softmax: per-wave maxima and sums meet in LDS.  The reference maximum
+//    of a head only moves when the new maximum exceeds it by more than 2^8,
+//    so the running output is rarely rescaled; the final division by the
+//    same-reference sum makes the result independent of that choice.
 //  * PV, output channels split across waves: wave w produces channels
-//    [128w, 128w+128) of every head, reading the raw codes of all 128 keys
-//    from LDS and re-pairing nibbles of neighbouring keys so that each
-//    packed fp16 pair holds two keys of one channel (the K-contiguous layout
-//    the B operand needs).
-// Each FP4 element is dequantized once per workgroup for QK^T and once for
-// PV; every dequantized value feeds all heads of the group.
+//    [64w, 64w+64) of every head from the raw codes of all 128 keys staged in
+//    LDS, re-pairing nibbles of neighbouring keys so that each packed fp16
+//    pair holds two keys of one channel (the K-contiguous B operand layout).
+// Every FP4 element is dequantized once for QK^T and once for PV per
+// workgroup, and each dequantized value feeds every head of the group.
 #include "csa2_common.h"
 
 #ifndef CSA2_HW_CVT
@@ -38,14 +39,16 @@
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kStep = 128;           // keys per step (32 per wave)
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kStep = 128;           // keys per step (16 per wave)
 constexpr int kCsStride = 272;       // bytes per staged code row (256 + 16 pad)
 constexpr int kScStride = 136;       // fp16 per staged scale row (128 keys + 8 pad)
 constexpr int kPStride = 136;        // fp16 per probability row
 constexpr int kQStride = 520;        // fp16 per query row (512 + 8 pad)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;        // log2 headroom before the reference maximum moves
 
 __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ half2v bits_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
@@ -87,8 +90,6 @@ __device__ __forceinline__ half2v e4m3x2_to_h2(uint32_t w) {
 #endif
 }
 
-__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
-
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -112,9 +113,9 @@ struct AttnArgs {
   float* lse;
   int splits;
   int keys_per_split;    // multiple of kStep
-  float* ws_o;           // [R, Hq, splits, 512]
-  float* ws_m;           // [R, Hq, splits]
-  float* ws_l;           // [R, Hq, splits]
+  float* ws_o;           // [R, Hq, splits, 512] split outputs, normalized
+  float* ws_m;           // [R, Hq, splits] reference maxima (log2 units)
+  float* ws_l;           // [R, Hq, splits] sums
 };
 
 template <int NHT, bool SPLITQ>
@@ -124,58 +125,46 @@ struct Smem {
   uint8_t cs[kStep * kCsStride];
   _Float16 sct[kGroups * kScStride];
   _Float16 p[16 * NHT * kPStride];
-  float red_max[4][64];
-  float red_sum[4][64];
+  float red_max[kWaves][64];
+  float red_sum[kWaves][64];
   float alpha[64];
   float lfin[64];
   float mfin[64];
 };
 
 struct Raw {
-  u32x4 c[2][4];  // [key tile][16-byte piece]: code bytes [64*q4, 64*q4+64) of the lane's key
-  u32x2 s[2];     // scale bytes [8*q4, 8*q4+8)
+  u32x4 c[4];  // code bytes [64*q4, 64*q4+64) of the lane's key
+  u32x2 s;     // scale bytes [8*q4, 8*q4+8)
 };
 
 // Branch-free gather: an invalid key loads row 0 of the cache (always
-// present) and is zeroed afterwards, so every load is issued unconditionally
-// and the compiler can keep them all in flight.
-__device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int64_t rs, int vis, int kpos0, int kend,
-                                         const int32_t (&j)[2], uint32_t (&valid)[2], int lane) {
-  const int m = lane & 15, q4 = lane >> 4;
+// present) and is zeroed before use, so every load is issued unconditionally
+// and the compiler keeps them all in flight.
+__device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int64_t rs, int vis, int i, int kend, int32_t j,
+                                         uint32_t& valid, int q4) {
+  const bool ok = i < kend && j >= 0 && j < vis;
+  valid = ok;
+  const int64_t row = ok ? rs + j : 0;
+  const u32x4* pc = reinterpret_cast<const u32x4*>(a.codes + row * kCodeBytes + 64 * q4);
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int i = kpos0 + 16 * kt + m;
-    const bool ok = i < kend && j[kt] >= 0 && j[kt] < vis;
-    valid[kt] = ok;
-    const int64_t row = ok ? rs + j[kt] : 0;
-    const u32x4* pc = reinterpret_cast<const u32x4*>(a.codes + row * kCodeBytes + 64 * q4);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) R.c[kt][c] = __builtin_nontemporal_load(pc + c);
-    R.s[kt] = *reinterpret_cast<const u32x2*>(a.scales + row * kGroups + 8 * q4);
-  }
+  for (int c = 0; c < 4; ++c) R.c[c] = __builtin_nontemporal_load(pc + c);
+  R.s = *reinterpret_cast<const u32x2*>(a.scales + row * kGroups + 8 * q4);
 }
 
-__device__ __forceinline__ void mask_raw(Raw& R, const uint32_t (&valid)[2]) {
+__device__ __forceinline__ void mask_raw(Raw& R, uint32_t valid) {
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) R.c[kt][c][e] = valid[kt] ? R.c[kt][c][e] : 0u;
-    R.s[kt][0] = valid[kt] ? R.s[kt][0] : 0u;
-    R.s[kt][1] = valid[kt] ? R.s[kt][1] : 0u;
-  }
+    for (int e = 0; e < 4; ++e) R.c[c][e] = valid ? R.c[c][e] : 0u;
+  R.s[0] = valid ? R.s[0] : 0u;
+  R.s[1] = valid ? R.s[1] : 0u;
 }
 
-__device__ __forceinline__ void load_idx(int32_t (&j)[2], const AttnArgs& a, int r, int kpos0, int kend, int lane) {
-  const int m = lane & 15;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int i = kpos0 + 16 * kt + m;
-    const int ic = i < kend ? i : kend - 1;  // kend > kpos0 >= 0 whenever this is called
-    const int32_t v = a.idx[(int64_t)r * a.top_k + ic];
-    j[kt] = (i < kend) ? v : -1;
-  }
+// index of key slot i of row r (-1 past the split end); kend > kbeg >= 0
+__device__ __forceinline__ int32_t load_idx(const AttnArgs& a, int r, int i, int kend) {
+  const int ic = i < kend ? i : kend - 1;
+  const int32_t v = a.idx[(int64_t)r * a.top_k + ic];
+  return i < kend ? v : -1;
 }
 
 template <int NHT, bool SPLITQ, int QDT>
@@ -183,6 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   Smem<NHT, SPLITQ>& sm = *reinterpret_cast<Smem<NHT, SPLITQ>*>(smem_raw);
   constexpr int HG = 16 * NHT;
+  constexpr int NQ = SPLITQ ? 2 : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
@@ -192,19 +182,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   const int nsteps = kend > kbeg ? (kend - kbeg + kStep - 1) / kStep : 0;
   const int vis = a.row_visible ? a.row_visible[r] : 0x7FFFFFFF;
   const int64_t rs = a.row_start[r];
+  const int myslot = 16 * w + n16;  // this lane's key within a step (QK^T role)
 
-  // ---- prologue: first step's keys in flight, queries to LDS
-  int32_t jcur[2], jnext[2];
-  uint32_t vcur[2], vnext[2];
-  Raw cur, nxt;
+  // ---- prologue: indices of steps 0 and 1, the keys of step 0 in flight, queries to LDS
+  int32_t jnext = -1;
+  uint32_t vA = 0, vB = 0;
+  Raw bufA, bufB;
   if (nsteps > 0) {
-    load_idx(jcur, a, r, min(kbeg + 32 * w, kend - 1), kend, lane);
-    if (kbeg + 32 * w >= kend) jcur[0] = jcur[1] = -1;
-    load_raw(cur, a, rs, vis, kbeg + 32 * w, kend, jcur, vcur, lane);
-  }
-  if (nsteps > 1) {
-    load_idx(jnext, a, r, min(kbeg + kStep + 32 * w, kend - 1), kend, lane);
-    if (kbeg + kStep + 32 * w >= kend) jnext[0] = jnext[1] = -1;
+    const int32_t j0 = load_idx(a, r, kbeg + myslot, kend);
+    if (nsteps > 1) jnext = load_idx(a, r, kbeg + kStep + myslot, kend);
+    load_raw(bufA, a, rs, vis, kbeg + myslot, kend, j0, vA, q4);
   }
   {
     // HG heads x 512 channels in 16-byte pieces; all loads issued before any conversion
@@ -252,84 +239,70 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  floatx4 O[NHT][8];
+  floatx4 O[NHT][4];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mrun[NHT], lrun[NHT];
+    for (int t = 0; t < 4; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mref[NHT], lrun[NHT];  // per head 16*ht + n16 (softmax role), replicated over q4
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
-    mrun[ht] = -INFINITY;
+    mref[ht] = -INFINITY;
     lrun[ht] = 0.0f;
   }
 
-  for (int st = 0; st < nsteps; ++st) {
+  // One step over keys [kstep0, kstep0+128) held in `cur`; at its start the
+  // gather of the next step is issued into `nxt` (a whole step ahead) and the
+  // indices of the step after that are loaded.
+  auto step = [&](int st, Raw& cur, uint32_t vcur, Raw& nxt, uint32_t& vnxt) {
     const int kstep0 = kbeg + st * kStep;
-    mask_raw(cur, vcur);
-    // scale bytes of this lane's two keys -> fp16 (groups 8*q4 .. 8*q4+7)
-    half2v sc[2][4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sc[kt][0] = e4m3x2_to_h2<false>(cur.s[kt][0]);
-      sc[kt][1] = e4m3x2_to_h2<true>(cur.s[kt][0]);
-      sc[kt][2] = e4m3x2_to_h2<false>(cur.s[kt][1]);
-      sc[kt][3] = e4m3x2_to_h2<true>(cur.s[kt][1]);
+    if (st + 1 < nsteps) {
+      load_raw(nxt, a, rs, vis, kstep0 + kStep + myslot, kend, jnext, vnxt, q4);
+      if (st + 2 < nsteps) jnext = load_idx(a, r, kstep0 + 2 * kStep + myslot, kend);
     }
+    mask_raw(cur, vcur);
+    // scale bytes of groups 8*q4 .. 8*q4+7 -> fp16
+    half2v sc[4];
+    sc[0] = e4m3x2_to_h2<false>(cur.s[0]);
+    sc[1] = e4m3x2_to_h2<true>(cur.s[0]);
+    sc[2] = e4m3x2_to_h2<false>(cur.s[1]);
+    sc[3] = e4m3x2_to_h2<true>(cur.s[1]);
 
-    // ---- QK^T: S^T[key][head] for this wave's 32 keys
-    floatx4 S[2][NHT];
+    // ---- QK^T: S^T[key][head] for this wave's 16 keys
+    floatx4 S[NHT];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < NHT; ++ht) S[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      // K-step ks covers channels 128*q4 + 8*ks .. +7 (the same mapping on both operands)
-      half8 bq[NHT * (SPLITQ ? 2 : 1)];
+      // K-step ks covers channels 128*q4 + 8*ks .. +7 on both operands
+      half8 bq[NHT * NQ];
 #pragma unroll
-      for (int ht = 0; ht < NHT * (SPLITQ ? 2 : 1); ++ht)
+      for (int ht = 0; ht < NHT * NQ; ++ht)
         bq[ht] = *reinterpret_cast<const half8*>(&sm.q[(16 * ht + n16) * kQStride + 128 * q4 + 8 * ks]);
+      const uint32_t word = cur.c[ks >> 2][ks & 3];
+      const half2v s1 = sc[ks >> 2];
+      const half2v ss = (ks & 2) ? half2v{s1[1], s1[1]} : half2v{s1[0], s1[0]};
+      const half8 av = cat4(fp4x2_to_h2<0>(word) * ss, fp4x2_to_h2<1>(word) * ss, fp4x2_to_h2<2>(word) * ss,
+                            fp4x2_to_h2<3>(word) * ss);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const uint32_t word = cur.c[kt][ks >> 2][ks & 3];
-        const half2v s1 = sc[kt][ks >> 2];
-        const half2v ss = (ks & 2) ? half2v{s1[1], s1[1]} : half2v{s1[0], s1[0]};
-        const half8 av = cat4(fp4x2_to_h2<0>(word) * ss, fp4x2_to_h2<1>(word) * ss, fp4x2_to_h2<2>(word) * ss,
-                              fp4x2_to_h2<3>(word) * ss);
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-          S[kt][ht] = mfma(av, bq[ht], S[kt][ht]);
-          if (SPLITQ) S[kt][ht] = mfma(av, bq[NHT + ht], S[kt][ht]);
-        }
+      for (int ht = 0; ht < NHT; ++ht) {
+        S[ht] = mfma(av, bq[ht], S[ht]);
+        if (SPLITQ) S[ht] = mfma(av, bq[NHT + ht], S[ht]);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep dequant of later K-steps from piling up registers
+      __builtin_amdgcn_sched_barrier(0);  // bound the live query fragments to one K-step
     }
 
-    // ---- prefetch the next step (registers), its indices one step further
-    if (st + 1 < nsteps) {
-      load_raw(nxt, a, rs, vis, kstep0 + kStep + 32 * w, kend, jnext, vnext, lane);
-      if (st + 2 < nsteps) {
-        load_idx(jnext, a, r, min(kstep0 + 2 * kStep + 32 * w, kend - 1), kend, lane);
-        if (kstep0 + 2 * kStep + 32 * w >= kend) jnext[0] = jnext[1] = -1;
-      }
-    }
-
-    // ---- softmax, part 1: scaled logits, masked, per-wave max per head
-    const unsigned long long vm0 = __ballot(vcur[0]), vm1 = __ballot(vcur[1]);
+    // ---- softmax, part 1: scaled logits, masked, per-wave maximum per head
+    const unsigned long long vm = __ballot(vcur);
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const unsigned long long vm = kt ? vm1 : vm0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = (vm >> (4 * q4 + i)) & 1ull;
-          const float z = ok ? S[kt][ht][i] * a.c2 : -INFINITY;
-          S[kt][ht][i] = z;
-          mx = fmaxf(mx, z);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (vm >> (4 * q4 + i)) & 1ull;
+        const float z = ok ? S[ht][i] * a.c2 : -INFINITY;
+        S[ht][i] = z;
+        mx = fmaxf(mx, z);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -339,39 +312,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 
     // ---- stage this step's raw codes and fp16 scales for PV
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = 32 * w + 16 * kt + n16;
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&sm.cs[myslot * kCsStride + 64 * q4 + 16 * c]) = cur.c[c];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&sm.cs[key * kCsStride + 64 * q4 + 16 * c]) = cur.c[kt][c];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        sm.sct[(8 * q4 + 2 * g) * kScStride + key] = sc[kt][g][0];
-        sm.sct[(8 * q4 + 2 * g + 1) * kScStride + key] = sc[kt][g][1];
-      }
+    for (int g = 0; g < 4; ++g) {
+      sm.sct[(8 * q4 + 2 * g) * kScStride + myslot] = sc[g][0];
+      sm.sct[(8 * q4 + 2 * g + 1) * kScStride + myslot] = sc[g][1];
     }
 
-    // ---- softmax, part 2: running max, probabilities (fp16), sums
+    // ---- softmax, part 2: reference maximum, probabilities (fp16), sums
     float alpha[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
-      const float mstep = fmaxf(fmaxf(sm.red_max[0][h], sm.red_max[1][h]), fmaxf(sm.red_max[2][h], sm.red_max[3][h]));
-      const float mnew = fmaxf(mrun[ht], mstep);
+      float mstep = sm.red_max[0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) mstep = fmaxf(mstep, sm.red_max[ww][h]);
+      const float mnew = (mstep > mref[ht] + kLazy) ? mstep : mref[ht];
       const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
-      alpha[ht] = __builtin_amdgcn_exp2f(mrun[ht] - muse);
-      mrun[ht] = mnew;
+      alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
+      mref[ht] = mnew;
+      _Float16 p[4];
       float sum = 0.0f;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        _Float16 p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = (_Float16)__builtin_amdgcn_exp2f(S[kt][ht][i] - muse);
-          sum += (float)p[i];
-        }
-        *reinterpret_cast<u32x2*>(&sm.p[h * kPStride + 32 * w + 16 * kt + 4 * q4]) =
-            u32x2{h2_bits(half2v{p[0], p[1]}), h2_bits(half2v{p[2], p[3]})};
+      for (int i = 0; i < 4; ++i) {
+        p[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
+        sum += (float)p[i];
       }
+      *reinterpret_cast<u32x2*>(&sm.p[h * kPStride + 16 * w + 4 * q4]) =
+          u32x2{h2_bits(half2v{p[0], p[1]}), h2_bits(half2v{p[2], p[3]})};
       sum += __shfl_xor(sum, 16, 64);
       sum += __shfl_xor(sum, 32, 64);
       if (q4 == 0) {
@@ -384,11 +352,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
-      lrun[ht] = lrun[ht] * alpha[ht] + (((sm.red_sum[0][h] + sm.red_sum[1][h]) + sm.red_sum[2][h]) + sm.red_sum[3][h]);
+      float add = sm.red_sum[0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) add += sm.red_sum[ww][h];
+      lrun[ht] = lrun[ht] * alpha[ht] + add;
     }
 
-    // ---- PV: channels [128w, 128w+128) of every head.  Rescale the running
-    // output only when some head's maximum moved (O is still zero on step 0).
+    // ---- PV: channels [64w, 64w+64) of every head; rescale only when a reference moved
     if (st > 0) {
       float al[NHT][4];
       bool moved = false;
@@ -405,51 +375,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) O[ht][t][i] *= al[ht][i];
+            for (int t = 0; t < 4; ++t) O[ht][t][i] *= al[ht][i];
       }
     }
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int key0 = 32 * kc + 8 * q4;  // this lane's 8 keys (slots 0..7)
+      // channels 64w + 4*n16 + {0..3}: 16 bits of codes per key
       uint32_t W[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        W[k] = *reinterpret_cast<const uint32_t*>(&sm.cs[(key0 + k) * kCsStride + 64 * w + 4 * n16]);
-      const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[(8 * w + (n16 >> 1)) * kScStride + key0]);
-      uint32_t Bw[8][4];
+        W[k] = *reinterpret_cast<const uint16_t*>(&sm.cs[(key0 + k) * kCsStride + 32 * w + 2 * n16]);
+      const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[(4 * w + (n16 >> 2)) * kScStride + key0]);
+      uint32_t Bw[4][4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        // E: byte b = channel 2b of keys (2p, 2p+1); D: channel 2b+1 of the same keys
-        const uint32_t E = bfi(0x0F0F0F0Fu, W[2 * p], W[2 * p + 1] << 4);
-        const uint32_t D = bfi(0x0F0F0F0Fu, W[2 * p] >> 4, W[2 * p + 1]);
+        // bytes of X: (keys 2p, 2p+1) of channels +0, +2, +1, +3
+        const uint32_t wa = W[2 * p], wb = W[2 * p + 1];
+        const uint32_t E = (wa & 0x0F0Fu) | ((wb & 0x0F0Fu) << 4);
+        const uint32_t D = ((wa >> 4) & 0x0F0Fu) | (wb & 0xF0F0u);
+        const uint32_t X = E | (D << 16);
         const half2v sp = bits_h2(spw[p]);
-        Bw[0][p] = h2_bits(fp4x2_to_h2<0>(E) * sp);
-        Bw[2][p] = h2_bits(fp4x2_to_h2<1>(E) * sp);
-        Bw[4][p] = h2_bits(fp4x2_to_h2<2>(E) * sp);
-        Bw[6][p] = h2_bits(fp4x2_to_h2<3>(E) * sp);
-        Bw[1][p] = h2_bits(fp4x2_to_h2<0>(D) * sp);
-        Bw[3][p] = h2_bits(fp4x2_to_h2<1>(D) * sp);
-        Bw[5][p] = h2_bits(fp4x2_to_h2<2>(D) * sp);
-        Bw[7][p] = h2_bits(fp4x2_to_h2<3>(D) * sp);
+        Bw[0][p] = h2_bits(fp4x2_to_h2<0>(X) * sp);
+        Bw[2][p] = h2_bits(fp4x2_to_h2<1>(X) * sp);
+        Bw[1][p] = h2_bits(fp4x2_to_h2<2>(X) * sp);
+        Bw[3][p] = h2_bits(fp4x2_to_h2<3>(X) * sp);
       }
-      half8 B[8];
+      half8 B[4];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) B[t] = __builtin_bit_cast(half8, u32x4{Bw[t][0], Bw[t][1], Bw[t][2], Bw[t][3]});
+      for (int t = 0; t < 4; ++t) B[t] = __builtin_bit_cast(half8, u32x4{Bw[t][0], Bw[t][1], Bw[t][2], Bw[t][3]});
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         const half8 av = *reinterpret_cast<const half8*>(&sm.p[(16 * ht + n16) * kPStride + key0]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) O[ht][t] = mfma(av, B[t], O[ht][t]);
+        for (int t = 0; t < 4; ++t) O[ht][t] = mfma(av, B[t], O[ht][t]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // rotate the prefetch registers
-    if (st + 1 < nsteps) {
-      cur = nxt;
-      vcur[0] = vnext[0];
-      vcur[1] = vnext[1];
-    }
+  };
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, bufA, vA, bufB, vB);
+    if (st + 1 < nsteps) step(st + 1, bufB, vB, bufA, vA);
   }
 
   // ---- epilogue
@@ -457,43 +424,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       sm.lfin[16 * ht + n16] = lrun[ht];
-      sm.mfin[16 * ht + n16] = mrun[ht];
+      sm.mfin[16 * ht + n16] = mref[ht];
     }
   }
   __syncthreads();
   const int64_t rowh = (int64_t)r * a.Hq + h0;
+  const int ch = 64 * w + 4 * n16;
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 16 * ht + 4 * q4 + i;
-      const int ch = 128 * w + 8 * n16;
       const float L = sm.lfin[h];
-      if (a.splits == 1) {
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        float v[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] = O[ht][t][i] * inv;
-        if (a.out_dtype == CSA2_F32) {
-          float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch);
-          o[0] = make_float4(v[0], v[1], v[2], v[3]);
-          o[1] = make_float4(v[4], v[5], v[6], v[7]);
-        } else {
-          uint32_t pk[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
-            lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
-            hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-            pk[k] = lo | (hi << 16);
-          }
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + ch) =
-              make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        }
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      const float v0 = O[ht][0][i] * inv, v1 = O[ht][1][i] * inv, v2 = O[ht][2][i] * inv, v3 = O[ht][3][i] * inv;
+      if (a.splits > 1) {
+        *reinterpret_cast<float4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch) = make_float4(v0, v1, v2, v3);
+      } else if (a.out_dtype == CSA2_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch) = make_float4(v0, v1, v2, v3);
       } else {
-        float4* o = reinterpret_cast<float4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch);
-        o[0] = make_float4(O[ht][0][i], O[ht][1][i], O[ht][2][i], O[ht][3][i]);
-        o[1] = make_float4(O[ht][4][i], O[ht][5][i], O[ht][6][i], O[ht][7][i]);
+        const float v[4] = {v0, v1, v2, v3};
+        uint32_t pk[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+          lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+          hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+          pk[k] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + ch) = make_uint2(pk[0], pk[1]);
       }
     }
   }
@@ -502,9 +461,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
       if (a.splits == 1) {
-        if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mrun[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
+        if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
       } else {
-        a.ws_m[(rowh + h) * a.splits + split] = mrun[ht];
+        a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
         a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
       }
     }
@@ -512,7 +471,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 }
 
 // one (row, head) per workgroup of 128 threads, 4 channels per thread;
-// splits merged in fixed order
+// splits merged in fixed order: o = sum_s w_s l_s o_s / sum_s w_s l_s
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_m,
                                                       const float* __restrict__ ws_l, int splits, void* out,
                                                       int out_dtype, float* lse) {
@@ -524,24 +483,23 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.0f;
   if (M != -INFINITY) {
-    // fixed split order; loads batched 8 at a time
     for (int s0 = 0; s0 < splits; s0 += 8) {
       float4 v[8];
-      float wgt[8];
+      float wl[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int s = s0 + k < splits ? s0 + k : splits - 1;
         v[k] = reinterpret_cast<const float4*>(ws_o + (rh * splits + s) * kDim)[threadIdx.x];
-        wgt[k] = __builtin_amdgcn_exp2f(m[s] - M);
+        wl[k] = __builtin_amdgcn_exp2f(m[s] - M) * l[s];
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if (s0 + k < splits) {
-          L += wgt[k] * l[s0 + k];
-          acc.x += wgt[k] * v[k].x;
-          acc.y += wgt[k] * v[k].y;
-          acc.z += wgt[k] * v[k].z;
-          acc.w += wgt[k] * v[k].w;
+          L += wl[k];
+          acc.x += wl[k] * v[k].x;
+          acc.y += wl[k] * v[k].y;
+          acc.z += wl[k] * v[k].z;
+          acc.w += wl[k] * v[k].w;
         }
       }
     }

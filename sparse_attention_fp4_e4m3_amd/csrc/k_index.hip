@@ -22,10 +22,11 @@
 //   k_collect   (Full) every wave compacts, in position order, the entries
 //               whose first digit reaches the threshold bin into its own
 //               slice of a candidate list (no block-wide syncs)
-//   k_finalize  one workgroup per row and series: exact threshold with two
-//               more radix digits over the candidates, then an ordered
-//               compaction: positions ascending, ties to the lower position,
-//               -1 padding; selected blocks expand into the pool
+//   k_finalize  one workgroup per row and series selects among the
+//               candidates (Full) or pool slots (Reindex), held in LDS
+// Exact selection: three radix digits give the K-th largest key, then an
+// ordered compaction writes positions ascending, ties to the lower position,
+// -1 padding; selected blocks expand into the pool.
 // Scores are non-negative fp32, so their bit patterns order like uint32;
 // invalid slots carry -1.0 (sign bit set) and are never counted.
 #include <algorithm>
@@ -333,6 +334,163 @@ __device__ __forceinline__ int series_len(const SelArgs& a, int series, int r) {
   return series == 0 ? v : (v + kBlock - 1) / kBlock;
 }
 
+// Exact selection for one (row, series) by one workgroup of NT threads.
+// Candidates: Full -> the per-slice lists written by k_collect, first packed
+// into one list; Reindex -> every pool slot.  The packed list lives in LDS
+// when it fits (cap entries), else in the second half of the candidate
+// arrays in global memory.  Three radix digits give the exact K-th largest
+// key T; an ordered compaction then writes positions ascending, taking ties
+// at T in candidate order (= ascending position), and pads with -1.
+template <int NT>
+__device__ void finalize_row(const SelArgs& a, int series, int r, uint32_t* hist, uint32_t* pre, uint32_t* red,
+                             uint32_t* lkey, int32_t* lpos, int cap) {
+  const Series& S = a.s[series];
+  const int n = series_len(a, series, r);
+  const bool full = a.mode == CSA2_FULL;
+  const int vis = clampv(a.row_visible[r], a.max_visible);
+  uint32_t M;
+  const uint32_t* keys;
+  const int32_t* posr;
+  if (full) {
+    const int nsub = (n + kSub - 1) / kSub;
+    uint32_t carry = 0;
+    for (int s0 = 0; s0 < nsub; s0 += NT) {
+      const int s = s0 + threadIdx.x;
+      const uint32_t c = (s < nsub) ? S.counts[(int64_t)r * S.nsub + s] : 0u;
+      uint32_t tot;
+      const uint32_t ex = block_excl_sum<NT>(c, red, &tot);
+      if (s < nsub) pre[s] = carry + ex;
+      carry += tot;
+    }
+    if (threadIdx.x == 0) pre[nsub] = carry;
+    __syncthreads();
+    M = pre[nsub];
+    const bool in_lds = M <= (uint32_t)cap;
+    const uint32_t* sk = reinterpret_cast<const uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride;
+    const int32_t* sp = S.cand_pos + (int64_t)r * 2 * S.stride;
+    uint32_t* dk = in_lds ? lkey : reinterpret_cast<uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride + S.stride;
+    int32_t* dp = in_lds ? lpos : S.cand_pos + (int64_t)r * 2 * S.stride + S.stride;
+#pragma unroll 4
+    for (uint32_t c = threadIdx.x; c < M; c += NT) {
+      int lo = 0, hi = nsub;  // largest s with pre[s] <= c
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= c) lo = mid;
+        else hi = mid;
+      }
+      const int64_t at = (int64_t)lo * kSub + (c - pre[lo]);
+      dk[c] = sk[at];
+      dp[c] = sp[at];
+    }
+    __syncthreads();
+    keys = dk;
+    posr = dp;
+  } else {
+    M = (uint32_t)n;
+    const uint32_t* sk = reinterpret_cast<const uint32_t*>(S.arr) + (int64_t)r * S.stride;
+    const int32_t* sp = a.pool + (int64_t)r * a.pool_stride;
+    if (M <= (uint32_t)cap) {
+#pragma unroll 4
+      for (uint32_t c = threadIdx.x; c < M; c += NT) {
+        lkey[c] = sk[c];
+        lpos[c] = sp[c];
+      }
+      __syncthreads();
+      keys = lkey;
+      posr = lpos;
+    } else {
+      keys = sk;
+      posr = sp;
+    }
+  }
+
+  // ---- exact threshold: three digits over the candidates
+  uint32_t K = (uint32_t)S.K;
+  uint32_t prefix = 0;  // resolved high bits
+  int shift_hi = 31;
+  bool all = false;
+  uint32_t need = 0;
+#pragma unroll 1
+  for (int lev = 0; lev < 3; ++lev) {
+    const int sh = lev == 0 ? kS1 : (lev == 1 ? kS2 : 0);
+    const int nb = lev == 0 ? kD1 : (lev == 1 ? kD2 : kD3);
+    for (int b = threadIdx.x; b < nb; b += NT) hist[b] = 0u;
+    __syncthreads();
+#pragma unroll 4
+    for (uint32_t i = threadIdx.x; i < M; i += NT) {
+      const uint32_t key = keys[i];
+      if (!(key >> 31) && (lev == 0 || (key >> shift_hi) == prefix)) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t above, total;
+    const int b = find_bin<NT>(hist, nb, K, &above, &total, red);
+    if (b < 0) {  // only at the first level: fewer than K valid candidates
+      all = true;
+      break;
+    }
+    prefix = (prefix << (shift_hi - sh)) | (uint32_t)b;
+    shift_hi = sh;
+    K -= above;
+    need = K;
+  }
+  const uint32_t T = prefix;  // the full 31-bit key of the K-th largest
+
+  // ---- ordered compaction: thread t owns candidates [t*per, (t+1)*per)
+  const uint32_t per = (M + NT - 1) / NT;
+  const uint32_t c0 = min(M, threadIdx.x * per), c1 = min(M, c0 + per);
+  uint32_t gt = 0, eq = 0;
+#pragma unroll 4
+  for (uint32_t c = c0; c < c1; ++c) {
+    const uint32_t key = keys[c];
+    gt += (!(key >> 31) && (all || key > T)) ? 1u : 0u;
+    eq += (!(key >> 31) && !all && key == T) ? 1u : 0u;
+  }
+  uint32_t tot_gt, tot_eq;
+  const uint32_t gt_before = block_excl_sum<NT>(gt, red, &tot_gt);
+  const uint32_t eq_before = block_excl_sum<NT>(eq, red, &tot_eq);
+  const uint32_t nsel = all ? tot_gt : (uint32_t)S.K;
+  uint32_t out = gt_before + (all ? 0u : min(eq_before, need));
+  uint32_t ties = eq_before;
+  bool last_block_kept = false;
+  for (uint32_t c = c0; c < c1; ++c) {
+    const uint32_t key = keys[c];
+    if (key >> 31) continue;
+    bool sel;
+    if (all || key > T) sel = true;
+    else if (key == T) sel = (ties++ < need);
+    else sel = false;
+    if (!sel || out >= nsel) continue;
+    const int32_t pos = posr[c];
+    if (series == 0) {
+      a.out_idx[(int64_t)r * S.K + out] = pos;
+    } else {
+      int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)out * kBlock;
+#pragma unroll
+      for (int m = 0; m < kBlock; ++m) o[m] = (pos * kBlock + m < vis) ? pos * kBlock + m : -1;
+      if (pos == n - 1) last_block_kept = true;
+    }
+    ++out;
+  }
+  // ---- padding and pool length
+  if (series == 0) {
+    int32_t* o = a.out_idx + (int64_t)r * S.K;
+    for (int i = (int)nsel + threadIdx.x; i < S.K; i += NT) o[i] = -1;
+  } else {
+    if (threadIdx.x == 0) red[20] = 0u;
+    __syncthreads();
+    if (last_block_kept) red[20] = 1u;
+    __syncthreads();
+    // the partial last block is the highest block, hence the last one written
+    int plen = (int)nsel * kBlock;
+    if (red[20] && (vis % kBlock) != 0) plen -= kBlock - (vis % kBlock);
+    int32_t* o = a.out_pool + (int64_t)r * a.pool_size;
+    for (int i = (int)nsel * kBlock + threadIdx.x; i < a.pool_size; i += NT) o[i] = -1;
+    if (threadIdx.x == 0) a.out_pool_len[r] = plen;
+  }
+}
+
+constexpr int kFinCap = 16384;  // candidates held in LDS by k_finalize
+
 // Full mode: each wave compacts its slice of kSub elements, keeping those
 // whose first digit is at least the threshold bin (all valid ones when the
 // row holds fewer than K).
@@ -379,146 +537,16 @@ __global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
   if (lane == 0) S.counts[(int64_t)r * S.nsub + sub] = cnt;
 }
 
-// One workgroup per (row, series): gather the candidates into one contiguous
-// list (Full), find the exact threshold with three radix digits, then the
-// ordered compaction into the outputs.
+// One workgroup per (row, series) runs the exact selection.
 __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
-  __shared__ uint32_t hist[kD1];
-  __shared__ uint32_t pre[1024 + 1];
-  __shared__ uint32_t red[32];
-  const int series = blockIdx.y, r = blockIdx.x;
-  if (series >= a.nseries) return;
-  const Series& S = a.s[series];
-  const int n = series_len(a, series, r);
-  const bool full = a.mode == CSA2_FULL;
-  const int vis = clampv(a.row_visible[r], a.max_visible);
-  const float* keys;
-  const int32_t* posr;
-  uint32_t M;
-  if (full) {
-    // slice s holds counts[s] candidates at [s*kSub, ...); pack them into the
-    // second half of the candidate arrays (rows are 2 * stride long)
-    const int nsub = (n + kSub - 1) / kSub;
-    uint32_t carry = 0;
-    for (int s0 = 0; s0 < nsub; s0 += kFinThreads) {
-      const int s = s0 + threadIdx.x;
-      const uint32_t c = (s < nsub) ? S.counts[(int64_t)r * S.nsub + s] : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_excl_sum<kFinThreads>(c, red, &tot);
-      if (s < nsub) pre[s] = carry + ex;
-      carry += tot;
-    }
-    if (threadIdx.x == 0) pre[nsub] = carry;
-    __syncthreads();
-    M = pre[nsub];
-    const float* sk = S.cand_key + (int64_t)r * 2 * S.stride;
-    const int32_t* sp = S.cand_pos + (int64_t)r * 2 * S.stride;
-    float* dk = S.cand_key + (int64_t)r * 2 * S.stride + S.stride;
-    int32_t* dp = S.cand_pos + (int64_t)r * 2 * S.stride + S.stride;
-#pragma unroll 4
-    for (uint32_t c = threadIdx.x; c < M; c += kFinThreads) {
-      int lo = 0, hi = nsub;  // largest s with pre[s] <= c
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid] <= c) lo = mid;
-        else hi = mid;
-      }
-      const int64_t at = (int64_t)lo * kSub + (c - pre[lo]);
-      dk[c] = sk[at];
-      dp[c] = sp[at];
-    }
-    __syncthreads();
-    keys = dk;
-    posr = dp;
-  } else {
-    keys = S.arr + (int64_t)r * S.stride;
-    posr = a.pool + (int64_t)r * a.pool_stride;
-    M = (uint32_t)n;
-  }
-
-  // ---- exact threshold: three digits over the candidates
-  uint32_t K = (uint32_t)S.K;
-  uint32_t prefix = 0;  // resolved high bits
-  int shift_hi = 31;
-  bool all = false;
-  uint32_t need = 0;
-#pragma unroll 1
-  for (int lev = 0; lev < 3; ++lev) {
-    const int sh = lev == 0 ? kS1 : (lev == 1 ? kS2 : 0);
-    const int nb = lev == 0 ? kD1 : (lev == 1 ? kD2 : kD3);
-    for (int b = threadIdx.x; b < nb; b += kFinThreads) hist[b] = 0u;
-    __syncthreads();
-#pragma unroll 4
-    for (uint32_t i = threadIdx.x; i < M; i += kFinThreads) {
-      const uint32_t key = __float_as_uint(keys[i]);
-      if (!(key >> 31) && (lev == 0 || (key >> shift_hi) == prefix)) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    uint32_t above, total;
-    const int b = find_bin<kFinThreads>(hist, nb, K, &above, &total, red);
-    if (b < 0) {  // only at the first level: fewer than K valid candidates
-      all = true;
-      break;
-    }
-    prefix = (prefix << (shift_hi - sh)) | (uint32_t)b;
-    shift_hi = sh;
-    K -= above;
-    need = K;
-  }
-  const uint32_t T = prefix;  // the full 31-bit key of the K-th largest
-
-  // ---- ordered compaction: thread t owns candidates [t*per, (t+1)*per)
-  const uint32_t per = (M + kFinThreads - 1) / kFinThreads;
-  const uint32_t c0 = min(M, threadIdx.x * per), c1 = min(M, c0 + per);
-  uint32_t gt = 0, eq = 0;
-#pragma unroll 4
-  for (uint32_t c = c0; c < c1; ++c) {
-    const uint32_t key = __float_as_uint(keys[c]);
-    gt += (!(key >> 31) && (all || key > T)) ? 1u : 0u;
-    eq += (!(key >> 31) && !all && key == T) ? 1u : 0u;
-  }
-  uint32_t tot_gt, tot_eq;
-  const uint32_t gt_before = block_excl_sum<kFinThreads>(gt, red, &tot_gt);
-  const uint32_t eq_before = block_excl_sum<kFinThreads>(eq, red, &tot_eq);
-  const uint32_t nsel = all ? tot_gt : (uint32_t)S.K;
-  uint32_t out = gt_before + (all ? 0u : min(eq_before, need));
-  uint32_t ties = eq_before;
-  bool last_block_kept = false;
-  for (uint32_t c = c0; c < c1; ++c) {
-    const uint32_t key = __float_as_uint(keys[c]);
-    if (key >> 31) continue;
-    bool sel;
-    if (all || key > T) sel = true;
-    else if (key == T) sel = (ties++ < need);
-    else sel = false;
-    if (!sel || out >= nsel) continue;
-    const int32_t pos = posr[c];
-    if (series == 0) {
-      a.out_idx[(int64_t)r * S.K + out] = pos;
-    } else {
-      int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)out * kBlock;
-#pragma unroll
-      for (int m = 0; m < kBlock; ++m) o[m] = (pos * kBlock + m < vis) ? pos * kBlock + m : -1;
-      if (pos == n - 1) last_block_kept = true;
-    }
-    ++out;
-  }
-  // ---- padding and pool length
-  if (series == 0) {
-    int32_t* o = a.out_idx + (int64_t)r * S.K;
-    for (int i = (int)nsel + threadIdx.x; i < S.K; i += kFinThreads) o[i] = -1;
-  } else {
-    if (threadIdx.x == 0) red[20] = 0u;
-    __syncthreads();
-    if (last_block_kept) red[20] = 1u;
-    __syncthreads();
-    // the partial last block is the highest block, hence the last one written
-    int plen = (int)nsel * kBlock;
-    if (red[20] && (vis % kBlock) != 0) plen -= kBlock - (vis % kBlock);
-    int32_t* o = a.out_pool + (int64_t)r * a.pool_size;
-    for (int i = (int)nsel * kBlock + threadIdx.x; i < a.pool_size; i += kFinThreads) o[i] = -1;
-    if (threadIdx.x == 0) a.out_pool_len[r] = plen;
-  }
+  extern __shared__ __align__(16) uint32_t fsm[];
+  uint32_t* hist = fsm;                       // kD1
+  uint32_t* pre = hist + kD1;                 // 1025
+  uint32_t* red = pre + 1028;                 // 32
+  uint32_t* lkey = red + 32;                  // kFinCap
+  int32_t* lpos = reinterpret_cast<int32_t*>(lkey + kFinCap);
+  if ((int)blockIdx.y >= a.nseries) return;
+  finalize_row<kFinThreads>(a, blockIdx.y, blockIdx.x, hist, pre, red, lkey, lpos, kFinCap);
 }
 
 struct Carve {
@@ -534,7 +562,7 @@ struct Carve {
 
 struct Layout {
   float* qf;
-  uint32_t* hist;  // [2][R][kD1]
+  uint32_t* hist;  // [2][R][kD1] first-digit histograms
   float* scores;
   float* bmax;
   float* cand_key[2];
@@ -669,7 +697,14 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
     const int gx = (int)ceil_div(std::max(L.nsub, pool_on ? L.nbsub : 1), 4);
     hipLaunchKernelGGL(k_collect, dim3((unsigned)gx, (unsigned)R, (unsigned)a.nseries), dim3(kThreads), 0, s, a);
   }
-  hipLaunchKernelGGL(k_finalize, dim3((unsigned)R, (unsigned)a.nseries), dim3(kFinThreads), 0, s, a);
+  const size_t lds = ((size_t)kD1 + 1028 + 32 + 2 * (size_t)kFinCap) * 4;
+  static bool configured = false;
+  if (!configured) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_finalize), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    configured = true;
+  }
+  hipLaunchKernelGGL(k_finalize, dim3((unsigned)R, (unsigned)a.nseries), dim3(kFinThreads), lds, s, a);
   return hipGetLastError();
 }
 
