@@ -1,0 +1,133 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times, checked against the CPU oracle on sampled sequences/rows.
+
+For every sampled sequence the oracle regenerates the raw inputs from the
+seeded generators and computes, on its own: FP4 codes of every entry the
+check touches, the Full indexer scores over the whole visible context, the
+top-K, the hierarchical pool, Reindex selections and the attention of every
+layer.  Indices, pools and codes must match bit for bit; attention outputs
+within 2e-3 (row-normwise per head).
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import gen
+import oracle
+from gpu_util import DEV, check_attention, dev, say
+from sparse_attention_fp4_e4m3_amd import Cache, LayerChain, LayerSpec, csa2
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+
+def _chain_fullsize(name, sample):
+    w = gen.get(name)
+    lens = gen.seq_lens(w)
+    say("%s: building the FP4 cache (%d entries)" % (name, int(lens.sum())))
+    cache, starts = bench.build_cache(w, lens, DEV)
+    qs, iqs = bench.layer_inputs(w, DEV)
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, cache.max_visible,
+                       qs[0].dtype, DEV)
+    chain.step(cache, qs, iqs, w.softmax_scale)
+    torch.cuda.synchronize()
+    for b in sample:
+        n, s0 = int(lens[b]), int(starts[b])
+        say("%s: oracle for sequence %d (n=%d)" % (name, b, n))
+        ik = gen.idx_k_rows(w, b, 0, n)
+        raw = gen.kv_rows(w, b, 0, n)
+        pool = sel = None
+        touched = set()
+        ref = []
+        for li, L in enumerate(w.layers):
+            if L.mode == "full":
+                sel, pool, plen = oracle.full_select(gen.index_q(w, li, b, b + 1)[0], ik, n, w.K, L.pool_size)
+            elif L.mode == "reindex":
+                sel = oracle.reindex_select(gen.index_q(w, li, b, b + 1)[0], ik, pool, n, w.K)
+            ref.append((sel.copy(), None if pool is None else pool.copy()))
+            touched.update(int(j) for j in sel if j >= 0)
+        rng = np.random.default_rng(b)
+        rows = np.array(sorted(touched | set(rng.integers(0, n, 2000).tolist()) | {0, n - 1}), np.int64)
+        oc_rows, os_rows = oracle.quantize(raw[rows])
+        gc = cache.kv_codes[s0 + torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        gs = cache.kv_scales[s0 + torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        assert np.array_equal(gc, oc_rows) and np.array_equal(gs, os_rows), "codes differ, sequence %d" % b
+        # the oracle's own cache for the rows attention reads (others stay zero and are never selected)
+        oc = np.zeros((n, 256), np.uint8)
+        os_ = np.zeros((n, 32), np.uint8)
+        oc[rows], os_[rows] = oc_rows, os_rows
+        for li, L in enumerate(w.layers):
+            sel, pool = ref[li]
+            if L.mode != "reuse":
+                got = chain.idx[li][b].cpu().numpy()
+                assert np.array_equal(got, sel), "indices differ: layer %d sequence %d" % (li, b)
+            if L.mode == "full" and L.pool_size:
+                gp, gl = chain.pool[li]
+                assert np.array_equal(gp[b].cpu().numpy(), pool), "pool differs: sequence %d" % b
+            o, lse = oracle.attention(gen.attn_q(w, li, b, b + 1)[0], oc, os_, sel, n, w.softmax_scale)
+            check_attention(chain.out[li][b:b + 1], chain.lse[li][b:b + 1], o[None], lse[None],
+                            "%s layer %d (%s) seq %d" % (name, li, L.mode, b))
+
+
+def test_decode_full_32x_32k_64k():
+    _chain_fullsize("c2", sample=[0, 17, 31])
+
+
+def test_chain_128k_batch16():
+    _chain_fullsize("c3", sample=[0, 9])
+
+
+def test_long_decode_1m_batch4():
+    _chain_fullsize("c5", sample=[2])
+
+
+def test_prefill_4096_on_256k():
+    """4096 new tokens appended causally to 262,144 cached: row r sees [0, 262144 + r]."""
+    w = gen.get("c4")
+    T = w.prefill_tokens
+    P0 = w.n - T
+    lens = np.array([w.n], np.int64)
+    say("c4: building the FP4 cache of the %d cached tokens" % P0)
+    codes = torch.empty(w.n, 256, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(w.n, 32, dtype=torch.uint8, device=DEV)
+    for t0 in range(0, P0, 65536):
+        t1 = min(P0, t0 + 65536)
+        csa2.quantize_kv_fp4(torch.from_numpy(gen.kv_rows(w, 0, t0, t1)).to(DEV), codes[t0:t1], scales[t0:t1])
+    ik_all = gen.idx_k_rows(w, 0, 0, w.n)
+    idx_k = torch.from_numpy(gen.bf16_bits(ik_all).view(np.int16)).view(torch.bfloat16).to(DEV)
+    # the chunk writes its own KV first (quantize-on-write at rows P0..P0+T-1)
+    new = torch.from_numpy(gen.kv_rows(w, 0, P0, w.n)).to(DEV)
+    csa2.quantize_kv_fp4(new, codes, scales, dev(np.arange(P0, w.n, dtype=np.int64)))
+    starts = dev(np.zeros(T, np.int64))
+    vis = dev((P0 + 1 + np.arange(T)).astype(np.int32))
+    iq = bench.to_dev(gen.index_q(w, 0), w.idx_dtype, DEV)
+    q = bench.to_dev(gen.attn_q(w, 0), w.q_dtype, DEV)
+    ws = torch.empty(csa2.index_topk_workspace_size(csa2.FULL, T, w.H, w.n, 0, w.K, 0), dtype=torch.uint8, device=DEV)
+    idx = torch.empty(T, w.K, dtype=torch.int32, device=DEV)
+    csa2.index_topk(csa2.FULL, iq, idx_k, starts, vis, w.n, w.K, idx, ws)
+    del ws
+    out = torch.empty(T, w.Hq, 512, dtype=torch.float32, device=DEV)
+    lse = torch.empty(T, w.Hq, dtype=torch.float32, device=DEV)
+    aws = torch.empty(max(256, csa2.sparse_attn_workspace_size(T, w.Hq, csa2.BF16, w.K)), dtype=torch.uint8,
+                      device=DEV)
+    csa2.sparse_attn(q, codes, scales, starts, idx, out, w.softmax_scale, row_visible=vis, lse=lse, workspace=aws)
+    torch.cuda.synchronize()
+    raw = gen.kv_rows(w, 0, 0, w.n)
+    for r in [0, 1, 777, 2048, T - 1]:
+        say("c4: oracle for query row %d (sees %d entries)" % (r, P0 + r + 1))
+        nvis = P0 + r + 1
+        sel = oracle.topk(oracle.index_scores(gen.index_q(w, 0, r, r + 1)[0], ik_all[:nvis]), w.K)
+        assert np.array_equal(idx[r].cpu().numpy(), sel), "indices differ, row %d" % r
+        rows = np.array(sorted(set(int(j) for j in sel if j >= 0) | {P0 + r}), np.int64)
+        oc_rows, os_rows = oracle.quantize(raw[rows])
+        assert np.array_equal(codes[torch.from_numpy(rows).to(DEV)].cpu().numpy(), oc_rows)
+        assert np.array_equal(scales[torch.from_numpy(rows).to(DEV)].cpu().numpy(), os_rows)
+        oc = np.zeros((w.n, 256), np.uint8)
+        os_ = np.zeros((w.n, 32), np.uint8)
+        oc[rows], os_[rows] = oc_rows, os_rows
+        o, l = oracle.attention(gen.attn_q(w, 0, r, r + 1)[0], oc, os_, sel, nvis, w.softmax_scale)
+        check_attention(out[r:r + 1], lse[r:r + 1], o[None], l[None], "c4 row %d" % r)
+    # causality: no row selects a position it cannot see
+    idx_np = idx.cpu().numpy()
+    limit = (P0 + np.arange(T))[:, None]
+    assert np.all((idx_np == -1) | ((idx_np >= 0) & (idx_np <= limit)))
