@@ -10,8 +10,7 @@
 // run on fp16 MFMA (v_mfma_f32_16x16x32_f16, fp32 accumulate): bf16 queries
 // convert to fp16 exactly; fp32 queries are split into hi + lo fp16 halves.
 // Probabilities are rounded to fp16 for the PV product and the row sums add
-// up those same rounded values.  Split-K partial outputs are stored
-// normalized in fp16 (their magnitude is bounded by max |x_hat| <= 2688).
+// up those same rounded values.
 //
 // Work split.  A workgroup (8 waves, two per SIMD so that one wave's memory
 // and LDS latency overlaps the other's math) owns one (row, head group of up
@@ -114,7 +113,7 @@ struct AttnArgs {
   float* lse;
   int splits;
   int keys_per_split;    // multiple of kStep
-  _Float16* ws_o;        // [R, Hq, splits, 512] split outputs, normalized, fp16
+  float* ws_o;           // [R, Hq, splits, 512] split outputs, normalized
   float* ws_m;           // [R, Hq, splits] reference maxima (log2 units)
   float* ws_l;           // [R, Hq, splits] sums
 };
@@ -440,8 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       const float v0 = O[ht][0][i] * inv, v1 = O[ht][1][i] * inv, v2 = O[ht][2][i] * inv, v3 = O[ht][3][i] * inv;
       if (a.splits > 1) {
-        *reinterpret_cast<u32x2*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch) =
-            u32x2{h2_bits(half2v{(_Float16)v0, (_Float16)v1}), h2_bits(half2v{(_Float16)v2, (_Float16)v3})};
+        *reinterpret_cast<float4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch) = make_float4(v0, v1, v2, v3);
       } else if (a.out_dtype == CSA2_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch) = make_float4(v0, v1, v2, v3);
       } else {
@@ -474,7 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 
 // one (row, head) per workgroup of 128 threads, 4 channels per thread;
 // splits merged in fixed order: o = sum_s w_s l_s o_s / sum_s w_s l_s
-__global__ __launch_bounds__(128) void k_attn_combine(const _Float16* __restrict__ ws_o, const float* __restrict__ ws_m,
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_m,
                                                       const float* __restrict__ ws_l, int splits, void* out,
                                                       int out_dtype, float* lse) {
   const int64_t rh = blockIdx.x;
@@ -491,9 +489,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(const _Float16* __restrict
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int s = s0 + k < splits ? s0 + k : splits - 1;
-        const u32x2 hv = reinterpret_cast<const u32x2*>(ws_o + (rh * splits + s) * kDim)[threadIdx.x];
-        const half2v h01 = bits_h2(hv[0]), h23 = bits_h2(hv[1]);
-        v[k] = make_float4((float)h01[0], (float)h01[1], (float)h23[0], (float)h23[1]);
+        v[k] = reinterpret_cast<const float4*>(ws_o + (rh * splits + s) * kDim)[threadIdx.x];
         wl[k] = __builtin_amdgcn_exp2f(m[s] - M) * l[s];
       }
 #pragma unroll
@@ -572,7 +568,7 @@ size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k) {
   const Plan p = plan(R, Hq, q_dtype, top_k);
   if (p.splits <= 1) return 0;
   const size_t n = (size_t)R * Hq * p.splits;
-  return ((n * kDim * 2 + 255) & ~size_t(255)) + 2 * ((n * 4 + 255) & ~size_t(255));
+  return ((n * kDim * 4 + 255) & ~size_t(255)) + 2 * ((n * 4 + 255) & ~size_t(255));
 }
 
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
@@ -598,8 +594,8 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
   if (p.splits > 1) {
     const size_t n = (size_t)R * Hq * p.splits;
     char* b = static_cast<char*>(ws);
-    a.ws_o = reinterpret_cast<_Float16*>(b);
-    b += (n * kDim * 2 + 255) & ~size_t(255);
+    a.ws_o = reinterpret_cast<float*>(b);
+    b += (n * kDim * 4 + 255) & ~size_t(255);
     a.ws_m = reinterpret_cast<float*>(b);
     b += (n * 4 + 255) & ~size_t(255);
     a.ws_l = reinterpret_cast<float*>(b);
