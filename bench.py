@@ -133,8 +133,8 @@ def traffic_from_profiles(kernel_file):
 
 # ------------------------------------------------------------------ CPU oracle baseline
 
-def cpu_baseline(w, lens, sample_rows):
-    """One decode step of the same chain for `sample_rows` sequences, run by the CPU oracle."""
+def cpu_baseline(w, lens, sample_rows, reps):
+    """`reps` decode steps of the same chain for `sample_rows` sequences, run by the CPU oracle."""
     import oracle
 
     rows = list(range(min(sample_rows, w.B)))
@@ -148,7 +148,7 @@ def cpu_baseline(w, lens, sample_rows):
     iqs = [gen.index_q(w, li, 0, len(rows)) if L.mode != "reuse" else None for li, L in enumerate(w.layers)]
     new_kv = [gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b])) for b in rows]
     t0 = time.perf_counter()
-    for b in rows:
+    for b in [b for _ in range(reps) for b in rows]:
         (codes, scales), ik = caches[b]
         n = int(lens[b])
         c1, s1 = oracle.quantize(new_kv[b])  # the newest token, written by the first Full layer
@@ -162,10 +162,66 @@ def cpu_baseline(w, lens, sample_rows):
                 sel = oracle.reindex_select(iqs[li][b], ik, pool, n, w.K)
             oracle.attention(qs[li][b], codes, scales, sel, n, w.softmax_scale)
     dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d sequences, one full decode step of the %d-layer chain (quantize newest token, "
-                      "indexer scan over %d tokens, top-K, pool, Reindex, attention per layer); %.1f s wall"
-                      % (len(rows), w.B, len(w.layers), int(lens[0]), dt)}
+    return {"value": reps * len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d sequences x %d repetitions of one full decode step of the %d-layer chain (quantize "
+                      "newest token, indexer scan over %d tokens, top-K, pool, Reindex, attention per layer); "
+                      "%.1f s wall" % (len(rows), w.B, reps, len(w.layers), int(lens[0]), dt)}
+
+
+# ------------------------------------------------------------------ HIP events without a system fence
+
+_HIP = None
+
+
+def _hip_runtime():
+    """The HIP runtime library already loaded into this process (the one torch uses)."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        _HIP = ctypes.CDLL(path or "libamdhip64.so")
+        P = ctypes.c_void_p
+        _HIP.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+        _HIP.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        _HIP.hipEventDestroy.argtypes = [P]
+    return _HIP
+
+
+class HipEvent:
+    """A timing event created with hipEventDisableSystemFence, so that recording it
+    around a kernel does not add a system-scope cache flush to the measured span."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+
+        self._h = ctypes.c_void_p()
+        rc = _hip_runtime().hipEventCreateWithFlags(ctypes.byref(self._h), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+        self.cuda_event = self._h.value
+
+    def elapsed_time(self, other) -> float:
+        import ctypes
+
+        ms = ctypes.c_float()
+        rc = _hip_runtime().hipEventElapsedTime(ctypes.byref(ms), self._h, other._h)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
+
+    def __del__(self):
+        try:
+            _hip_runtime().hipEventDestroy(self._h)
+        except Exception:
+            pass
 
 
 # ------------------------------------------------------------------ main
@@ -176,9 +232,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5"])
-    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--cpu-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
+    ap.add_argument("--event-kind", default="nofence", choices=["nofence", "torch"],
+                    help="per-kernel timing events: created without a system fence, or torch's default")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -258,9 +317,12 @@ def main():
                 "attention": len(w.layers), "attention_combine": len(w.layers)}
 
     def arm(kid):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        e.record()  # materialize the handles
+        if args.event_kind == "torch":
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            e.record()  # materialize the handles
+        else:
+            s, e = HipEvent(), HipEvent()
         csa2.profile_kernel_events(kid, s, e)
         return s, e
 
@@ -332,7 +394,7 @@ def main():
     }
     res["chain_hbm_GBps"] = byt["total"] / (ms_step * 1e-3) / 1e9
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_rows)
+        res["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
