@@ -12,24 +12,29 @@
 // Probabilities are rounded to fp16 for the PV product and the row sums add
 // up those same rounded values.
 //
-// Work split.  A workgroup (8 waves, two per SIMD so that one wave's memory
-// and LDS latency overlaps the other's math) owns one (row, head group of up
-// to 64 heads, key split) and walks its keys in steps of 128:
+// Work split.  A workgroup (8 waves, two per SIMD so that one wave's memory,
+// LDS and exp latency overlaps the other's math) owns one (row, group of
+// 16*NHT heads, key split) and walks its keys in steps of 128:
 //  * QK^T, keys split across waves: wave w takes keys [16w, 16w+16) of the
-//    step and every head of the group.  Its lanes load their keys' 288-byte
-//    rows straight from HBM into registers (prefetched one step ahead) and
-//    dequantize them into the A operand (key rows); queries sit in LDS as
+//    step and every head of the group.  Its lanes load their key's 288-byte
+//    row straight from HBM into registers (prefetched a whole step ahead)
+//    and dequantize it into the A operand (key rows); queries sit in LDS as
 //    the B operand.  The result S^T gives each lane 4 keys of one head.
-//  * softmax: per-wave maxima and sums meet in LDS.  The reference maximum
-//    of a head only moves when the new maximum exceeds it by more than 2^8,
-//    so the running output is rarely rescaled; the final division by the
-//    same-reference sum makes the result independent of that choice.
-//  * PV, output channels split across waves: wave w produces channels
-//    [64w, 64w+64) of every head from the raw codes of all 128 keys staged in
-//    LDS, re-pairing nibbles of neighbouring keys so that each packed fp16
-//    pair holds two keys of one channel (the K-contiguous B operand layout).
+//  * softmax: per-wave maxima and sums meet in LDS (lane reductions use
+//    permlane swaps).  The reference maximum of a head only moves when the
+//    new maximum exceeds it by more than 2^8, so the running output is
+//    rarely rescaled; the final division by the same-reference sum makes
+//    the result independent of that choice.
+//  * PV, output channels and key halves split across waves: wave w produces
+//    channels [128(w%4), +128) of every head over keys [64(w/4), +64) of the
+//    step, from raw codes staged in LDS.  A lane owns 8 consecutive
+//    channels; nibbles of two keys are interleaved with bit operations so
+//    that each converted fp16 pair holds two keys of one channel (the
+//    K-contiguous B operand layout), and all 8 channels share one scale
+//    pair.  The two key halves are summed through LDS at the end.
 // Every FP4 element is dequantized once for QK^T and once for PV per
-// workgroup, and each dequantized value feeds every head of the group.
+// workgroup.  Small head groups keep the split partials (16*NHT heads x 512
+// fp32 per workgroup) small, so decode-sized batches use 2 head tiles.
 #include "csa2_common.h"
 
 #ifndef CSA2_HW_CVT
@@ -41,11 +46,12 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = 8;
-constexpr int kStep = 128;           // keys per step (16 per wave)
+constexpr int kStep = 128;           // keys per step (16 per wave in QK^T)
 constexpr int kCsStride = 272;       // bytes per staged code row (256 + 16 pad)
 constexpr int kScStride = 136;       // fp16 per staged scale row (128 keys + 8 pad)
 constexpr int kPStride = 136;        // fp16 per probability row
 constexpr int kQStride = 520;        // fp16 per query row (512 + 8 pad)
+constexpr int kOStride = 516;        // fp32 per row of the epilogue reduction buffer
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;        // log2 headroom before the reference maximum moves
@@ -118,19 +124,45 @@ struct AttnArgs {
   float* ws_l;           // [R, Hq, splits] sums
 };
 
+// byte offset of staged code row k.  Rows are padded to 272 bytes and each
+// group of 8 rows inside a 32-row block is shifted by another 64 bytes, so
+// the rows 8 apart that one PV k-group reads land 16 banks apart.
+constexpr int kCsBlock = 32 * kCsStride + 3 * 64;
+__device__ __forceinline__ int cs_off(int k) {
+  return (k >> 5) * kCsBlock + (k & 31) * kCsStride + 64 * ((k >> 3) & 3);
+}
+
 template <int NHT, bool SPLITQ>
 struct Smem {
   static constexpr int kQRows = 16 * NHT * (SPLITQ ? 2 : 1);
-  _Float16 q[kQRows * kQStride];
-  uint8_t cs[kStep * kCsStride];
-  _Float16 sct[kGroups * kScStride];
-  _Float16 p[16 * NHT * kPStride];
+  union {
+    struct {
+      _Float16 q[kQRows * kQStride];
+      uint8_t cs[(kStep / 32) * kCsBlock];
+      _Float16 sct[kGroups * kScStride];
+      _Float16 p[16 * NHT * kPStride];
+    } s;
+    float ored[16 * NHT * kOStride];  // after the key loop: outputs of the second key half
+  } u;
   float red_max[kWaves][64];
   float red_sum[kWaves][64];
   float alpha[64];
   float lfin[64];
-  float mfin[64];
 };
+
+// lane reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 struct Raw {
   u32x4 c[4];  // code bytes [64*q4, 64*q4+64) of the lane's key
@@ -140,14 +172,14 @@ struct Raw {
 // Branch-free gather: an invalid key loads row 0 of the cache (always
 // present) and is zeroed before use, so every load is issued unconditionally
 // and the compiler keeps them all in flight.
-__device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int64_t rs, int vis, int i, int kend, int32_t j,
-                                         uint32_t& valid, int q4) {
-  const bool ok = i < kend && j >= 0 && j < vis;
+__device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int64_t rs, int vis, int32_t j, int i,
+                                         int kend, uint32_t& valid, int q4) {
+  const bool ok = (i < kend) & ((uint32_t)j < (uint32_t)vis);
   valid = ok;
   const int64_t row = ok ? rs + j : 0;
   const u32x4* pc = reinterpret_cast<const u32x4*>(a.codes + row * kCodeBytes + 64 * q4);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) R.c[c] = __builtin_nontemporal_load(pc + c);
+  for (int c = 0; c < 4; ++c) R.c[c] = pc[c];
   R.s = *reinterpret_cast<const u32x2*>(a.scales + row * kGroups + 8 * q4);
 }
 
@@ -160,21 +192,23 @@ __device__ __forceinline__ void mask_raw(Raw& R, uint32_t valid) {
   R.s[1] = valid ? R.s[1] : 0u;
 }
 
-// index of key slot i of row r (-1 past the split end); kend > kbeg >= 0
+// index stored in key slot i of row r, clamped to the split's last slot
+// (kend > kbeg >= 0).  Slots >= kend are rejected later by load_raw; the
+// loaded value is not inspected here, so the load can stay in flight.
 __device__ __forceinline__ int32_t load_idx(const AttnArgs& a, int r, int i, int kend) {
-  const int ic = i < kend ? i : kend - 1;
-  const int32_t v = a.idx[(int64_t)r * a.top_k + ic];
-  return i < kend ? v : -1;
+  return a.idx[(int64_t)r * a.top_k + (i < kend ? i : kend - 1)];
 }
 
 template <int NHT, bool SPLITQ, int QDT>
 __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   Smem<NHT, SPLITQ>& sm = *reinterpret_cast<Smem<NHT, SPLITQ>*>(smem_raw);
+  auto& ss = sm.u.s;
   constexpr int HG = 16 * NHT;
   constexpr int NQ = SPLITQ ? 2 : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
+  const int cq = w & 3, kh = w >> 2;  // PV role: channel quarter, key half
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
   const int h0 = hg * HG;
   const int kbeg = split * a.keys_per_split;
@@ -184,15 +218,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   const int64_t rs = a.row_start[r];
   const int myslot = 16 * w + n16;  // this lane's key within a step (QK^T role)
 
-  // ---- prologue: indices of steps 0 and 1, the keys of step 0 in flight, queries to LDS
-  int32_t jnext = -1;
+  // ---- prologue: indices of steps 0 and 1, the keys of step 0 in flight, queries to LDS.
+  // Every load below and in the step prefetch is unconditional: slots past
+  // the split end read the split's last index slot and the gather then
+  // reads cache row 0, so no branch makes the compiler wait for loads early.
   uint32_t vA = 0, vB = 0;
   Raw bufA, bufB;
-  if (nsteps > 0) {
-    const int32_t j0 = load_idx(a, r, kbeg + myslot, kend);
-    if (nsteps > 1) jnext = load_idx(a, r, kbeg + kStep + myslot, kend);
-    load_raw(bufA, a, rs, vis, kbeg + myslot, kend, j0, vA, q4);
-  }
+  const int32_t j0 = load_idx(a, r, kbeg + myslot, kend);
+  int32_t jn = load_idx(a, r, kbeg + kStep + myslot, kend);
+  load_raw(bufA, a, rs, vis, j0, kbeg + myslot, kend, vA, q4);
   {
     // HG heads x 512 channels in 16-byte pieces; all loads issued before any conversion
     if (QDT == CSA2_BF16) {
@@ -213,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
           hv[2 * k] = (_Float16)__uint_as_float(v[i][k] << 16);
           hv[2 * k + 1] = (_Float16)__uint_as_float(v[i][k] & 0xFFFF0000u);
         }
-        *reinterpret_cast<half8*>(&sm.q[(p / (kDim / 8)) * kQStride + (p % (kDim / 8)) * 8]) = hv;
+        *reinterpret_cast<half8*>(&ss.q[(p / (kDim / 8)) * kQStride + (p % (kDim / 8)) * 8]) = hv;
       }
     } else {
       constexpr int NP = HG * kDim / 4 / kThreads;
@@ -231,20 +265,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const _Float16 hi = (_Float16)v[i][k];
-          sm.q[h * kQStride + c4 + k] = hi;
-          if (SPLITQ) sm.q[(HG + h) * kQStride + c4 + k] = (_Float16)(v[i][k] - (float)hi);
+          ss.q[h * kQStride + c4 + k] = hi;
+          if (SPLITQ) ss.q[(HG + h) * kQStride + c4 + k] = (_Float16)(v[i][k] - (float)hi);
         }
       }
     }
   }
   __syncthreads();
 
-  floatx4 O[NHT][4];
+  floatx4 O[NHT][8];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mref[NHT], lrun[NHT];  // per head 16*ht + n16 (softmax role), replicated over q4
+    for (int t = 0; t < 8; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mref[NHT], lrun[NHT];  // per head 16*ht + n16 (softmax role), replicated over q4 and waves
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     mref[ht] = -INFINITY;
@@ -253,13 +287,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 
   // One step over keys [kstep0, kstep0+128) held in `cur`; at its start the
   // gather of the next step is issued into `nxt` (a whole step ahead) and the
-  // indices of the step after that are loaded.
+  // index of the step after that is loaded (past the end: harmless in-bounds
+  // loads whose keys are masked).
   auto step = [&](int st, Raw& cur, uint32_t vcur, Raw& nxt, uint32_t& vnxt) {
     const int kstep0 = kbeg + st * kStep;
-    if (st + 1 < nsteps) {
-      load_raw(nxt, a, rs, vis, kstep0 + kStep + myslot, kend, jnext, vnxt, q4);
-      if (st + 2 < nsteps) jnext = load_idx(a, r, kstep0 + 2 * kStep + myslot, kend);
-    }
+    load_raw(nxt, a, rs, vis, jn, kstep0 + kStep + myslot, kend, vnxt, q4);
+    jn = load_idx(a, r, kstep0 + 2 * kStep + myslot, kend);
     mask_raw(cur, vcur);
     // scale bytes of groups 8*q4 .. 8*q4+7 -> fp16
     half2v sc[4];
@@ -272,24 +305,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
     floatx4 S[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) S[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // query fragments are read from LDS two K-steps ahead of their use
+    constexpr int NB = NHT * NQ;
+    half8 bq[3][NB];
+    auto load_bq = [&](half8* dst, int ks) {
+#pragma unroll
+      for (int ht = 0; ht < NB; ++ht)
+        dst[ht] = *reinterpret_cast<const half8*>(&ss.q[(16 * ht + n16) * kQStride + 128 * q4 + 8 * ks]);
+    };
+    load_bq(bq[0], 0);
+    load_bq(bq[1], 1);
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       // K-step ks covers channels 128*q4 + 8*ks .. +7 on both operands
-      half8 bq[NHT * NQ];
-#pragma unroll
-      for (int ht = 0; ht < NHT * NQ; ++ht)
-        bq[ht] = *reinterpret_cast<const half8*>(&sm.q[(16 * ht + n16) * kQStride + 128 * q4 + 8 * ks]);
+      if (ks + 2 < 16) load_bq(bq[(ks + 2) % 3], ks + 2);
       const uint32_t word = cur.c[ks >> 2][ks & 3];
       const half2v s1 = sc[ks >> 2];
-      const half2v ss = (ks & 2) ? half2v{s1[1], s1[1]} : half2v{s1[0], s1[0]};
-      const half8 av = cat4(fp4x2_to_h2<0>(word) * ss, fp4x2_to_h2<1>(word) * ss, fp4x2_to_h2<2>(word) * ss,
-                            fp4x2_to_h2<3>(word) * ss);
+      const half2v sv = (ks & 2) ? half2v{s1[1], s1[1]} : half2v{s1[0], s1[0]};
+      const half8 av = cat4(fp4x2_to_h2<0>(word) * sv, fp4x2_to_h2<1>(word) * sv, fp4x2_to_h2<2>(word) * sv,
+                            fp4x2_to_h2<3>(word) * sv);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        S[ht] = mfma(av, bq[ht], S[ht]);
-        if (SPLITQ) S[ht] = mfma(av, bq[NHT + ht], S[ht]);
+        S[ht] = mfma(av, bq[ks % 3][ht], S[ht]);
+        if (SPLITQ) S[ht] = mfma(av, bq[ks % 3][NHT + ht], S[ht]);
       }
-      __builtin_amdgcn_sched_barrier(0);  // bound the live query fragments to one K-step
     }
 
     // ---- softmax, part 1: scaled logits, masked, per-wave maximum per head
@@ -304,19 +343,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
         S[ht][i] = z;
         mx = fmaxf(mx, z);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows_max(mx);
       if (q4 == 0) sm.red_max[w][16 * ht + n16] = mx;
     }
     lds_barrier();  // B1: maxima visible; every wave is past the previous PV
 
     // ---- stage this step's raw codes and fp16 scales for PV
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&sm.cs[myslot * kCsStride + 64 * q4 + 16 * c]) = cur.c[c];
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&ss.cs[cs_off(myslot) + 64 * q4 + 16 * c]) = cur.c[c];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      sm.sct[(8 * q4 + 2 * g) * kScStride + myslot] = sc[g][0];
-      sm.sct[(8 * q4 + 2 * g + 1) * kScStride + myslot] = sc[g][1];
+      ss.sct[(8 * q4 + 2 * g) * kScStride + myslot] = sc[g][0];
+      ss.sct[(8 * q4 + 2 * g + 1) * kScStride + myslot] = sc[g][1];
     }
 
     // ---- softmax, part 2: reference maximum, probabilities (fp16), sums
@@ -331,17 +369,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
       alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
       mref[ht] = mnew;
-      _Float16 p[4];
+      _Float16 pv[4];
       float sum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
-        sum += (float)p[i];
+        pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
+        sum += (float)pv[i];
       }
-      *reinterpret_cast<u32x2*>(&sm.p[h * kPStride + 16 * w + 4 * q4]) =
-          u32x2{h2_bits(half2v{p[0], p[1]}), h2_bits(half2v{p[2], p[3]})};
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
+      *reinterpret_cast<u32x2*>(&ss.p[h * kPStride + 16 * w + 4 * q4]) =
+          u32x2{h2_bits(half2v{pv[0], pv[1]}), h2_bits(half2v{pv[2], pv[3]})};
+      sum = rows_sum(sum);
       if (q4 == 0) {
         sm.red_sum[w][h] = sum;
         if (w == 0) sm.alpha[h] = alpha[ht];
@@ -358,7 +395,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       lrun[ht] = lrun[ht] * alpha[ht] + add;
     }
 
-    // ---- PV: channels [64w, 64w+64) of every head; rescale only when a reference moved
+    // ---- PV: channels 128*cq + 8*n16 + t (t = 0..7) of every head over keys [64kh, 64kh+64);
+    // rescale only when a reference moved
     if (st > 0) {
       float al[NHT][4];
       bool moved = false;
@@ -375,134 +413,163 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) O[ht][t][i] *= al[ht][i];
+            for (int t = 0; t < 8; ++t) O[ht][t][i] *= al[ht][i];
       }
     }
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int key0 = 32 * kc + 8 * q4;  // this lane's 8 keys (slots 0..7)
-      // channels 64w + 4*n16 + {0..3}: 16 bits of codes per key
+    for (int kk = 0; kk < 2; ++kk) {
+      const int key0 = 64 * kh + 32 * kk + 8 * q4;  // this lane's 8 keys (k-slots 0..7)
+      // channels 128*cq + 8*n16 .. +7: one 32-bit code word per key
       uint32_t W[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        W[k] = *reinterpret_cast<const uint16_t*>(&sm.cs[(key0 + k) * kCsStride + 32 * w + 2 * n16]);
-      const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[(4 * w + (n16 >> 2)) * kScStride + key0]);
-      uint32_t Bw[4][4];
+        W[k] = *reinterpret_cast<const uint32_t*>(&ss.cs[cs_off(key0 + k) + 64 * cq + 4 * n16]);
+      // the 8 channels share scale group 8*cq + n16/2
+      const u32x4 spw = *reinterpret_cast<const u32x4*>(&ss.sct[(8 * cq + (n16 >> 1)) * kScStride + key0]);
+      uint32_t Bw[8][4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        // bytes of X: (keys 2p, 2p+1) of channels +0, +2, +1, +3
+        // byte b of E: channel 2b of keys (2p, 2p+1); byte b of D: channel 2b+1
         const uint32_t wa = W[2 * p], wb = W[2 * p + 1];
-        const uint32_t E = (wa & 0x0F0Fu) | ((wb & 0x0F0Fu) << 4);
-        const uint32_t D = ((wa >> 4) & 0x0F0Fu) | (wb & 0xF0F0u);
-        const uint32_t X = E | (D << 16);
+        const uint32_t E = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
+        const uint32_t D = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
         const half2v sp = bits_h2(spw[p]);
-        Bw[0][p] = h2_bits(fp4x2_to_h2<0>(X) * sp);
-        Bw[2][p] = h2_bits(fp4x2_to_h2<1>(X) * sp);
-        Bw[1][p] = h2_bits(fp4x2_to_h2<2>(X) * sp);
-        Bw[3][p] = h2_bits(fp4x2_to_h2<3>(X) * sp);
+        Bw[0][p] = h2_bits(fp4x2_to_h2<0>(E) * sp);
+        Bw[2][p] = h2_bits(fp4x2_to_h2<1>(E) * sp);
+        Bw[4][p] = h2_bits(fp4x2_to_h2<2>(E) * sp);
+        Bw[6][p] = h2_bits(fp4x2_to_h2<3>(E) * sp);
+        Bw[1][p] = h2_bits(fp4x2_to_h2<0>(D) * sp);
+        Bw[3][p] = h2_bits(fp4x2_to_h2<1>(D) * sp);
+        Bw[5][p] = h2_bits(fp4x2_to_h2<2>(D) * sp);
+        Bw[7][p] = h2_bits(fp4x2_to_h2<3>(D) * sp);
       }
-      half8 B[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) B[t] = __builtin_bit_cast(half8, u32x4{Bw[t][0], Bw[t][1], Bw[t][2], Bw[t][3]});
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        const half8 av = *reinterpret_cast<const half8*>(&sm.p[(16 * ht + n16) * kPStride + key0]);
+        const half8 av = *reinterpret_cast<const half8*>(&ss.p[(16 * ht + n16) * kPStride + key0]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) O[ht][t] = mfma(av, B[t], O[ht][t]);
+        for (int t = 0; t < 8; ++t)
+          O[ht][t] = mfma(av, __builtin_bit_cast(half8, u32x4{Bw[t][0], Bw[t][1], Bw[t][2], Bw[t][3]}), O[ht][t]);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-
   };
   for (int st = 0; st < nsteps; st += 2) {
     step(st, bufA, vA, bufB, vB);
     if (st + 1 < nsteps) step(st + 1, bufB, vB, bufA, vA);
   }
 
-  // ---- epilogue
+  // ---- epilogue: the second key half hands its outputs over through LDS
+  __syncthreads();  // every wave is past its last PV: the staging area is free
+  const int ch = 128 * cq + 8 * n16;
+  if (kh == 1) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4* dst = reinterpret_cast<float4*>(&sm.u.ored[(16 * ht + 4 * q4 + i) * kOStride + ch]);
+        dst[0] = make_float4(O[ht][0][i], O[ht][1][i], O[ht][2][i], O[ht][3][i]);
+        dst[1] = make_float4(O[ht][4][i], O[ht][5][i], O[ht][6][i], O[ht][7][i]);
+      }
+  }
   if (w == 0 && q4 == 0) {
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      sm.lfin[16 * ht + n16] = lrun[ht];
-      sm.mfin[16 * ht + n16] = mref[ht];
-    }
+    for (int ht = 0; ht < NHT; ++ht) sm.lfin[16 * ht + n16] = lrun[ht];
   }
   __syncthreads();
-  const int64_t rowh = (int64_t)r * a.Hq + h0;
-  const int ch = 64 * w + 4 * n16;
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * ht + 4 * q4 + i;
-      const float L = sm.lfin[h];
-      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      const float v0 = O[ht][0][i] * inv, v1 = O[ht][1][i] * inv, v2 = O[ht][2][i] * inv, v3 = O[ht][3][i] * inv;
-      if (a.splits > 1) {
-        *reinterpret_cast<float4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch) = make_float4(v0, v1, v2, v3);
-      } else if (a.out_dtype == CSA2_F32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch) = make_float4(v0, v1, v2, v3);
-      } else {
-        const float v[4] = {v0, v1, v2, v3};
-        uint32_t pk[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
-          lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
-          hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-          pk[k] = lo | (hi << 16);
-        }
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + ch) = make_uint2(pk[0], pk[1]);
-      }
-    }
-  }
-  if (w == 0 && q4 == 0) {
+  if (kh == 0) {
+    const int64_t rowh = (int64_t)r * a.Hq + h0;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-      const int h = 16 * ht + n16;
-      if (a.splits == 1) {
-        if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
-      } else {
-        a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
-        a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * ht + 4 * q4 + i;
+        const float L = sm.lfin[h];
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const float4* src = reinterpret_cast<const float4*>(&sm.u.ored[h * kOStride + ch]);
+        const float4 o0 = src[0], o1 = src[1];
+        float v[8] = {O[ht][0][i] + o0.x, O[ht][1][i] + o0.y, O[ht][2][i] + o0.z, O[ht][3][i] + o0.w,
+                      O[ht][4][i] + o1.x, O[ht][5][i] + o1.y, O[ht][6][i] + o1.z, O[ht][7][i] + o1.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] *= inv;
+        if (a.splits > 1) {
+          // streaming stores: the partials are read once, by the combine kernel
+          floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch);
+          __builtin_nontemporal_store(floatx4{v[0], v[1], v[2], v[3]}, dst);
+          __builtin_nontemporal_store(floatx4{v[4], v[5], v[6], v[7]}, dst + 1);
+        } else if (a.out_dtype == CSA2_F32) {
+          float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch);
+          dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+          dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          uint32_t pk[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+            lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+            hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+            pk[k] = lo | (hi << 16);
+          }
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + ch) =
+              make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+      }
+    }
+    if (w == 0 && q4 == 0) {
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        const int h = 16 * ht + n16;
+        if (a.splits == 1) {
+          if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
+        } else {
+          a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
+          a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+        }
       }
     }
   }
 }
 
 // one (row, head) per workgroup of 128 threads, 4 channels per thread;
-// splits merged in fixed order: o = sum_s w_s l_s o_s / sum_s w_s l_s
+// splits merged in fixed order with a running maximum, 8 splits per batch of
+// loads: o = sum_s w_s l_s o_s / sum_s w_s l_s,  w_s = 2^(m_s - max m)
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_m,
                                                       const float* __restrict__ ws_l, int splits, void* out,
                                                       int out_dtype, float* lse) {
   const int64_t rh = blockIdx.x;
   const float* m = ws_m + rh * splits;
   const float* l = ws_l + rh * splits;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, m[s]);
+  float M = -INFINITY, L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.0f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < splits; s0 += 8) {
-      float4 v[8];
-      float wl[8];
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float4 v[8];
+    float mm[8], ll[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int s = s0 + k < splits ? s0 + k : splits - 1;
-        v[k] = reinterpret_cast<const float4*>(ws_o + (rh * splits + s) * kDim)[threadIdx.x];
-        wl[k] = __builtin_amdgcn_exp2f(m[s] - M) * l[s];
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (s0 + k < splits) {
-          L += wl[k];
-          acc.x += wl[k] * v[k].x;
-          acc.y += wl[k] * v[k].y;
-          acc.z += wl[k] * v[k].z;
-          acc.w += wl[k] * v[k].w;
-        }
-      }
+    for (int k = 0; k < 8; ++k) {
+      const int s = s0 + k < splits ? s0 + k : splits - 1;
+      v[k] = reinterpret_cast<const float4*>(ws_o + (rh * splits + s) * kDim)[threadIdx.x];
+      mm[k] = s0 + k < splits ? m[s] : -INFINITY;
+      ll[k] = l[s];
     }
+    float bm = mm[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) bm = fmaxf(bm, mm[k]);
+    const float Mn = fmaxf(M, bm);
+    if (Mn == -INFINITY) continue;  // every split so far is empty
+    const float sc = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M is still -inf
+    L *= sc;
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float wl = __builtin_amdgcn_exp2f(mm[k] - Mn) * ll[k];  // 0 for empty or missing splits
+      L += wl;
+      acc.x += wl * v[k].x;
+      acc.y += wl * v[k].y;
+      acc.z += wl * v[k].z;
+      acc.w += wl * v[k].w;
+    }
+    M = Mn;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
@@ -527,22 +594,18 @@ struct Plan {
   bool splitq;
 };
 
+// Launch plan.  A workgroup takes 32 heads (16 if the head count is an odd
+// number of 16-head tiles) and, when rows x head groups do not fill the
+// chip, the keys are split so that >= 256 workgroups run.
 Plan plan(int R, int Hq, int q_dtype, int top_k) {
   Plan p{};
   p.splitq = q_dtype == CSA2_F32;
+  const int tiles = Hq / 16;
   const int max_splits = (int)std::max<int64_t>(1, ceil_div(top_k, kStep));
-  const int cand[4] = {4, 3, 2, 1};
-  p.nht = 1;
-  for (int c : cand) {
-    if (p.splitq && c > 2) continue;
-    if ((Hq / 16) % c) continue;
-    p.nht = c;
-    const int64_t wgs = (int64_t)R * (Hq / (16 * c)) * max_splits;
-    if (wgs >= 256) break;
-  }
-  p.head_groups = Hq / (16 * p.nht);
+  p.nht = tiles % 2 == 0 ? 2 : 1;
+  p.head_groups = tiles / p.nht;
   const int64_t base = (int64_t)R * p.head_groups;
-  int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(256, base)));
+  const int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(256, base)));
   p.keys_per_split = (int)round_up(ceil_div(top_k, splits), kStep);
   p.splits = (int)ceil_div(top_k, p.keys_per_split);
   return p;
@@ -605,8 +668,6 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
   hipError_t e;
   if (q_dtype == CSA2_BF16) {
     switch (p.nht) {
-      case 4: e = go<4, false, CSA2_BF16>(p, R, a, s); break;
-      case 3: e = go<3, false, CSA2_BF16>(p, R, a, s); break;
       case 2: e = go<2, false, CSA2_BF16>(p, R, a, s); break;
       default: e = go<1, false, CSA2_BF16>(p, R, a, s); break;
     }
