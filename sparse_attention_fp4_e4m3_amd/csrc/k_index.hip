@@ -43,32 +43,48 @@ constexpr int kSub = 2048;  // elements per collect wave (one candidate slice)
 // radix digits over the 31 value bits: 12 / 11 / 8
 constexpr int kD1 = 4096, kD2 = 2048, kD3 = 256;
 constexpr int kS1 = 19, kS2 = 8;
-constexpr int kFullTilesPerWG = 8;
+constexpr int kScanSlots = 768;  // resident scan workgroups on 256 CUs (3 each)
 constexpr int kMaxHeads = 32;
 
+// One wave scores 64 keys at a time (one key per lane).  The keys' rows are
+// loaded with fully coalesced 16-byte pieces, staged in the wave's own LDS
+// area and read back one row per lane, so no workgroup barrier is needed
+// between tiles and the waves of a workgroup drift freely.
 template <int KDT>
 struct KeyTile {
-  static constexpr int kBytes = KDT == CSA2_BF16 ? 128 : 256;   // one indexer key row
-  static constexpr int kKeys = 256;                             // one key per thread
-  static constexpr int kStride = kBytes + 16;                   // padded LDS row
-  static constexpr int kPieces = kBytes / 16;                   // 16-byte pieces per row
-  static constexpr int kPerThread = kKeys * kPieces / kThreads;  // 8 (bf16) or 16 (fp32)
+  static constexpr int kBytes = KDT == CSA2_BF16 ? 128 : 256;  // one indexer key row
+  static constexpr int kKeys = 64;                             // keys per wave tile
+  static constexpr int kStride = kBytes + 16;                  // padded LDS row
+  static constexpr int kPieces = kBytes / 16;                  // 16-byte pieces per row
+  static constexpr int kPerLane = kKeys * kPieces / 64;        // 8 (bf16) or 16 (fp32)
+  static constexpr int kWaveBytes = kKeys * kStride;           // LDS per wave
 };
+constexpr int kWavesPerWG = kThreads / 64;
+constexpr int kWGKeys = kWavesPerWG * 64;  // keys per workgroup tile (one wave tile per wave)
 
 __device__ __forceinline__ int clampv(int v, int maxv) { return v < 0 ? 0 : (v > maxv ? maxv : v); }
 
 // ------------------------------------------------------------ block helpers
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts of
+// 1, 2, 4, 8 within each 16-lane row, then the row totals carried across
+// rows by broadcasting lane 15 (to rows 1, 3) and lane 31 (to rows 2, 3).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive prefix sum over the block; *total = the block sum.  lds >= NT/64 words.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* lds, uint32_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_sum(v);
   if (lane == 63) lds[wave] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;
@@ -83,31 +99,38 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* lds, ui
   return before + x - v;
 }
 
-// Bin holding the K-th largest element of a histogram in global or shared
-// memory (bins scanned from the top); -1 when it holds fewer than K.
-// *above = elements in higher bins, *total = all elements.  lds >= 20 words.
-template <int NT>
-__device__ int find_bin(const uint32_t* h, int nbins, uint32_t K, uint32_t* above, uint32_t* total, uint32_t* lds) {
-  const int per = (nbins + NT - 1) / NT;
-  const int hi = nbins - (int)threadIdx.x * per;  // this thread: bins [max(hi-per,0), hi), descending
-  const int lo = hi - per < 0 ? 0 : hi - per;
+// Bin holding the K-th largest element of a histogram of NB bins in global
+// or shared memory (bins scanned from the top); -1 when it holds fewer than
+// K.  *above = elements in higher bins, *total = all elements.  Each thread
+// owns NB/NT consecutive bins, all loaded at once.  lds >= 20 words.
+template <int NT, int NB>
+__device__ int find_bin(const uint32_t* h, uint32_t K, uint32_t* above, uint32_t* total, uint32_t* lds) {
+  static_assert(NB % NT == 0, "bins per thread");
+  constexpr int PER = NB / NT;
+  const int hi = NB - (int)threadIdx.x * PER;  // this thread: bins [hi-PER, hi), descending
+  uint32_t c[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) c[k] = h[hi - 1 - k];
   uint32_t local = 0;
-  for (int b = hi - 1; b >= lo; --b) local += h[b];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) local += c[k];
   uint32_t tot;
   const uint32_t before = block_excl_sum<NT>(local, lds, &tot);
   if (threadIdx.x == 0) lds[16] = 0xFFFFFFFFu;
   __syncthreads();
-  if (hi > 0 && before < K && K <= before + local) {
-    uint32_t c = before;
-    for (int b = hi - 1; b >= lo; --b) {
-      const uint32_t n = h[b];
-      if (K <= c + n) {
-        lds[16] = (uint32_t)b;
-        lds[17] = c;
-        break;
+  if (before < K && K <= before + local) {
+    uint32_t run = before, ab = 0;
+    int bin = -1;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {  // this thread's bins from the top
+      if (bin < 0 && K <= run + c[k]) {
+        bin = hi - 1 - k;
+        ab = run;
       }
-      c += n;
+      run += c[k];
     }
+    lds[16] = (uint32_t)bin;
+    lds[17] = ab;
   }
   __syncthreads();
   const uint32_t bin = lds[16], ab = lds[17];
@@ -161,86 +184,95 @@ struct ScoreArgs {
 
 template <int KDT>
 struct Staged {
-  u32x4 v[KeyTile<KDT>::kPerThread];
+  u32x4 v[KeyTile<KDT>::kPerLane];
 };
+
+// First-digit histograms are kept as packed 16-bit counters (two bins per
+// word): a workgroup scores at most 255 x 256 entries, so no counter overflows.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) { atomicAdd(&h[bin >> 1], 1u << (16 * (bin & 1))); }
+
+__device__ __forceinline__ void flush_packed(uint32_t* __restrict__ g, const uint32_t* __restrict__ l) {
+  for (int w = threadIdx.x; w < kD1 / 2; w += blockDim.x) {
+    const uint32_t v = l[w];
+    if (v & 0xFFFFu) atomicAdd(g + 2 * w, v & 0xFFFFu);
+    if (v >> 16) atomicAdd(g + 2 * w + 1, v >> 16);
+  }
+}
 
 // HC: compile-time head count (0 = runtime a.H, at most 32)
 template <int KDT, int HC, bool REINDEX, bool POOL>
-__global__ __launch_bounds__(kThreads, 2) void k_score(ScoreArgs a, const float* __restrict__ qf) {
+__global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float* __restrict__ qf) {
   using T = KeyTile<KDT>;
   constexpr int NACC = HC > 0 ? HC : kMaxHeads;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* tile = smem;                                                   // kKeys * kStride
-  uint32_t* h1 = reinterpret_cast<uint32_t*>(smem + T::kKeys * T::kStride);  // kD1
-  uint32_t* hb = h1 + kD1;                                                // kD1 (POOL)
-  int32_t* posb = reinterpret_cast<int32_t*>(hb + (POOL ? kD1 : 0));     // kKeys (Reindex)
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint8_t* tile = smem + wv * T::kWaveBytes;                                       // this wave's rows
+  uint32_t* h1 = reinterpret_cast<uint32_t*>(smem + kWavesPerWG * T::kWaveBytes);  // kD1/2 packed
+  uint32_t* hb = h1 + kD1 / 2;                                                     // kD1/2 packed (POOL)
 
   const int H = HC > 0 ? HC : a.H;
   const int r = blockIdx.y;
   const int vis = clampv(a.row_visible[r], a.max_visible);
   const int n = REINDEX ? a.pool_stride : vis;
-  const int64_t base0 = (int64_t)blockIdx.x * a.tiles_per_wg * T::kKeys;
+  const int64_t base0 = (int64_t)blockIdx.x * a.tiles_per_wg * kWGKeys;
   if (base0 >= n) return;
-  const int ntiles = (int)std::min<int64_t>(a.tiles_per_wg, ceil_div(n - base0, T::kKeys));
+  const int ntiles = (int)std::min<int64_t>(a.tiles_per_wg, ceil_div(n - base0, kWGKeys));
   int plen = 0;
   if (REINDEX) plen = a.pool_len ? clampv(a.pool_len[r], a.pool_stride) : a.pool_stride;
-  for (int b = threadIdx.x; b < kD1; b += kThreads) {
-    h1[b] = 0u;
-    if (POOL) hb[b] = 0u;
-  }
-  if (REINDEX) {
-    for (int k = threadIdx.x; k < T::kKeys; k += kThreads) {
-      const int64_t i = base0 + k;
-      const int p = (i < plen) ? a.pool[(int64_t)r * a.pool_stride + i] : -1;
-      posb[k] = (p >= 0 && p < vis) ? p : -1;
+  if (!REINDEX) {
+    for (int b = threadIdx.x; b < kD1 / 2; b += kThreads) {
+      h1[b] = 0u;
+      if (POOL) hb[b] = 0u;
     }
     __syncthreads();
   }
   const int64_t rs = a.row_start[r];
   const uint8_t* kbase = static_cast<const uint8_t*>(a.idx_k);
   float* srow = a.scores + (int64_t)r * a.n_pad;
+  const int32_t* prow = REINDEX ? a.pool + (int64_t)r * a.pool_stride : nullptr;
 
-  // piece id = tid + 256*i -> key id / kPieces, piece id % kPieces (16 consecutive bytes of the tile)
+  // entry position of slot i (Full: the slot itself; Reindex: the pool entry), -1 if invalid
+  auto position = [&](int64_t i) -> int64_t {
+    if (REINDEX) {
+      const int p = (i < plen) ? prow[i] : -1;
+      return (p >= 0 && p < vis) ? p : -1;
+    }
+    return i < vis ? i : -1;
+  };
+  // piece id = lane + 64*i -> key id / kPieces, piece id % kPieces (coalesced 16-byte pieces)
   auto load_tile = [&](int64_t base, Staged<KDT>& st) {
 #pragma unroll
-    for (int i = 0; i < T::kPerThread; ++i) {
-      const int id = threadIdx.x + kThreads * i;
+    for (int i = 0; i < T::kPerLane; ++i) {
+      const int id = lane + 64 * i;
       const int k = id / T::kPieces, piece = id % T::kPieces;
-      int64_t pos;
-      bool ok;
-      if (REINDEX) {
-        pos = posb[k];
-        ok = pos >= 0;
-      } else {
-        pos = base + k;
-        ok = pos < vis;
-      }
+      const int64_t pos = position(base + k);
       // invalid keys read row 0 of the key array (always present) and are zeroed: no branch around the load
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (ok ? rs + pos : 0) * T::kBytes) +
-                                                 piece);
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kbase + (pos >= 0 ? rs + pos : 0) * T::kBytes) + piece);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st.v[i][e] = ok ? v[e] : 0u;
+      for (int e = 0; e < 4; ++e) st.v[i][e] = pos >= 0 ? v[e] : 0u;
     }
   };
 
+  // wave tiles of this workgroup: wave wv takes tiles wv, wv + 4, ... (64 keys each)
+  const int nwt = (int)std::min<int64_t>((int64_t)ntiles * kWavesPerWG, ceil_div(n - base0, T::kKeys));
   Staged<KDT> st;
-  load_tile(base0, st);
-  for (int t = 0; t < ntiles; ++t) {
-    const int64_t base = base0 + (int64_t)t * T::kKeys;
-    __syncthreads();  // the previous tile is consumed
+  if (wv < nwt) load_tile(base0 + (int64_t)wv * T::kKeys, st);
+  for (int j = wv; j < nwt; j += kWavesPerWG) {
+    const int64_t base = base0 + (int64_t)j * T::kKeys;
+    // (the LDS operations of one wave execute in order: the previous tile's reads are done)
 #pragma unroll
-    for (int i = 0; i < T::kPerThread; ++i) {
-      const int id = threadIdx.x + kThreads * i;
+    for (int i = 0; i < T::kPerLane; ++i) {
+      const int id = lane + 64 * i;
       *reinterpret_cast<u32x4*>(tile + (id / T::kPieces) * T::kStride + (id % T::kPieces) * 16) = st.v[i];
     }
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(base + T::kKeys, st);
+    if (j + kWavesPerWG < nwt) load_tile(base + (int64_t)kWavesPerWG * T::kKeys, st);
 
-    // the H fmaf chains of key tid, channels in order
+    // the H fmaf chains of key `lane`, channels in order
     float acc[NACC];
 #pragma unroll
     for (int h = 0; h < NACC; ++h) acc[h] = 0.0f;
-    const uint8_t* row = tile + threadIdx.x * T::kStride;
+    const uint8_t* row = tile + lane * T::kStride;
 #pragma unroll 2
     for (int c4 = 0; c4 < 16; ++c4) {
       float kv[4];
@@ -253,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_score(ScoreArgs a, const float*
       } else {
         const u32x4 w = *reinterpret_cast<const u32x4*>(row + c4 * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kv[j] = __uint_as_float(w[j]);
+        for (int e = 0; e < 4; ++e) kv[e] = __uint_as_float(w[e]);
       }
       // the H x 4 query values of this channel quad are wave-uniform: scalar loads
       const float* qrow = qf + (int64_t)r * H * kIdxDim + c4 * H * 4;
@@ -261,45 +293,42 @@ __global__ __launch_bounds__(kThreads, 2) void k_score(ScoreArgs a, const float*
 #pragma unroll
         for (int h = 0; h < HC; ++h) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[h] = __builtin_fmaf(qrow[h * 4 + j], kv[j], acc[h]);
+          for (int e = 0; e < 4; ++e) acc[h] = __builtin_fmaf(qrow[h * 4 + e], kv[e], acc[h]);
         }
       } else {
 #pragma unroll
         for (int h = 0; h < kMaxHeads; ++h) {
           if (h < H) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[h] = __builtin_fmaf(qrow[h * 4 + j], kv[j], acc[h]);
+            for (int e = 0; e < 4; ++e) acc[h] = __builtin_fmaf(qrow[h * 4 + e], kv[e], acc[h]);
           }
         }
       }
     }
-    float s = acc[0] > 0.0f ? acc[0] : 0.0f;
+    float sc = acc[0] > 0.0f ? acc[0] : 0.0f;
 #pragma unroll
     for (int h = 1; h < NACC; ++h)
-      if (HC > 0 || h < H) s = __fadd_rn(s, acc[h] > 0.0f ? acc[h] : 0.0f);
-    const int k = threadIdx.x;
-    const int64_t i = base + k;
-    bool ok;
-    if (REINDEX) ok = posb[k] >= 0;
-    else ok = i < vis;
-    if (i < n) srow[i] = ok ? s : -1.0f;
-    if (!REINDEX && ok) atomicAdd(&h1[__float_as_uint(s) >> kS1], 1u);
+      if (HC > 0 || h < H) sc = __fadd_rn(sc, acc[h] > 0.0f ? acc[h] : 0.0f);
+    const int64_t i = base + lane;
+    const bool ok = position(i) >= 0;
+    if (i < n) srow[i] = ok ? sc : -1.0f;
+    if (!REINDEX && ok) hist_add(h1, __float_as_uint(sc) >> kS1);
     if (POOL) {
       // a block of 8 consecutive positions = 8 consecutive lanes
-      float m = ok ? s : -1.0f;
+      float m = ok ? sc : -1.0f;
       m = fmaxf(m, __shfl_xor(m, 1, 64));
       m = fmaxf(m, __shfl_xor(m, 2, 64));
       m = fmaxf(m, __shfl_xor(m, 4, 64));
-      if (ok && (threadIdx.x & 7) == 0) {
+      if (ok && (lane & 7) == 0) {
         a.bmax[(int64_t)r * a.nb_pad + i / kBlock] = m;
-        atomicAdd(&hb[__float_as_uint(m) >> kS1], 1u);
+        hist_add(hb, __float_as_uint(m) >> kS1);
       }
     }
   }
-  __syncthreads();
   if (!REINDEX) {
-    flush_hist(a.hist_s + (int64_t)r * kD1, h1, kD1);
-    if (POOL) flush_hist(a.hist_b + (int64_t)r * kD1, hb, kD1);
+    __syncthreads();
+    flush_packed(a.hist_s + (int64_t)r * kD1, h1);
+    if (POOL) flush_packed(a.hist_b + (int64_t)r * kD1, hb);
   }
 }
 
@@ -351,12 +380,19 @@ __device__ void finalize_row(const SelArgs& a, int series, int r, uint32_t* hist
   uint32_t M;
   const uint32_t* keys;
   const int32_t* posr;
+  uint32_t above0 = 0;
+  int b0 = -1;
   if (full) {
     const int nsub = (n + kSub - 1) / kSub;
+    const uint32_t c_first = ((int)threadIdx.x < nsub) ? S.counts[(int64_t)r * S.nsub + threadIdx.x] : 0u;
+    // the first digit is already resolved by the scan's histogram (the same
+    // threshold bin k_collect used): candidates above it are all selected
+    uint32_t total0;
+    b0 = find_bin<NT, kD1>(S.hist + (int64_t)r * kD1, (uint32_t)S.K, &above0, &total0, red);
     uint32_t carry = 0;
     for (int s0 = 0; s0 < nsub; s0 += NT) {
       const int s = s0 + threadIdx.x;
-      const uint32_t c = (s < nsub) ? S.counts[(int64_t)r * S.nsub + s] : 0u;
+      const uint32_t c = s0 == 0 ? c_first : ((s < nsub) ? S.counts[(int64_t)r * S.nsub + s] : 0u);
       uint32_t tot;
       const uint32_t ex = block_excl_sum<NT>(c, red, &tot);
       if (s < nsub) pre[s] = carry + ex;
@@ -410,11 +446,25 @@ __device__ void finalize_row(const SelArgs& a, int series, int r, uint32_t* hist
   int shift_hi = 31;
   bool all = false;
   uint32_t need = 0;
+  int lev0 = 0;
+  if (full) {
+    if (b0 < 0) {
+      all = true;  // fewer than K valid entries: every candidate is selected
+      lev0 = 3;
+    } else {
+      prefix = (uint32_t)b0;
+      shift_hi = kS1;
+      K -= above0;
+      need = K;
+      lev0 = 1;
+    }
+  }
 #pragma unroll 1
-  for (int lev = 0; lev < 3; ++lev) {
+  for (int lev = lev0; lev < 3; ++lev) {
     const int sh = lev == 0 ? kS1 : (lev == 1 ? kS2 : 0);
     const int nb = lev == 0 ? kD1 : (lev == 1 ? kD2 : kD3);
-    for (int b = threadIdx.x; b < nb; b += NT) hist[b] = 0u;
+    const int nz = nb < NT ? NT : nb;  // the last level's scan covers NT bins (the extra ones stay empty)
+    for (int b = threadIdx.x; b < nz; b += NT) hist[b] = 0u;
     __syncthreads();
 #pragma unroll 4
     for (uint32_t i = threadIdx.x; i < M; i += NT) {
@@ -423,7 +473,9 @@ __device__ void finalize_row(const SelArgs& a, int series, int r, uint32_t* hist
     }
     __syncthreads();
     uint32_t above, total;
-    const int b = find_bin<NT>(hist, nb, K, &above, &total, red);
+    const int b = lev == 0 ? find_bin<NT, kD1>(hist, K, &above, &total, red)
+                           : (lev == 1 ? find_bin<NT, kD2>(hist, K, &above, &total, red)
+                                       : find_bin<NT, kD3 < NT ? NT : kD3>(hist, K, &above, &total, red));
     if (b < 0) {  // only at the first level: fewer than K valid candidates
       all = true;
       break;
@@ -502,25 +554,26 @@ __global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
   const int n = series_len(a, series, r);
   const int64_t wg_base = (int64_t)blockIdx.x * 4 * kSub;
   if (wg_base >= n) return;
-  uint32_t above, total;
-  const int b1 = find_bin<kThreads>(S.hist + (int64_t)r * kD1, kD1, (uint32_t)S.K, &above, &total, red);
-  const uint32_t thr = b1 < 0 ? 0u : (uint32_t)b1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t base = wg_base + (int64_t)wave * kSub;
-  if (base >= n) return;
-  const int sub = (int)(base / kSub);
-  const int end = (int)std::min<int64_t>(n, base + kSub);
+  const int end = (int)std::min<int64_t>(n, base + kSub);  // <= base for a wave past the end
   const float* arr = S.arr + (int64_t)r * S.stride;
-  float* ck = S.cand_key + (int64_t)r * 2 * S.stride + base;
-  int32_t* cp = S.cand_pos + (int64_t)r * 2 * S.stride + base;
-  uint32_t cnt = 0;
-  constexpr int kPer = kSub / 64;  // 32 elements per lane, all loads in flight at once
+  // the slice's keys are in flight while the threshold bin is found
+  constexpr int kPer = kSub / 64;  // 32 elements per lane
   float v[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int i = (int)base + 64 * k + lane;
-    v[k] = arr[i < end ? i : end - 1];
+    v[k] = arr[i < end ? i : n - 1];
   }
+  uint32_t above, total;
+  const int b1 = find_bin<kThreads, kD1>(S.hist + (int64_t)r * kD1, (uint32_t)S.K, &above, &total, red);
+  const uint32_t thr = b1 < 0 ? 0u : (uint32_t)b1;
+  if (base >= n) return;
+  const int sub = (int)(base / kSub);
+  float* ck = S.cand_key + (int64_t)r * 2 * S.stride + base;
+  int32_t* cp = S.cand_pos + (int64_t)r * 2 * S.stride + base;
+  uint32_t cnt = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int i = (int)base + 64 * k + lane;
@@ -537,7 +590,6 @@ __global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
   if (lane == 0) S.counts[(int64_t)r * S.nsub + sub] = cnt;
 }
 
-// One workgroup per (row, series) runs the exact selection.
 __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
   extern __shared__ __align__(16) uint32_t fsm[];
   uint32_t* hist = fsm;                       // kD1
@@ -605,13 +657,12 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
 template <int KDT, int HC, bool REINDEX, bool POOL>
 void launch_score(const ScoreArgs& sa, const float* qf, dim3 grid, hipStream_t s) {
   using T = KeyTile<KDT>;
-  const size_t lds = (size_t)T::kKeys * T::kStride + (size_t)kD1 * 4 * (POOL ? 2 : 1) +
-                     (REINDEX ? (size_t)T::kKeys * 4 : 0);
+  const size_t lds = (size_t)kWavesPerWG * T::kWaveBytes + (REINDEX ? 0 : (size_t)kD1 / 2 * 4 * (POOL ? 2 : 1));
   auto kern = k_score<KDT, HC, REINDEX, POOL>;
   static bool configured = false;
   if (!configured) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)((size_t)T::kKeys * T::kStride + (size_t)kD1 * 8 + T::kKeys * 4));
+                              (int)lds);
     configured = true;
   }
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, sa, qf);
@@ -662,8 +713,14 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
     sa.nb_pad = L.nb_pad;
     sa.hist_s = L.hist;
     sa.hist_b = L.hist + (size_t)R * kD1;
-    sa.tiles_per_wg = full ? kFullTilesPerWG : 1;
-    const dim3 grid((unsigned)ceil_div(n, (int64_t)256 * sa.tiles_per_wg), (unsigned)R);
+    // Full: about three workgroups per CU over the whole batch (each scans
+    // tiles_per_wg x 256 consecutive entries); Reindex: 256 pool slots each
+    const int64_t tiles = ceil_div(n, (int64_t)kWGKeys);
+    // (at most 255 tiles = 65,280 entries per workgroup: its packed 16-bit histogram counters cannot overflow)
+    sa.tiles_per_wg =
+        full ? (int)std::min<int64_t>(255, ceil_div(tiles, std::max<int64_t>(1, ceil_div((int64_t)kScanSlots, R))))
+             : 1;
+    const dim3 grid((unsigned)ceil_div(tiles, (int64_t)sa.tiles_per_wg), (unsigned)R);
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
     if (ev.start) (void)hipEventRecord(ev.start, s);
     if (k_dtype == CSA2_BF16) {
