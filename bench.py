@@ -11,7 +11,11 @@ Prints one JSON line: tokens/s over the timed steps, the roofline of the
 dominant kernel (HIP events on the launch stream via the library's
 measurement hook), and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--workload c3|c2|c5] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload c3|c2|c5|c4] [--gpus 1]
+
+The prefill workload (c4) times one 4,096-token chunk appended causally to a
+262,144-token cache: quantize-on-write of the chunk, the Full indexer and
+exact top-K for each of its rows, and sparse attention for each row.
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ import gen  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+VALU_F32_PEAK_TFLOPS = 157.3
 METRIC = "CSA2 decode tokens/s + achieved HBM GB/s (FP4 KV) at 128K ctx, 1 GPU"
 KV_ROW_BYTES = 288
 
@@ -70,6 +75,38 @@ def build_cache(w, lens, device, chunk=65536):
                  torch.from_numpy(lens.astype(np.int32)).to(device), int(lens.max())), starts
 
 
+def build_prefill(w, device, chunk=65536):
+    """The prefill workload: a cache of n - T tokens plus the chunk's own T rows.
+
+    Row r of the chunk sits at cache position P0 + r and sees positions
+    [0, P0 + r].  Indexer keys of every position are resident up front; the
+    chunk's KV rows are (re)written by the timed step's quantize-on-write.
+    Returns (cache, q per layer, idx_q per layer, new_kv, new_kv_rows, lens)."""
+    import torch
+
+    from sparse_attention_fp4_e4m3_amd import Cache, csa2
+
+    T = w.prefill_tokens
+    P0 = w.n - T
+    codes = torch.empty(w.n, 256, dtype=torch.uint8, device=device)
+    scales = torch.empty(w.n, 32, dtype=torch.uint8, device=device)
+    kdt = torch.bfloat16 if w.idx_dtype == "bf16" else torch.float32
+    idx_k = torch.empty(w.n, 64, dtype=kdt, device=device)
+    for t0 in range(0, w.n, chunk):
+        t1 = min(w.n, t0 + chunk)
+        csa2.quantize_kv_fp4(torch.from_numpy(gen.kv_rows(w, 0, t0, t1)).to(device), codes[t0:t1], scales[t0:t1])
+        idx_k[t0:t1] = to_dev(gen.idx_k_rows(w, 0, t0, t1), w.idx_dtype, device)
+    torch.cuda.synchronize()
+    starts = torch.zeros(T, dtype=torch.int64, device=device)
+    vis = torch.from_numpy((P0 + 1 + np.arange(T)).astype(np.int32)).to(device)
+    cache = Cache(codes, scales, idx_k, starts, vis, w.n)
+    qs = [to_dev(gen.attn_q(w, 0), w.q_dtype, device)]
+    iqs = [to_dev(gen.index_q(w, 0), w.idx_dtype, device)]
+    new_kv = torch.from_numpy(gen.kv_rows(w, 0, P0, w.n)).to(device)
+    new_rows = torch.from_numpy(np.arange(P0, w.n, dtype=np.int64)).to(device)
+    return cache, qs, iqs, new_kv, new_rows, (P0 + 1 + np.arange(T)).astype(np.int64)
+
+
 def to_dev(a, kind, device):
     import torch
 
@@ -89,8 +126,8 @@ def layer_inputs(w, device):
 # ------------------------------------------------------------------ accounting
 
 def algorithmic_bytes(w, lens):
-    """Bytes the method must move per decode step, by kernel family."""
-    R, K = w.B, w.K
+    """Bytes the method must move per step (one decode token per sequence, or one prefill chunk), by kernel family."""
+    R, K = w.rows, w.K
     qb = 2 if w.q_dtype == "bf16" else 4
     kb = 2 if w.idx_dtype == "bf16" else 4
     out = {"quantize": R * (512 * 4 + KV_ROW_BYTES)}
@@ -111,7 +148,36 @@ def algorithmic_bytes(w, lens):
 
 
 def attention_flops(w):
-    return 4.0 * w.B * w.Hq * w.K * 512
+    return 4.0 * w.rows * w.Hq * w.K * 512
+
+
+def index_flops(w, lens):
+    """fp32 multiply-adds of the indexer scan: every visible entry, every indexer head, 64 channels."""
+    return 2.0 * float(np.sum(lens)) * w.H * 64
+
+
+def cpu_baseline_prefill(w, sample_rows):
+    """The CPU oracle on `sample_rows` rows of the prefill chunk: indexer scan over the row's visible
+    entries, exact top-K and attention."""
+    import oracle
+
+    T = w.prefill_tokens
+    P0 = w.n - T
+    rows = [int(r) for r in np.linspace(0, T - 1, sample_rows)]
+    log("cpu baseline: preparing the oracle cache (%d entries)" % w.n)
+    codes, scales = oracle.quantize(gen.kv_rows(w, 0, 0, w.n))
+    ik = gen.idx_k_rows(w, 0, 0, w.n)
+    iq = gen.index_q(w, 0)
+    q = gen.attn_q(w, 0)
+    t0 = time.perf_counter()
+    for r in rows:
+        nvis = P0 + r + 1
+        sel = oracle.topk(oracle.index_scores(iq[r], ik[:nvis]), w.K)
+        oracle.attention(q[r], codes, scales, sel, nvis, w.softmax_scale)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d chunk rows (indexer scan over ~%d entries, top-K, attention each); %.1f s wall"
+                      % (len(rows), T, P0, dt)}
 
 
 def traffic_from_profiles(kernel_file):
@@ -190,6 +256,7 @@ def _hip_runtime():
         _HIP.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
         _HIP.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
         _HIP.hipEventDestroy.argtypes = [P]
+        _HIP.hipEventRecord.argtypes = [P, P]
     return _HIP
 
 
@@ -207,6 +274,10 @@ class HipEvent:
         if rc != 0:
             raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
         self.cuda_event = self._h.value
+        # recorded once up front, so that a kernel a step never launches reads as 0
+        import torch
+
+        _hip_runtime().hipEventRecord(self._h, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
 
     def elapsed_time(self, other) -> float:
         import ctypes
@@ -231,7 +302,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5"])
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5", "c4"])
     ap.add_argument("--cpu-rows", type=int, default=16)
     ap.add_argument("--cpu-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -252,17 +323,20 @@ def main():
 
     device = torch.device("cuda:0")
     w = gen.get(args.workload)
-    lens = gen.seq_lens(w)
     log("workload %s: %s" % (w.name, w.description))
     t = time.time()
-    cache, _ = build_cache(w, lens, device)
-    log("cache built in %.1f s (%d rows)" % (time.time() - t, int(lens.sum())))
-    qs, iqs = layer_inputs(w, device)
-    new_rows = np.concatenate([[0], np.cumsum(lens)[:-1]]) + lens - 1
-    new_kv = torch.from_numpy(np.concatenate([gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b]))
-                                              for b in range(w.B)])).to(device)
-    new_rows_t = torch.from_numpy(new_rows.astype(np.int64)).to(device)
-    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, cache.max_visible,
+    if w.is_prefill:
+        cache, qs, iqs, new_kv, new_rows_t, lens = build_prefill(w, device)
+    else:
+        lens = gen.seq_lens(w)
+        cache, _ = build_cache(w, lens, device)
+        qs, iqs = layer_inputs(w, device)
+        new_rows = np.concatenate([[0], np.cumsum(lens)[:-1]]) + lens - 1
+        new_kv = torch.from_numpy(np.concatenate([gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b]))
+                                                  for b in range(w.B)])).to(device)
+        new_rows_t = torch.from_numpy(new_rows.astype(np.int64)).to(device)
+    log("inputs built in %.1f s (%d cache rows)" % (time.time() - t, int(cache.kv_codes.shape[0])))
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.rows, w.Hq, w.H, w.K, cache.max_visible,
                        qs[0].dtype, device)
 
     def step():
@@ -343,7 +417,7 @@ def main():
     byt = algorithmic_bytes(w, lens)
     attn_flops = attention_flops(w)
     kern = {
-        "index_scan": {"avg_us": per_kernel_us["index_scan"], "bytes": byt["index_scan"]},
+        "index_scan": {"avg_us": per_kernel_us["index_scan"], "bytes": byt["index_scan"], "flops": index_flops(w, lens)},
         "reindex_score": {"avg_us": per_kernel_us["reindex_score"], "bytes": byt["reindex_score"] //
                           max(1, n_launch["reindex_score"])},
         "attention": {"avg_us": per_kernel_us["attention"], "bytes": byt["attention_per_layer"],
@@ -357,7 +431,10 @@ def main():
             v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
         if "flops" in v and v["avg_us"] > 0:
             v["TFLOPs"] = v["flops"] / (v["avg_us"] * 1e6)
-            v["mfma_frac"] = v["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+            if k == "attention":
+                v["mfma_frac"] = v["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+            else:
+                v["valu_fp32_frac"] = v["TFLOPs"] / VALU_F32_PEAK_TFLOPS
         v["per_step_us"] = v["avg_us"] * n_launch.get(k, 1)
     dominant = max(["index_scan", "attention", "reindex_score"], key=lambda k: kern[k]["per_step_us"])
     dk = kern[dominant]
@@ -365,14 +442,18 @@ def main():
         roof = {"kernel": "k_sparse_attn", "bound": "mfma", "achieved": dk["TFLOPs"],
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": dk["mfma_frac"],
                 "traffic": traffic_from_profiles("k_attn.hip")}
+    elif dominant == "index_scan" and w.is_prefill:
+        # every chunk row rescans the (cache-resident) keys: the fp32 fmaf chains bound it
+        roof = {"kernel": "k_scan_full", "bound": "alu", "achieved": dk["TFLOPs"], "peak": VALU_F32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": dk["valu_fp32_frac"], "traffic": traffic_from_profiles("k_index.hip")}
     else:
         roof = {"kernel": "k_scan_full" if dominant == "index_scan" else "k_score_pool", "bound": "hbm",
                 "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["hbm_frac"],
                 "traffic": traffic_from_profiles("k_index.hip")}
 
-    tokens_s = w.B / (ms_step * 1e-3)
+    tokens_s = w.rows / (ms_step * 1e-3)
     res = {
-        "metric": METRIC,
+        "metric": METRIC if not w.is_prefill else "CSA2 prefill tokens/s (FP4 KV), 4096-token chunk at 262K ctx, 1 GPU",
         "value": tokens_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -384,17 +465,19 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: %s" % (w.name, w.description), "batch": w.B, "ctx": int(lens.max()),
+        "config": {"workload": "%s: %s" % (w.name, w.description), "batch": w.B, "rows": w.rows,
+                   "ctx": int(lens.max()),
                    "layers": [L.mode for L in w.layers], "top_k": w.K, "q_heads": w.Hq, "indexer_heads": w.H,
                    "kv": "fp4 e2m1 + e4m3 scale per 16 ch (288 B/entry)",
                    "compute": "indexer fp32 fmaf; attention f16 MFMA, f32 accumulate", "parallelism": "single GPU",
-                   "launch": "eager" if graph is None else "hip graph replay of one decode step"},
+                   "launch": "eager" if graph is None else "hip graph replay of one step"},
         "roofline": roof,
         "kernels": kern,
     }
     res["chain_hbm_GBps"] = byt["total"] / (ms_step * 1e-3) / 1e9
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps)
+        res["cpu_baseline"] = (cpu_baseline_prefill(w, args.cpu_rows) if w.is_prefill
+                               else cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
