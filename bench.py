@@ -99,7 +99,7 @@ def build_prefill(w, device, chunk=65536):
     torch.cuda.synchronize()
     starts = torch.zeros(T, dtype=torch.int64, device=device)
     vis = torch.from_numpy((P0 + 1 + np.arange(T)).astype(np.int32)).to(device)
-    cache = Cache(codes, scales, idx_k, starts, vis, w.n)
+    cache = Cache(codes, scales, idx_k, starts, vis, w.n, shared_segment=True)
     qs = [to_dev(gen.attn_q(w, 0), w.q_dtype, device)]
     iqs = [to_dev(gen.index_q(w, 0), w.idx_dtype, device)]
     new_kv = torch.from_numpy(gen.kv_rows(w, 0, P0, w.n)).to(device)
@@ -337,7 +337,7 @@ def main():
         new_rows_t = torch.from_numpy(new_rows.astype(np.int64)).to(device)
     log("inputs built in %.1f s (%d cache rows)" % (time.time() - t, int(cache.kv_codes.shape[0])))
     chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.rows, w.Hq, w.H, w.K, cache.max_visible,
-                       qs[0].dtype, device)
+                       qs[0].dtype, device, shared_segment=cache.shared_segment)
 
     def step():
         chain.step(cache, qs, iqs, w.softmax_scale, new_kv=new_kv, new_kv_rows=new_rows_t)
@@ -443,9 +443,10 @@ def main():
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": dk["mfma_frac"],
                 "traffic": traffic_from_profiles("k_attn.hip")}
     elif dominant == "index_scan" and w.is_prefill:
-        # every chunk row rescans the (cache-resident) keys: the fp32 fmaf chains bound it
-        roof = {"kernel": "k_scan_full", "bound": "alu", "achieved": dk["TFLOPs"], "peak": VALU_F32_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": dk["valu_fp32_frac"], "traffic": traffic_from_profiles("k_index.hip")}
+        # the chunk's rows share one key segment: the scores are a bf16 MFMA product (two passes)
+        roof = {"kernel": "k_pf_pass", "bound": "mfma", "achieved": dk["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": dk["TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
+                "traffic": traffic_from_profiles("k_index.hip")}
     else:
         roof = {"kernel": "k_scan_full" if dominant == "index_scan" else "k_score_pool", "bound": "hbm",
                 "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["hbm_frac"],

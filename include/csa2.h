@@ -58,6 +58,7 @@ extern "C" {
 /* indexer modes */
 #define CSA2_FULL 0
 #define CSA2_REINDEX 1
+#define CSA2_FULL_SHARED 2 /* Full for rows that share one key segment (a prefill chunk) */
 
 /* geometry of one cache entry ("FP4 cache entries, and why they're safe":
  * 512 values x 4 bits + 512/16 scales x 1 byte = 256 + 32 = 288 bytes) */
@@ -113,6 +114,17 @@ int32_t csa2_quantize_kv_fp4(const void* x, int32_t x_dtype, int64_t n_tokens, i
  *   i < pool_stride if pool_len is NULL); entries < 0 or >= row_visible[r]
  *   are skipped.  Valid entries must be unique and ascending (as
  *   CSA2_FULL emits them); ties are broken by pool order.
+ * mode = CSA2_FULL_SHARED: CSA2_FULL for query rows that all read the same
+ *   key segment, the one starting at row_kv_start[0] (row_kv_start[r] for
+ *   r > 0 is not read), row r seeing its first row_visible[r] entries: a
+ *   prefill chunk whose token r sits at position P0 + r sees
+ *   row_visible[r] = P0 + r + 1.  Results are identical to CSA2_FULL over
+ *   that segment.  With bf16 queries and keys, n_heads in {4, 8, 16} and no
+ *   pool, the rows are first scored as one bf16 MFMA product with a proven
+ *   bound on its error, every entry that the bound cannot exclude from the
+ *   top_k is rescored with the exact chain above, and the selection among
+ *   them is exact; a row with more than 16,384 such candidates is scanned
+ *   exactly in full.  Otherwise it runs as CSA2_FULL does.
  *
  * idx_q        [n_rows, n_heads, head_dim] of q_dtype.
  * idx_k        [cache rows, head_dim] of k_dtype; row_kv_start[r] + j.

@@ -34,6 +34,7 @@ class Cache:
     row_kv_start: torch.Tensor  # [R] int64
     row_visible: torch.Tensor   # [R] int32
     max_visible: int
+    shared_segment: bool = False  # every row reads the segment at row_kv_start[0] (a prefill chunk)
 
 
 @dataclass(frozen=True)
@@ -69,9 +70,11 @@ class LayerChain:
     """Runs a fixed mode sequence for R query rows over one cache."""
 
     def __init__(self, layers: Sequence[LayerSpec], n_rows: int, n_heads: int, idx_heads: int, top_k: int,
-                 max_visible: int, q_dtype: torch.dtype, device="cuda", out_dtype=torch.float32):
+                 max_visible: int, q_dtype: torch.dtype, device="cuda", out_dtype=torch.float32,
+                 shared_segment: bool = False):
         validate_modes(layers)
         self.layers = list(layers)
+        self.full_mode = csa2.FULL_SHARED if shared_segment else csa2.FULL
         self.R, self.Hq, self.H, self.K = n_rows, n_heads, idx_heads, top_k
         self.max_visible = max_visible
         dev = torch.device(device)
@@ -82,8 +85,8 @@ class LayerChain:
         last_pool = 0
         for i, L in enumerate(self.layers):
             if L.mode == "full":
-                ws = max(ws, csa2.index_topk_workspace_size(csa2.FULL, n_rows, idx_heads, max_visible, 0, top_k,
-                                                            L.pool_size))
+                ws = max(ws, csa2.index_topk_workspace_size(self.full_mode, n_rows, idx_heads, max_visible, 0,
+                                                            top_k, L.pool_size))
                 last_pool = L.pool_size
                 if L.pool_size:
                     self.pool[i] = (torch.empty(n_rows, L.pool_size, dtype=torch.int32, device=dev),
@@ -109,7 +112,7 @@ class LayerChain:
                 if new_kv is not None and i == 0:
                     csa2.quantize_kv_fp4(new_kv, cache.kv_codes, cache.kv_scales, new_kv_rows, stream=stream)
                 pool, plen = self.pool.get(i, (None, None))
-                csa2.index_topk(csa2.FULL, idx_q[i], cache.idx_k, cache.row_kv_start, cache.row_visible,
+                csa2.index_topk(self.full_mode, idx_q[i], cache.idx_k, cache.row_kv_start, cache.row_visible,
                                 cache.max_visible, self.K, self.idx[i], self.ws_index, pool_size=L.pool_size,
                                 out_pool=pool, out_pool_len=plen, stream=stream)
                 last_full_pool = (pool, plen)

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
 F32, BF16 = 0, 1
-FULL, REINDEX = 0, 1
+FULL, REINDEX, FULL_SHARED = 0, 1, 2
 MAX_TOP_K = 4096
 KERNEL_QUANT, KERNEL_INDEX_SCAN, KERNEL_REINDEX_SCORE, KERNEL_ATTN, KERNEL_ATTN_COMBINE = 1, 2, 3, 4, 5
 EXPORTED = (

@@ -85,7 +85,8 @@ int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t
                         int32_t pool_size, int32_t block_size, int32_t* out_pool, int32_t* out_pool_len,
                         void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "csa2_index_topk";
-  if (mode != CSA2_FULL && mode != CSA2_REINDEX) return fail(CSA2_E_INVALID, "%s: unknown mode %d", fn, mode);
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_FULL_SHARED)
+    return fail(CSA2_E_INVALID, "%s: unknown mode %d", fn, mode);
   if (n_rows < 0) return fail(CSA2_E_INVALID, "%s: n_rows < 0", fn);
   if (!dtype_ok(q_dtype) || !dtype_ok(k_dtype)) return fail(CSA2_E_INVALID, "%s: dtype is not F32/BF16", fn);
   if (head_dim != kIdxDim) return fail(CSA2_E_UNSUPPORTED, "%s: head_dim %d (only 64 is built)", fn, head_dim);
@@ -106,7 +107,7 @@ int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t
     if (pool_stride < 1) return fail(CSA2_E_INVALID, "%s: REINDEX needs pool_stride >= 1", fn);
     if (pool_size != 0) return fail(CSA2_E_INVALID, "%s: REINDEX does not emit a pool (pool_size must be 0)", fn);
   }
-  if (mode == CSA2_FULL && pool_size != 0) {
+  if (mode != CSA2_REINDEX && pool_size != 0) {
     if (pool_size < 0 || block_size != kBlock || pool_size % kBlock != 0)
       return fail(CSA2_E_INVALID, "%s: pool_size %d must be a positive multiple of block_size 8 (got %d)", fn,
                   pool_size, block_size);

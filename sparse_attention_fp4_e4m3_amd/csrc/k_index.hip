@@ -164,6 +164,17 @@ __global__ __launch_bounds__(256) void k_prep(const void* __restrict__ idx_q, in
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nhist; i += stride) hist[i] = 0u;
 }
 
+// zero the approximate path's histograms and accumulators (three arrays and one word)
+__global__ __launch_bounds__(256) void k_zero(uint32_t* __restrict__ x, int64_t nx, uint32_t* __restrict__ y,
+                                              int64_t ny, uint32_t* __restrict__ z, int64_t nz,
+                                              uint32_t* __restrict__ one) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nx; i += stride) x[i] = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ny; i += stride) y[i] = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nz; i += stride) z[i] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *one = 0u;
+}
+
 struct ScoreArgs {
   int H;
   const void* idx_k;
@@ -180,6 +191,8 @@ struct ScoreArgs {
   uint32_t* hist_s;           // [R][kD1]
   uint32_t* hist_b;           // [R][kD1]
   int tiles_per_wg;
+  const uint32_t* row_mask;   // [R] nonzero = score this row; null = every row
+  int shared_start;           // every row reads the segment at row_start[0]
 };
 
 template <int KDT>
@@ -212,13 +225,14 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
 
   const int H = HC > 0 ? HC : a.H;
   const int r = blockIdx.y;
+  if (a.row_mask && !a.row_mask[r]) return;
   const int vis = clampv(a.row_visible[r], a.max_visible);
-  const int n = REINDEX ? a.pool_stride : vis;
+  int plen = 0;
+  if (REINDEX) plen = a.pool_len ? clampv(a.pool_len[r], a.pool_stride) : a.pool_stride;
+  const int n = REINDEX ? plen : vis;  // slots scored: Reindex, the pool's valid length
   const int64_t base0 = (int64_t)blockIdx.x * a.tiles_per_wg * kWGKeys;
   if (base0 >= n) return;
   const int ntiles = (int)std::min<int64_t>(a.tiles_per_wg, ceil_div(n - base0, kWGKeys));
-  int plen = 0;
-  if (REINDEX) plen = a.pool_len ? clampv(a.pool_len[r], a.pool_stride) : a.pool_stride;
   if (!REINDEX) {
     for (int b = threadIdx.x; b < kD1 / 2; b += kThreads) {
       h1[b] = 0u;
@@ -226,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
     }
     __syncthreads();
   }
-  const int64_t rs = a.row_start[r];
+  const int64_t rs = a.row_start[a.shared_start ? 0 : r];
   const uint8_t* kbase = static_cast<const uint8_t*>(a.idx_k);
   float* srow = a.scores + (int64_t)r * a.n_pad;
   const int32_t* prow = REINDEX ? a.pool + (int64_t)r * a.pool_stride : nullptr;
@@ -355,10 +369,12 @@ struct SelArgs {
   int32_t* out_pool;     // [R, pool_size]
   int32_t* out_pool_len; // [R]
   int pool_size;
+  const int32_t* pool_len;   // Reindex: valid slots per row (null = pool_stride)
+  const uint32_t* row_mask;  // [R] nonzero = select for this row; null = every row
 };
 
 __device__ __forceinline__ int series_len(const SelArgs& a, int series, int r) {
-  if (a.mode == CSA2_REINDEX) return a.pool_stride;
+  if (a.mode == CSA2_REINDEX) return a.pool_len ? clampv(a.pool_len[r], a.pool_stride) : a.pool_stride;
   const int v = clampv(a.row_visible[r], a.max_visible);
   return series == 0 ? v : (v + kBlock - 1) / kBlock;
 }
@@ -550,6 +566,7 @@ __global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
   __shared__ uint32_t red[32];
   const int series = blockIdx.z, r = blockIdx.y;
   if (series >= a.nseries) return;
+  if (a.row_mask && !a.row_mask[r]) return;
   const Series& S = a.s[series];
   const int n = series_len(a, series, r);
   const int64_t wg_base = (int64_t)blockIdx.x * 4 * kSub;
@@ -598,7 +615,354 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
   uint32_t* lkey = red + 32;                  // kFinCap
   int32_t* lpos = reinterpret_cast<int32_t*>(lkey + kFinCap);
   if ((int)blockIdx.y >= a.nseries) return;
+  if (a.row_mask && !a.row_mask[blockIdx.x]) return;
   finalize_row<kFinThreads>(a, blockIdx.y, blockIdx.x, hist, pre, red, lkey, lpos, kFinCap);
+}
+
+// ------------------------------------------------------------ prefill: approximate MFMA passes
+//
+// When every query row reads the same key segment (a prefill chunk over one
+// cache), the indexer scores form a GEMM of (rows x heads) against keys.  The
+// chunk's rows are first scored with bf16 MFMA (fp32 accumulate): one pass
+// builds each row's first-digit histogram of the approximate scores A, a
+// second pass marks as candidates every entry whose A could still belong to
+// the exact top-K.  Let E be the exact score (the fmaf-chain definition) and
+// S the real-number score.  The MFMA dot and the exact chain each differ from
+// S by at most gamma_64 * sum_c |q_c k_c| per head, and the head sums by at
+// most gamma_7 of their size, with gamma_n = n u / (1 - n u); u = 2^-23 covers
+// any fp32 summation order with round-to-nearest or truncation.  By
+// Cauchy-Schwarz sum_c |q_c k_c| <= |q_h| |k|, so
+//   |A - E| <= eps_j = c |k_j| sum_h |q_h|,   c = 2 (gamma_64 + gamma_7 (1 + gamma_64)),
+// taken here with further safety factors.  If t_A is the K-th largest A,
+// at least K entries have E >= t_A - eps_max, so every entry of the exact
+// top-K (ties included) has A_j + eps_j >= t_A - eps_max >= lo(b) - eps_max,
+// where lo(b) is the lower edge of the histogram bin holding t_A.  Those
+// candidates are then rescored exactly and selected exactly, so the result is
+// the exact top-K.  A row whose candidates overflow the list falls back to
+// the exact full scan.
+
+constexpr int kPfRows = 8;       // query rows per workgroup of the approximate passes
+constexpr int kPfRange = 32768;  // keys per workgroup of the candidate pass
+constexpr int kPfCap = 16384;    // candidates kept per row (more: exact fallback for that row)
+constexpr int kPfDepth = 4;      // 32-key steps in flight per wave
+constexpr int kPfSample = 16;    // the provisional bound samples every 16th 32-key step
+// error constant c of the bound above for H heads, with a factor 8 of safety
+// on top (so the margin stays valid even if an accumulator kept fewer bits)
+__host__ __device__ constexpr float pf_err(int H) { return 16.0f * (64.0f + (float)H) * 1.1920929e-07f; }
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct PfArgs {
+  const uint16_t* q;          // [R][H][64] bf16 indexer queries
+  const uint8_t* k;           // indexer keys, bf16 rows of 128 bytes
+  const int64_t* row_start;   // segment start = row_start[0]
+  const int32_t* row_visible; // [R]
+  int max_visible;
+  int R;
+  int K;
+  float* knorm;               // [max_visible] |k_j| bound
+  uint32_t* kmax;             // [1] max |k_j| (float bits)
+  float* qn;                  // [R] sum_h |q_h| bound
+  uint32_t* hist;             // [R][kD1] first-digit histograms of A (of a sample, or of every entry)
+  float* plo;                 // [R] candidate bound lo(b) - eps_max (-inf: every valid entry)
+  float* thi;                 // [R] sampled bound lo(b) that the candidate pass certifies
+  uint32_t* nhi;              // [R] entries with A >= thi (certification count)
+  uint32_t* failed;           // [R] 1 = the sampled bound was not certified: full histogram pass
+  const uint32_t* mask;       // [R] rows to process (null = all)
+  int sample;                 // MODE 0: every sample-th 32-key step
+  uint32_t target;            // entries the threshold bin must cover (K, or more for a sample)
+  uint32_t* bits;             // [R][nwords] candidate bitmap
+  int nwords;
+  int32_t* cand;              // [R][kPfCap] candidate positions, ascending
+  int32_t* ccnt;              // [R] candidates (0 on overflow)
+  uint32_t* over;             // [R] 1 = overflow: exact fallback
+  uint32_t* sink;             // one scratch word: target of the stores of lanes that own no bitmap word
+};
+
+// max(x, +0) as one integer max: negative floats (sign bit set, -0 included) compare below 0
+__device__ __forceinline__ float relu0(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// norms: one thread per key of the shared segment, then one per (row, head) query
+__global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
+  const int64_t seg = a.row_start[0];
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.max_visible) {
+    const u32x4* row = reinterpret_cast<const u32x4*>(a.k + (seg + i) * 128);
+    float ss = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const u32x4 v = row[p];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xFFFF0000u);
+        ss = __builtin_fmaf(lo, lo, ss);
+        ss = __builtin_fmaf(hi, hi, ss);
+      }
+    }
+    const float nrm = __fsqrt_rn(ss) * 1.00001f;
+    a.knorm[i] = nrm;
+    atomicMax(a.kmax, __float_as_uint(nrm));  // non-negative floats order like their bits
+  }
+  if (i < (int64_t)a.R * H) {
+    const u32x4* row = reinterpret_cast<const u32x4*>(a.q + i * 64);
+    float ss = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const u32x4 v = row[p];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xFFFF0000u);
+        ss = __builtin_fmaf(lo, lo, ss);
+        ss = __builtin_fmaf(hi, hi, ss);
+      }
+    }
+    atomicAdd(&a.qn[i / H], __fsqrt_rn(ss) * 1.00001f);
+  }
+}
+
+// MODE 0: first-digit histogram of A per row.  MODE 1: candidate bitmap.
+// A workgroup (4 waves) takes kPfRows rows; MODE 0 all keys, MODE 1 one
+// range of kPfRange keys.  Each wave walks 32-key steps (two 16-key MFMA
+// tiles, keys [32p, 32p+32) for p = w, w+4, ...), kPfDepth steps in flight:
+// B operand = the keys, loaded straight from global; A operand = the rows'
+// queries held in registers (M = 16 (row, head) pairs per MFMA tile).  In
+// MODE 1 a step yields one whole bitmap word per row, stored directly.
+template <int MODE, int H>
+__global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
+  constexpr int MT = kPfRows * H / 16;  // M tiles
+  constexpr int RPM = 16 / H;           // rows per M tile
+  extern __shared__ __align__(16) uint32_t pl[];  // MODE 0: kPfRows x kD1/2 packed counters
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int r0 = blockIdx.x * kPfRows;
+  const int64_t seg = a.row_start[0];
+
+  int kend = 0;
+#pragma unroll
+  for (int i = 0; i < kPfRows; ++i)
+    if (r0 + i < a.R) kend = max(kend, clampv(a.row_visible[r0 + i], a.max_visible));
+  const int kbeg = MODE == 0 ? 0 : (int)blockIdx.y * kPfRange;
+  const int klim = MODE == 0 ? kend : min(kend, kbeg + kPfRange);
+  if (kbeg >= klim) return;
+  if (a.mask) {
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < kPfRows; ++i) any |= (r0 + i < a.R) && a.mask[r0 + i] != 0u;
+    if (!any) return;
+  }
+
+  if (MODE == 0) {
+    for (int i = threadIdx.x; i < kPfRows * kD1 / 2; i += 256) pl[i] = 0u;
+  }
+
+  // queries of this lane's M rows: (row, head) = (mt*RPM + n16/H, n16%H), channels 32ks + 8g
+  bf16x8 qa[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = r0 + mt * RPM + n16 / H;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (row < a.R)
+        v = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)row * H + n16 % H) * 64 + 32 * ks + 8 * g);
+      qa[mt][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // this lane's output rows (epilogue role): M row 4g + i -> row mt*RPM + (4g)/H
+  const bool owner = H == 4 ? true : (H == 8 ? (g & 1) == 0 : g == 0);
+  int vis[MT], rowo[MT];
+  uint32_t* wrow[MT];  // MODE 1: this lane's bitmap row, or a scratch word for lanes that do not own one
+  float lo[MT], cq[MT], hi[MT];
+  uint32_t nh[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = r0 + mt * RPM + (4 * g) / H;
+    rowo[mt] = row;
+    wrow[mt] = (owner && n16 == 0 && row < a.R) ? a.bits + (int64_t)row * a.nwords : a.sink;
+    vis[mt] = row < a.R ? min(clampv(a.row_visible[row], a.max_visible), klim) : 0;
+    lo[mt] = 0.0f;
+    cq[mt] = 0.0f;
+    hi[mt] = INFINITY;
+    nh[mt] = 0u;
+    if (MODE == 1 && row < a.R) {
+      lo[mt] = a.plo[row];
+      hi[mt] = a.thi[row];
+      cq[mt] = a.qn[row] * pf_err(H);
+    }
+  }
+  if (MODE == 0) __syncthreads();
+
+  const int sample = MODE == 0 ? a.sample : 1;
+  const int nsteps = ((klim - kbeg + 31) / 32 + sample - 1) / sample;  // steps this workgroup takes
+  struct Step {
+    u32x4 b[2][2];  // [tile][k step]
+    float kn[2];
+  };
+  const uint8_t* kseg = a.k + seg * 128;  // uniform base: loads take a 32-bit lane offset
+  auto load_step = [&](int p, Step& st) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t j = (uint32_t)min(kbeg + 32 * p * sample + 16 * tt + n16, klim - 1);
+      const uint32_t off = j * 128u + 16u * (uint32_t)g;
+      st.b[tt][0] = *reinterpret_cast<const u32x4*>(kseg + off);
+      st.b[tt][1] = *reinterpret_cast<const u32x4*>(kseg + off + 64u);
+      st.kn[tt] = MODE == 1 ? a.knorm[j] : 0.0f;
+    }
+  };
+  // approximate score of (this lane's row of M tile mt, key j): ReLU per head, summed over the row's heads
+  auto score = [&](const bf16x8& q0, const bf16x8& q1, const u32x4* b) {
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q0, __builtin_bit_cast(bf16x8, b[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1, __builtin_bit_cast(bf16x8, b[1]), acc, 0, 0, 0);
+    float sc = (relu0(acc[0]) + relu0(acc[1])) + (relu0(acc[2]) + relu0(acc[3]));
+    if (H >= 8) {
+      auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
+      sc = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+    if (H >= 16) {
+      auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
+      sc = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+    return sc;
+  };
+
+  Step ring[kPfDepth];
+#pragma unroll
+  for (int d = 0; d < kPfDepth; ++d) load_step(min(w + 4 * d, nsteps - 1), ring[d]);
+  for (int p0 = w; p0 < nsteps; p0 += 4 * kPfDepth) {
+#pragma unroll
+    for (int d = 0; d < kPfDepth; ++d) {
+      const int p = p0 + 4 * d;
+      if (p >= nsteps) break;
+      const Step cur = ring[d];
+      load_step(min(p + 4 * kPfDepth, nsteps - 1), ring[d]);  // clamped: always in bounds
+      const int j0 = kbeg + 32 * p * sample;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (MODE == 0) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const float sc = score(qa[mt][0], qa[mt][1], cur.b[tt]);
+            if (owner && j0 + 16 * tt + n16 < vis[mt]) hist_add(pl + (rowo[mt] - r0) * (kD1 / 2), __float_as_uint(sc) >> kS1);
+          }
+        } else {
+          unsigned long long m[2];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const float sc = score(qa[mt][0], qa[mt][1], cur.b[tt]);
+            const bool ok = j0 + 16 * tt + n16 < vis[mt];
+            m[tt] = __ballot(ok && __builtin_fmaf(cq[mt], cur.kn[tt], sc) >= lo[mt]);
+            nh[mt] += (ok && sc >= hi[mt]) ? 1u : 0u;
+          }
+          // the bitmap words of the rows of lane groups 0 and 2 (wave-uniform), then this lane's
+          const uint32_t w0 = (uint32_t)(m[0] & 0xFFFFull) | ((uint32_t)(m[1] & 0xFFFFull) << 16);
+          const uint32_t w1 = (uint32_t)((m[0] >> 16) & 0xFFFFull) | ((uint32_t)((m[1] >> 16) & 0xFFFFull) << 16);
+          const uint32_t w2 = (uint32_t)((m[0] >> 32) & 0xFFFFull) | ((uint32_t)((m[1] >> 32) & 0xFFFFull) << 16);
+          const uint32_t w3 = (uint32_t)(m[0] >> 48) | ((uint32_t)(m[1] >> 48) << 16);
+          const uint32_t word = g == 0 ? w0 : (g == 1 ? w1 : (g == 2 ? w2 : w3));
+          wrow[mt][wrow[mt] == a.sink ? 0 : j0 / 32] = word;  // every lane stores: no branch
+        }
+      }
+    }
+  }
+  if (MODE == 1) {
+    // per-lane counts of the entries reaching thi: sum over the 16 lanes of each owner group
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      uint32_t c = nh[mt];
+      c += __shfl_xor(c, 1, 64);
+      c += __shfl_xor(c, 2, 64);
+      c += __shfl_xor(c, 4, 64);
+      c += __shfl_xor(c, 8, 64);
+      if (owner && n16 == 0 && rowo[mt] < a.R && c) atomicAdd(a.nhi + rowo[mt], c);
+    }
+  }
+  if (MODE == 0) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kPfRows * (kD1 / 2); i += 256) {
+      const int rloc = i / (kD1 / 2), wd = i % (kD1 / 2);
+      const uint32_t v = pl[i];
+      if (r0 + rloc < a.R && v) {
+        uint32_t* gh = a.hist + (int64_t)(r0 + rloc) * kD1 + 2 * wd;
+        if (v & 0xFFFFu) atomicAdd(gh, v & 0xFFFFu);
+        if (v >> 16) atomicAdd(gh + 1, v >> 16);
+      }
+    }
+  }
+}
+
+// per row: the bin holding the target-th largest approximate score -> candidate bound.
+// From a sample (sampled = 1) the bound is provisional: the candidate pass
+// counts the entries with A >= thi and k_pf_certify checks that at least K
+// do; a row whose sample is too small is left failed at once.
+__global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a, int H, int sampled) {
+  __shared__ uint32_t red[32];
+  const int r = blockIdx.x;
+  if (a.mask && !a.mask[r]) return;
+  uint32_t above, total;
+  const int b = find_bin<256, kD1>(a.hist + (int64_t)r * kD1, a.target, &above, &total, red);
+  if (threadIdx.x == 0) {
+    if (b < 0) {
+      // sample: too few entries to place the bound -> no candidates now, certification fails;
+      // every entry: fewer than K valid entries, all of them are candidates
+      a.plo[r] = sampled ? INFINITY : -INFINITY;
+      a.thi[r] = sampled ? INFINITY : -INFINITY;
+    } else {
+      const float edge = __uint_as_float((uint32_t)b << kS1);
+      const float emax = a.qn[r] * pf_err(H) * __uint_as_float(*a.kmax);
+      a.plo[r] = (edge - emax) - 1e-6f * edge;  // nudged down: rounding of the subtraction
+      a.thi[r] = edge;
+    }
+  }
+}
+
+// per row: the provisional bound holds if at least K entries reach it
+__global__ __launch_bounds__(256) void k_pf_certify(PfArgs a) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < a.R) a.failed[r] = a.nhi[r] < (uint32_t)a.K ? 1u : 0u;
+}
+
+// per row: candidate bitmap -> ascending positions (or the overflow flag).
+// The row's words are staged in LDS with coalesced loads (in chunks of
+// kPfCompactWords); thread t then owns a contiguous run of each chunk.
+constexpr int kPfCompactWords = 8192;
+__global__ __launch_bounds__(256) void k_pf_compact(PfArgs a) {
+  __shared__ uint32_t red[32];
+  __shared__ uint32_t wl[kPfCompactWords];
+  const int r = blockIdx.x;
+  const int vis = clampv(a.row_visible[r], a.max_visible);
+  const int nw = (vis + 31) / 32;
+  const uint32_t* bw = a.bits + (int64_t)r * a.nwords;
+  int32_t* out = a.cand + (int64_t)r * kPfCap;
+  uint32_t base = 0;  // candidates in earlier chunks
+  for (int c0 = 0; c0 < nw; c0 += kPfCompactWords) {
+    const int cn = min(kPfCompactWords, nw - c0);
+    __syncthreads();  // the previous chunk is consumed
+    for (int i = threadIdx.x; i < cn; i += 256) wl[i] = bw[c0 + i];
+    __syncthreads();
+    const int per = (cn + 255) / 256;
+    const int w0 = min(cn, (int)threadIdx.x * per), w1 = min(cn, w0 + per);
+    uint32_t c = 0;
+    for (int i = w0; i < w1; ++i) c += __popc(wl[i]);
+    uint32_t total;
+    uint32_t at = base + block_excl_sum<256>(c, red, &total);
+    if (base + total <= (uint32_t)kPfCap) {
+      for (int i = w0; i < w1; ++i) {
+        uint32_t m = wl[i];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          out[at++] = 32 * (c0 + i) + bit;
+        }
+      }
+    }
+    base += total;
+  }
+  if (threadIdx.x == 0) {
+    const bool overflow = base > (uint32_t)kPfCap;
+    a.ccnt[r] = overflow ? 0 : (int32_t)base;
+    a.over[r] = overflow ? 1u : 0u;
+  }
 }
 
 struct Carve {
@@ -613,6 +977,7 @@ struct Carve {
 };
 
 struct Layout {
+  // exact path (Full and Reindex; the per-row fallback of the shared-segment mode)
   float* qf;
   uint32_t* hist;  // [2][R][kD1] first-digit histograms
   float* scores;
@@ -622,13 +987,31 @@ struct Layout {
   uint32_t* counts[2];
   int64_t n_pad, nb_pad;
   int nsub, nbsub;
+  // shared-segment (prefill) approximate path
+  float* knorm;
+  uint32_t* kmax;
+  float* qn;
+  uint32_t* phist;
+  float* plo;
+  float* thi;
+  uint32_t* nhi;
+  uint32_t* failed;
+  uint32_t* phist2;
+  uint32_t* bits;
+  int nwords;
+  int32_t* cand;
+  int32_t* ccnt;
+  uint32_t* over;
+  uint32_t* sink;
+  float* cscore;   // [R][kPfCap] exact scores of the candidates
   size_t bytes;
 };
 
 Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stride, int pool_size) {
   Layout L{};
   Carve c{static_cast<char*>(base)};
-  const bool full = mode == CSA2_FULL;
+  const bool shared = mode == CSA2_FULL_SHARED;
+  const bool full = mode == CSA2_FULL || shared;
   const int64_t n = full ? max_visible : pool_stride;
   const bool pool_on = full && pool_size > 0;
   const int64_t nb = pool_on ? ceil_div(max_visible, kBlock) : 0;
@@ -649,6 +1032,24 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
     L.cand_key[1] = c.take<float>((size_t)R * 2 * L.nb_pad);
     L.cand_pos[1] = c.take<int32_t>((size_t)R * 2 * L.nb_pad);
     L.counts[1] = c.take<uint32_t>((size_t)R * L.nbsub);
+  }
+  if (shared && !pool_on) {
+    L.nwords = (int)ceil_div(std::max<int64_t>(max_visible, 1), 32);
+    L.knorm = c.take<float>((size_t)std::max(max_visible, 1));
+    L.kmax = c.take<uint32_t>(1);
+    L.qn = c.take<float>((size_t)R);
+    L.phist = c.take<uint32_t>((size_t)R * kD1);
+    L.plo = c.take<float>((size_t)R);
+    L.thi = c.take<float>((size_t)R);
+    L.nhi = c.take<uint32_t>((size_t)R);
+    L.failed = c.take<uint32_t>((size_t)R);
+    L.phist2 = c.take<uint32_t>((size_t)R * kD1);
+    L.bits = c.take<uint32_t>((size_t)R * L.nwords);
+    L.cand = c.take<int32_t>((size_t)R * kPfCap);
+    L.ccnt = c.take<int32_t>((size_t)R);
+    L.over = c.take<uint32_t>((size_t)R);
+    L.sink = c.take<uint32_t>(64);
+    L.cscore = c.take<float>((size_t)R * kPfCap);
   }
   L.bytes = c.off;
   return L;
@@ -683,19 +1084,23 @@ size_t topk_workspace_bytes(int mode, int R, int H, int max_visible, int pool_st
 
 int topk_max_visible() { return 1024 * kSub; }
 
-hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k, int k_dtype,
-                             const int64_t* row_start, const int32_t* row_visible, int max_visible,
-                             const int32_t* pool, const int32_t* pool_len, int pool_stride, int top_k,
-                             int32_t* out_idx, int pool_size, int32_t* out_pool, int32_t* out_pool_len, void* ws,
-                             hipStream_t s) {
+namespace {
+
+// the exact path: scan (Full: every visible entry; Reindex: the pool), then
+// the exact selection; row_mask restricts it to flagged rows
+void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H, const void* idx_k, int k_dtype,
+               const int64_t* row_start, const int32_t* row_visible, int max_visible, const int32_t* pool,
+               const int32_t* pool_len, int pool_stride, int top_k, int32_t* out_idx, int pool_size,
+               int32_t* out_pool, int32_t* out_pool_len, const uint32_t* row_mask, float* scores,
+               int64_t score_stride, bool prep_done, bool record, const void* idx_q, hipStream_t s) {
   const bool full = mode == CSA2_FULL;
   const bool pool_on = full && pool_size > 0;
-  Layout L = layout(ws, mode, R, H, max_visible, pool_stride, pool_size);
-  const int64_t nq = (int64_t)R * H * kIdxDim;
-  const int64_t nhist = full ? (int64_t)R * kD1 * 2 : 0;
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(std::max(nq, nhist), 256))), dim3(256),
-                     0, s, idx_q, q_dtype, R, H, L.qf, L.hist, nhist);
-
+  if (!prep_done) {
+    const int64_t nq = (int64_t)R * H * kIdxDim;
+    const int64_t nhist = full ? (int64_t)R * kD1 * 2 : 0;
+    hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(std::max(nq, nhist), 256))),
+                       dim3(256), 0, s, idx_q, q_dtype, R, H, L.qf, L.hist, nhist);
+  }
   const int64_t n = full ? max_visible : pool_stride;
   if (n > 0) {
     ScoreArgs sa{};
@@ -707,22 +1112,23 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
     sa.pool = pool;
     sa.pool_len = pool_len;
     sa.pool_stride = pool_stride;
-    sa.scores = L.scores;
-    sa.n_pad = L.n_pad;
+    sa.scores = scores;
+    sa.n_pad = score_stride;
     sa.bmax = L.bmax;
     sa.nb_pad = L.nb_pad;
     sa.hist_s = L.hist;
     sa.hist_b = L.hist + (size_t)R * kD1;
+    sa.row_mask = row_mask;
+    sa.shared_start = shared ? 1 : 0;
     // Full: about three workgroups per CU over the whole batch (each scans
     // tiles_per_wg x 256 consecutive entries); Reindex: 256 pool slots each
-    const int64_t tiles = ceil_div(n, (int64_t)kWGKeys);
     // (at most 255 tiles = 65,280 entries per workgroup: its packed 16-bit histogram counters cannot overflow)
+    const int64_t tiles = ceil_div(n, (int64_t)kWGKeys);
     sa.tiles_per_wg =
-        full ? (int)std::min<int64_t>(255, ceil_div(tiles, std::max<int64_t>(1, ceil_div((int64_t)kScanSlots, R))))
-             : 1;
+        (int)std::min<int64_t>(255, ceil_div(tiles, std::max<int64_t>(1, ceil_div((int64_t)kScanSlots, R))));
     const dim3 grid((unsigned)ceil_div(tiles, (int64_t)sa.tiles_per_wg), (unsigned)R);
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
-    if (ev.start) (void)hipEventRecord(ev.start, s);
+    if (record && ev.start) (void)hipEventRecord(ev.start, s);
     if (k_dtype == CSA2_BF16) {
       if (!full) dispatch_heads<CSA2_BF16, true, false>(H, sa, L.qf, grid, s);
       else if (pool_on) dispatch_heads<CSA2_BF16, false, true>(H, sa, L.qf, grid, s);
@@ -732,7 +1138,7 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
       else if (pool_on) dispatch_heads<CSA2_F32, false, true>(H, sa, L.qf, grid, s);
       else dispatch_heads<CSA2_F32, false, false>(H, sa, L.qf, grid, s);
     }
-    if (ev.stop) (void)hipEventRecord(ev.stop, s);
+    if (record && ev.stop) (void)hipEventRecord(ev.stop, s);
   }
 
   SelArgs a{};
@@ -741,12 +1147,14 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   a.max_visible = max_visible;
   a.pool_stride = pool_stride;
   a.pool = pool;
+  a.pool_len = pool_len;
+  a.row_mask = row_mask;
   a.out_idx = out_idx;
   a.out_pool = out_pool;
   a.out_pool_len = out_pool_len;
   a.pool_size = pool_size;
   a.nseries = pool_on ? 2 : 1;
-  a.s[0] = Series{L.scores, L.n_pad, L.hist, L.cand_key[0], L.cand_pos[0], L.counts[0], L.nsub, top_k};
+  a.s[0] = Series{scores, score_stride, L.hist, L.cand_key[0], L.cand_pos[0], L.counts[0], L.nsub, top_k};
   if (pool_on)
     a.s[1] = Series{L.bmax, L.nb_pad, L.hist + (size_t)R * kD1, L.cand_key[1], L.cand_pos[1], L.counts[1], L.nbsub,
                     pool_size / kBlock};
@@ -762,6 +1170,127 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
     configured = true;
   }
   hipLaunchKernelGGL(k_finalize, dim3((unsigned)R, (unsigned)a.nseries), dim3(kFinThreads), lds, s, a);
+}
+
+template <int H>
+void launch_pf_pass(int mode, const PfArgs& p, int R, int max_visible, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(R, kPfRows), mode == 0 ? 1u : (unsigned)ceil_div(max_visible, kPfRange));
+  const size_t lds = mode == 0 ? (size_t)kPfRows * kD1 / 2 * 4 : 0;
+  static bool configured[2] = {false, false};
+  if (mode == 0) {
+    if (!configured[0]) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pf_pass<0, H>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      configured[0] = true;
+    }
+    hipLaunchKernelGGL((k_pf_pass<0, H>), grid, dim3(256), lds, s, p);
+  } else {
+    if (!configured[1]) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pf_pass<1, H>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      configured[1] = true;
+    }
+    hipLaunchKernelGGL((k_pf_pass<1, H>), grid, dim3(256), lds, s, p);
+  }
+}
+
+}  // namespace
+
+bool topk_uses_prefill_path(int mode, int q_dtype, int k_dtype, int H, int pool_size) {
+  return mode == CSA2_FULL_SHARED && pool_size == 0 && q_dtype == CSA2_BF16 && k_dtype == CSA2_BF16 &&
+         (H == 4 || H == 8 || H == 16);
+}
+
+hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k, int k_dtype,
+                             const int64_t* row_start, const int32_t* row_visible, int max_visible,
+                             const int32_t* pool, const int32_t* pool_len, int pool_stride, int top_k,
+                             int32_t* out_idx, int pool_size, int32_t* out_pool, int32_t* out_pool_len, void* ws,
+                             hipStream_t s) {
+  const bool shared = mode == CSA2_FULL_SHARED;
+  const int emode = shared ? CSA2_FULL : mode;
+  Layout L = layout(ws, mode, R, H, max_visible, pool_stride, pool_size);
+  if (!topk_uses_prefill_path(mode, q_dtype, k_dtype, H, pool_size)) {
+    run_exact(L, emode, shared, R, q_dtype, H, idx_k, k_dtype, row_start, row_visible, max_visible, pool, pool_len,
+              pool_stride, top_k, out_idx, pool_size, out_pool, out_pool_len, nullptr, L.scores, L.n_pad, false, true,
+              idx_q, s);
+    return hipGetLastError();
+  }
+  // shared segment: approximate MFMA passes -> candidates -> exact rescoring and selection
+  PfArgs p{};
+  p.q = static_cast<const uint16_t*>(idx_q);
+  p.k = static_cast<const uint8_t*>(idx_k);
+  p.row_start = row_start;
+  p.row_visible = row_visible;
+  p.max_visible = max_visible;
+  p.R = R;
+  p.K = top_k;
+  p.knorm = L.knorm;
+  p.kmax = L.kmax;
+  p.qn = L.qn;
+  p.hist = L.phist;
+  p.plo = L.plo;
+  p.thi = L.thi;
+  p.nhi = L.nhi;
+  p.failed = L.failed;
+  p.sample = 1;
+  p.target = (uint32_t)top_k;
+  p.bits = L.bits;
+  p.nwords = L.nwords;
+  p.cand = L.cand;
+  p.ccnt = L.ccnt;
+  p.over = L.over;
+  p.sink = L.sink;
+  {
+    // one pass zeroes every histogram and accumulator: the exact path's (fallback), the approximate
+    // histograms, the query-norm sums and the key-norm maximum (they are contiguous in the layout)
+    const int64_t nq = (int64_t)R * H * kIdxDim;
+    const int64_t nhist = (int64_t)R * kD1 * 2;
+    hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(std::max(nq, nhist), 256))),
+                       dim3(256), 0, s, idx_q, q_dtype, R, H, L.qf, L.hist, nhist);
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>(2048, ceil_div((int64_t)R * kD1, 256))), dim3(256),
+                       0, s, L.phist, (int64_t)R * kD1, L.phist2, (int64_t)R * kD1, L.nhi, (int64_t)R, L.kmax);
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)ceil_div((int64_t)R, 256)), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t*>(L.qn), (int64_t)R, L.failed, (int64_t)0, L.failed, (int64_t)0,
+                       L.sink);
+  }
+  const int64_t nn = std::max<int64_t>((int64_t)max_visible, (int64_t)R * H);
+  hipLaunchKernelGGL(k_pf_norms, dim3((unsigned)ceil_div(nn, 256)), dim3(256), 0, s, p, H);
+  auto& ev = profile_events(CSA2_KERNEL_INDEX_SCAN);
+  if (ev.start) (void)hipEventRecord(ev.start, s);
+  auto pass = [&](int mode, const PfArgs& pa) {
+    if (H == 4) launch_pf_pass<4>(mode, pa, R, max_visible, s);
+    else if (H == 8) launch_pf_pass<8>(mode, pa, R, max_visible, s);
+    else launch_pf_pass<16>(mode, pa, R, max_visible, s);
+  };
+  // 1. a provisional bound per row from a 1/kPfSample sample of the keys, with headroom
+  PfArgs ps = p;
+  ps.hist = L.phist;
+  ps.sample = kPfSample;
+  ps.mask = nullptr;
+  ps.target = (uint32_t)ceil_div((int64_t)top_k * 3, 2 * kPfSample);
+  pass(0, ps);
+  hipLaunchKernelGGL(k_pf_thresh, dim3((unsigned)R), dim3(256), 0, s, ps, H, 1);
+  // 2. the candidate pass over every key, counting the entries that certify the bound
+  pass(1, ps);
+  hipLaunchKernelGGL(k_pf_certify, dim3((unsigned)ceil_div(R, 256)), dim3(256), 0, s, ps);
+  // 3. rows whose bound failed: the full histogram, the exact bin bound, the candidate pass again
+  //    (every workgroup without such a row returns at once)
+  PfArgs pf = p;
+  pf.hist = L.phist2;
+  pf.sample = 1;
+  pf.mask = L.failed;
+  pf.target = (uint32_t)top_k;
+  pass(0, pf);
+  hipLaunchKernelGGL(k_pf_thresh, dim3((unsigned)R), dim3(256), 0, s, pf, H, 0);
+  pass(1, pf);
+  if (ev.stop) (void)hipEventRecord(ev.stop, s);
+  hipLaunchKernelGGL(k_pf_compact, dim3((unsigned)R), dim3(256), 0, s, p);
+  // exact scores of the candidates and the exact selection among them (Reindex over the candidate lists)
+  run_exact(L, CSA2_REINDEX, true, R, q_dtype, H, idx_k, k_dtype, row_start, row_visible, max_visible, L.cand,
+            L.ccnt, kPfCap, top_k, out_idx, 0, nullptr, nullptr, nullptr, L.cscore, kPfCap, true, true, idx_q, s);
+  // rows whose candidates overflowed: the exact full scan and selection, for those rows only
+  run_exact(L, CSA2_FULL, true, R, q_dtype, H, idx_k, k_dtype, row_start, row_visible, max_visible, nullptr,
+            nullptr, 0, top_k, out_idx, 0, nullptr, nullptr, L.over, L.scores, L.n_pad, true, false, idx_q, s);
   return hipGetLastError();
 }
 

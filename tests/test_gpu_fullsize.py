@@ -102,9 +102,11 @@ def test_prefill_4096_on_256k():
     vis = dev((P0 + 1 + np.arange(T)).astype(np.int32))
     iq = bench.to_dev(gen.index_q(w, 0), w.idx_dtype, DEV)
     q = bench.to_dev(gen.attn_q(w, 0), w.q_dtype, DEV)
-    ws = torch.empty(csa2.index_topk_workspace_size(csa2.FULL, T, w.H, w.n, 0, w.K, 0), dtype=torch.uint8, device=DEV)
+    # the benchmark's configuration: one shared segment (approximate MFMA passes + exact rescoring)
+    ws = torch.empty(csa2.index_topk_workspace_size(csa2.FULL_SHARED, T, w.H, w.n, 0, w.K, 0), dtype=torch.uint8,
+                     device=DEV)
     idx = torch.empty(T, w.K, dtype=torch.int32, device=DEV)
-    csa2.index_topk(csa2.FULL, iq, idx_k, starts, vis, w.n, w.K, idx, ws)
+    csa2.index_topk(csa2.FULL_SHARED, iq, idx_k, starts, vis, w.n, w.K, idx, ws)
     del ws
     out = torch.empty(T, w.Hq, 512, dtype=torch.float32, device=DEV)
     lse = torch.empty(T, w.Hq, dtype=torch.float32, device=DEV)
