@@ -477,7 +477,7 @@ def main():
     }
     res["chain_hbm_GBps"] = byt["total"] / (ms_step * 1e-3) / 1e9
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = (cpu_baseline_prefill(w, args.cpu_rows) if w.is_prefill
+        res["cpu_baseline"] = (cpu_baseline_prefill(w, max(args.cpu_rows, 128)) if w.is_prefill
                                else cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps))
     else:
         res["cpu_baseline"] = None
