@@ -131,7 +131,11 @@ def algorithmic_bytes(w, lens):
     qb = 2 if w.q_dtype == "bf16" else 4
     kb = 2 if w.idx_dtype == "bf16" else 4
     out = {"quantize": R * (512 * 4 + KV_ROW_BYTES)}
-    out["index_scan"] = int(lens.sum()) * 64 * kb
+    if w.is_prefill:
+        # the chunk's rows share one key segment: each key and each query is read once
+        out["index_scan"] = int(lens.max()) * 64 * kb + R * w.H * 64 * qb
+    else:
+        out["index_scan"] = int(lens.sum()) * 64 * kb
     pool = 0
     reindex = 0
     for L in w.layers:
@@ -180,8 +184,8 @@ def cpu_baseline_prefill(w, sample_rows):
                       % (len(rows), T, P0, dt)}
 
 
-def traffic_from_profiles(kernel_file):
-    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
+def traffic_from_profiles(workload, kernel_file):
+    """HBM bytes per launch measured with rocprofv3 counters on this workload, if taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic_counters.json")
     if not os.path.exists(path):
         return None
@@ -189,7 +193,7 @@ def traffic_from_profiles(kernel_file):
         rec = json.load(open(path))
         src = os.path.join(ROOT, "sparse_attention_fp4_e4m3_amd", "csrc", kernel_file)
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        ent = rec.get(kernel_file)
+        ent = rec.get("workloads", {}).get(workload, {}).get(kernel_file)
         if ent and ent.get("source_sha256_16") == h:
             return ent.get("bytes_per_launch")
     except Exception:
@@ -441,16 +445,16 @@ def main():
     if dominant == "attention":
         roof = {"kernel": "k_sparse_attn", "bound": "mfma", "achieved": dk["TFLOPs"],
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": dk["mfma_frac"],
-                "traffic": traffic_from_profiles("k_attn.hip")}
+                "traffic": traffic_from_profiles(w.name, "k_attn.hip")}
     elif dominant == "index_scan" and w.is_prefill:
         # the chunk's rows share one key segment: the scores are a bf16 MFMA product (two passes)
         roof = {"kernel": "k_pf_pass", "bound": "mfma", "achieved": dk["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": dk["TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
-                "traffic": traffic_from_profiles("k_index.hip")}
+                "traffic": traffic_from_profiles(w.name, "k_index.hip")}
     else:
         roof = {"kernel": "k_scan_full" if dominant == "index_scan" else "k_score_pool", "bound": "hbm",
                 "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["hbm_frac"],
-                "traffic": traffic_from_profiles("k_index.hip")}
+                "traffic": traffic_from_profiles(w.name, "k_index.hip")}
 
     tokens_s = w.rows / (ms_step * 1e-3)
     res = {
