@@ -33,8 +33,8 @@
 //    K-contiguous B operand layout), and all 8 channels share one scale
 //    pair.  The two key halves are summed through LDS at the end.
 // Every FP4 element is dequantized once for QK^T and once for PV per
-// workgroup.  Small head groups keep the split partials (16*NHT heads x 512
-// fp32 per workgroup) small, so decode-sized batches use 2 head tiles.
+// workgroup.  The split partials total rows x heads x splits x 512 fp32, so
+// the launch plan trades head tiles per workgroup against key splits.
 #include "csa2_common.h"
 
 #ifndef CSA2_HW_CVT
@@ -596,13 +596,17 @@ struct Plan {
 
 // Launch plan.  A workgroup takes 32 heads (16 if the head count is an odd
 // number of 16-head tiles) and, when rows x head groups do not fill the
-// chip, the keys are split so that >= 256 workgroups run.
+// chip, the keys are split so that >= 256 workgroups run.  Small batches
+// (at most 64 row x 16-head tiles) take 16 heads per workgroup: each key is
+// then dequantized by twice as many workgroups, but half as many key splits
+// fill the chip, which halves the split partials written here and read by
+// the combine (measured faster at 4 and 16 rows of 64 heads, slower at 32).
 Plan plan(int R, int Hq, int q_dtype, int top_k) {
   Plan p{};
   p.splitq = q_dtype == CSA2_F32;
   const int tiles = Hq / 16;
   const int max_splits = (int)std::max<int64_t>(1, ceil_div(top_k, kStep));
-  p.nht = tiles % 2 == 0 ? 2 : 1;
+  p.nht = (tiles % 2 == 0 && (int64_t)R * tiles > 64) ? 2 : 1;
   p.head_groups = tiles / p.nht;
   const int64_t base = (int64_t)R * p.head_groups;
   const int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(256, base)));
