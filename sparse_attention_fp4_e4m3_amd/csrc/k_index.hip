@@ -104,7 +104,7 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* lds, ui
 // K.  *above = elements in higher bins, *total = all elements.  Each thread
 // owns NB/NT consecutive bins, all loaded at once.  lds >= 20 words.
 template <int NT, int NB>
-__device__ int find_bin(const uint32_t* h, uint32_t K, uint32_t* above, uint32_t* total, uint32_t* lds) {
+__device__ __forceinline__ int find_bin(const uint32_t* h, uint32_t K, uint32_t* above, uint32_t* total, uint32_t* lds) {
   static_assert(NB % NT == 0, "bins per thread");
   constexpr int PER = NB / NT;
   const int hi = NB - (int)threadIdx.x * PER;  // this thread: bins [hi-PER, hi), descending
@@ -233,13 +233,11 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
   const int64_t base0 = (int64_t)blockIdx.x * a.tiles_per_wg * kWGKeys;
   if (base0 >= n) return;
   const int ntiles = (int)std::min<int64_t>(a.tiles_per_wg, ceil_div(n - base0, kWGKeys));
-  if (!REINDEX) {
-    for (int b = threadIdx.x; b < kD1 / 2; b += kThreads) {
-      h1[b] = 0u;
-      if (POOL) hb[b] = 0u;
-    }
-    __syncthreads();
+  for (int b = threadIdx.x; b < kD1 / 2; b += kThreads) {
+    h1[b] = 0u;
+    if (POOL) hb[b] = 0u;
   }
+  __syncthreads();
   const int64_t rs = a.row_start[a.shared_start ? 0 : r];
   const uint8_t* kbase = static_cast<const uint8_t*>(a.idx_k);
   float* srow = a.scores + (int64_t)r * a.n_pad;
@@ -326,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
     const int64_t i = base + lane;
     const bool ok = position(i) >= 0;
     if (i < n) srow[i] = ok ? sc : -1.0f;
-    if (!REINDEX && ok) hist_add(h1, __float_as_uint(sc) >> kS1);
+    if (ok) hist_add(h1, __float_as_uint(sc) >> kS1);
     if (POOL) {
       // a block of 8 consecutive positions = 8 consecutive lanes
       float m = ok ? sc : -1.0f;
@@ -339,17 +337,16 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
       }
     }
   }
-  if (!REINDEX) {
-    __syncthreads();
-    flush_packed(a.hist_s + (int64_t)r * kD1, h1);
-    if (POOL) flush_packed(a.hist_b + (int64_t)r * kD1, hb);
-  }
+  __syncthreads();
+  flush_packed(a.hist_s + (int64_t)r * kD1, h1);
+  if (POOL) flush_packed(a.hist_b + (int64_t)r * kD1, hb);
 }
 
 struct Series {
   const float* arr;      // [R, stride] keys (sign bit set = invalid)
   int64_t stride;
-  const uint32_t* hist;  // [R, kD1] first-digit histogram (Full)
+  const uint32_t* hist;  // [R, kD1] first-digit histogram of the scores
+  uint32_t* thr;         // [R, 2] Full: threshold bin (-1: fewer than K valid) and the count above it
   float* cand_key;       // [R, 2*stride] candidate keys (Full): per-slice lists, then the packed list
   int32_t* cand_pos;     // [R, 2*stride] candidate positions (Full)
   uint32_t* counts;      // [R, nsub] candidates per slice (Full)
@@ -379,32 +376,105 @@ __device__ __forceinline__ int series_len(const SelArgs& a, int series, int r) {
   return series == 0 ? v : (v + kBlock - 1) / kBlock;
 }
 
+constexpr int kFinCap = 16384;  // candidates a finalize workgroup keeps in LDS (16 per thread)
+
+// where candidate c of a row's list sits in its source arrays: Full, slice
+// lo = the largest s with pre[s] <= c (a fixed-step search without branches)
+__device__ __forceinline__ int64_t fin_src(bool full, int nsub, const uint32_t* pre, uint32_t c) {
+  if (!full) return c;
+  int lo = 0;
+#pragma unroll
+  for (int step = 512; step > 0; step >>= 1) {
+    const int t = lo + step;
+    lo = (t <= nsub && pre[min(t, nsub)] <= c) ? t : lo;
+  }
+  return (int64_t)lo * kSub + (c - pre[lo]);
+}
+
+// Loads the candidates [w0, w1) of this wave (MAXCH chunks of 64, all loads
+// in flight together: slots past the run read entry 0 of the row and, like
+// slots at or past nvalid, are masked afterwards), finds the first digit for
+// Reindex (its barriers wait for the loads), then keeps, in order, the valid
+// candidates whose first digit reaches it: they go to lkey/lpos[w0 ...].
+// Returns their count.
+template <int NT, int MAXCH>
+__device__ __forceinline__ uint32_t fin_gather(const Series& S, int r, bool full, int nsub, const uint32_t* pre,
+                                              const uint32_t* sk, const int32_t* sp, uint32_t w0, uint32_t w1,
+                                              uint32_t nvalid, int& b0, uint32_t& above0, uint32_t* red,
+                                              uint32_t* lkey, int32_t* lpos) {
+  const int lane = threadIdx.x & 63;
+  const int nch = (int)((w1 - w0 + 63u) / 64u);
+  uint32_t kr[MAXCH];
+  int32_t pr[MAXCH];
+#pragma unroll
+  for (int j = 0; j < MAXCH; ++j) {
+    const uint32_t c = w0 + 64u * j + lane;
+    const int64_t at = (j < nch && c < w1) ? fin_src(full, nsub, pre, c) : 0;
+    kr[j] = sk[at];
+    pr[j] = sp[at];
+  }
+#pragma unroll
+  for (int j = 0; j < MAXCH; ++j) {
+    const uint32_t c = w0 + 64u * j + lane;
+    kr[j] = (j < nch && c < w1 && c < nvalid) ? kr[j] : 0x80000000u;
+  }
+  if (!full) {
+    uint32_t total0;
+    b0 = find_bin<NT, kD1>(S.hist + (int64_t)r * kD1, (uint32_t)S.K, &above0, &total0, red);
+  }
+  const uint32_t lo_key = b0 < 0 ? 0u : ((uint32_t)b0 << kS1);  // smaller keys cannot be selected
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < MAXCH; ++j) {
+    const bool keep = !(kr[j] >> 31) && kr[j] >= lo_key;
+    const unsigned long long m = __ballot(keep);
+    if (keep) {
+      const uint32_t at =
+          w0 + cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      lkey[at] = kr[j];
+      lpos[at] = pr[j];
+    }
+    cnt += (uint32_t)__popcll(m);
+  }
+  return cnt;
+}
+
 // Exact selection for one (row, series) by one workgroup of NT threads.
-// Candidates: Full -> the per-slice lists written by k_collect, first packed
-// into one list; Reindex -> every pool slot.  The packed list lives in LDS
-// when it fits (cap entries), else in the second half of the candidate
-// arrays in global memory.  Three radix digits give the exact K-th largest
-// key T; an ordered compaction then writes positions ascending, taking ties
-// at T in candidate order (= ascending position), and pads with -1.
+// The first radix digit comes from the scan's histogram (Full: the bin
+// k_collect used; Reindex: found here).  Candidates: Full -> the per-slice
+// lists written by k_collect, in slice order; Reindex -> every pool slot.
+// Wave w owns the candidates [w0, w1) of that order.  Up to kFinCap of them
+// are loaded at once and only those that can still be selected are kept, in
+// order, in LDS (each wave then works on its own run); beyond kFinCap
+// (massive ties, very large pools) they are read from global memory, a Full
+// row's list first packed into the second half of its candidate arrays.
+// Two more digits give the exact K-th largest key T; the ordered compaction
+// then writes positions ascending, taking ties at T in candidate order
+// (= ascending position), and pads with -1.
 template <int NT>
-__device__ void finalize_row(const SelArgs& a, int series, int r, uint32_t* hist, uint32_t* pre, uint32_t* red,
-                             uint32_t* lkey, int32_t* lpos, int cap) {
+__device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r, uint32_t* hist, uint32_t* hist2,
+                                             uint32_t* pre,
+                             uint32_t* red, uint32_t* lkey, int32_t* lpos) {
+  constexpr int NW = NT / 64;
   const Series& S = a.s[series];
   const int n = series_len(a, series, r);
   const bool full = a.mode == CSA2_FULL;
   const int vis = clampv(a.row_visible[r], a.max_visible);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the two digit histograms start at zero (ordered by the barriers below)
+  for (int b = threadIdx.x; b < NT; b += NT) hist[b] = 0u;
+  for (int b = threadIdx.x; b < kD2; b += NT) hist2[b] = 0u;
   uint32_t M;
-  const uint32_t* keys;
-  const int32_t* posr;
   uint32_t above0 = 0;
   int b0 = -1;
+  int nsub = 0;
+  const uint32_t* sk;
+  const int32_t* sp;
   if (full) {
-    const int nsub = (n + kSub - 1) / kSub;
+    nsub = (n + kSub - 1) / kSub;
     const uint32_t c_first = ((int)threadIdx.x < nsub) ? S.counts[(int64_t)r * S.nsub + threadIdx.x] : 0u;
-    // the first digit is already resolved by the scan's histogram (the same
-    // threshold bin k_collect used): candidates above it are all selected
-    uint32_t total0;
-    b0 = find_bin<NT, kD1>(S.hist + (int64_t)r * kD1, (uint32_t)S.K, &above0, &total0, red);
+    b0 = (int)S.thr[2 * r];
+    above0 = S.thr[2 * r + 1];
     uint32_t carry = 0;
     for (int s0 = 0; s0 < nsub; s0 += NT) {
       const int s = s0 + threadIdx.x;
@@ -417,147 +487,155 @@ __device__ void finalize_row(const SelArgs& a, int series, int r, uint32_t* hist
     if (threadIdx.x == 0) pre[nsub] = carry;
     __syncthreads();
     M = pre[nsub];
-    const bool in_lds = M <= (uint32_t)cap;
-    const uint32_t* sk = reinterpret_cast<const uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride;
-    const int32_t* sp = S.cand_pos + (int64_t)r * 2 * S.stride;
-    uint32_t* dk = in_lds ? lkey : reinterpret_cast<uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride + S.stride;
-    int32_t* dp = in_lds ? lpos : S.cand_pos + (int64_t)r * 2 * S.stride + S.stride;
-#pragma unroll 4
-    for (uint32_t c = threadIdx.x; c < M; c += NT) {
-      int lo = 0, hi = nsub;  // largest s with pre[s] <= c
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid] <= c) lo = mid;
-        else hi = mid;
-      }
-      const int64_t at = (int64_t)lo * kSub + (c - pre[lo]);
-      dk[c] = sk[at];
-      dp[c] = sp[at];
-    }
-    __syncthreads();
-    keys = dk;
-    posr = dp;
+    sk = reinterpret_cast<const uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride;
+    sp = S.cand_pos + (int64_t)r * 2 * S.stride;
   } else {
-    M = (uint32_t)n;
-    const uint32_t* sk = reinterpret_cast<const uint32_t*>(S.arr) + (int64_t)r * S.stride;
-    const int32_t* sp = a.pool + (int64_t)r * a.pool_stride;
-    if (M <= (uint32_t)cap) {
+    // the row is split by its pool capacity when that fits, so the candidate
+    // loads need not wait for the pool length (slots past it are masked)
+    M = a.pool_stride <= kFinCap ? (uint32_t)a.pool_stride : (uint32_t)n;
+    sk = reinterpret_cast<const uint32_t*>(S.arr) + (int64_t)r * S.stride;
+    sp = a.pool + (int64_t)r * a.pool_stride;
+  }
+  const uint32_t per_w = ((M + NW - 1) / NW + 63u) & ~63u;
+  const uint32_t w0 = min(M, (uint32_t)wave * per_w), w1 = min(M, w0 + per_w);
+  const uint32_t* keys;
+  const int32_t* posr;
+  uint32_t cend;  // this wave works on [w0, cend) of keys/posr
+  if (M <= (uint32_t)kFinCap) {
+    const int nchmax = (int)(per_w / 64u);  // uniform
+    const uint32_t nv = full ? M : (uint32_t)n;  // Reindex: the valid slots
+    uint32_t sw;
+    if (nchmax <= 2) sw = fin_gather<NT, 2>(S, r, full, nsub, pre, sk, sp, w0, w1, nv, b0, above0, red, lkey, lpos);
+    else if (nchmax <= 4) sw = fin_gather<NT, 4>(S, r, full, nsub, pre, sk, sp, w0, w1, nv, b0, above0, red, lkey, lpos);
+    else if (nchmax <= 8) sw = fin_gather<NT, 8>(S, r, full, nsub, pre, sk, sp, w0, w1, nv, b0, above0, red, lkey, lpos);
+    else sw = fin_gather<NT, 16>(S, r, full, nsub, pre, sk, sp, w0, w1, nv, b0, above0, red, lkey, lpos);
+    // (each wave reads back only its own run; LDS operations of a wave execute in order)
+    keys = lkey;
+    posr = lpos;
+    cend = w0 + sw;
+  } else {
+    if (full) {
+      uint32_t* dk = reinterpret_cast<uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride + S.stride;
+      int32_t* dp = S.cand_pos + (int64_t)r * 2 * S.stride + S.stride;
 #pragma unroll 4
       for (uint32_t c = threadIdx.x; c < M; c += NT) {
-        lkey[c] = sk[c];
-        lpos[c] = sp[c];
+        const int64_t at = fin_src(full, nsub, pre, c);
+        dk[c] = sk[at];
+        dp[c] = sp[at];
       }
       __syncthreads();
-      keys = lkey;
-      posr = lpos;
+      keys = dk;
+      posr = dp;
     } else {
+      uint32_t total0;
+      b0 = find_bin<NT, kD1>(S.hist + (int64_t)r * kD1, (uint32_t)S.K, &above0, &total0, red);
       keys = sk;
       posr = sp;
     }
+    cend = w1;
   }
 
-  // ---- exact threshold: three digits over the candidates
-  uint32_t K = (uint32_t)S.K;
-  uint32_t prefix = 0;  // resolved high bits
-  int shift_hi = 31;
-  bool all = false;
+  // ---- exact threshold: digits 2 and 3 among the candidates of the first digit's bin
   uint32_t need = 0;
-  int lev0 = 0;
-  if (full) {
-    if (b0 < 0) {
-      all = true;  // fewer than K valid entries: every candidate is selected
-      lev0 = 3;
-    } else {
-      prefix = (uint32_t)b0;
-      shift_hi = kS1;
-      K -= above0;
-      need = K;
-      lev0 = 1;
-    }
-  }
+  uint32_t prefix = 0;
+  const bool all = b0 < 0;  // fewer than K valid entries: every valid candidate is selected
+  if (!all) {
+    uint32_t K = (uint32_t)S.K - above0;
+    prefix = (uint32_t)b0;
+    int shift_hi = kS1;
 #pragma unroll 1
-  for (int lev = lev0; lev < 3; ++lev) {
-    const int sh = lev == 0 ? kS1 : (lev == 1 ? kS2 : 0);
-    const int nb = lev == 0 ? kD1 : (lev == 1 ? kD2 : kD3);
-    const int nz = nb < NT ? NT : nb;  // the last level's scan covers NT bins (the extra ones stay empty)
-    for (int b = threadIdx.x; b < nz; b += NT) hist[b] = 0u;
-    __syncthreads();
+    for (int lev = 1; lev < 3; ++lev) {
+      const int sh = lev == 1 ? kS2 : 0;
+      const int nb = lev == 1 ? kD2 : kD3;
+      uint32_t* h = lev == 1 ? hist2 : hist;
 #pragma unroll 4
-    for (uint32_t i = threadIdx.x; i < M; i += NT) {
-      const uint32_t key = keys[i];
-      if (!(key >> 31) && (lev == 0 || (key >> shift_hi) == prefix)) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
+      for (uint32_t c = w0 + lane; c < cend; c += 64) {
+        const uint32_t key = keys[c];
+        if (!(key >> 31) && (key >> shift_hi) == prefix) atomicAdd(&h[(key >> sh) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t above, total;
+      // (the last digit's scan covers NT bins; the ones past kD3 stay empty)
+      const int b = lev == 1 ? find_bin<NT, kD2>(hist2, K, &above, &total, red)
+                             : find_bin<NT, kD3 < NT ? NT : kD3>(hist, K, &above, &total, red);
+      prefix = (prefix << (shift_hi - sh)) | (uint32_t)b;
+      shift_hi = sh;
+      K -= above;
     }
-    __syncthreads();
-    uint32_t above, total;
-    const int b = lev == 0 ? find_bin<NT, kD1>(hist, K, &above, &total, red)
-                           : (lev == 1 ? find_bin<NT, kD2>(hist, K, &above, &total, red)
-                                       : find_bin<NT, kD3 < NT ? NT : kD3>(hist, K, &above, &total, red));
-    if (b < 0) {  // only at the first level: fewer than K valid candidates
-      all = true;
-      break;
-    }
-    prefix = (prefix << (shift_hi - sh)) | (uint32_t)b;
-    shift_hi = sh;
-    K -= above;
-    need = K;
+    need = K;  // ties at T to take, in candidate order
   }
   const uint32_t T = prefix;  // the full 31-bit key of the K-th largest
 
-  // ---- ordered compaction: thread t owns candidates [t*per, (t+1)*per)
-  const uint32_t per = (M + NT - 1) / NT;
-  const uint32_t c0 = min(M, threadIdx.x * per), c1 = min(M, c0 + per);
+  // ---- ordered compaction over each wave's run, 64 candidates at a time
+  auto is_gt = [&](uint32_t key) { return !(key >> 31) && (all || key > T); };
+  auto is_eq = [&](uint32_t key) { return !(key >> 31) && !all && key == T; };
   uint32_t gt = 0, eq = 0;
-#pragma unroll 4
-  for (uint32_t c = c0; c < c1; ++c) {
-    const uint32_t key = keys[c];
-    gt += (!(key >> 31) && (all || key > T)) ? 1u : 0u;
-    eq += (!(key >> 31) && !all && key == T) ? 1u : 0u;
+  for (uint32_t c0 = w0; c0 < cend; c0 += 64) {
+    const uint32_t c = c0 + lane;
+    const uint32_t key = c < cend ? keys[c] : 0x80000000u;
+    gt += (uint32_t)__popcll(__ballot(is_gt(key)));
+    eq += (uint32_t)__popcll(__ballot(is_eq(key)));
   }
-  uint32_t tot_gt, tot_eq;
-  const uint32_t gt_before = block_excl_sum<NT>(gt, red, &tot_gt);
-  const uint32_t eq_before = block_excl_sum<NT>(eq, red, &tot_eq);
+  if (lane == 0) {
+    red[wave] = gt;
+    red[NW + wave] = eq;
+  }
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0, tot_gt = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    const uint32_t g = red[ww], e = red[NW + ww];
+    gt_before += ww < wave ? g : 0u;
+    eq_before += ww < wave ? e : 0u;
+    tot_gt += g;
+  }
+  __syncthreads();
   const uint32_t nsel = all ? tot_gt : (uint32_t)S.K;
   uint32_t out = gt_before + (all ? 0u : min(eq_before, need));
   uint32_t ties = eq_before;
   bool last_block_kept = false;
-  for (uint32_t c = c0; c < c1; ++c) {
-    const uint32_t key = keys[c];
-    if (key >> 31) continue;
-    bool sel;
-    if (all || key > T) sel = true;
-    else if (key == T) sel = (ties++ < need);
-    else sel = false;
-    if (!sel || out >= nsel) continue;
-    const int32_t pos = posr[c];
-    if (series == 0) {
-      a.out_idx[(int64_t)r * S.K + out] = pos;
-    } else {
-      int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)out * kBlock;
+  for (uint32_t c0 = w0; c0 < cend; c0 += 64) {
+    const uint32_t c = c0 + lane;
+    const uint32_t key = c < cend ? keys[c] : 0x80000000u;
+    const bool e = is_eq(key);
+    const unsigned long long me = __ballot(e);
+    const uint32_t rank =
+        ties + __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+    const bool sel = is_gt(key) || (e && rank < need);
+    const unsigned long long ms = __ballot(sel);
+    const uint32_t at =
+        out + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
+    if (sel && at < nsel) {
+      const int32_t pos = posr[c];
+      if (series == 0) {
+        a.out_idx[(int64_t)r * S.K + at] = pos;
+      } else {
+        int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)at * kBlock;
 #pragma unroll
-      for (int m = 0; m < kBlock; ++m) o[m] = (pos * kBlock + m < vis) ? pos * kBlock + m : -1;
-      if (pos == n - 1) last_block_kept = true;
+        for (int m = 0; m < kBlock; ++m) o[m] = (pos * kBlock + m < vis) ? pos * kBlock + m : -1;
+        if (pos == n - 1) last_block_kept = true;
+      }
     }
-    ++out;
+    out += (uint32_t)__popcll(ms);
+    ties += (uint32_t)__popcll(me);
   }
   // ---- padding and pool length
   if (series == 0) {
     int32_t* o = a.out_idx + (int64_t)r * S.K;
     for (int i = (int)nsel + threadIdx.x; i < S.K; i += NT) o[i] = -1;
   } else {
-    if (threadIdx.x == 0) red[20] = 0u;
+    if (threadIdx.x == 0) red[0] = 0u;
     __syncthreads();
-    if (last_block_kept) red[20] = 1u;
+    if (last_block_kept) red[0] = 1u;
     __syncthreads();
     // the partial last block is the highest block, hence the last one written
     int plen = (int)nsel * kBlock;
-    if (red[20] && (vis % kBlock) != 0) plen -= kBlock - (vis % kBlock);
+    if (red[0] && (vis % kBlock) != 0) plen -= kBlock - (vis % kBlock);
     int32_t* o = a.out_pool + (int64_t)r * a.pool_size;
     for (int i = (int)nsel * kBlock + threadIdx.x; i < a.pool_size; i += NT) o[i] = -1;
     if (threadIdx.x == 0) a.out_pool_len[r] = plen;
   }
 }
-
-constexpr int kFinCap = 16384;  // candidates held in LDS by k_finalize
 
 // Full mode: each wave compacts its slice of kSub elements, keeping those
 // whose first digit is at least the threshold bin (all valid ones when the
@@ -570,21 +648,26 @@ __global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
   const Series& S = a.s[series];
   const int n = series_len(a, series, r);
   const int64_t wg_base = (int64_t)blockIdx.x * 4 * kSub;
-  if (wg_base >= n) return;
+  if (wg_base >= n && blockIdx.x != 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t base = wg_base + (int64_t)wave * kSub;
   const int end = (int)std::min<int64_t>(n, base + kSub);  // <= base for a wave past the end
   const float* arr = S.arr + (int64_t)r * S.stride;
   // the slice's keys are in flight while the threshold bin is found
   constexpr int kPer = kSub / 64;  // 32 elements per lane
+  const int last = n > 0 ? n - 1 : 0;  // the row's score array holds at least kSub slots
   float v[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int i = (int)base + 64 * k + lane;
-    v[k] = arr[i < end ? i : n - 1];
+    v[k] = arr[i < end ? i : last];
   }
   uint32_t above, total;
   const int b1 = find_bin<kThreads, kD1>(S.hist + (int64_t)r * kD1, (uint32_t)S.K, &above, &total, red);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    S.thr[2 * r] = (uint32_t)b1;
+    S.thr[2 * r + 1] = above;
+  }
   const uint32_t thr = b1 < 0 ? 0u : (uint32_t)b1;
   if (base >= n) return;
   const int sub = (int)(base / kSub);
@@ -607,16 +690,19 @@ __global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
   if (lane == 0) S.counts[(int64_t)r * S.nsub + sub] = cnt;
 }
 
+constexpr size_t kFinLdsWords = kFinThreads + kD2 + 1028 + 32 + 2 * (size_t)kFinCap;
+
 __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
   extern __shared__ __align__(16) uint32_t fsm[];
-  uint32_t* hist = fsm;                       // kD1
-  uint32_t* pre = hist + kD1;                 // 1025
+  uint32_t* hist = fsm;                       // kFinThreads (last digit)
+  uint32_t* hist2 = hist + kFinThreads;       // kD2 (second digit)
+  uint32_t* pre = hist2 + kD2;                // 1025
   uint32_t* red = pre + 1028;                 // 32
   uint32_t* lkey = red + 32;                  // kFinCap
   int32_t* lpos = reinterpret_cast<int32_t*>(lkey + kFinCap);
   if ((int)blockIdx.y >= a.nseries) return;
   if (a.row_mask && !a.row_mask[blockIdx.x]) return;
-  finalize_row<kFinThreads>(a, blockIdx.y, blockIdx.x, hist, pre, red, lkey, lpos, kFinCap);
+  finalize_row<kFinThreads>(a, blockIdx.y, blockIdx.x, hist, hist2, pre, red, lkey, lpos);
 }
 
 // ------------------------------------------------------------ prefill: approximate MFMA passes
@@ -979,7 +1065,8 @@ struct Carve {
 struct Layout {
   // exact path (Full and Reindex; the per-row fallback of the shared-segment mode)
   float* qf;
-  uint32_t* hist;  // [2][R][kD1] first-digit histograms
+  uint32_t* hist;  // [2][R][kD1] first-digit histograms (Full: entries, blocks; Reindex: the second)
+  uint32_t* thr[2];  // [R][2] threshold bins found by k_collect (Full)
   float* scores;
   float* bmax;
   float* cand_key[2];
@@ -1021,6 +1108,8 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
   L.nbsub = (int)(L.nb_pad / kSub);
   L.qf = c.take<float>((size_t)R * H * kIdxDim);
   L.hist = c.take<uint32_t>((size_t)R * kD1 * 2);
+  L.thr[0] = c.take<uint32_t>((size_t)R * 2);
+  L.thr[1] = c.take<uint32_t>((size_t)R * 2);
   L.scores = c.take<float>((size_t)R * L.n_pad);
   L.bmax = pool_on ? c.take<float>((size_t)R * L.nb_pad) : nullptr;
   if (full) {
@@ -1058,7 +1147,7 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
 template <int KDT, int HC, bool REINDEX, bool POOL>
 void launch_score(const ScoreArgs& sa, const float* qf, dim3 grid, hipStream_t s) {
   using T = KeyTile<KDT>;
-  const size_t lds = (size_t)kWavesPerWG * T::kWaveBytes + (REINDEX ? 0 : (size_t)kD1 / 2 * 4 * (POOL ? 2 : 1));
+  const size_t lds = (size_t)kWavesPerWG * T::kWaveBytes + (size_t)kD1 / 2 * 4 * (POOL ? 2 : 1);
   auto kern = k_score<KDT, HC, REINDEX, POOL>;
   static bool configured = false;
   if (!configured) {
@@ -1097,7 +1186,7 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
   const bool pool_on = full && pool_size > 0;
   if (!prep_done) {
     const int64_t nq = (int64_t)R * H * kIdxDim;
-    const int64_t nhist = full ? (int64_t)R * kD1 * 2 : 0;
+    const int64_t nhist = (int64_t)R * kD1 * 2;
     hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(std::max(nq, nhist), 256))),
                        dim3(256), 0, s, idx_q, q_dtype, R, H, L.qf, L.hist, nhist);
   }
@@ -1116,7 +1205,9 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     sa.n_pad = score_stride;
     sa.bmax = L.bmax;
     sa.nb_pad = L.nb_pad;
-    sa.hist_s = L.hist;
+    // Reindex counts into the second histogram, so that the shared-segment mode's
+    // rescoring (Reindex over candidate lists) leaves the first one to its Full fallback
+    sa.hist_s = full ? L.hist : L.hist + (size_t)R * kD1;
     sa.hist_b = L.hist + (size_t)R * kD1;
     sa.row_mask = row_mask;
     sa.shared_start = shared ? 1 : 0;
@@ -1154,15 +1245,17 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
   a.out_pool_len = out_pool_len;
   a.pool_size = pool_size;
   a.nseries = pool_on ? 2 : 1;
-  a.s[0] = Series{scores, score_stride, L.hist, L.cand_key[0], L.cand_pos[0], L.counts[0], L.nsub, top_k};
+  a.s[0] = Series{scores, score_stride, full ? L.hist : L.hist + (size_t)R * kD1, L.thr[0], L.cand_key[0],
+                  L.cand_pos[0], L.counts[0], L.nsub, top_k};
   if (pool_on)
-    a.s[1] = Series{L.bmax, L.nb_pad, L.hist + (size_t)R * kD1, L.cand_key[1], L.cand_pos[1], L.counts[1], L.nbsub,
+    a.s[1] = Series{L.bmax, L.nb_pad, L.hist + (size_t)R * kD1, L.thr[1], L.cand_key[1], L.cand_pos[1], L.counts[1],
+                    L.nbsub,
                     pool_size / kBlock};
   if (full) {
     const int gx = (int)ceil_div(std::max(L.nsub, pool_on ? L.nbsub : 1), 4);
     hipLaunchKernelGGL(k_collect, dim3((unsigned)gx, (unsigned)R, (unsigned)a.nseries), dim3(kThreads), 0, s, a);
   }
-  const size_t lds = ((size_t)kD1 + 1028 + 32 + 2 * (size_t)kFinCap) * 4;
+  const size_t lds = kFinLdsWords * 4;
   static bool configured = false;
   if (!configured) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_finalize), hipFuncAttributeMaxDynamicSharedMemorySize,
