@@ -251,34 +251,40 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
     }
     return i < vis ? i : -1;
   };
-  // piece id = lane + 64*i -> key id / kPieces, piece id % kPieces (coalesced 16-byte pieces)
+  // piece id = lane + 64*i -> key id / kPieces, piece id % kPieces (coalesced 16-byte pieces).
+  // Slots without a visible entry load some valid key row instead (Full: the
+  // last visible one; Reindex: row 0 of the key array) and their scores are
+  // discarded below; the loaded values are not inspected here, so the loads
+  // of the next tile stay in flight while the current one is scored.
   auto load_tile = [&](int64_t base, Staged<KDT>& st) {
 #pragma unroll
     for (int i = 0; i < T::kPerLane; ++i) {
       const int id = lane + 64 * i;
       const int k = id / T::kPieces, piece = id % T::kPieces;
-      const int64_t pos = position(base + k);
-      // invalid keys read row 0 of the key array (always present) and are zeroed: no branch around the load
-      const u32x4 v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(kbase + (pos >= 0 ? rs + pos : 0) * T::kBytes) + piece);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st.v[i][e] = pos >= 0 ? v[e] : 0u;
+      int64_t row;
+      if (REINDEX) {
+        const int64_t pos = position(base + k);
+        row = pos >= 0 ? rs + pos : 0;
+      } else {
+        row = rs + std::min<int64_t>(base + k, (int64_t)vis - 1);
+      }
+      st.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + row * T::kBytes) + piece);
     }
   };
 
-  // wave tiles of this workgroup: wave wv takes tiles wv, wv + 4, ... (64 keys each)
+  // wave tiles of this workgroup: wave wv takes tiles wv, wv + 4, ... (64 keys each); the
+  // next tile's loads are in flight while the current one is scored
   const int nwt = (int)std::min<int64_t>((int64_t)ntiles * kWavesPerWG, ceil_div(n - base0, T::kKeys));
-  Staged<KDT> st;
-  if (wv < nwt) load_tile(base0 + (int64_t)wv * T::kKeys, st);
-  for (int j = wv; j < nwt; j += kWavesPerWG) {
-    const int64_t base = base0 + (int64_t)j * T::kKeys;
+  auto tile_base = [&](int j) { return base0 + (int64_t)j * T::kKeys; };
+  auto score_tile = [&](int j, Staged<KDT>& st) {
+    const int64_t base = tile_base(j);
     // (the LDS operations of one wave execute in order: the previous tile's reads are done)
 #pragma unroll
     for (int i = 0; i < T::kPerLane; ++i) {
       const int id = lane + 64 * i;
       *reinterpret_cast<u32x4*>(tile + (id / T::kPieces) * T::kStride + (id % T::kPieces) * 16) = st.v[i];
     }
-    if (j + kWavesPerWG < nwt) load_tile(base + (int64_t)kWavesPerWG * T::kKeys, st);
+    if (j + kWavesPerWG < nwt) load_tile(tile_base(j + kWavesPerWG), st);
 
     // the H fmaf chains of key `lane`, channels in order
     float acc[NACC];
@@ -336,6 +342,11 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
         hist_add(hb, __float_as_uint(m) >> kS1);
       }
     }
+  };
+  if (wv < nwt) {
+    Staged<KDT> st;
+    load_tile(tile_base(wv), st);
+    for (int j = wv; j < nwt; j += kWavesPerWG) score_tile(j, st);
   }
   __syncthreads();
   flush_packed(a.hist_s + (int64_t)r * kD1, h1);
