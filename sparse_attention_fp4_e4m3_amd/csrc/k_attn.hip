@@ -35,6 +35,8 @@
 // Every FP4 element is dequantized once for QK^T and once for PV per
 // workgroup.  The split partials total rows x heads x splits x 512 fp32, so
 // the launch plan trades head tiles per workgroup against key splits.
+#include <type_traits>
+
 #include "csa2_common.h"
 
 #ifndef CSA2_HW_CVT
@@ -426,30 +428,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
         W[k] = *reinterpret_cast<const uint32_t*>(&ss.cs[cs_off(key0 + k) + 64 * cq + 4 * n16]);
       // the 8 channels share scale group 8*cq + n16/2
       const u32x4 spw = *reinterpret_cast<const u32x4*>(&ss.sct[(8 * cq + (n16 >> 1)) * kScStride + key0]);
-      uint32_t Bw[8][4];
+      // byte b of E[p]: channel 2b of keys (2p, 2p+1); byte b of D[p]: channel 2b+1
+      uint32_t E[4], D[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        // byte b of E: channel 2b of keys (2p, 2p+1); byte b of D: channel 2b+1
         const uint32_t wa = W[2 * p], wb = W[2 * p + 1];
-        const uint32_t E = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
-        const uint32_t D = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
-        const half2v sp = bits_h2(spw[p]);
-        Bw[0][p] = h2_bits(fp4x2_to_h2<0>(E) * sp);
-        Bw[2][p] = h2_bits(fp4x2_to_h2<1>(E) * sp);
-        Bw[4][p] = h2_bits(fp4x2_to_h2<2>(E) * sp);
-        Bw[6][p] = h2_bits(fp4x2_to_h2<3>(E) * sp);
-        Bw[1][p] = h2_bits(fp4x2_to_h2<0>(D) * sp);
-        Bw[3][p] = h2_bits(fp4x2_to_h2<1>(D) * sp);
-        Bw[5][p] = h2_bits(fp4x2_to_h2<2>(D) * sp);
-        Bw[7][p] = h2_bits(fp4x2_to_h2<3>(D) * sp);
+        E[p] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
+        D[p] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
       }
+      half8 av[NHT];
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        const half8 av = *reinterpret_cast<const half8*>(&ss.p[(16 * ht + n16) * kPStride + key0]);
+      for (int ht = 0; ht < NHT; ++ht)
+        av[ht] = *reinterpret_cast<const half8*>(&ss.p[(16 * ht + n16) * kPStride + key0]);
+      // tile t (channel 128*cq + 8*n16 + t) is converted just before its products
+      auto tile = [&](auto sel_c, const uint32_t(&src)[4], int t) {
+        constexpr int SEL = decltype(sel_c)::value;
+        u32x4 b;
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          O[ht][t] = mfma(av, __builtin_bit_cast(half8, u32x4{Bw[t][0], Bw[t][1], Bw[t][2], Bw[t][3]}), O[ht][t]);
-      }
+        for (int p = 0; p < 4; ++p) b[p] = h2_bits(fp4x2_to_h2<SEL>(src[p]) * bits_h2(spw[p]));
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) O[ht][t] = mfma(av[ht], __builtin_bit_cast(half8, b), O[ht][t]);
+      };
+      tile(std::integral_constant<int, 0>{}, E, 0);
+      tile(std::integral_constant<int, 0>{}, D, 1);
+      tile(std::integral_constant<int, 1>{}, E, 2);
+      tile(std::integral_constant<int, 1>{}, D, 3);
+      tile(std::integral_constant<int, 2>{}, E, 4);
+      tile(std::integral_constant<int, 2>{}, D, 5);
+      tile(std::integral_constant<int, 3>{}, E, 6);
+      tile(std::integral_constant<int, 3>{}, D, 7);
     }
   };
   for (int st = 0; st < nsteps; st += 2) {

@@ -195,6 +195,42 @@ def test_reindex_bit_exact_and_all_positions_equals_full():
     assert torch.equal(full_idx, re_idx)
 
 
+def test_selection_massive_ties_and_partly_filled_pools():
+    """All-zero queries tie every entry at score 0, so the threshold bin holds whole rows (more
+    candidates than a selection workgroup keeps on chip): the K lowest positions must come out.
+    Reindex pools are filled to different lengths, with valid-looking positions past each length
+    that must be ignored."""
+    lens, H, K = [40000, 20001, 3], 8, 2048
+    R = len(lens)
+    q, k, starts = _idx_inputs(11, R, H, lens, "bf16")
+    q[:] = 0.0
+    vis = dev(np.array(lens, np.int32))
+    idx, _, _ = index_topk(csa2.FULL, dev_bf16(q), dev_bf16(k), dev(starts), vis, max(lens), K)
+    want, _, _ = _oracle_full(q, k, starts, lens, K)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    # Reindex: stride 6000, lengths 5000 / 1 / 0; slots past the length hold positions that would win
+    rng = np.random.default_rng(12)
+    q2 = bf16_round(rng.standard_normal((R, H, 64)).astype(np.float32))
+    stride, plens = 6000, [5000, 1, 0]
+    gpu_pool = np.zeros((R, stride), np.int32)
+    ref_pool = np.full((R, stride), -1, np.int32)
+    for r in range(R):
+        kr = k[starts[r]:starts[r] + lens[r]]
+        sc = oracle.index_scores(q2[r], kr)
+        order = np.argsort(-sc, kind="stable")
+        m = min(plens[r], lens[r])
+        chosen = np.sort(order[len(order) - m:]) if m else np.zeros(0, np.int64)  # the lowest-scoring entries
+        ref_pool[r, :m] = chosen
+        gpu_pool[r, :m] = chosen
+        gpu_pool[r, m:] = order[:stride - m] if len(order) >= stride - m else np.resize(order, stride - m)
+    idx2, _, _ = index_topk(csa2.REINDEX, dev_bf16(q2), dev_bf16(k), dev(starts), vis, max(lens), K,
+                            pool=dev(gpu_pool), pool_len=dev(np.array(plens, np.int32)))
+    got = idx2.cpu().numpy()
+    for r in range(R):
+        kr = k[starts[r]:starts[r] + lens[r]]
+        assert np.array_equal(got[r], oracle.reindex_select(q2[r], kr, ref_pool[r], lens[r], K)), "row %d" % r
+
+
 def test_topk_deterministic():
     lens, H, K = [50000, 50000], 8, 2048
     q, k, starts = _idx_inputs(9, 2, H, lens, "bf16")
