@@ -198,6 +198,7 @@ struct ScoreArgs {
 template <int KDT>
 struct Staged {
   u32x4 v[KeyTile<KDT>::kPerLane];
+  int32_t pos;  // Reindex: the entry position of this lane's own slot (-1: none)
 };
 
 // First-digit histograms are kept as packed 16-bit counters (two bins per
@@ -257,13 +258,16 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
   // discarded below; the loaded values are not inspected here, so the loads
   // of the next tile stay in flight while the current one is scored.
   auto load_tile = [&](int64_t base, Staged<KDT>& st) {
+    // Reindex: each lane reads its own slot's pool entry once; the lanes loading a key's pieces take it
+    // from that lane
+    if (REINDEX) st.pos = (int32_t)position(base + lane);
 #pragma unroll
     for (int i = 0; i < T::kPerLane; ++i) {
       const int id = lane + 64 * i;
       const int k = id / T::kPieces, piece = id % T::kPieces;
       int64_t row;
       if (REINDEX) {
-        const int64_t pos = position(base + k);
+        const int32_t pos = __shfl(st.pos, k, 64);
         row = pos >= 0 ? rs + pos : 0;
       } else {
         row = rs + std::min<int64_t>(base + k, (int64_t)vis - 1);
@@ -278,6 +282,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
   auto tile_base = [&](int j) { return base0 + (int64_t)j * T::kKeys; };
   auto score_tile = [&](int j, Staged<KDT>& st) {
     const int64_t base = tile_base(j);
+    const int32_t own = st.pos;  // (st is refilled with the next tile below)
     // (the LDS operations of one wave execute in order: the previous tile's reads are done)
 #pragma unroll
     for (int i = 0; i < T::kPerLane; ++i) {
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
     for (int h = 1; h < NACC; ++h)
       if (HC > 0 || h < H) sc = __fadd_rn(sc, acc[h] > 0.0f ? acc[h] : 0.0f);
     const int64_t i = base + lane;
-    const bool ok = position(i) >= 0;
+    const bool ok = REINDEX ? own >= 0 : i < vis;
     if (i < n) srow[i] = ok ? sc : -1.0f;
     if (ok) hist_add(h1, __float_as_uint(sc) >> kS1);
     if (POOL) {
