@@ -134,20 +134,23 @@ __device__ __forceinline__ int cs_off(int k) {
   return (k >> 5) * kCsBlock + (k & 31) * kCsStride + 64 * ((k >> 3) & 3);
 }
 
+// Staged operands, probabilities and per-wave maxima and sums are double
+// buffered by step parity: a wave writes those of step s+1 before the one
+// barrier of that step, while slower waves may still read those of step s.
 template <int NHT, bool SPLITQ>
 struct Smem {
   static constexpr int kQRows = 16 * NHT * (SPLITQ ? 2 : 1);
   union {
     struct {
       _Float16 q[kQRows * kQStride];
-      uint8_t cs[(kStep / 32) * kCsBlock];
-      _Float16 sct[kGroups * kScStride];
-      _Float16 p[16 * NHT * kPStride];
+      uint8_t cs[2][(kStep / 32) * kCsBlock];
+      _Float16 sct[2][kGroups * kScStride];
+      _Float16 p[2][16 * NHT * kPStride];
     } s;
     float ored[16 * NHT * kOStride];  // after the key loop: outputs of the second key half
   } u;
-  float red_max[kWaves][64];
-  float red_sum[kWaves][64];
+  float red_max[2][kWaves][64];
+  float red_sum[2][kWaves][64];
   float alpha[64];
   float lfin[64];
 };
@@ -208,6 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   auto& ss = sm.u.s;
   constexpr int HG = 16 * NHT;
   constexpr int NQ = SPLITQ ? 2 : 1;
+  constexpr bool kFastSoftmax = NHT == 2;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int cq = w & 3, kh = w >> 2;  // PV role: channel quarter, key half
@@ -333,44 +337,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       }
     }
 
-    // ---- softmax, part 1: scaled logits, masked, per-wave maximum per head
+    // ---- softmax.  The reference maximum of each head is kept lazily: it
+    // only moves when a new maximum exceeds it by more than 2^kLazy.
+    // Two-tile workgroups (long key loops) first take the probabilities
+    // against the current references and publish them with the per-wave
+    // maxima and sums behind one barrier; every wave reads the same maxima
+    // and takes the same decision: if a reference has to move (always at the
+    // first step with a valid key), the probabilities are recomputed behind
+    // a second barrier.  One-tile workgroups (short key loops, where that
+    // first attempt rarely pays) exchange the maxima first.  Both give the
+    // same probabilities.  Staged data are double buffered by step parity
+    // in the first scheme, since a wave writes those of step s+1 before its
+    // barrier while slower waves may still read those of step s.
+    const int pb = kFastSoftmax ? (st & 1) : 0;
     const unsigned long long vm = __ballot(vcur);
+    float mx[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-      float mx = -INFINITY;
+      mx[ht] = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = (vm >> (4 * q4 + i)) & 1ull;
         const float z = ok ? S[ht][i] * a.c2 : -INFINITY;
         S[ht][i] = z;
-        mx = fmaxf(mx, z);
+        mx[ht] = fmaxf(mx[ht], z);
       }
-      mx = rows_max(mx);
-      if (q4 == 0) sm.red_max[w][16 * ht + n16] = mx;
+      mx[ht] = rows_max(mx[ht]);
     }
-    lds_barrier();  // B1: maxima visible; every wave is past the previous PV
-
-    // ---- stage this step's raw codes and fp16 scales for PV
-#pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&ss.cs[cs_off(myslot) + 64 * q4 + 16 * c]) = cur.c[c];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      ss.sct[(8 * q4 + 2 * g) * kScStride + myslot] = sc[g][0];
-      ss.sct[(8 * q4 + 2 * g + 1) * kScStride + myslot] = sc[g][1];
-    }
-
-    // ---- softmax, part 2: reference maximum, probabilities (fp16), sums
-    float alpha[NHT];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
+    // probabilities of this wave's keys against the references muse; sums to red_sum
+    auto probs = [&](int ht, float muse) {
       const int h = 16 * ht + n16;
-      float mstep = sm.red_max[0][h];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) mstep = fmaxf(mstep, sm.red_max[ww][h]);
-      const float mnew = (mstep > mref[ht] + kLazy) ? mstep : mref[ht];
-      const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
-      alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
-      mref[ht] = mnew;
       _Float16 pv[4];
       float sum = 0.0f;
 #pragma unroll
@@ -378,28 +374,71 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
         pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
         sum += (float)pv[i];
       }
-      *reinterpret_cast<u32x2*>(&ss.p[h * kPStride + 16 * w + 4 * q4]) =
+      *reinterpret_cast<u32x2*>(&ss.p[pb][h * kPStride + 16 * w + 4 * q4]) =
           u32x2{h2_bits(half2v{pv[0], pv[1]}), h2_bits(half2v{pv[2], pv[3]})};
       sum = rows_sum(sum);
-      if (q4 == 0) {
-        sm.red_sum[w][h] = sum;
-        if (w == 0) sm.alpha[h] = alpha[ht];
+      if (q4 == 0) sm.red_sum[pb][w][h] = sum;
+    };
+    auto stage = [&]() {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(&ss.cs[pb][cs_off(myslot) + 64 * q4 + 16 * c]) = cur.c[c];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        ss.sct[pb][(8 * q4 + 2 * g) * kScStride + myslot] = sc[g][0];
+        ss.sct[pb][(8 * q4 + 2 * g + 1) * kScStride + myslot] = sc[g][1];
       }
+    };
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      if (kFastSoftmax) probs(ht, mref[ht] == -INFINITY ? 0.0f : mref[ht]);
+      if (q4 == 0) sm.red_max[pb][w][16 * ht + n16] = mx[ht];
     }
-    lds_barrier();  // B2: probabilities, sums, alpha and staged codes visible
+    if (kFastSoftmax) stage();
+    lds_barrier();  // B1: maxima (and, first scheme, probabilities, sums, staged codes) visible;
+                    // every wave is past the PV of the previous step
+    if (!kFastSoftmax) stage();
+
+    float mstep[NHT];
+    bool move = false;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      mstep[ht] = sm.red_max[pb][0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) mstep[ht] = fmaxf(mstep[ht], sm.red_max[pb][ww][h]);
+      move |= mstep[ht] > mref[ht] + kLazy;  // (true for any valid key while the reference is -inf)
+    }
+    const bool slow = !kFastSoftmax || __ballot(move) != 0ull;  // the same in every wave
+    float alpha[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) alpha[ht] = 1.0f;
+    if (slow) {
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        const int h = 16 * ht + n16;
+        const float mnew = (mstep[ht] > mref[ht] + kLazy) ? mstep[ht] : mref[ht];
+        const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+        alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
+        mref[ht] = mnew;
+        probs(ht, muse);
+        if (q4 == 0 && w == 0) sm.alpha[h] = alpha[ht];
+      }
+      lds_barrier();  // B2: probabilities, sums, alpha (and, second scheme, staged codes) visible
+    }
 
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
-      float add = sm.red_sum[0][h];
+      float add = sm.red_sum[pb][0][h];
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) add += sm.red_sum[ww][h];
+      for (int ww = 1; ww < kWaves; ++ww) add += sm.red_sum[pb][ww][h];
       lrun[ht] = lrun[ht] * alpha[ht] + add;
     }
 
     // ---- PV: channels 128*cq + 8*n16 + t (t = 0..7) of every head over keys [64kh, 64kh+64);
     // rescale only when a reference moved
-    if (st > 0) {
+    if (slow && st > 0) {
       float al[NHT][4];
       bool moved = false;
 #pragma unroll
@@ -425,9 +464,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       uint32_t W[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        W[k] = *reinterpret_cast<const uint32_t*>(&ss.cs[cs_off(key0 + k) + 64 * cq + 4 * n16]);
+        W[k] = *reinterpret_cast<const uint32_t*>(&ss.cs[pb][cs_off(key0 + k) + 64 * cq + 4 * n16]);
       // the 8 channels share scale group 8*cq + n16/2
-      const u32x4 spw = *reinterpret_cast<const u32x4*>(&ss.sct[(8 * cq + (n16 >> 1)) * kScStride + key0]);
+      const u32x4 spw = *reinterpret_cast<const u32x4*>(&ss.sct[pb][(8 * cq + (n16 >> 1)) * kScStride + key0]);
       // byte b of E[p]: channel 2b of keys (2p, 2p+1); byte b of D[p]: channel 2b+1
       uint32_t E[4], D[4];
 #pragma unroll
@@ -439,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       half8 av[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht)
-        av[ht] = *reinterpret_cast<const half8*>(&ss.p[(16 * ht + n16) * kPStride + key0]);
+        av[ht] = *reinterpret_cast<const half8*>(&ss.p[pb][(16 * ht + n16) * kPStride + key0]);
       // tile t (channel 128*cq + 8*n16 + t) is converted just before its products
       auto tile = [&](auto sel_c, const uint32_t(&src)[4], int t) {
         constexpr int SEL = decltype(sel_c)::value;
@@ -608,12 +647,14 @@ struct Plan {
 // then dequantized by twice as many workgroups, but half as many key splits
 // fill the chip, which halves the split partials written here and read by
 // the combine (measured faster at 4 and 16 rows of 64 heads, slower at 32).
+// fp32 queries (hi and lo halves) always take 16 heads: 32 would not fit the
+// double-buffered staging in LDS.
 Plan plan(int R, int Hq, int q_dtype, int top_k) {
   Plan p{};
   p.splitq = q_dtype == CSA2_F32;
   const int tiles = Hq / 16;
   const int max_splits = (int)std::max<int64_t>(1, ceil_div(top_k, kStep));
-  p.nht = (tiles % 2 == 0 && (int64_t)R * tiles > 64) ? 2 : 1;
+  p.nht = (tiles % 2 == 0 && (int64_t)R * tiles > 64 && !p.splitq) ? 2 : 1;
   p.head_groups = tiles / p.nht;
   const int64_t base = (int64_t)R * p.head_groups;
   const int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(256, base)));
@@ -683,10 +724,7 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
       default: e = go<1, false, CSA2_BF16>(p, R, a, s); break;
     }
   } else {
-    switch (p.nht) {
-      case 2: e = go<2, true, CSA2_F32>(p, R, a, s); break;
-      default: e = go<1, true, CSA2_F32>(p, R, a, s); break;
-    }
+    e = go<1, true, CSA2_F32>(p, R, a, s);
   }
   if (ev.stop) (void)hipEventRecord(ev.stop, s);
   if (e != hipSuccess) return e;
