@@ -746,7 +746,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
 constexpr int kPfRows = 8;       // query rows per workgroup of the approximate passes
 constexpr int kPfRange = 32768;  // keys per workgroup of the candidate pass
 constexpr int kPfCap = 16384;    // candidates kept per row (more: exact fallback for that row)
-constexpr int kPfDepth = 4;      // 32-key steps in flight per wave
+constexpr int kPfDepth = 2;      // 32-key steps in flight per wave
 constexpr int kPfSample = 16;    // the provisional bound samples every 16th 32-key step
 // error constant c of the bound above for H heads, with a factor 8 of safety
 // on top (so the margin stays valid even if an accumulator kept fewer bits)
@@ -830,7 +830,7 @@ __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
 // queries held in registers (M = 16 (row, head) pairs per MFMA tile).  In
 // MODE 1 a step yields one whole bitmap word per row, stored directly.
 template <int MODE, int H>
-__global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
+__global__ __launch_bounds__(256, H == 16 ? 2 : 3) void k_pf_pass(PfArgs a) {
   constexpr int MT = kPfRows * H / 16;  // M tiles
   constexpr int RPM = 16 / H;           // rows per M tile
   extern __shared__ __align__(16) uint32_t pl[];  // MODE 0: kPfRows x kD1/2 packed counters
