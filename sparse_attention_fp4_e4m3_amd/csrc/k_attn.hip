@@ -574,6 +574,287 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   }
 }
 
+// ---- 64-head workgroups (bf16 queries) for batches whose rows alone fill
+// the chip.  Every key is then dequantized once per 64 heads instead of once
+// per 32, for QK^T and for PV.  QK^T is as above with four head tiles; PV
+// gives wave w the channels [64w, 64w+64) of all 64 heads over all keys of
+// the step: a lane owns the 4 channels 64w + 4*n16 + t (t = 0..3, one per
+// output tile, all in one scale group), reads their 16-bit code pieces and
+// interleaves two keys' nibbles per byte, two key pairs per 32-bit word, so
+// that each converted fp16 pair again holds two keys of one channel.  With
+// no key halves, each wave writes its own channels at the end.
+struct SmemWide {
+  _Float16 q[64 * kQStride];
+  uint8_t cs[(kStep / 32) * kCsBlock];
+  _Float16 sct[kGroups * kScStride];
+  _Float16 p[64 * kPStride];
+  float red_max[kWaves][64];
+  float red_sum[kWaves][64];
+  float alpha[64];
+  float lfin[64];
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  SmemWide& sm = *reinterpret_cast<SmemWide*>(smem_raw);
+  constexpr int NHT = 4, HG = 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
+  const int h0 = hg * HG;
+  const int kbeg = split * a.keys_per_split;
+  const int kend = min(a.top_k, kbeg + a.keys_per_split);
+  const int nsteps = kend > kbeg ? (kend - kbeg + kStep - 1) / kStep : 0;
+  const int vis = a.row_visible ? a.row_visible[r] : 0x7FFFFFFF;
+  const int64_t rs = a.row_start[r];
+  const int myslot = 16 * w + n16;  // this lane's key within a step (QK^T role)
+
+  // ---- prologue (as in k_sparse_attn): indices, the keys of step 0 in flight, queries to LDS
+  uint32_t vA = 0, vB = 0;
+  Raw bufA, bufB;
+  const int32_t j0 = load_idx(a, r, kbeg + myslot, kend);
+  int32_t jn = load_idx(a, r, kbeg + kStep + myslot, kend);
+  load_raw(bufA, a, rs, vis, j0, kbeg + myslot, kend, vA, q4);
+  {
+    constexpr int NP = HG * kDim / 8 / kThreads;  // 16-byte pieces per thread
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
+    u32x4 v[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + kThreads * i;
+      v[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)(p / (kDim / 8)) * kDim + (p % (kDim / 8)) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + kThreads * i;
+      half8 hv;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        hv[2 * k] = (_Float16)__uint_as_float(v[i][k] << 16);
+        hv[2 * k + 1] = (_Float16)__uint_as_float(v[i][k] & 0xFFFF0000u);
+      }
+      *reinterpret_cast<half8*>(&sm.q[(p / (kDim / 8)) * kQStride + (p % (kDim / 8)) * 8]) = hv;
+    }
+  }
+  __syncthreads();
+
+  floatx4 O[NHT][4];  // [head tile][channel 64w + 4*n16 + t]: heads 16*ht + 4*q4 + i
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mref[NHT], lrun[NHT];  // per head 16*ht + n16 (softmax role), replicated over q4 and waves
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    mref[ht] = -INFINITY;
+    lrun[ht] = 0.0f;
+  }
+  const int cb = 32 * w + 2 * n16;     // byte of this lane's PV channels in a code row
+  const int grp = 4 * w + (n16 >> 2);  // their scale group
+
+  auto step = [&](int st, Raw& cur, uint32_t vcur, Raw& nxt, uint32_t& vnxt) {
+    const int kstep0 = kbeg + st * kStep;
+    load_raw(nxt, a, rs, vis, jn, kstep0 + kStep + myslot, kend, vnxt, q4);
+    jn = load_idx(a, r, kstep0 + 2 * kStep + myslot, kend);
+    mask_raw(cur, vcur);
+    half2v sc[4];
+    sc[0] = e4m3x2_to_h2<false>(cur.s[0]);
+    sc[1] = e4m3x2_to_h2<true>(cur.s[0]);
+    sc[2] = e4m3x2_to_h2<false>(cur.s[1]);
+    sc[3] = e4m3x2_to_h2<true>(cur.s[1]);
+
+    // ---- QK^T: S^T[key][head] for this wave's 16 keys and the 64 heads
+    floatx4 S[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) S[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+    half8 bq[2][NHT];  // query fragments, one K-step ahead
+    auto load_bq = [&](half8* dst, int ks) {
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+        dst[ht] = *reinterpret_cast<const half8*>(&sm.q[(16 * ht + n16) * kQStride + 128 * q4 + 8 * ks]);
+    };
+    load_bq(bq[0], 0);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks + 1 < 16) load_bq(bq[(ks + 1) & 1], ks + 1);
+      const uint32_t word = cur.c[ks >> 2][ks & 3];
+      const half2v s1 = sc[ks >> 2];
+      const half2v sv = (ks & 2) ? half2v{s1[1], s1[1]} : half2v{s1[0], s1[0]};
+      const half8 av = cat4(fp4x2_to_h2<0>(word) * sv, fp4x2_to_h2<1>(word) * sv, fp4x2_to_h2<2>(word) * sv,
+                            fp4x2_to_h2<3>(word) * sv);
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) S[ht] = mfma(av, bq[ks & 1][ht], S[ht]);
+    }
+
+    // ---- softmax (maxima exchanged first, then probabilities; lazy references as above)
+    const unsigned long long vm = __ballot(vcur);
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (vm >> (4 * q4 + i)) & 1ull;
+        const float z = ok ? S[ht][i] * a.c2 : -INFINITY;
+        S[ht][i] = z;
+        mx = fmaxf(mx, z);
+      }
+      mx = rows_max(mx);
+      if (q4 == 0) sm.red_max[w][16 * ht + n16] = mx;
+    }
+    lds_barrier();  // B1: maxima visible; every wave is past the previous PV
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&sm.cs[cs_off(myslot) + 64 * q4 + 16 * c]) = cur.c[c];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      sm.sct[(8 * q4 + 2 * g) * kScStride + myslot] = sc[g][0];
+      sm.sct[(8 * q4 + 2 * g + 1) * kScStride + myslot] = sc[g][1];
+    }
+    float alpha[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      float mstep = sm.red_max[0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) mstep = fmaxf(mstep, sm.red_max[ww][h]);
+      const float mnew = (mstep > mref[ht] + kLazy) ? mstep : mref[ht];
+      const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+      alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
+      mref[ht] = mnew;
+      _Float16 pv[4];
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
+        sum += (float)pv[i];
+      }
+      *reinterpret_cast<u32x2*>(&sm.p[h * kPStride + 16 * w + 4 * q4]) =
+          u32x2{h2_bits(half2v{pv[0], pv[1]}), h2_bits(half2v{pv[2], pv[3]})};
+      sum = rows_sum(sum);
+      if (q4 == 0) {
+        sm.red_sum[w][h] = sum;
+        if (w == 0) sm.alpha[h] = alpha[ht];
+      }
+    }
+    lds_barrier();  // B2: probabilities, sums, alpha and staged codes visible
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      float add = sm.red_sum[0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) add += sm.red_sum[ww][h];
+      lrun[ht] = lrun[ht] * alpha[ht] + add;
+    }
+    if (st > 0) {
+      float al[NHT][4];
+      bool moved = false;
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          al[ht][i] = sm.alpha[16 * ht + 4 * q4 + i];
+          moved |= al[ht][i] != 1.0f;
+        }
+      if (__ballot(moved)) {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) O[ht][t][i] *= al[ht][i];
+      }
+    }
+
+    // ---- PV over the step's 128 keys, 32 per K-step: this lane's keys key0 .. key0+7
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int key0 = 32 * kk + 8 * q4;
+      uint32_t W[8];  // the 4 code nibbles (channels 64w + 4*n16 .. +3) of each key
+#pragma unroll
+      for (int k = 0; k < 8; ++k) W[k] = *reinterpret_cast<const uint16_t*>(&sm.cs[cs_off(key0 + k) + cb]);
+      const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[grp * kScStride + key0]);
+      // bytes of E: channel 0 of keys (0,1), channel 2 of keys (0,1), channel 0 of keys (2,3),
+      // channel 2 of keys (2,3) (first two key pairs; the second word the next two); D: channels 1, 3
+      uint32_t E[2], D[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const uint32_t A = W[4 * h2] | (W[4 * h2 + 2] << 16), B = W[4 * h2 + 1] | (W[4 * h2 + 3] << 16);
+        E[h2] = (A & 0x0F0F0F0Fu) | ((B << 4) & 0xF0F0F0F0u);
+        D[h2] = ((A >> 4) & 0x0F0F0F0Fu) | (B & 0xF0F0F0F0u);
+      }
+      half8 av[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+        av[ht] = *reinterpret_cast<const half8*>(&sm.p[(16 * ht + n16) * kPStride + key0]);
+      // tile t: channel 64w + 4*n16 + t; key pairs 0..3 from bytes (lo, hi) of the two words
+      auto tile = [&](auto lo_c, const uint32_t(&src)[2], int t) {
+        constexpr int LO = decltype(lo_c)::value;  // byte of the first key pair of a word (0 or 1)
+        const u32x4 b = u32x4{h2_bits(fp4x2_to_h2<LO>(src[0]) * bits_h2(spw[0])),
+                              h2_bits(fp4x2_to_h2<LO + 2>(src[0]) * bits_h2(spw[1])),
+                              h2_bits(fp4x2_to_h2<LO>(src[1]) * bits_h2(spw[2])),
+                              h2_bits(fp4x2_to_h2<LO + 2>(src[1]) * bits_h2(spw[3]))};
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) O[ht][t] = mfma(av[ht], __builtin_bit_cast(half8, b), O[ht][t]);
+      };
+      tile(std::integral_constant<int, 0>{}, E, 0);
+      tile(std::integral_constant<int, 0>{}, D, 1);
+      tile(std::integral_constant<int, 1>{}, E, 2);
+      tile(std::integral_constant<int, 1>{}, D, 3);
+    }
+  };
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, bufA, vA, bufB, vB);
+    if (st + 1 < nsteps) step(st + 1, bufB, vB, bufA, vA);
+  }
+
+  // ---- epilogue: each wave writes its 64 channels of the 64 heads
+  if (w == 0 && q4 == 0) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) sm.lfin[16 * ht + n16] = lrun[ht];
+  }
+  __syncthreads();
+  const int64_t rowh = (int64_t)r * a.Hq + h0;
+  const int ch = 64 * w + 4 * n16;
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * ht + 4 * q4 + i;
+      const float L = sm.lfin[h];
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      const float v0 = O[ht][0][i] * inv, v1 = O[ht][1][i] * inv, v2 = O[ht][2][i] * inv, v3 = O[ht][3][i] * inv;
+      if (a.splits > 1) {
+        floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch);
+        __builtin_nontemporal_store(floatx4{v0, v1, v2, v3}, dst);
+      } else if (a.out_dtype == CSA2_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch) = make_float4(v0, v1, v2, v3);
+      } else {
+        const float vv[4] = {v0, v1, v2, v3};
+        uint32_t pk[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          uint32_t lo = __float_as_uint(vv[2 * k]), hi = __float_as_uint(vv[2 * k + 1]);
+          lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+          hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+          pk[k] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + ch) = make_uint2(pk[0], pk[1]);
+      }
+    }
+  }
+  if (w == 0 && q4 == 0) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      if (a.splits == 1) {
+        if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
+      } else {
+        a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
+        a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+      }
+    }
+  }
+}
+
 // one (row, head) per workgroup of 128 threads, 4 channels per thread;
 // splits merged in fixed order with a running maximum, 8 splits per batch of
 // loads: o = sum_s w_s l_s o_s / sum_s w_s l_s,  w_s = 2^(m_s - max m)
@@ -638,6 +919,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
 struct Plan {
   int nht, head_groups, splits, keys_per_split;
   bool splitq;
+  bool wide;  // 64-head workgroups (k_sparse_attn_wide)
 };
 
 // Launch plan.  A workgroup takes 32 heads (16 if the head count is an odd
@@ -648,12 +930,21 @@ struct Plan {
 // fill the chip, which halves the split partials written here and read by
 // the combine (measured faster at 4 and 16 rows of 64 heads, slower at 32).
 // fp32 queries (hi and lo halves) always take 16 heads: 32 would not fit the
-// double-buffered staging in LDS.
+// double-buffered staging in LDS.  When rows x 64-head groups alone fill the
+// chip (bf16 queries), workgroups take 64 heads and no keys are split.
 Plan plan(int R, int Hq, int q_dtype, int top_k) {
   Plan p{};
   p.splitq = q_dtype == CSA2_F32;
   const int tiles = Hq / 16;
   const int max_splits = (int)std::max<int64_t>(1, ceil_div(top_k, kStep));
+  p.wide = !p.splitq && tiles % 4 == 0 && (int64_t)R * (tiles / 4) >= 256;
+  if (p.wide) {
+    p.nht = 4;
+    p.head_groups = tiles / 4;
+    p.keys_per_split = (int)round_up(top_k, kStep);
+    p.splits = 1;
+    return p;
+  }
   p.nht = (tiles % 2 == 0 && (int64_t)R * tiles > 64 && !p.splitq) ? 2 : 1;
   p.head_groups = tiles / p.nht;
   const int64_t base = (int64_t)R * p.head_groups;
@@ -718,7 +1009,17 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
   auto& ev = profile_events(CSA2_KERNEL_ATTN);
   if (ev.start) (void)hipEventRecord(ev.start, s);
   hipError_t e;
-  if (q_dtype == CSA2_BF16) {
+  if (p.wide) {
+    const size_t lds = sizeof(SmemWide);
+    static bool configured = false;
+    if (!configured) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_sparse_attn_wide),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      configured = true;
+    }
+    hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.splits, R, p.head_groups), dim3(kThreads), lds, s, a);
+    e = hipGetLastError();
+  } else if (q_dtype == CSA2_BF16) {
     switch (p.nht) {
       case 2: e = go<2, false, CSA2_BF16>(p, R, a, s); break;
       default: e = go<1, false, CSA2_BF16>(p, R, a, s); break;

@@ -259,6 +259,8 @@ def _cache(seed, n, outliers=False):
     (48, "bf16", 2, 700, 3000),
     (128, "bf16", 2, 512, 3000),   # two head groups
     (32, "f32", 3, 640, 3000),
+    (64, "bf16", 256, 300, 5000),  # rows alone fill the chip: 64-head workgroups, ragged step
+    (128, "bf16", 160, 200, 3000),  # 64-head workgroups, two per row
 ])
 def test_attention_matches_oracle(Hq, qkind, R, K, n):
     rng = np.random.default_rng(Hq * 1000 + K)
@@ -278,21 +280,24 @@ def test_attention_matches_oracle(Hq, qkind, R, K, n):
     check_attention(out, lse, ro, rl, "attn Hq=%d %s R=%d K=%d" % (Hq, qkind, R, K))
 
 
-def test_attention_all_selected_equals_dense_and_edge_rows():
+@pytest.mark.parametrize("R", [4, 256])  # 256 rows: 64-head workgroups
+def test_attention_all_selected_equals_dense_and_edge_rows(R):
     n, Hq = 700, 64
     rng = np.random.default_rng(3)
     x = _cache(3, n)
     oc, os_ = oracle.quantize(x)
-    q = bf16_round(rng.standard_normal((4, Hq, 512)).astype(np.float32))
+    q = bf16_round(rng.standard_normal((R, Hq, 512)).astype(np.float32))
     K = 1024  # K >= n: dense attention over every entry
-    idx = np.full((4, K), -1, np.int32)
+    idx = np.full((R, K), -1, np.int32)
     idx[0, :n] = np.arange(n)
     idx[1, :n] = rng.permutation(n)
     idx[2, :] = -1  # empty selection: zeros and -inf
     idx[3, 5] = 17  # a single entry
-    out, lse = attention(dev_bf16(q), dev(oc), dev(os_), dev(np.zeros(4, np.int64)), dev(idx), 0.0441941738,
-                         vis=dev(np.full(4, n, np.int32)))
-    ro, rl = oracle.attention_rows(q, oc, os_, np.zeros(4, np.int64), idx, np.full(4, n), 0.0441941738)
+    for r in range(4, R):
+        idx[r, :300] = rng.permutation(n)[:300]
+    out, lse = attention(dev_bf16(q), dev(oc), dev(os_), dev(np.zeros(R, np.int64)), dev(idx), 0.0441941738,
+                         vis=dev(np.full(R, n, np.int32)))
+    ro, rl = oracle.attention_rows(q, oc, os_, np.zeros(R, np.int64), idx, np.full(R, n), 0.0441941738)
     check_attention(out, lse, ro, rl, "dense/edge rows")
     o = out.cpu().numpy()
     assert np.all(o[2] == 0) and np.all(np.isneginf(lse.cpu().numpy()[2]))
