@@ -175,8 +175,8 @@ struct Raw {
 };
 
 // Branch-free gather: an invalid key loads row 0 of the cache (always
-// present) and is zeroed before use, so every load is issued unconditionally
-// and the compiler keeps them all in flight.
+// present) and is masked before use (mask_raw), so every load is issued
+// unconditionally and the compiler keeps them all in flight.
 __device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int64_t rs, int vis, int32_t j, int i,
                                          int kend, uint32_t& valid, int q4) {
   const bool ok = (i < kend) & ((uint32_t)j < (uint32_t)vis);
@@ -188,11 +188,10 @@ __device__ __forceinline__ void load_raw(Raw& R, const AttnArgs& a, int64_t rs, 
   R.s = *reinterpret_cast<const u32x2*>(a.scales + row * kGroups + 8 * q4);
 }
 
+// An invalid key's scales are zeroed, so its dequantized values are 0 in PV
+// (its codes are finite E2M1 values whatever row was read; its logits are
+// masked separately).
 __device__ __forceinline__ void mask_raw(Raw& R, uint32_t valid) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) R.c[c][e] = valid ? R.c[c][e] : 0u;
   R.s[0] = valid ? R.s[0] : 0u;
   R.s[1] = valid ? R.s[1] : 0u;
 }
@@ -327,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
       if (ks + 2 < 16) load_bq(bq[(ks + 2) % 3], ks + 2);
       const uint32_t word = cur.c[ks >> 2][ks & 3];
       const half2v s1 = sc[ks >> 2];
-      const half2v sv = (ks & 2) ? half2v{s1[1], s1[1]} : half2v{s1[0], s1[0]};
+      const half2v sv = (ks & 2) ? __builtin_shufflevector(s1, s1, 1, 1) : __builtin_shufflevector(s1, s1, 0, 0);
       const half8 av = cat4(fp4x2_to_h2<0>(word) * sv, fp4x2_to_h2<1>(word) * sv, fp4x2_to_h2<2>(word) * sv,
                             fp4x2_to_h2<3>(word) * sv);
 #pragma unroll
@@ -574,6 +573,345 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
   }
 }
 
+// ---- Pipelined workgroups (bf16 queries, 16 or 32 heads).  Waves 0-3 and
+// 4-7 take different roles so that the two waves sharing a SIMD run
+// different code at the same time instead of meeting at every barrier with
+// the same work.  Iteration i has two phases, each ended by a barrier:
+//  * waves 0-3 (QK^T role) score step i: phase 1 gathers and dequantizes
+//    their 32 keys (two 16-key tiles, the gather of step i+1 in flight) and
+//    runs QK^T with the query fragments shared by both tiles, then
+//    publishes per-wave maxima; phase 2 moves the lazy references, writes
+//    the probabilities and sums and stages the raw codes and scales of step
+//    i in buffer i%2;
+//  * waves 4-7 (PV role) run PV for step i-1 from buffer (i-1)%2, half of
+//    its keys per phase; wave 4+c owns channels [128c, 128c+128) of every
+//    head over all keys of the step (no key halves, so each writes its own
+//    channels at the end).
+// The running sums live in the QK^T waves (updated one iteration later from
+// the published sums), the outputs in the PV waves, which rescale them by
+// the published factors when a reference moved.
+template <int NHT>
+struct SmemPP {
+  _Float16 q[16 * NHT * kQStride];
+  uint8_t cs[2][(kStep / 32) * kCsBlock];
+  _Float16 sct[2][kGroups * kScStride];
+  _Float16 p[2][16 * NHT * kPStride];
+  float red_max[4][64];
+  float red_sum[4][64];
+  float alpha[64];
+  float lfin[64];
+  float mfin[64];
+};
+
+template <int NHT>
+__global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  SmemPP<NHT>& sm = *reinterpret_cast<SmemPP<NHT>*>(smem_raw);
+  constexpr int HG = 16 * NHT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const bool qk_role = w < 4;
+  const int c4 = w & 3;  // QK^T: key quarter of the step; PV: channel quarter
+  const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
+  const int h0 = hg * HG;
+  const int kbeg = split * a.keys_per_split;
+  const int kend = min(a.top_k, kbeg + a.keys_per_split);
+  const int nsteps = kend > kbeg ? (kend - kbeg + kStep - 1) / kStep : 0;
+  const int vis = a.row_visible ? a.row_visible[r] : 0x7FFFFFFF;
+  const int64_t rs = a.row_start[r];
+  int slot[2];  // QK^T role: this lane's keys within a step
+  slot[0] = 32 * c4 + n16;
+  slot[1] = 32 * c4 + 16 + n16;
+
+  Raw bufA[2], bufB[2];
+  uint32_t vA[2] = {0u, 0u}, vB[2] = {0u, 0u};
+  int32_t jn[2] = {0, 0};
+  if (qk_role) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int32_t j0 = load_idx(a, r, kbeg + slot[kt], kend);
+      jn[kt] = load_idx(a, r, kbeg + kStep + slot[kt], kend);
+      load_raw(bufA[kt], a, rs, vis, j0, kbeg + slot[kt], kend, vA[kt], q4);
+    }
+  }
+  {
+    constexpr int NP = HG * kDim / 8 / kThreads;  // 16-byte query pieces per thread
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
+    u32x4 v[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + kThreads * i;
+      v[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)(p / (kDim / 8)) * kDim + (p % (kDim / 8)) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + kThreads * i;
+      half8 hv;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        hv[2 * k] = (_Float16)__uint_as_float(v[i][k] << 16);
+        hv[2 * k + 1] = (_Float16)__uint_as_float(v[i][k] & 0xFFFF0000u);
+      }
+      *reinterpret_cast<half8*>(&sm.q[(p / (kDim / 8)) * kQStride + (p % (kDim / 8)) * 8]) = hv;
+    }
+  }
+  __syncthreads();
+
+  // QK^T role state: lazy references and running sums per head 16*ht + n16 (replicated over q4 and waves)
+  float mref[NHT], lrun[NHT], alpha_prev[NHT];
+  floatx4 S[2][NHT];
+  // PV role state: outputs of channels 128*c4 + 8*n16 + t, heads 16*ht + 4*q4 + i
+  floatx4 O[NHT][8];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    mref[ht] = -INFINITY;
+    lrun[ht] = 0.0f;
+    alpha_prev[ht] = 1.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // PV over keys [32kk, 32kk+32) of the step staged in buffer b
+  auto pv_part = [&](int b, int kk) {
+    const int key0 = 32 * kk + 8 * q4;
+    uint32_t W[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      W[k] = *reinterpret_cast<const uint32_t*>(&sm.cs[b][cs_off(key0 + k) + 64 * c4 + 4 * n16]);
+    const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[b][(8 * c4 + (n16 >> 1)) * kScStride + key0]);
+    uint32_t E[4], D[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t wa = W[2 * p], wb = W[2 * p + 1];
+      E[p] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
+      D[p] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+    }
+    half8 av[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) av[ht] = *reinterpret_cast<const half8*>(&sm.p[b][(16 * ht + n16) * kPStride + key0]);
+    auto tile = [&](auto sel_c, const uint32_t(&src)[4], int t) {
+      constexpr int SEL = decltype(sel_c)::value;
+      u32x4 bb;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) bb[p] = h2_bits(fp4x2_to_h2<SEL>(src[p]) * bits_h2(spw[p]));
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) O[ht][t] = mfma(av[ht], __builtin_bit_cast(half8, bb), O[ht][t]);
+    };
+    tile(std::integral_constant<int, 0>{}, E, 0);
+    tile(std::integral_constant<int, 0>{}, D, 1);
+    tile(std::integral_constant<int, 1>{}, E, 2);
+    tile(std::integral_constant<int, 1>{}, D, 3);
+    tile(std::integral_constant<int, 2>{}, E, 4);
+    tile(std::integral_constant<int, 2>{}, D, 5);
+    tile(std::integral_constant<int, 3>{}, E, 6);
+    tile(std::integral_constant<int, 3>{}, D, 7);
+  };
+
+  auto iter = [&](int it, Raw (&cur)[2], uint32_t (&vcur)[2], Raw (&nxt)[2], uint32_t (&vnxt)[2]) {
+    const int bw = it & 1, br = bw ^ 1;
+    half2v sc[2][4];
+    // ---------------- phase 1
+    if (qk_role) {
+      if (it > 0) {  // running sums of step it-1
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          const int h = 16 * ht + n16;
+          const float add = (sm.red_sum[0][h] + sm.red_sum[1][h]) + (sm.red_sum[2][h] + sm.red_sum[3][h]);
+          lrun[ht] = lrun[ht] * alpha_prev[ht] + add;
+        }
+      }
+      if (it < nsteps) {
+        const int kstep0 = kbeg + it * kStep;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          load_raw(nxt[kt], a, rs, vis, jn[kt], kstep0 + kStep + slot[kt], kend, vnxt[kt], q4);
+          jn[kt] = load_idx(a, r, kstep0 + 2 * kStep + slot[kt], kend);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          mask_raw(cur[kt], vcur[kt]);
+          sc[kt][0] = e4m3x2_to_h2<false>(cur[kt].s[0]);
+          sc[kt][1] = e4m3x2_to_h2<true>(cur[kt].s[0]);
+          sc[kt][2] = e4m3x2_to_h2<false>(cur[kt].s[1]);
+          sc[kt][3] = e4m3x2_to_h2<true>(cur[kt].s[1]);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+        half8 bq[2][NHT];
+        auto load_bq = [&](half8* dst, int ks) {
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht)
+            dst[ht] = *reinterpret_cast<const half8*>(&sm.q[(16 * ht + n16) * kQStride + 128 * q4 + 8 * ks]);
+        };
+        load_bq(bq[0], 0);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          if (ks + 1 < 16) load_bq(bq[(ks + 1) & 1], ks + 1);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const uint32_t word = cur[kt].c[ks >> 2][ks & 3];
+            const half2v s1 = sc[kt][ks >> 2];
+            const half2v sv = (ks & 2) ? __builtin_shufflevector(s1, s1, 1, 1) : __builtin_shufflevector(s1, s1, 0, 0);
+            const half8 av = cat4(fp4x2_to_h2<0>(word) * sv, fp4x2_to_h2<1>(word) * sv,
+                                  fp4x2_to_h2<2>(word) * sv, fp4x2_to_h2<3>(word) * sv);
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = mfma(av, bq[ks & 1][ht], S[kt][ht]);
+          }
+        }
+        // scaled, masked logits and the per-wave maxima (keys 32*c4 + 16*kt + 4*q4 + i)
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const unsigned long long vm = __ballot(vcur[kt]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool ok = (vm >> (4 * q4 + i)) & 1ull;
+              const float z = ok ? S[kt][ht][i] * a.c2 : -INFINITY;
+              S[kt][ht][i] = z;
+              mx = fmaxf(mx, z);
+            }
+          }
+          mx = rows_max(mx);
+          if (q4 == 0) sm.red_max[c4][16 * ht + n16] = mx;
+        }
+      }
+    } else if (it > 0) {
+      // rescale when a reference moved at step it-1, then the first half of its keys
+      float al[NHT][4];
+      bool moved = false;
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          al[ht][i] = sm.alpha[16 * ht + 4 * q4 + i];
+          moved |= al[ht][i] != 1.0f;
+        }
+      if (__ballot(moved)) {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) O[ht][t][i] *= al[ht][i];
+      }
+      pv_part(br, 0);
+      pv_part(br, 1);
+      pv_part(br, 2);
+    }
+    lds_barrier();
+    // ---------------- phase 2
+    if (qk_role) {
+      if (it < nsteps) {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          const int h = 16 * ht + n16;
+          const float mstep = fmaxf(fmaxf(sm.red_max[0][h], sm.red_max[1][h]), fmaxf(sm.red_max[2][h], sm.red_max[3][h]));
+          const float mnew = (mstep > mref[ht] + kLazy) ? mstep : mref[ht];
+          const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+          alpha_prev[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
+          mref[ht] = mnew;
+          float sum = 0.0f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            _Float16 pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[kt][ht][i] - muse);
+              sum += (float)pv[i];
+            }
+            *reinterpret_cast<u32x2*>(&sm.p[bw][h * kPStride + 32 * c4 + 16 * kt + 4 * q4]) =
+                u32x2{h2_bits(half2v{pv[0], pv[1]}), h2_bits(half2v{pv[2], pv[3]})};
+          }
+          sum = rows_sum(sum);
+          if (q4 == 0) {
+            sm.red_sum[c4][h] = sum;
+            if (c4 == 0) sm.alpha[h] = alpha_prev[ht];
+          }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<u32x4*>(&sm.cs[bw][cs_off(slot[kt]) + 64 * q4 + 16 * c]) = cur[kt].c[c];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            sm.sct[bw][(8 * q4 + 2 * g) * kScStride + slot[kt]] = sc[kt][g][0];
+            sm.sct[bw][(8 * q4 + 2 * g + 1) * kScStride + slot[kt]] = sc[kt][g][1];
+          }
+        }
+      }
+    } else if (it > 0) {
+      pv_part(br, 3);
+    }
+    lds_barrier();
+  };
+  for (int it = 0; it <= nsteps; it += 2) {
+    iter(it, bufA, vA, bufB, vB);
+    if (it + 1 <= nsteps) iter(it + 1, bufB, vB, bufA, vA);
+  }
+
+  // ---- epilogue: running sums and references through LDS, each PV wave writes its channels
+  if (qk_role && c4 == 0 && q4 == 0) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      sm.lfin[16 * ht + n16] = lrun[ht];
+      sm.mfin[16 * ht + n16] = mref[ht];
+    }
+  }
+  __syncthreads();
+  const int64_t rowh = (int64_t)r * a.Hq + h0;
+  if (!qk_role) {
+    const int ch = 128 * c4 + 8 * n16;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * ht + 4 * q4 + i;
+        const float L = sm.lfin[h];
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = O[ht][t][i] * inv;
+        if (a.splits > 1) {
+          floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch);
+          __builtin_nontemporal_store(floatx4{v[0], v[1], v[2], v[3]}, dst);
+          __builtin_nontemporal_store(floatx4{v[4], v[5], v[6], v[7]}, dst + 1);
+        } else if (a.out_dtype == CSA2_F32) {
+          float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch);
+          dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+          dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          uint32_t pk[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+            lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+            hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+            pk[k] = lo | (hi << 16);
+          }
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + ch) =
+              make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+      }
+    }
+  } else if (c4 == 0 && q4 == 0) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      if (a.splits == 1) {
+        if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
+      } else {
+        a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
+        a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+      }
+    }
+  }
+}
+
 // ---- 64-head workgroups (bf16 queries) for batches whose rows alone fill
 // the chip.  Every key is then dequantized once per 64 heads instead of once
 // per 32, for QK^T and for PV.  QK^T is as above with four head tiles; PV
@@ -679,7 +1017,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
       if (ks + 1 < 16) load_bq(bq[(ks + 1) & 1], ks + 1);
       const uint32_t word = cur.c[ks >> 2][ks & 3];
       const half2v s1 = sc[ks >> 2];
-      const half2v sv = (ks & 2) ? half2v{s1[1], s1[1]} : half2v{s1[0], s1[0]};
+      const half2v sv = (ks & 2) ? __builtin_shufflevector(s1, s1, 1, 1) : __builtin_shufflevector(s1, s1, 0, 0);
       const half8 av = cat4(fp4x2_to_h2<0>(word) * sv, fp4x2_to_h2<1>(word) * sv, fp4x2_to_h2<2>(word) * sv,
                             fp4x2_to_h2<3>(word) * sv);
 #pragma unroll
@@ -954,6 +1292,20 @@ Plan plan(int R, int Hq, int q_dtype, int top_k) {
   return p;
 }
 
+template <int NHT>
+hipError_t go_pp(const Plan& p, int R, const AttnArgs& a, hipStream_t s) {
+  auto kern = k_attn_pp<NHT>;
+  const size_t lds = sizeof(SmemPP<NHT>);
+  static bool configured = false;
+  if (!configured) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    configured = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(p.splits, R, p.head_groups), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int NHT, bool SPLITQ, int QDT>
 hipError_t go(const Plan& p, int R, const AttnArgs& a, hipStream_t s) {
   auto kern = k_sparse_attn<NHT, SPLITQ, QDT>;
@@ -1020,10 +1372,11 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
     hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.splits, R, p.head_groups), dim3(kThreads), lds, s, a);
     e = hipGetLastError();
   } else if (q_dtype == CSA2_BF16) {
-    switch (p.nht) {
-      case 2: e = go<2, false, CSA2_BF16>(p, R, a, s); break;
-      default: e = go<1, false, CSA2_BF16>(p, R, a, s); break;
-    }
+    // 16-head workgroups with at least two steps of keys take the pipelined kernel (its
+    // first and last iterations run one role only, which a single step cannot amortize)
+    if (p.nht == 2) e = go<2, false, CSA2_BF16>(p, R, a, s);
+    else if (p.keys_per_split >= 2 * kStep) e = go_pp<1>(p, R, a, s);
+    else e = go<1, false, CSA2_BF16>(p, R, a, s);
   } else {
     e = go<1, true, CSA2_F32>(p, R, a, s);
   }
