@@ -151,6 +151,21 @@ def algorithmic_bytes(w, lens):
     return out
 
 
+def attention_kernel_name(w):
+    """Name of the attention kernel the library's launch plan picks for this workload (a label
+    for the report: 64-head workgroups when rows x 64-head groups fill 256 workgroups, the
+    pipelined 16-head kernel for small batches with splits of two or more 128-key steps)."""
+    tiles = w.Hq // 16
+    if w.q_dtype == "bf16" and tiles % 4 == 0 and w.rows * (tiles // 4) >= 256:
+        return "k_sparse_attn_wide"
+    if w.q_dtype == "bf16" and w.rows * tiles <= 64:
+        splits = min(max(1, -(-w.K // 128)), max(1, -(-256 // (w.rows * tiles))))
+        kps = -(-(-(-w.K // splits)) // 128) * 128
+        if kps >= 256:
+            return "k_attn_pp"
+    return "k_sparse_attn"
+
+
 def attention_flops(w):
     return 4.0 * w.rows * w.Hq * w.K * 512
 
@@ -443,7 +458,7 @@ def main():
     dominant = max(["index_scan", "attention", "reindex_score"], key=lambda k: kern[k]["per_step_us"])
     dk = kern[dominant]
     if dominant == "attention":
-        roof = {"kernel": "k_sparse_attn", "bound": "mfma", "achieved": dk["TFLOPs"],
+        roof = {"kernel": attention_kernel_name(w), "bound": "mfma", "achieved": dk["TFLOPs"],
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": dk["mfma_frac"],
                 "traffic": traffic_from_profiles(w.name, "k_attn.hip")}
     elif dominant == "index_scan" and w.is_prefill:
