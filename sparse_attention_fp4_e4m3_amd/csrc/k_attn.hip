@@ -590,25 +590,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 // The running sums live in the QK^T waves (updated one iteration later from
 // the published sums), the outputs in the PV waves, which rescale them by
 // the published factors when a reference moved.
-template <int NHT>
+template <int NHT, int KT>
 struct SmemPP {
+  static constexpr int kKeys = 64 * KT;  // keys per step
   _Float16 q[16 * NHT * kQStride];
-  uint8_t cs[2][(kStep / 32) * kCsBlock];
+  uint8_t cs[2][(kKeys / 32) * kCsBlock];
   _Float16 sct[2][kGroups * kScStride];
   _Float16 p[2][16 * NHT * kPStride];
   float red_max[4][64];
   float red_sum[4][64];
   float alpha[64];
   float lfin[64];
-  float mfin[64];
 };
 
-template <int NHT>
+template <int NHT, int KT>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  SmemPP<NHT>& sm = *reinterpret_cast<SmemPP<NHT>*>(smem_raw);
+  SmemPP<NHT, KT>& sm = *reinterpret_cast<SmemPP<NHT, KT>*>(smem_raw);
+  constexpr int kKeys = SmemPP<NHT, KT>::kKeys;  // keys per step: KT 16-key tiles per QK^T wave
   constexpr int HG = 16 * NHT;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so each role branches as a whole
   const int n16 = lane & 15, q4 = lane >> 4;
   const bool qk_role = w < 4;
   const int c4 = w & 3;  // QK^T: key quarter of the step; PV: channel quarter
@@ -616,27 +618,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
   const int h0 = hg * HG;
   const int kbeg = split * a.keys_per_split;
   const int kend = min(a.top_k, kbeg + a.keys_per_split);
-  const int nsteps = kend > kbeg ? (kend - kbeg + kStep - 1) / kStep : 0;
+  const int nsteps = kend > kbeg ? (kend - kbeg + kKeys - 1) / kKeys : 0;
   const int vis = a.row_visible ? a.row_visible[r] : 0x7FFFFFFF;
   const int64_t rs = a.row_start[r];
-  int slot[2];  // QK^T role: this lane's keys within a step
-  slot[0] = 32 * c4 + n16;
-  slot[1] = 32 * c4 + 16 + n16;
+  const int64_t rowh = (int64_t)r * a.Hq + h0;
+  int slot[KT];  // QK^T role: this lane's keys within a step
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) slot[kt] = 16 * KT * c4 + 16 * kt + n16;
 
-  Raw bufA[2], bufB[2];
-  uint32_t vA[2] = {0u, 0u}, vB[2] = {0u, 0u};
-  int32_t jn[2] = {0, 0};
+  Raw bufA[KT], bufB[KT];
+  uint32_t vA[KT], vB[KT];
+  int32_t jn[KT];
   if (qk_role) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       const int32_t j0 = load_idx(a, r, kbeg + slot[kt], kend);
-      jn[kt] = load_idx(a, r, kbeg + kStep + slot[kt], kend);
+      jn[kt] = load_idx(a, r, kbeg + kKeys + slot[kt], kend);
       load_raw(bufA[kt], a, rs, vis, j0, kbeg + slot[kt], kend, vA[kt], q4);
     }
   }
   {
     constexpr int NP = HG * kDim / 8 / kThreads;  // 16-byte query pieces per thread
-    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + rowh * kDim;
     u32x4 v[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -657,61 +660,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
   }
   __syncthreads();
 
-  // QK^T role state: lazy references and running sums per head 16*ht + n16 (replicated over q4 and waves)
-  float mref[NHT], lrun[NHT], alpha_prev[NHT];
-  floatx4 S[2][NHT];
-  // PV role state: outputs of channels 128*c4 + 8*n16 + t, heads 16*ht + 4*q4 + i
-  floatx4 O[NHT][8];
+  // Each role runs a loop of its own with the same barriers (two per
+  // iteration, nsteps + 1 iterations), so only one role's state is live in
+  // either loop.
+  if (qk_role) {
+    // lazy references and running sums per head 16*ht + n16 (replicated over q4 and waves)
+    float mref[NHT], lrun[NHT], alpha_prev[NHT];
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    mref[ht] = -INFINITY;
-    lrun[ht] = 0.0f;
-    alpha_prev[ht] = 1.0f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // PV over keys [32kk, 32kk+32) of the step staged in buffer b
-  auto pv_part = [&](int b, int kk) {
-    const int key0 = 32 * kk + 8 * q4;
-    uint32_t W[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      W[k] = *reinterpret_cast<const uint32_t*>(&sm.cs[b][cs_off(key0 + k) + 64 * c4 + 4 * n16]);
-    const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[b][(8 * c4 + (n16 >> 1)) * kScStride + key0]);
-    uint32_t E[4], D[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t wa = W[2 * p], wb = W[2 * p + 1];
-      E[p] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
-      D[p] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+    for (int ht = 0; ht < NHT; ++ht) {
+      mref[ht] = -INFINITY;
+      lrun[ht] = 0.0f;
+      alpha_prev[ht] = 1.0f;
     }
-    half8 av[NHT];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) av[ht] = *reinterpret_cast<const half8*>(&sm.p[b][(16 * ht + n16) * kPStride + key0]);
-    auto tile = [&](auto sel_c, const uint32_t(&src)[4], int t) {
-      constexpr int SEL = decltype(sel_c)::value;
-      u32x4 bb;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) bb[p] = h2_bits(fp4x2_to_h2<SEL>(src[p]) * bits_h2(spw[p]));
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) O[ht][t] = mfma(av[ht], __builtin_bit_cast(half8, bb), O[ht][t]);
-    };
-    tile(std::integral_constant<int, 0>{}, E, 0);
-    tile(std::integral_constant<int, 0>{}, D, 1);
-    tile(std::integral_constant<int, 1>{}, E, 2);
-    tile(std::integral_constant<int, 1>{}, D, 3);
-    tile(std::integral_constant<int, 2>{}, E, 4);
-    tile(std::integral_constant<int, 2>{}, D, 5);
-    tile(std::integral_constant<int, 3>{}, E, 6);
-    tile(std::integral_constant<int, 3>{}, D, 7);
-  };
-
-  auto iter = [&](int it, Raw (&cur)[2], uint32_t (&vcur)[2], Raw (&nxt)[2], uint32_t (&vnxt)[2]) {
-    const int bw = it & 1, br = bw ^ 1;
-    half2v sc[2][4];
-    // ---------------- phase 1
-    if (qk_role) {
+    auto iter = [&](int it, Raw (&cur)[KT], uint32_t (&vcur)[KT], Raw (&nxt)[KT], uint32_t (&vnxt)[KT]) {
+      const int bw = it & 1;
+      half2v sc[KT][4];
+      floatx4 S[KT][NHT];
+      // ---------------- phase 1
       if (it > 0) {  // running sums of step it-1
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
@@ -721,14 +686,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
         }
       }
       if (it < nsteps) {
-        const int kstep0 = kbeg + it * kStep;
+        const int kstep0 = kbeg + it * kKeys;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          load_raw(nxt[kt], a, rs, vis, jn[kt], kstep0 + kStep + slot[kt], kend, vnxt[kt], q4);
-          jn[kt] = load_idx(a, r, kstep0 + 2 * kStep + slot[kt], kend);
+        for (int kt = 0; kt < KT; ++kt) {
+          load_raw(nxt[kt], a, rs, vis, jn[kt], kstep0 + kKeys + slot[kt], kend, vnxt[kt], q4);
+          jn[kt] = load_idx(a, r, kstep0 + 2 * kKeys + slot[kt], kend);
         }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
           mask_raw(cur[kt], vcur[kt]);
           sc[kt][0] = e4m3x2_to_h2<false>(cur[kt].s[0]);
           sc[kt][1] = e4m3x2_to_h2<true>(cur[kt].s[0]);
@@ -736,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
           sc[kt][3] = e4m3x2_to_h2<true>(cur[kt].s[1]);
         }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = floatx4{0.f, 0.f, 0.f, 0.f};
         half8 bq[2][NHT];
@@ -750,7 +715,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
         for (int ks = 0; ks < 16; ++ks) {
           if (ks + 1 < 16) load_bq(bq[(ks + 1) & 1], ks + 1);
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
+          for (int kt = 0; kt < KT; ++kt) {
             const uint32_t word = cur[kt].c[ks >> 2][ks & 3];
             const half2v s1 = sc[kt][ks >> 2];
             const half2v sv = (ks & 2) ? __builtin_shufflevector(s1, s1, 1, 1) : __builtin_shufflevector(s1, s1, 0, 0);
@@ -760,12 +725,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
             for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = mfma(av, bq[ks & 1][ht], S[kt][ht]);
           }
         }
-        // scaled, masked logits and the per-wave maxima (keys 32*c4 + 16*kt + 4*q4 + i)
+        // scaled, masked logits and the per-wave maxima (keys 16*KT*c4 + 16*kt + 4*q4 + i)
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
           float mx = -INFINITY;
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
+          for (int kt = 0; kt < KT; ++kt) {
             const unsigned long long vm = __ballot(vcur[kt]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -779,32 +744,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
           if (q4 == 0) sm.red_max[c4][16 * ht + n16] = mx;
         }
       }
-    } else if (it > 0) {
-      // rescale when a reference moved at step it-1, then the first half of its keys
-      float al[NHT][4];
-      bool moved = false;
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          al[ht][i] = sm.alpha[16 * ht + 4 * q4 + i];
-          moved |= al[ht][i] != 1.0f;
-        }
-      if (__ballot(moved)) {
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) O[ht][t][i] *= al[ht][i];
-      }
-      pv_part(br, 0);
-      pv_part(br, 1);
-      pv_part(br, 2);
-    }
-    lds_barrier();
-    // ---------------- phase 2
-    if (qk_role) {
+      lds_barrier();
+      // ---------------- phase 2: references, probabilities, sums, staging of step it
       if (it < nsteps) {
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
@@ -816,14 +757,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
           mref[ht] = mnew;
           float sum = 0.0f;
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
+          for (int kt = 0; kt < KT; ++kt) {
             _Float16 pv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[kt][ht][i] - muse);
               sum += (float)pv[i];
             }
-            *reinterpret_cast<u32x2*>(&sm.p[bw][h * kPStride + 32 * c4 + 16 * kt + 4 * q4]) =
+            *reinterpret_cast<u32x2*>(&sm.p[bw][h * kPStride + 16 * KT * c4 + 16 * kt + 4 * q4]) =
                 u32x2{h2_bits(half2v{pv[0], pv[1]}), h2_bits(half2v{pv[2], pv[3]})};
           }
           sum = rows_sum(sum);
@@ -833,7 +774,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
           }
         }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
           for (int c = 0; c < 4; ++c)
             *reinterpret_cast<u32x4*>(&sm.cs[bw][cs_off(slot[kt]) + 64 * q4 + 16 * c]) = cur[kt].c[c];
@@ -844,27 +785,105 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
           }
         }
       }
-    } else if (it > 0) {
-      pv_part(br, 3);
+      lds_barrier();
+    };
+    for (int it = 0; it <= nsteps; it += 2) {
+      iter(it, bufA, vA, bufB, vB);
+      if (it + 1 <= nsteps) iter(it + 1, bufB, vB, bufA, vA);
     }
-    lds_barrier();
-  };
-  for (int it = 0; it <= nsteps; it += 2) {
-    iter(it, bufA, vA, bufB, vB);
-    if (it + 1 <= nsteps) iter(it + 1, bufB, vB, bufA, vA);
-  }
-
-  // ---- epilogue: running sums and references through LDS, each PV wave writes its channels
-  if (qk_role && c4 == 0 && q4 == 0) {
+    // epilogue: running sums to the PV waves through LDS
+    if (c4 == 0 && q4 == 0) {
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      sm.lfin[16 * ht + n16] = lrun[ht];
-      sm.mfin[16 * ht + n16] = mref[ht];
+      for (int ht = 0; ht < NHT; ++ht) sm.lfin[16 * ht + n16] = lrun[ht];
     }
-  }
-  __syncthreads();
-  const int64_t rowh = (int64_t)r * a.Hq + h0;
-  if (!qk_role) {
+    __syncthreads();
+    if (c4 == 0 && q4 == 0) {
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        const int h = 16 * ht + n16;
+        if (a.splits == 1) {
+          if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
+        } else {
+          a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
+          a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+        }
+      }
+    }
+  } else {
+    // outputs of channels 128*c4 + 8*n16 + t, heads 16*ht + 4*q4 + i
+    floatx4 O[NHT][8];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // PV over keys [32kk, 32kk+32) of the step staged in buffer b
+    auto pv_part = [&](int b, int kk) {
+      const int key0 = 32 * kk + 8 * q4;
+      uint32_t W[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        W[k] = *reinterpret_cast<const uint32_t*>(&sm.cs[b][cs_off(key0 + k) + 64 * c4 + 4 * n16]);
+      const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[b][(8 * c4 + (n16 >> 1)) * kScStride + key0]);
+      uint32_t E[4], D[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t wa = W[2 * p], wb = W[2 * p + 1];
+        E[p] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
+        D[p] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+      }
+      half8 av[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) av[ht] = *reinterpret_cast<const half8*>(&sm.p[b][(16 * ht + n16) * kPStride + key0]);
+      auto tile = [&](auto sel_c, const uint32_t(&src)[4], int t) {
+        constexpr int SEL = decltype(sel_c)::value;
+        u32x4 bb;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) bb[p] = h2_bits(fp4x2_to_h2<SEL>(src[p]) * bits_h2(spw[p]));
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) O[ht][t] = mfma(av[ht], __builtin_bit_cast(half8, bb), O[ht][t]);
+      };
+      tile(std::integral_constant<int, 0>{}, E, 0);
+      tile(std::integral_constant<int, 0>{}, D, 1);
+      tile(std::integral_constant<int, 1>{}, E, 2);
+      tile(std::integral_constant<int, 1>{}, D, 3);
+      tile(std::integral_constant<int, 2>{}, E, 4);
+      tile(std::integral_constant<int, 2>{}, D, 5);
+      tile(std::integral_constant<int, 3>{}, E, 6);
+      tile(std::integral_constant<int, 3>{}, D, 7);
+    };
+    for (int it = 0; it <= nsteps; ++it) {
+      const int br = (it & 1) ^ 1;
+      // ---------------- phase 1: rescale when a reference moved at step it-1, then all but the
+      // last 32 keys of the step
+      if (it > 0) {
+        float al[NHT][4];
+        bool moved = false;
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            al[ht][i] = sm.alpha[16 * ht + 4 * q4 + i];
+            moved |= al[ht][i] != 1.0f;
+          }
+        if (__ballot(moved)) {
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int t = 0; t < 8; ++t) O[ht][t][i] *= al[ht][i];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2 * KT - 1; ++kk) pv_part(br, kk);
+      }
+      lds_barrier();
+      // ---------------- phase 2: the last 32 keys
+      if (it > 0) pv_part(br, 2 * KT - 1);
+      lds_barrier();
+    }
+    __syncthreads();
+    // epilogue: each PV wave writes its channels of every head
     const int ch = 128 * c4 + 8 * n16;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -896,17 +915,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
           *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + ch) =
               make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
-      }
-    }
-  } else if (c4 == 0 && q4 == 0) {
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      const int h = 16 * ht + n16;
-      if (a.splits == 1) {
-        if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
-      } else {
-        a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
-        a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
       }
     }
   }
@@ -1292,10 +1300,10 @@ Plan plan(int R, int Hq, int q_dtype, int top_k) {
   return p;
 }
 
-template <int NHT>
+template <int NHT, int KT>
 hipError_t go_pp(const Plan& p, int R, const AttnArgs& a, hipStream_t s) {
-  auto kern = k_attn_pp<NHT>;
-  const size_t lds = sizeof(SmemPP<NHT>);
+  auto kern = k_attn_pp<NHT, KT>;
+  const size_t lds = sizeof(SmemPP<NHT, KT>);
   static bool configured = false;
   if (!configured) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1372,11 +1380,11 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
     hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.splits, R, p.head_groups), dim3(kThreads), lds, s, a);
     e = hipGetLastError();
   } else if (q_dtype == CSA2_BF16) {
-    // 16-head workgroups with at least two steps of keys take the pipelined kernel (its
-    // first and last iterations run one role only, which a single step cannot amortize)
-    if (p.nht == 2) e = go<2, false, CSA2_BF16>(p, R, a, s);
-    else if (p.keys_per_split >= 2 * kStep) e = go_pp<1>(p, R, a, s);
-    else e = go<1, false, CSA2_BF16>(p, R, a, s);
+    // splits of at least two steps take the pipelined kernel (its first and last
+    // iterations run one role only, which a single step cannot amortize)
+    const bool pipelined = p.keys_per_split >= 2 * kStep;
+    if (p.nht == 2) e = pipelined ? go_pp<2, 2>(p, R, a, s) : go<2, false, CSA2_BF16>(p, R, a, s);
+    else e = pipelined ? go_pp<1, 2>(p, R, a, s) : go<1, false, CSA2_BF16>(p, R, a, s);
   } else {
     e = go<1, true, CSA2_F32>(p, R, a, s);
   }

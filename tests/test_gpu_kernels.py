@@ -254,6 +254,9 @@ def _cache(seed, n, outliers=False):
 @pytest.mark.parametrize("Hq,qkind,R,K,n", [
     (16, "f32", 1, 256, 4096),     # the tiny decode shape
     (64, "bf16", 3, 2048, 9000),   # several splits
+    (64, "bf16", 16, 2048, 9000),  # pipelined 16-head workgroups, four steps per split
+    (64, "bf16", 32, 2048, 9000),  # pipelined 32-head workgroups, four steps per split
+    (64, "bf16", 24, 1500, 6000),  # pipelined 32-head workgroups, ragged last split
     (64, "bf16", 40, 300, 5000),   # many rows, one split each, ragged step
     (32, "bf16", 5, 1000, 7000),
     (48, "bf16", 2, 700, 3000),
