@@ -261,6 +261,14 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
     // Reindex: each lane reads its own slot's pool entry once; the lanes loading a key's pieces take it
     // from that lane
     if (REINDEX) st.pos = (int32_t)position(base + lane);
+    if (!REINDEX && base + T::kKeys <= vis) {
+      // Full, a wholly visible tile: piece i of this lane is 1 KiB after piece i-1
+      const u32x4* p = reinterpret_cast<const u32x4*>(kbase + (rs + base + lane / T::kPieces) * T::kBytes) +
+                       lane % T::kPieces;
+#pragma unroll
+      for (int i = 0; i < T::kPerLane; ++i) st.v[i] = __builtin_nontemporal_load(p + 64 * i);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < T::kPerLane; ++i) {
       const int id = lane + 64 * i;
@@ -328,23 +336,27 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
         }
       }
     }
-    float sc = acc[0] > 0.0f ? acc[0] : 0.0f;
+    // ReLU as an integer max on the bits: a positive float keeps its bits,
+    // anything else (negative, -0) becomes +0, exactly x > 0 ? x : 0
+    auto relu = [](float x) { return __int_as_float(max(__float_as_int(x), 0)); };
+    float sc = relu(acc[0]);
 #pragma unroll
     for (int h = 1; h < NACC; ++h)
-      if (HC > 0 || h < H) sc = __fadd_rn(sc, acc[h] > 0.0f ? acc[h] : 0.0f);
+      if (HC > 0 || h < H) sc = __fadd_rn(sc, relu(acc[h]));
     const int64_t i = base + lane;
     const bool ok = REINDEX ? own >= 0 : i < vis;
     if (i < n) srow[i] = ok ? sc : -1.0f;
     if (ok) hist_add(h1, __float_as_uint(sc) >> kS1);
     if (POOL) {
-      // a block of 8 consecutive positions = 8 consecutive lanes
-      float m = ok ? sc : -1.0f;
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
-      m = fmaxf(m, __shfl_xor(m, 2, 64));
-      m = fmaxf(m, __shfl_xor(m, 4, 64));
+      // a block of 8 consecutive positions = 8 consecutive lanes; scores are
+      // >= +0 or -1.0 (invalid), so their bits order like int32
+      int m = __float_as_int(ok ? sc : -1.0f);
+      m = max(m, __shfl_xor(m, 1, 64));
+      m = max(m, __shfl_xor(m, 2, 64));
+      m = max(m, __shfl_xor(m, 4, 64));
       if (ok && (lane & 7) == 0) {
-        a.bmax[(int64_t)r * a.nb_pad + i / kBlock] = m;
-        hist_add(hb, __float_as_uint(m) >> kS1);
+        a.bmax[(int64_t)r * a.nb_pad + i / kBlock] = __int_as_float(m);
+        hist_add(hb, (uint32_t)m >> kS1);
       }
     }
   };
