@@ -10,20 +10,22 @@
 // head sum) so that selection is reproducible bit for bit.
 //
 // Pipeline of one csa2_index_topk call (one stream, no host sync):
-//   k_prep      indexer queries -> fp32 ([channel quad][head][4] order);
-//               zero the first-digit histograms
+//   k_prep      (Full) indexer queries -> fp32 ([channel quad][head][4]
+//               order); zero the first-digit histograms
 //   k_score     Full: every visible entry; Reindex: the pool entries.  Key
 //               rows are staged through LDS with fully coalesced 16-byte
 //               loads (the next tile prefetched into registers), queries
-//               are broadcast from LDS, each thread runs the H fmaf chains of
-//               one key.  Full also writes the 8-entry block maxima and
+//               reach every lane through scalar loads, each thread runs the H
+//               fmaf chains of one key.  Full also writes the 8-entry block maxima and
 //               builds the first radix histogram (12 bits) of scores and
 //               block maxima in the same pass.  HBM-bound on the key rows.
 //   k_collect   (Full) every wave compacts, in position order, the entries
 //               whose first digit reaches the threshold bin into its own
 //               slice of a candidate list (no block-wide syncs)
 //   k_finalize  one workgroup per row and series selects among the
-//               candidates (Full) or pool slots (Reindex), held in LDS
+//               candidates (Full) or pool slots (Reindex), held in LDS;
+//               Reindex counts the first digit of the pool's scores here
+//               (its scoring reads the queries as given and counts nothing)
 // Exact selection: three radix digits give the K-th largest key, then an
 // ordered compaction writes positions ascending, ties to the lower position,
 // -1 padding; selected blocks expand into the pool.
@@ -213,9 +215,13 @@ __device__ __forceinline__ void flush_packed(uint32_t* __restrict__ g, const uin
   }
 }
 
-// HC: compile-time head count (0 = runtime a.H, at most 32)
-template <int KDT, int HC, bool REINDEX, bool POOL>
-__global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float* __restrict__ qf) {
+// HC: compile-time head count (0 = runtime a.H, at most 32).  Full reads the
+// prepared fp32 queries (qsrc: [row][channel quad][head][4]); Reindex reads the
+// caller's queries as they are (qsrc: [row][head][64] of dtype QDT), so it needs
+// no preparation kernel, and builds no histogram (its selection counts the
+// pool's scores itself).
+template <int KDT, int HC, bool REINDEX, bool POOL, int QDT>
+__global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* __restrict__ qsrc) {
   using T = KeyTile<KDT>;
   constexpr int NACC = HC > 0 ? HC : kMaxHeads;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -234,11 +240,13 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
   const int64_t base0 = (int64_t)blockIdx.x * a.tiles_per_wg * kWGKeys;
   if (base0 >= n) return;
   const int ntiles = (int)std::min<int64_t>(a.tiles_per_wg, ceil_div(n - base0, kWGKeys));
-  for (int b = threadIdx.x; b < kD1 / 2; b += kThreads) {
-    h1[b] = 0u;
-    if (POOL) hb[b] = 0u;
+  if (!REINDEX) {
+    for (int b = threadIdx.x; b < kD1 / 2; b += kThreads) {
+      h1[b] = 0u;
+      if (POOL) hb[b] = 0u;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const int64_t rs = a.row_start[a.shared_start ? 0 : r];
   const uint8_t* kbase = static_cast<const uint8_t*>(a.idx_k);
   float* srow = a.scores + (int64_t)r * a.n_pad;
@@ -258,28 +266,35 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
   // discarded below; the loaded values are not inspected here, so the loads
   // of the next tile stay in flight while the current one is scored.
   auto load_tile = [&](int64_t base, Staged<KDT>& st) {
-    // Reindex: each lane reads its own slot's pool entry once; the lanes loading a key's pieces take it
-    // from that lane
-    if (REINDEX) st.pos = (int32_t)position(base + lane);
-    if (!REINDEX && base + T::kKeys <= vis) {
-      // Full, a wholly visible tile: piece i of this lane is 1 KiB after piece i-1
-      const u32x4* p = reinterpret_cast<const u32x4*>(kbase + (rs + base + lane / T::kPieces) * T::kBytes) +
-                       lane % T::kPieces;
+    if (!REINDEX) {
+      // Full: 32-bit offsets into the row's key segment (at most 2^21 entries of 256 bytes)
+      const uint8_t* kseg = kbase + rs * T::kBytes;
+      if (base + T::kKeys <= vis) {
+        // a wholly visible tile: piece i of this lane is 1 KiB after piece i-1
+        const uint32_t off0 = (uint32_t)(base + lane / T::kPieces) * T::kBytes + (lane % T::kPieces) * 16u;
 #pragma unroll
-      for (int i = 0; i < T::kPerLane; ++i) st.v[i] = __builtin_nontemporal_load(p + 64 * i);
+        for (int i = 0; i < T::kPerLane; ++i)
+          st.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kseg + off0 + 1024u * i));
+      } else {
+#pragma unroll
+        for (int i = 0; i < T::kPerLane; ++i) {
+          const int id = lane + 64 * i;
+          const uint32_t row = (uint32_t)std::min<int64_t>(base + id / T::kPieces, (int64_t)vis - 1);
+          st.v[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(kseg + row * T::kBytes + (id % T::kPieces) * 16u));
+        }
+      }
       return;
     }
+    // Reindex: each lane reads its own slot's pool entry once; the lanes loading a key's pieces take it
+    // from that lane
+    st.pos = (int32_t)position(base + lane);
 #pragma unroll
     for (int i = 0; i < T::kPerLane; ++i) {
       const int id = lane + 64 * i;
       const int k = id / T::kPieces, piece = id % T::kPieces;
-      int64_t row;
-      if (REINDEX) {
-        const int32_t pos = __shfl(st.pos, k, 64);
-        row = pos >= 0 ? rs + pos : 0;
-      } else {
-        row = rs + std::min<int64_t>(base + k, (int64_t)vis - 1);
-      }
+      const int32_t pos = __shfl(st.pos, k, 64);
+      const int64_t row = pos >= 0 ? rs + pos : 0;
       st.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + row * T::kBytes) + piece);
     }
   };
@@ -319,7 +334,30 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
         for (int e = 0; e < 4; ++e) kv[e] = __uint_as_float(w[e]);
       }
       // the H x 4 query values of this channel quad are wave-uniform: scalar loads
-      const float* qrow = qf + (int64_t)r * H * kIdxDim + c4 * H * 4;
+      if constexpr (REINDEX) {
+#pragma unroll
+        for (int h = 0; h < NACC; ++h) {
+          if (HC > 0 || h < H) {
+            float qv[4];
+            if constexpr (QDT == CSA2_BF16) {
+              const uint32_t* qp = static_cast<const uint32_t*>(qsrc) + ((int64_t)r * H + h) * (kIdxDim / 2) + 2 * c4;
+              const uint32_t w0 = qp[0], w1 = qp[1];
+              qv[0] = __uint_as_float(w0 << 16);
+              qv[1] = __uint_as_float(w0 & 0xFFFF0000u);
+              qv[2] = __uint_as_float(w1 << 16);
+              qv[3] = __uint_as_float(w1 & 0xFFFF0000u);
+            } else {
+              const float* qp = static_cast<const float*>(qsrc) + ((int64_t)r * H + h) * kIdxDim + 4 * c4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) qv[e] = qp[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[h] = __builtin_fmaf(qv[e], kv[e], acc[h]);
+          }
+        }
+        continue;
+      }
+      const float* qrow = static_cast<const float*>(qsrc) + (int64_t)r * H * kIdxDim + c4 * H * 4;
       if constexpr (HC > 0) {
 #pragma unroll
         for (int h = 0; h < HC; ++h) {
@@ -346,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
     const int64_t i = base + lane;
     const bool ok = REINDEX ? own >= 0 : i < vis;
     if (i < n) srow[i] = ok ? sc : -1.0f;
-    if (ok) hist_add(h1, __float_as_uint(sc) >> kS1);
+    if (!REINDEX && ok) hist_add(h1, __float_as_uint(sc) >> kS1);
     if (POOL) {
       // a block of 8 consecutive positions = 8 consecutive lanes; scores are
       // >= +0 or -1.0 (invalid), so their bits order like int32
@@ -365,6 +403,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const float*
     load_tile(tile_base(wv), st);
     for (int j = wv; j < nwt; j += kWavesPerWG) score_tile(j, st);
   }
+  if (REINDEX) return;
   __syncthreads();
   flush_packed(a.hist_s + (int64_t)r * kD1, h1);
   if (POOL) flush_packed(a.hist_b + (int64_t)r * kD1, hb);
@@ -447,8 +486,16 @@ __device__ __forceinline__ uint32_t fin_gather(const Series& S, int r, bool full
     kr[j] = (j < nch && c < w1 && c < nvalid) ? kr[j] : 0x80000000u;
   }
   if (!full) {
+    // Reindex: the first-digit histogram of the row's valid scores, counted here
+    // in the candidate area (written only after find_bin has read it)
+    for (int b = threadIdx.x; b < kD1; b += NT) lkey[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j)
+      if (!(kr[j] >> 31)) atomicAdd(&lkey[kr[j] >> kS1], 1u);
+    __syncthreads();
     uint32_t total0;
-    b0 = find_bin<NT, kD1>(S.hist + (int64_t)r * kD1, (uint32_t)S.K, &above0, &total0, red);
+    b0 = find_bin<NT, kD1>(lkey, (uint32_t)S.K, &above0, &total0, red);
   }
   const uint32_t lo_key = b0 < 0 ? 0u : ((uint32_t)b0 << kS1);  // smaller keys cannot be selected
   uint32_t cnt = 0;
@@ -555,8 +602,16 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
       keys = dk;
       posr = dp;
     } else {
+      // Reindex beyond the LDS capacity: the first-digit histogram from the scores in place
+      for (int b = threadIdx.x; b < kD1; b += NT) lkey[b] = 0u;
+      __syncthreads();
+      for (int c = threadIdx.x; c < n; c += NT) {
+        const uint32_t key = sk[c];
+        if (!(key >> 31)) atomicAdd(&lkey[key >> kS1], 1u);
+      }
+      __syncthreads();
       uint32_t total0;
-      b0 = find_bin<NT, kD1>(S.hist + (int64_t)r * kD1, (uint32_t)S.K, &above0, &total0, red);
+      b0 = find_bin<NT, kD1>(lkey, (uint32_t)S.K, &above0, &total0, red);
       keys = sk;
       posr = sp;
     }
@@ -1172,25 +1227,25 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
   return L;
 }
 
-template <int KDT, int HC, bool REINDEX, bool POOL>
-void launch_score(const ScoreArgs& sa, const float* qf, dim3 grid, hipStream_t s) {
+template <int KDT, int HC, bool REINDEX, bool POOL, int QDT>
+void launch_score(const ScoreArgs& sa, const void* qsrc, dim3 grid, hipStream_t s) {
   using T = KeyTile<KDT>;
-  const size_t lds = (size_t)kWavesPerWG * T::kWaveBytes + (size_t)kD1 / 2 * 4 * (POOL ? 2 : 1);
-  auto kern = k_score<KDT, HC, REINDEX, POOL>;
+  const size_t lds = (size_t)kWavesPerWG * T::kWaveBytes + (REINDEX ? 0 : (size_t)kD1 / 2 * 4 * (POOL ? 2 : 1));
+  auto kern = k_score<KDT, HC, REINDEX, POOL, QDT>;
   static bool configured = false;
   if (!configured) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
     configured = true;
   }
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, sa, qf);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, sa, qsrc);
 }
 
-template <int KDT, bool REINDEX, bool POOL>
-void dispatch_heads(int H, const ScoreArgs& sa, const float* qf, dim3 grid, hipStream_t s) {
-  if (H == 8) launch_score<KDT, 8, REINDEX, POOL>(sa, qf, grid, s);
-  else if (H == 4) launch_score<KDT, 4, REINDEX, POOL>(sa, qf, grid, s);
-  else launch_score<KDT, 0, REINDEX, POOL>(sa, qf, grid, s);
+template <int KDT, bool REINDEX, bool POOL, int QDT>
+void dispatch_heads(int H, const ScoreArgs& sa, const void* qsrc, dim3 grid, hipStream_t s) {
+  if (H == 8) launch_score<KDT, 8, REINDEX, POOL, QDT>(sa, qsrc, grid, s);
+  else if (H == 4) launch_score<KDT, 4, REINDEX, POOL, QDT>(sa, qsrc, grid, s);
+  else launch_score<KDT, 0, REINDEX, POOL, QDT>(sa, qsrc, grid, s);
 }
 
 }  // namespace
@@ -1212,7 +1267,7 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
                int64_t score_stride, bool prep_done, bool record, const void* idx_q, hipStream_t s) {
   const bool full = mode == CSA2_FULL;
   const bool pool_on = full && pool_size > 0;
-  if (!prep_done) {
+  if (!prep_done && full) {  // (Reindex reads the queries as given and counts in its selection)
     const int64_t nq = (int64_t)R * H * kIdxDim;
     const int64_t nhist = (int64_t)R * kD1 * 2;
     hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(std::max(nq, nhist), 256))),
@@ -1248,14 +1303,17 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     const dim3 grid((unsigned)ceil_div(tiles, (int64_t)sa.tiles_per_wg), (unsigned)R);
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
     if (record && ev.start) (void)hipEventRecord(ev.start, s);
+    const bool qbf = q_dtype == CSA2_BF16;
     if (k_dtype == CSA2_BF16) {
-      if (!full) dispatch_heads<CSA2_BF16, true, false>(H, sa, L.qf, grid, s);
-      else if (pool_on) dispatch_heads<CSA2_BF16, false, true>(H, sa, L.qf, grid, s);
-      else dispatch_heads<CSA2_BF16, false, false>(H, sa, L.qf, grid, s);
+      if (!full && qbf) dispatch_heads<CSA2_BF16, true, false, CSA2_BF16>(H, sa, idx_q, grid, s);
+      else if (!full) dispatch_heads<CSA2_BF16, true, false, CSA2_F32>(H, sa, idx_q, grid, s);
+      else if (pool_on) dispatch_heads<CSA2_BF16, false, true, CSA2_F32>(H, sa, L.qf, grid, s);
+      else dispatch_heads<CSA2_BF16, false, false, CSA2_F32>(H, sa, L.qf, grid, s);
     } else {
-      if (!full) dispatch_heads<CSA2_F32, true, false>(H, sa, L.qf, grid, s);
-      else if (pool_on) dispatch_heads<CSA2_F32, false, true>(H, sa, L.qf, grid, s);
-      else dispatch_heads<CSA2_F32, false, false>(H, sa, L.qf, grid, s);
+      if (!full && qbf) dispatch_heads<CSA2_F32, true, false, CSA2_BF16>(H, sa, idx_q, grid, s);
+      else if (!full) dispatch_heads<CSA2_F32, true, false, CSA2_F32>(H, sa, idx_q, grid, s);
+      else if (pool_on) dispatch_heads<CSA2_F32, false, true, CSA2_F32>(H, sa, L.qf, grid, s);
+      else dispatch_heads<CSA2_F32, false, false, CSA2_F32>(H, sa, L.qf, grid, s);
     }
     if (record && ev.stop) (void)hipEventRecord(ev.stop, s);
   }
