@@ -153,17 +153,18 @@ def algorithmic_bytes(w, lens):
 
 def attention_kernel_name(w):
     """Name of the attention kernel the library's launch plan picks for this workload (a label
-    for the report: 64-head workgroups when rows x 64-head groups fill 256 workgroups, the
-    pipelined 16-head kernel for small batches with splits of two or more 128-key steps)."""
+    for the report): 64-head workgroups when rows x 64-head groups fill 256 workgroups; else 16
+    heads per workgroup for at most 64 row x 16-head tiles, 32 otherwise, and the pipelined
+    kernel when a key split holds two or more 128-key steps."""
     tiles = w.Hq // 16
-    if w.q_dtype == "bf16" and tiles % 4 == 0 and w.rows * (tiles // 4) >= 256:
+    if w.q_dtype != "bf16":
+        return "k_sparse_attn"
+    if tiles % 4 == 0 and w.rows * (tiles // 4) >= 256:
         return "k_sparse_attn_wide"
-    if w.q_dtype == "bf16" and w.rows * tiles <= 64:
-        splits = min(max(1, -(-w.K // 128)), max(1, -(-256 // (w.rows * tiles))))
-        kps = -(-(-(-w.K // splits)) // 128) * 128
-        if kps >= 256:
-            return "k_attn_pp"
-    return "k_sparse_attn"
+    nht = 2 if tiles % 2 == 0 and w.rows * tiles > 64 else 1
+    splits = min(max(1, -(-w.K // 128)), max(1, -(-256 // (w.rows * (tiles // nht)))))
+    kps = -(-(-(-w.K // splits)) // 128) * 128
+    return "k_attn_pp<%d, 2>" % nht if kps >= 256 else "k_sparse_attn"
 
 
 def attention_flops(w):
