@@ -142,6 +142,69 @@ __device__ __forceinline__ int find_bin(const uint32_t* h, uint32_t K, uint32_t*
   return (bin == 0xFFFFFFFFu) ? -1 : (int)bin;
 }
 
+// find_bin for a histogram in LDS that the block has finished (a barrier
+// since its last update): wave 0 alone scans it and publishes the bin, so the
+// block meets at two barriers instead of four.  Lane l owns the NB/64
+// consecutive bins below NB - l*NB/64 (lane 0 the highest), summed per
+// 16-byte group; the lane holding the K-th largest element descends through
+// its group sums, then through the four bins of that group.
+template <int NB>
+__device__ __forceinline__ int find_bin_wave(const uint32_t* h, uint32_t K, uint32_t* above, uint32_t* total,
+                                             uint32_t* lds) {
+  static_assert(NB % 256 == 0, "whole 16-byte groups per lane");
+  constexpr int PER = NB / 64, NG = PER / 4;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int lo = NB - (lane + 1) * PER;  // this lane: bins [lo, lo + PER)
+    const u32x4* p = reinterpret_cast<const u32x4*>(h + lo);
+    uint32_t gs[NG];
+    uint32_t local = 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const u32x4 v = p[g];
+      gs[g] = (v[0] + v[1]) + (v[2] + v[3]);
+      local += gs[g];
+    }
+    const uint32_t incl = wave_incl_sum(local);
+    const uint32_t before = incl - local;
+    const uint32_t tot = (uint32_t)__shfl((int)incl, 63, 64);
+    if (lane == 0) {
+      lds[16] = 0xFFFFFFFFu;  // (overwritten below by the lane that holds the K-th element)
+      lds[18] = tot;
+    }
+    if (before < K && K <= incl) {
+      uint32_t run = before;
+      int gsel = 0;
+      bool found = false;
+#pragma unroll
+      for (int g = NG - 1; g >= 0; --g) {
+        const bool here = !found && K <= run + gs[g];
+        gsel = here ? g : gsel;
+        run += (!found && !here) ? gs[g] : 0u;
+        found = found || here;
+      }
+      const u32x4 v = p[gsel];
+      int bin = lo + 4 * gsel;
+      found = false;
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const bool here = !found && K <= run + v[e];
+        bin = here ? lo + 4 * gsel + e : bin;
+        run += (!found && !here) ? v[e] : 0u;
+        found = found || here;
+      }
+      lds[16] = (uint32_t)bin;
+      lds[17] = run;
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = lds[16], ab = lds[17], tot = lds[18];
+  __syncthreads();
+  *total = tot;
+  *above = (bin == 0xFFFFFFFFu) ? tot : ab;
+  return (bin == 0xFFFFFFFFu) ? -1 : (int)bin;
+}
+
 __device__ __forceinline__ void flush_hist(uint32_t* __restrict__ g, const uint32_t* __restrict__ l, int n) {
   for (int b = threadIdx.x; b < n; b += blockDim.x) {
     const uint32_t v = l[b];
@@ -495,7 +558,7 @@ __device__ __forceinline__ uint32_t fin_gather(const Series& S, int r, bool full
       if (!(kr[j] >> 31)) atomicAdd(&lkey[kr[j] >> kS1], 1u);
     __syncthreads();
     uint32_t total0;
-    b0 = find_bin<NT, kD1>(lkey, (uint32_t)S.K, &above0, &total0, red);
+    b0 = find_bin_wave<kD1>(lkey, (uint32_t)S.K, &above0, &total0, red);
   }
   const uint32_t lo_key = b0 < 0 ? 0u : ((uint32_t)b0 << kS1);  // smaller keys cannot be selected
   uint32_t cnt = 0;
@@ -611,7 +674,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
       }
       __syncthreads();
       uint32_t total0;
-      b0 = find_bin<NT, kD1>(lkey, (uint32_t)S.K, &above0, &total0, red);
+      b0 = find_bin_wave<kD1>(lkey, (uint32_t)S.K, &above0, &total0, red);
       keys = sk;
       posr = sp;
     }
@@ -638,9 +701,8 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
       }
       __syncthreads();
       uint32_t above, total;
-      // (the last digit's scan covers NT bins; the ones past kD3 stay empty)
-      const int b = lev == 1 ? find_bin<NT, kD2>(hist2, K, &above, &total, red)
-                             : find_bin<NT, kD3 < NT ? NT : kD3>(hist, K, &above, &total, red);
+      const int b = lev == 1 ? find_bin_wave<kD2>(hist2, K, &above, &total, red)
+                             : find_bin_wave<kD3>(hist, K, &above, &total, red);
       prefix = (prefix << (shift_hi - sh)) | (uint32_t)b;
       shift_hi = sh;
       K -= above;
