@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void k_prep(const void* __restrict__ idx_q, in
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nhist; i += stride) hist[i] = 0u;
 }
 
-// zero the approximate path's histograms and accumulators (three arrays and one word)
+// zero the approximate path's histograms and accumulators (three arrays and, if given, one word)
 __global__ __launch_bounds__(256) void k_zero(uint32_t* __restrict__ x, int64_t nx, uint32_t* __restrict__ y,
                                               int64_t ny, uint32_t* __restrict__ z, int64_t nz,
                                               uint32_t* __restrict__ one) {
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void k_zero(uint32_t* __restrict__ x, int64_t 
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nx; i += stride) x[i] = 0u;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ny; i += stride) y[i] = 0u;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nz; i += stride) z[i] = 0u;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *one = 0u;
+  if (one && blockIdx.x == 0 && threadIdx.x == 0) *one = 0u;
 }
 
 struct ScoreArgs {
@@ -875,7 +875,6 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
 constexpr int kPfRows = 8;       // query rows per workgroup of the approximate passes
 constexpr int kPfRange = 32768;  // keys per workgroup of the candidate pass
 constexpr int kPfCap = 16384;    // candidates kept per row (more: exact fallback for that row)
-constexpr int kPfDepth = 2;      // 32-key steps in flight per wave
 constexpr int kPfSample = 16;    // the provisional bound samples every 16th 32-key step
 // error constant c of the bound above for H heads, with a factor 8 of safety
 // on top (so the margin stays valid even if an accumulator kept fewer bits)
@@ -907,7 +906,6 @@ struct PfArgs {
   int32_t* cand;              // [R][kPfCap] candidate positions, ascending
   int32_t* ccnt;              // [R] candidates (0 on overflow)
   uint32_t* over;             // [R] 1 = overflow: exact fallback
-  uint32_t* sink;             // one scratch word: target of the stores of lanes that own no bitmap word
 };
 
 // max(x, +0) as one integer max: negative floats (sign bit set, -0 included) compare below 0
@@ -954,14 +952,19 @@ __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
 // MODE 0: first-digit histogram of A per row.  MODE 1: candidate bitmap.
 // A workgroup (4 waves) takes kPfRows rows; MODE 0 all keys, MODE 1 one
 // range of kPfRange keys.  Each wave walks 32-key steps (two 16-key MFMA
-// tiles, keys [32p, 32p+32) for p = w, w+4, ...), kPfDepth steps in flight:
+// tiles, keys [32p, 32p+32) for p = w, w+4, ...), two steps in flight:
 // B operand = the keys, loaded straight from global; A operand = the rows'
-// queries held in registers (M = 16 (row, head) pairs per MFMA tile).  In
-// MODE 1 a step yields one whole bitmap word per row, stored directly.
+// queries held in registers.  The rows go in groups of four; M tile t of a
+// group holds heads [4t, 4t+4) of its four rows (M row 4*row + head - 4t),
+// so the accumulator lanes of row group g = lane/16 hold four heads of row g
+// for key lane%16 in every tile, and each lane sums its row's H ReLU'd heads
+// by itself: every (row, key) score lives in exactly one lane.  In MODE 1 a
+// step yields one whole bitmap word per row, stored directly.
 template <int MODE, int H>
 __global__ __launch_bounds__(256, H == 16 ? 2 : 3) void k_pf_pass(PfArgs a) {
-  constexpr int MT = kPfRows * H / 16;  // M tiles
-  constexpr int RPM = 16 / H;           // rows per M tile
+  static_assert(H % 4 == 0 && kPfRows % 4 == 0, "heads and rows in fours");
+  constexpr int TG = H / 4;             // M tiles per group of four rows
+  constexpr int NG = kPfRows / 4;       // row groups
   extern __shared__ __align__(16) uint32_t pl[];  // MODE 0: kPfRows x kD1/2 packed counters
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n16 = lane & 15, g = lane >> 4;
@@ -986,39 +989,41 @@ __global__ __launch_bounds__(256, H == 16 ? 2 : 3) void k_pf_pass(PfArgs a) {
     for (int i = threadIdx.x; i < kPfRows * kD1 / 2; i += 256) pl[i] = 0u;
   }
 
-  // queries of this lane's M rows: (row, head) = (mt*RPM + n16/H, n16%H), channels 32ks + 8g
-  bf16x8 qa[MT][2];
+  // A operand of tile t of row group rg: M row n16 = (row 4rg + n16/4, head 4t + n16%4), channels 32ks + 8g
+  bf16x8 qa[NG][TG][2];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = r0 + mt * RPM + n16 / H;
+  for (int rg = 0; rg < NG; ++rg) {
+    const int row = r0 + 4 * rg + n16 / 4;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (row < a.R)
-        v = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)row * H + n16 % H) * 64 + 32 * ks + 8 * g);
-      qa[mt][ks] = __builtin_bit_cast(bf16x8, v);
+    for (int t = 0; t < TG; ++t) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (row < a.R)
+          v = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)row * H + 4 * t + n16 % 4) * 64 + 32 * ks + 8 * g);
+        qa[rg][t][ks] = __builtin_bit_cast(bf16x8, v);
+      }
     }
   }
-  // this lane's output rows (epilogue role): M row 4g + i -> row mt*RPM + (4g)/H
-  const bool owner = H == 4 ? true : (H == 8 ? (g & 1) == 0 : g == 0);
-  int vis[MT], rowo[MT];
-  uint32_t* wrow[MT];  // MODE 1: this lane's bitmap row, or a scratch word for lanes that do not own one
-  float lo[MT], cq[MT], hi[MT];
-  uint32_t nh[MT];
+  // this lane's output row in row group rg: 4rg + g; key lane n16 of each 16-key tile
+  int vis[NG], rowo[NG];
+  uint32_t* wrow[NG];  // MODE 1: this row's bitmap (stored by lane n16 == 0), null past the last row
+  float lo[NG], cq[NG], hi[NG];
+  uint32_t nh[NG];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = r0 + mt * RPM + (4 * g) / H;
-    rowo[mt] = row;
-    wrow[mt] = (owner && n16 == 0 && row < a.R) ? a.bits + (int64_t)row * a.nwords : a.sink;
-    vis[mt] = row < a.R ? min(clampv(a.row_visible[row], a.max_visible), klim) : 0;
-    lo[mt] = 0.0f;
-    cq[mt] = 0.0f;
-    hi[mt] = INFINITY;
-    nh[mt] = 0u;
+  for (int rg = 0; rg < NG; ++rg) {
+    const int row = r0 + 4 * rg + g;
+    rowo[rg] = row;
+    wrow[rg] = row < a.R ? a.bits + (int64_t)row * a.nwords : nullptr;
+    vis[rg] = row < a.R ? min(clampv(a.row_visible[row], a.max_visible), klim) : 0;
+    lo[rg] = 0.0f;
+    cq[rg] = 0.0f;
+    hi[rg] = INFINITY;
+    nh[rg] = 0u;
     if (MODE == 1 && row < a.R) {
-      lo[mt] = a.plo[row];
-      hi[mt] = a.thi[row];
-      cq[mt] = a.qn[row] * pf_err(H);
+      lo[rg] = a.plo[row];
+      hi[rg] = a.thi[row];
+      cq[rg] = a.qn[row] * pf_err(H);
     }
   }
   if (MODE == 0) __syncthreads();
@@ -1040,72 +1045,86 @@ __global__ __launch_bounds__(256, H == 16 ? 2 : 3) void k_pf_pass(PfArgs a) {
       st.kn[tt] = MODE == 1 ? a.knorm[j] : 0.0f;
     }
   };
-  // approximate score of (this lane's row of M tile mt, key j): ReLU per head, summed over the row's heads
-  auto score = [&](const bf16x8& q0, const bf16x8& q1, const u32x4* b) {
-    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q0, __builtin_bit_cast(bf16x8, b[0]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1, __builtin_bit_cast(bf16x8, b[1]), acc, 0, 0, 0);
-    float sc = (relu0(acc[0]) + relu0(acc[1])) + (relu0(acc[2]) + relu0(acc[3]));
-    if (H >= 8) {
-      auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
-      sc = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-    }
-    if (H >= 16) {
-      auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
-      sc = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  // the products of one step: every (row group, key tile, head tile) accumulator
+  // first, so the epilogue reads results issued well before it
+  auto products = [&](const Step& st, floatx4 (&acc)[NG][2][TG]) {
+#pragma unroll
+    for (int rg = 0; rg < NG; ++rg)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int t = 0; t < TG; ++t) {
+          floatx4 c = floatx4{0.f, 0.f, 0.f, 0.f};
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rg][t][0], __builtin_bit_cast(bf16x8, st.b[tt][0]), c, 0, 0, 0);
+          acc[rg][tt][t] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rg][t][1], __builtin_bit_cast(bf16x8, st.b[tt][1]), c, 0, 0, 0);
+        }
+  };
+  // approximate score of (row 4rg + g, key lane of a tile): ReLU per head, summed over the row's heads
+  auto score = [&](const floatx4 (&acc)[TG]) {
+    float sc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float part = (relu0(acc[t][0]) + relu0(acc[t][1])) + (relu0(acc[t][2]) + relu0(acc[t][3]));
+      sc = t == 0 ? part : sc + part;
     }
     return sc;
   };
 
-  Step ring[kPfDepth];
+  // wave step i (keys of step p = w + 4i) sits in slot i % 3: while step i is
+  // scored, steps i+1 and i+2 are in flight (each slot is refilled with the
+  // step two ahead before it is used, no register copies)
+  Step sA, sB, sC;
+  load_step(min(w, nsteps - 1), sA);
+  load_step(min(w + 4, nsteps - 1), sB);
+  auto body = [&](int p, Step& cur, Step& ahead) {
+    load_step(min(p + 8, nsteps - 1), ahead);  // clamped: always in bounds
+    const int j0 = kbeg + 32 * p * sample;
+    floatx4 acc[NG][2][TG];
+    products(cur, acc);
 #pragma unroll
-  for (int d = 0; d < kPfDepth; ++d) load_step(min(w + 4 * d, nsteps - 1), ring[d]);
-  for (int p0 = w; p0 < nsteps; p0 += 4 * kPfDepth) {
+    for (int rg = 0; rg < NG; ++rg) {
+      if (MODE == 0) {
 #pragma unroll
-    for (int d = 0; d < kPfDepth; ++d) {
-      const int p = p0 + 4 * d;
-      if (p >= nsteps) break;
-      const Step cur = ring[d];
-      load_step(min(p + 4 * kPfDepth, nsteps - 1), ring[d]);  // clamped: always in bounds
-      const int j0 = kbeg + 32 * p * sample;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (MODE == 0) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const float sc = score(qa[mt][0], qa[mt][1], cur.b[tt]);
-            if (owner && j0 + 16 * tt + n16 < vis[mt]) hist_add(pl + (rowo[mt] - r0) * (kD1 / 2), __float_as_uint(sc) >> kS1);
-          }
-        } else {
-          unsigned long long m[2];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const float sc = score(qa[mt][0], qa[mt][1], cur.b[tt]);
-            const bool ok = j0 + 16 * tt + n16 < vis[mt];
-            m[tt] = __ballot(ok && __builtin_fmaf(cq[mt], cur.kn[tt], sc) >= lo[mt]);
-            nh[mt] += (ok && sc >= hi[mt]) ? 1u : 0u;
-          }
-          // the bitmap words of the rows of lane groups 0 and 2 (wave-uniform), then this lane's
-          const uint32_t w0 = (uint32_t)(m[0] & 0xFFFFull) | ((uint32_t)(m[1] & 0xFFFFull) << 16);
-          const uint32_t w1 = (uint32_t)((m[0] >> 16) & 0xFFFFull) | ((uint32_t)((m[1] >> 16) & 0xFFFFull) << 16);
-          const uint32_t w2 = (uint32_t)((m[0] >> 32) & 0xFFFFull) | ((uint32_t)((m[1] >> 32) & 0xFFFFull) << 16);
-          const uint32_t w3 = (uint32_t)(m[0] >> 48) | ((uint32_t)(m[1] >> 48) << 16);
-          const uint32_t word = g == 0 ? w0 : (g == 1 ? w1 : (g == 2 ? w2 : w3));
-          wrow[mt][wrow[mt] == a.sink ? 0 : j0 / 32] = word;  // every lane stores: no branch
+        for (int tt = 0; tt < 2; ++tt) {
+          const float sc = score(acc[rg][tt]);
+          if (j0 + 16 * tt + n16 < vis[rg]) hist_add(pl + (rowo[rg] - r0) * (kD1 / 2), __float_as_uint(sc) >> kS1);
         }
+      } else {
+        unsigned long long m[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const float sc = score(acc[rg][tt]);
+          const bool ok = j0 + 16 * tt + n16 < vis[rg];
+          m[tt] = __ballot(ok && __builtin_fmaf(cq[rg], cur.kn[tt], sc) >= lo[rg]);
+          nh[rg] += (ok && sc >= hi[rg]) ? 1u : 0u;
+        }
+        // bitmap word of row g: its 16 keys of each tile (lanes 16g .. 16g+15)
+        const uint32_t word = ((uint32_t)(m[0] >> (16 * g)) & 0xFFFFu) | ((uint32_t)(m[1] >> (16 * g)) << 16);
+        if (n16 == 0 && wrow[rg]) wrow[rg][j0 / 32] = word;
       }
     }
+  };
+  // whole rounds of three steps (no conditional step in the loop body, so the
+  // waits for the loads in flight stay exact), then the last steps
+  int p0 = w;
+  for (; p0 + 8 < nsteps; p0 += 12) {
+    body(p0, sA, sC);
+    body(p0 + 4, sB, sA);
+    body(p0 + 8, sC, sB);
   }
+  if (p0 < nsteps) body(p0, sA, sC);
+  if (p0 + 4 < nsteps) body(p0 + 4, sB, sA);
   if (MODE == 1) {
-    // per-lane counts of the entries reaching thi: sum over the 16 lanes of each owner group
+    // counts of the entries reaching thi: sum over the 16 lanes of each row
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      uint32_t c = nh[mt];
+    for (int rg = 0; rg < NG; ++rg) {
+      uint32_t c = nh[rg];
       c += __shfl_xor(c, 1, 64);
       c += __shfl_xor(c, 2, 64);
       c += __shfl_xor(c, 4, 64);
       c += __shfl_xor(c, 8, 64);
-      if (owner && n16 == 0 && rowo[mt] < a.R && c) atomicAdd(a.nhi + rowo[mt], c);
+      if (n16 == 0 && rowo[rg] < a.R && c) atomicAdd(a.nhi + rowo[rg], c);
     }
   }
   if (MODE == 0) {
@@ -1234,7 +1253,6 @@ struct Layout {
   int32_t* cand;
   int32_t* ccnt;
   uint32_t* over;
-  uint32_t* sink;
   float* cscore;   // [R][kPfCap] exact scores of the candidates
   size_t bytes;
 };
@@ -1282,7 +1300,6 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
     L.cand = c.take<int32_t>((size_t)R * kPfCap);
     L.ccnt = c.take<int32_t>((size_t)R);
     L.over = c.take<uint32_t>((size_t)R);
-    L.sink = c.take<uint32_t>(64);
     L.cscore = c.take<float>((size_t)R * kPfCap);
   }
   L.bytes = c.off;
@@ -1480,7 +1497,6 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   p.cand = L.cand;
   p.ccnt = L.ccnt;
   p.over = L.over;
-  p.sink = L.sink;
   {
     // one pass zeroes every histogram and accumulator: the exact path's (fallback), the approximate
     // histograms, the query-norm sums and the key-norm maximum (they are contiguous in the layout)
@@ -1492,7 +1508,7 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
                        0, s, L.phist, (int64_t)R * kD1, L.phist2, (int64_t)R * kD1, L.nhi, (int64_t)R, L.kmax);
     hipLaunchKernelGGL(k_zero, dim3((unsigned)ceil_div((int64_t)R, 256)), dim3(256), 0, s,
                        reinterpret_cast<uint32_t*>(L.qn), (int64_t)R, L.failed, (int64_t)0, L.failed, (int64_t)0,
-                       L.sink);
+                       nullptr);
   }
   const int64_t nn = std::max<int64_t>((int64_t)max_visible, (int64_t)R * H);
   hipLaunchKernelGGL(k_pf_norms, dim3((unsigned)ceil_div(nn, 256)), dim3(256), 0, s, p, H);
