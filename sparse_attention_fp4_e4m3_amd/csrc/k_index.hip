@@ -872,7 +872,10 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
 // the exact top-K.  A row whose candidates overflow the list falls back to
 // the exact full scan.
 
-constexpr int kPfRows = 8;       // query rows per workgroup of the approximate passes
+// query rows per workgroup of the approximate passes: each key a wave loads feeds
+// every row of its workgroup (16 rows for up to 8 heads; 8 keep 16 heads in registers)
+template <int H>
+__host__ __device__ constexpr int pf_rows() { return H <= 8 ? 16 : 8; }
 constexpr int kPfRange = 32768;  // keys per workgroup of the candidate pass
 constexpr int kPfCap = 16384;    // candidates kept per row (more: exact fallback for that row)
 constexpr int kPfSample = 16;    // the provisional bound samples every 16th 32-key step
@@ -950,7 +953,7 @@ __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
 }
 
 // MODE 0: first-digit histogram of A per row.  MODE 1: candidate bitmap.
-// A workgroup (4 waves) takes kPfRows rows; MODE 0 all keys, MODE 1 one
+// A workgroup (4 waves) takes pf_rows<H>() rows; MODE 0 all keys, MODE 1 one
 // range of kPfRange keys.  Each wave walks 32-key steps (two 16-key MFMA
 // tiles, keys [32p, 32p+32) for p = w, w+4, ...), two steps in flight:
 // B operand = the keys, loaded straight from global; A operand = the rows'
@@ -961,7 +964,8 @@ __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
 // by itself: every (row, key) score lives in exactly one lane.  In MODE 1 a
 // step yields one whole bitmap word per row, stored directly.
 template <int MODE, int H>
-__global__ __launch_bounds__(256, H == 16 ? 2 : 3) void k_pf_pass(PfArgs a) {
+__global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
+  constexpr int kPfRows = pf_rows<H>();
   static_assert(H % 4 == 0 && kPfRows % 4 == 0, "heads and rows in fours");
   constexpr int TG = H / 4;             // M tiles per group of four rows
   constexpr int NG = kPfRows / 4;       // row groups
@@ -1432,8 +1436,8 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
 
 template <int H>
 void launch_pf_pass(int mode, const PfArgs& p, int R, int max_visible, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(R, kPfRows), mode == 0 ? 1u : (unsigned)ceil_div(max_visible, kPfRange));
-  const size_t lds = mode == 0 ? (size_t)kPfRows * kD1 / 2 * 4 : 0;
+  const dim3 grid((unsigned)ceil_div(R, pf_rows<H>()), mode == 0 ? 1u : (unsigned)ceil_div(max_visible, kPfRange));
+  const size_t lds = mode == 0 ? (size_t)pf_rows<H>() * kD1 / 2 * 4 : 0;
   static bool configured[2] = {false, false};
   if (mode == 0) {
     if (!configured[0]) {
