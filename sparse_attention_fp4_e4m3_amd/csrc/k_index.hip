@@ -498,6 +498,7 @@ struct SelArgs {
   int pool_size;
   const int32_t* pool_len;   // Reindex: valid slots per row (null = pool_stride)
   const uint32_t* row_mask;  // [R] nonzero = select for this row; null = every row
+  int by_len;                // Reindex: split each row by its valid slots, not its capacity
 };
 
 __device__ __forceinline__ int series_len(const SelArgs& a, int series, int r) {
@@ -629,8 +630,9 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
     sp = S.cand_pos + (int64_t)r * 2 * S.stride;
   } else {
     // the row is split by its pool capacity when that fits, so the candidate
-    // loads need not wait for the pool length (slots past it are masked)
-    M = a.pool_stride <= kFinCap ? (uint32_t)a.pool_stride : (uint32_t)n;
+    // loads need not wait for the pool length (slots past it are masked);
+    // sparsely filled lists (the prefill candidates) by their length instead
+    M = (a.pool_stride <= kFinCap && !a.by_len) ? (uint32_t)a.pool_stride : (uint32_t)n;
     sk = reinterpret_cast<const uint32_t*>(S.arr) + (int64_t)r * S.stride;
     sp = a.pool + (int64_t)r * a.pool_stride;
   }
@@ -1408,6 +1410,7 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
   a.pool_stride = pool_stride;
   a.pool = pool;
   a.pool_len = pool_len;
+  a.by_len = shared ? 1 : 0;  // the prefill candidate lists are mostly empty
   a.row_mask = row_mask;
   a.out_idx = out_idx;
   a.out_pool = out_pool;
