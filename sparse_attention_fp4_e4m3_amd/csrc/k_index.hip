@@ -920,6 +920,7 @@ __device__ __forceinline__ float relu0(float x) { return __int_as_float(max(__fl
 __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
   const int64_t seg = a.row_start[0];
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float nrm = 0.0f;
   if (i < a.max_visible) {
     const u32x4* row = reinterpret_cast<const u32x4*>(a.k + (seg + i) * 128);
     float ss = 0.0f;
@@ -933,10 +934,18 @@ __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
         ss = __builtin_fmaf(hi, hi, ss);
       }
     }
-    const float nrm = __fsqrt_rn(ss) * 1.00001f;
+    nrm = __fsqrt_rn(ss) * 1.00001f;
     a.knorm[i] = nrm;
-    atomicMax(a.kmax, __float_as_uint(nrm));  // non-negative floats order like their bits
   }
+  // the wave's largest norm, then one atomic per wave (non-negative floats order like their bits)
+  uint32_t m = __float_as_uint(nrm);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 8, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(a.kmax, m);
   if (i < (int64_t)a.R * H) {
     const u32x4* row = reinterpret_cast<const u32x4*>(a.q + i * 64);
     float ss = 0.0f;
