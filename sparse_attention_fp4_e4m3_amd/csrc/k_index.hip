@@ -1188,44 +1188,51 @@ __global__ __launch_bounds__(256) void k_pf_certify(PfArgs a) {
 }
 
 // per row: candidate bitmap -> ascending positions (or the overflow flag).
-// The row's words are staged in LDS with coalesced loads (in chunks of
-// kPfCompactWords); thread t then owns a contiguous run of each chunk.
-constexpr int kPfCompactWords = 8192;
+// Wave w owns a contiguous quarter of the row's words: a first pass counts
+// its bits (coalesced 64-word loads), one barrier gives each wave its output
+// offset, and a second pass expands 64 words at a time: a DPP prefix sum of
+// the lanes' bit counts places each lane's positions, written one bit per
+// lane per store, so a store's lanes write neighbouring slots.
 __global__ __launch_bounds__(256) void k_pf_compact(PfArgs a) {
-  __shared__ uint32_t red[32];
-  __shared__ uint32_t wl[kPfCompactWords];
+  __shared__ uint32_t red[4];
   const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vis = clampv(a.row_visible[r], a.max_visible);
   const int nw = (vis + 31) / 32;
   const uint32_t* bw = a.bits + (int64_t)r * a.nwords;
   int32_t* out = a.cand + (int64_t)r * kPfCap;
-  uint32_t base = 0;  // candidates in earlier chunks
-  for (int c0 = 0; c0 < nw; c0 += kPfCompactWords) {
-    const int cn = min(kPfCompactWords, nw - c0);
-    __syncthreads();  // the previous chunk is consumed
-    for (int i = threadIdx.x; i < cn; i += 256) wl[i] = bw[c0 + i];
-    __syncthreads();
-    const int per = (cn + 255) / 256;
-    const int w0 = min(cn, (int)threadIdx.x * per), w1 = min(cn, w0 + per);
-    uint32_t c = 0;
-    for (int i = w0; i < w1; ++i) c += __popc(wl[i]);
-    uint32_t total;
-    uint32_t at = base + block_excl_sum<256>(c, red, &total);
-    if (base + total <= (uint32_t)kPfCap) {
-      for (int i = w0; i < w1; ++i) {
-        uint32_t m = wl[i];
-        while (m) {
-          const int bit = __ffs(m) - 1;
-          m &= m - 1;
-          out[at++] = 32 * (c0 + i) + bit;
+  const int per = ((nw + 3) / 4 + 63) & ~63;
+  const int w0 = min(nw, wave * per), w1 = min(nw, w0 + per);
+  uint32_t cnt = 0;
+  for (int i = w0 + lane; i < w1; i += 64) cnt += __popc(bw[i]);
+  cnt = wave_incl_sum(cnt);
+  if (lane == 63) red[wave] = cnt;
+  __syncthreads();
+  uint32_t base = 0, total = 0;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    base += ww < wave ? red[ww] : 0u;
+    total += red[ww];
+  }
+  if (total <= (uint32_t)kPfCap) {
+    for (int i0 = w0; i0 < w1; i0 += 64) {
+      const int i = i0 + lane;
+      uint32_t m = i < w1 ? bw[i] : 0u;
+      const uint32_t c = (uint32_t)__popc(m);
+      const uint32_t incl = wave_incl_sum(c);
+      uint32_t at = base + incl - c;
+      base += (uint32_t)__shfl((int)incl, 63, 64);
+      while (__ballot(m != 0u)) {
+        if (m) {
+          out[at++] = 32 * i + (__ffs(m) - 1);
+          m &= m - 1u;
         }
       }
     }
-    base += total;
   }
   if (threadIdx.x == 0) {
-    const bool overflow = base > (uint32_t)kPfCap;
-    a.ccnt[r] = overflow ? 0 : (int32_t)base;
+    const bool overflow = total > (uint32_t)kPfCap;
+    a.ccnt[r] = overflow ? 0 : (int32_t)total;
     a.over[r] = overflow ? 1u : 0u;
   }
 }
