@@ -69,6 +69,10 @@ def _lib():
             "oracle_hsi_pool": (i64, [P, i64, i32, i32, P]),
             "oracle_attention_row": (None, [P, i32, P, P, P, i32, i64, f64, P, P]),
             "oracle_attention_rows": (None, [i32, P, i32, P, P, P, P, i32, P, f64, P, P]),
+            "oracle_e4m3_encode_signed": (ctypes.c_uint8, [ctypes.c_float]),
+            "oracle_e4m3_encode_signed_array": (None, [P, i64, P]),
+            "oracle_attention_row_swa": (None, [P, i32, P, P, P, i32, i64, P, i64, i32, f64, P, P]),
+            "oracle_attention_rows_swa": (None, [i32, P, i32, P, P, P, P, i32, P, P, P, P, f64, P, P]),
             "oracle_num_threads": (i32, []),
         }
         for name, (res, args) in sig.items():
@@ -102,6 +106,20 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     out = np.empty(v.shape, dtype=np.uint8)
     _lib().oracle_e4m3_encode_array(_p(v), v.size, _p(out))
     return out
+
+
+def e4m3_encode_signed(v: np.ndarray) -> np.ndarray:
+    """Signed E4M3 byte per element (the FP8 local-window cache format)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _lib().oracle_e4m3_encode_signed_array(_p(v), v.size, _p(out))
+    return out
+
+
+def fp8_dequant(codes: np.ndarray) -> np.ndarray:
+    """Signed E4M3 bytes -> float64 values (the format definition, per byte)."""
+    table = np.array([e4m3_value(b) for b in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
 
 
 def e2m1_encode(v: np.ndarray) -> np.ndarray:
@@ -190,6 +208,30 @@ def attention_rows(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, row_sta
     lse = np.empty((R, Hq), dtype=np.float32)
     _lib().oracle_attention_rows(R, _p(q), Hq, _p(codes), _p(scales), _p(row_start), _p(idx),
                                  idx.shape[1], _p(visible), float(scale), _p(o), _p(lse))
+    return o, lse
+
+
+def attention_rows_swa(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, row_start: np.ndarray,
+                       idx: np.ndarray, visible: np.ndarray, win_codes: np.ndarray, win_start: np.ndarray,
+                       win_len: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """R rows, each attending over its selected FP4 entries joined with its
+    FP8 window (rows win_start[r] .. + min(win_len[r], 128) of win_codes
+    [*, 512]) in one softmax."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    row_start = np.ascontiguousarray(row_start, dtype=np.int64)
+    visible = np.ascontiguousarray(visible, dtype=np.int64)
+    win_codes = np.ascontiguousarray(win_codes, dtype=np.uint8)
+    win_start = np.ascontiguousarray(win_start, dtype=np.int64)
+    win_len = np.ascontiguousarray(win_len, dtype=np.int32)
+    R, Hq, _ = q.shape
+    o = np.empty((R, Hq, D), dtype=np.float32)
+    lse = np.empty((R, Hq), dtype=np.float32)
+    _lib().oracle_attention_rows_swa(R, _p(q), Hq, _p(codes), _p(scales), _p(row_start), _p(idx), idx.shape[1],
+                                     _p(visible), _p(win_codes), _p(win_start), _p(win_len), float(scale),
+                                     _p(o), _p(lse))
     return o, lse
 
 

@@ -108,6 +108,21 @@ void oracle_e2m1_encode_array(const float* v, int64_t n, uint8_t* out) {
     for (i = 0; i < n; ++i) out[i] = oracle_e2m1_encode(v[i]);
 }
 
+/* Signed E4M3 of one value: the sign bit of v, then the nearest magnitude
+ * as oracle_e4m3_encode picks it (ties to the even code, saturating at 448).
+ * A negative value that rounds to zero encodes as 0x80 (negative zero).
+ * This is the element format of the local sliding-window cache, which
+ * [Brief] "FP4 cache entries, and why they're safe" keeps in FP8. */
+uint8_t oracle_e4m3_encode_signed(float v) {
+    return (uint8_t)((signbit(v) ? 0x80 : 0) | oracle_e4m3_encode(fabsf(v)));
+}
+
+void oracle_e4m3_encode_signed_array(const float* v, int64_t n, uint8_t* out) {
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i) out[i] = oracle_e4m3_encode_signed(v[i]);
+}
+
 /* ------------------------------------------------------- quantize on write */
 
 /* One 512-channel row -> 256 code bytes + 32 scale bytes ([Brief] "FP4 cache
@@ -274,35 +289,16 @@ int64_t oracle_hsi_pool(const float* scores, int64_t n, int32_t block, int32_t P
 
 /* ---------------------------------------------------------- attention */
 
-/* Sparse attention of one query row ([Review] "The Paper": K and V are the
- * same Main KV entry; the selected entries are attended with the normal
- * attention operation; [Brief] "The global branch": one 512-dim latent per
- * entry shared by every query head).  For each head h over the set S of
- * selected positions j with 0 <= j < visible:
- *   z_j = scale * sum_c q[h][c] * x_hat_j[c]          (double)
- *   m = max z;  w_j = exp(z_j - m)
- *   o[h] = sum_j w_j x_hat_j / sum_j w_j;  lse[h] = m + ln(sum_j w_j)
- * S empty: o[h] = 0 and lse[h] = -inf.
- * codes/scales point at the row's cache segment (entry j at row j). */
-void oracle_attention_row(const float* q, int32_t Hq, const uint8_t* codes, const uint8_t* scales,
-                          const int32_t* idx, int32_t K, int64_t visible, double scale,
-                          float* o, float* lse) {
-    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
-    double* xh = NULL;
-    double* z = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+/* Softmax attention of Hq query heads over ns entries given as dequantized
+ * 512-channel rows xh[ns][512] (K = V = the entry).  For each head h:
+ *   z_i = scale * sum_c q[h][c] * xh_i[c]          (double)
+ *   m = max z;  w_i = exp(z_i - m)
+ *   o[h] = sum_i w_i xh_i / sum_i w_i;  lse[h] = m + ln(sum_i w_i)
+ * ns = 0: o[h] = 0 and lse[h] = -inf. */
+static void attend(const float* q, int32_t Hq, const double* xh, int32_t ns, double scale, float* o, float* lse) {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(ns > 0 ? ns : 1));
     double* acc = (double*)malloc(sizeof(double) * OR_D);
-    int32_t ns = 0, i, h, c;
-    for (i = 0; i < K; ++i)
-        if (idx[i] >= 0 && idx[i] < visible) sel[ns++] = idx[i];
-    xh = (double*)malloc(sizeof(double) * (size_t)(ns > 0 ? ns : 1) * OR_D);
-    for (i = 0; i < ns; ++i) {
-        for (c = 0; c < OR_D; ++c) {
-            uint8_t byte = codes[(int64_t)sel[i] * (OR_D / 2) + c / 2];
-            uint8_t code = (c & 1) ? (byte >> 4) : (byte & 15);
-            xh[(int64_t)i * OR_D + c] =
-                oracle_e2m1_value(code) * oracle_e4m3_value(scales[(int64_t)sel[i] * OR_NG + c / OR_G]);
-        }
-    }
+    int32_t i, h, c;
     for (h = 0; h < Hq; ++h) {
         double m = -INFINITY, l = 0.0;
         if (ns == 0) {
@@ -325,10 +321,43 @@ void oracle_attention_row(const float* q, int32_t Hq, const uint8_t* codes, cons
         for (c = 0; c < OR_D; ++c) o[(int64_t)h * OR_D + c] = (float)(acc[c] / l);
         if (lse) lse[h] = (float)(m + log(l));
     }
-    free(sel);
-    free(xh);
     free(z);
     free(acc);
+}
+
+/* The selected FP4 entries of one row, dequantized: positions idx[i] with
+ * 0 <= idx[i] < visible, in list order (duplicates kept), entry j at row j
+ * of codes/scales.  x_hat[c] = E2M1(code_c) * E4M3(scale of group c/16).
+ * Writes up to K rows into xh; returns how many. */
+static int32_t gather_fp4(const uint8_t* codes, const uint8_t* scales, const int32_t* idx, int32_t K,
+                          int64_t visible, double* xh) {
+    int32_t ns = 0, i, c;
+    for (i = 0; i < K; ++i) {
+        int64_t j = idx[i];
+        if (j < 0 || j >= visible) continue;
+        for (c = 0; c < OR_D; ++c) {
+            uint8_t byte = codes[j * (OR_D / 2) + c / 2];
+            uint8_t code = (c & 1) ? (byte >> 4) : (byte & 15);
+            xh[(int64_t)ns * OR_D + c] = oracle_e2m1_value(code) * oracle_e4m3_value(scales[j * OR_NG + c / OR_G]);
+        }
+        ++ns;
+    }
+    return ns;
+}
+
+/* Sparse attention of one query row ([Review] "The Paper": K and V are the
+ * same Main KV entry; the selected entries are attended with the normal
+ * attention operation; [Brief] "The global branch": one 512-dim latent per
+ * entry shared by every query head): attend() over S = the selected
+ * positions j with 0 <= j < visible.  codes/scales point at the row's cache
+ * segment (entry j at row j). */
+void oracle_attention_row(const float* q, int32_t Hq, const uint8_t* codes, const uint8_t* scales,
+                          const int32_t* idx, int32_t K, int64_t visible, double scale,
+                          float* o, float* lse) {
+    double* xh = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1) * OR_D);
+    int32_t ns = gather_fp4(codes, scales, idx, K, visible, xh);
+    attend(q, Hq, xh, ns, scale, o, lse);
+    free(xh);
 }
 
 /* Several rows at once (rows are independent): row r reads q + r*Hq*512,
@@ -342,6 +371,45 @@ void oracle_attention_rows(int32_t R, const float* q, int32_t Hq, const uint8_t*
         oracle_attention_row(q + (int64_t)r * Hq * OR_D, Hq, codes + row_start[r] * (OR_D / 2),
                              scales + row_start[r] * OR_NG, idx + (int64_t)r * K, K, visible[r], scale,
                              o + (int64_t)r * Hq * OR_D, lse ? lse + (int64_t)r * Hq : NULL);
+}
+
+/* The local branch joined with the global one ([Review] "The Paper": every
+ * layer runs sliding-window attention over the 128 most recent tokens, and
+ * the selected Main KV entries are joined to the window's KV for a single
+ * attention; [Brief] "Two attention paths in every layer", "The global
+ * branch" and the mode table of "CSA2: most layers don't keep their own
+ * cache": each layer keeps its own window; "FP4 cache entries, and why
+ * they're safe": the local cache stays in FP8).  One softmax over the union of
+ *   - the selected FP4 entries, as oracle_attention_row takes them, and
+ *   - the row's window entries: rows win_start .. win_start + n - 1 of
+ *     win_codes [*][512] (one signed E4M3 byte per channel, no scale),
+ *     n = win_len clamped to [0, 128], value E4M3(byte) per channel;
+ * window entries are 512-channel latents with K = V, like Main KV entries. */
+void oracle_attention_row_swa(const float* q, int32_t Hq, const uint8_t* codes, const uint8_t* scales,
+                              const int32_t* idx, int32_t K, int64_t visible, const uint8_t* win_codes,
+                              int64_t win_start, int32_t win_len, double scale, float* o, float* lse) {
+    int32_t n = win_len < 0 ? 0 : (win_len > 128 ? 128 : win_len);
+    double* xh = (double*)malloc(sizeof(double) * (size_t)(K + n > 0 ? K + n : 1) * OR_D);
+    int32_t ns = gather_fp4(codes, scales, idx, K, visible, xh), i, c;
+    for (i = 0; i < n; ++i) {
+        for (c = 0; c < OR_D; ++c)
+            xh[(int64_t)(ns + i) * OR_D + c] = oracle_e4m3_value(win_codes[(win_start + i) * OR_D + c]);
+    }
+    attend(q, Hq, xh, ns + n, scale, o, lse);
+    free(xh);
+}
+
+void oracle_attention_rows_swa(int32_t R, const float* q, int32_t Hq, const uint8_t* codes,
+                               const uint8_t* scales, const int64_t* row_start, const int32_t* idx, int32_t K,
+                               const int64_t* visible, const uint8_t* win_codes, const int64_t* win_start,
+                               const int32_t* win_len, double scale, float* o, float* lse) {
+    int32_t r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < R; ++r)
+        oracle_attention_row_swa(q + (int64_t)r * Hq * OR_D, Hq, codes + row_start[r] * (OR_D / 2),
+                                 scales + row_start[r] * OR_NG, idx + (int64_t)r * K, K, visible[r], win_codes,
+                                 win_start[r], win_len[r], scale, o + (int64_t)r * Hq * OR_D,
+                                 lse ? lse + (int64_t)r * Hq : NULL);
 }
 
 int32_t oracle_num_threads(void) {
