@@ -82,7 +82,8 @@ extern "C" {
  *              of 16.  Values must be finite.
  * dst_rows     [n_tokens] int64 cache row of each token, or NULL for rows
  *              0..n_tokens-1 (then n_tokens <= cap_rows is required).  A
- *              destination outside [0, cap_rows) is skipped.
+ *              destination outside [0, cap_rows) is skipped; two tokens of
+ *              one call with the same destination leave either one there.
  * kv_codes     [cap_rows, 256] uint8: byte i = code of channel 2i (low
  *              nibble) | code of channel 2i+1 (high nibble).
  * kv_scales    [cap_rows, 32] uint8: E4M3 scale byte of group g.
@@ -181,6 +182,70 @@ int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t
 
 size_t csa2_sparse_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t q_dtype, int32_t top_k);
 
+/*
+ * Local sliding-window branch.  Every CSA2 layer also runs exact sliding-
+ * window attention over the 128 most recent tokens with its own window
+ * cache, kept in FP8, and the selected Main KV entries are joined to that
+ * window's KV for one attention ("The Paper" in the talk write-up "DeepSeek
+ * V4.1 Flash: pushing the limits"; course brief "DeepSeek-V4.1-Flash",
+ * sections "Two attention paths in every layer", "The global branch" and
+ * "FP4 cache entries, and why they're safe").  The first layers are window
+ * only (top_k = 0 below).
+ *
+ * Window entry: 512 bytes, one signed E4M3 (E4M3FN) byte per channel of the
+ * layer's 512-channel latent, no scale; K = V = the entry, as for Main KV.
+ */
+#define CSA2_SWA_WINDOW 128
+
+/*
+ * Quantize-on-write of window entries: byte c = nearest E4M3 value of
+ * x[t, c] (round to nearest even, |x| > 448 saturating to 448, sign bit of
+ * x kept, so a negative value that rounds to zero is 0x80).
+ * x            [n_tokens, x_row_stride] of x_dtype (CSA2_F32 or CSA2_BF16),
+ *              16-byte aligned rows; values must be finite.
+ * dst_rows     [n_tokens] int64 window-cache row per token, or NULL for rows
+ *              0..n_tokens-1 (then n_tokens <= cap_rows).  A destination
+ *              outside [0, cap_rows) is skipped; two tokens of one call with
+ *              the same destination leave either one there.  A per-sequence
+ *              ring of 128 rows (row = position mod 128) keeps a decode window.
+ * win_codes    [cap_rows, 512] uint8, 16-byte aligned.
+ * Errors: CSA2_E_INVALID for null buffers, n_tokens < 0, bad dtype,
+ * misalignment, x_row_stride < 512, or (dst_rows NULL and n_tokens > cap_rows).
+ */
+int32_t csa2_quantize_swa_fp8(const void* x, int32_t x_dtype, int64_t n_tokens, int64_t x_row_stride,
+                              const int64_t* dst_rows, uint8_t* win_codes, int64_t cap_rows, void* stream);
+
+/*
+ * csa2_sparse_attn with the row's window joined into the same softmax.
+ * For row r, head h, the attended set is S (as csa2_sparse_attn defines it,
+ * empty when top_k = 0) plus the window entries W_r = rows
+ * row_win_start[r] .. row_win_start[r] + n_r - 1 of win_codes, with
+ * n_r = row_win_len[r] clamped to [0, 128]:
+ *   w_i = E4M3(win_codes[i, c]) per channel;  z over S and W_r as in
+ *   csa2_sparse_attn;  p = softmax over S and W_r together;
+ *   out[r,h] = sum p x over S + sum p w over W_r;  lse over both.
+ * Entries are not de-duplicated between S and W_r (they come from
+ * different caches).  Nothing to attend: out = 0, lse = -inf.
+ * Window entries of a row may be stored in any order (a ring buffer's valid
+ * prefix works as it is): the result does not depend on their order.
+ *
+ * Arguments as for csa2_sparse_attn, plus:
+ * top_k        0..CSA2_MAX_TOP_K; with 0, kv_codes, kv_scales, row_kv_start,
+ *              idx and row_visible are not read and may be NULL.
+ * win_codes    window entries written by csa2_quantize_swa_fp8, 16-byte aligned.
+ * row_win_start [n_rows] int64;  row_win_len [n_rows] int32.
+ * workspace    csa2_sparse_attn_swa_workspace_size(...) bytes, 256-byte aligned.
+ * Results are deterministic.
+ */
+int32_t csa2_sparse_attn_swa(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                             const uint8_t* kv_codes, const uint8_t* kv_scales, const int64_t* row_kv_start,
+                             const int32_t* idx, int32_t top_k, const int32_t* row_visible,
+                             const uint8_t* win_codes, const int64_t* row_win_start, const int32_t* row_win_len,
+                             float softmax_scale, void* out, int32_t out_dtype, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+size_t csa2_sparse_attn_swa_workspace_size(int32_t n_rows, int32_t n_heads, int32_t q_dtype, int32_t top_k);
+
 /* Thread-local description of the last non-zero status of this thread. */
 const char* csa2_last_error(void);
 
@@ -196,6 +261,8 @@ const char* csa2_last_error(void);
 #define CSA2_KERNEL_REINDEX_SCORE 3
 #define CSA2_KERNEL_ATTN 4
 #define CSA2_KERNEL_ATTN_COMBINE 5
+#define CSA2_KERNEL_QUANT_FP8 6
+#define CSA2_KERNEL_SWA_ATTN 7
 int32_t csa2_profile_kernel_events(int32_t kernel_id, void* start_event, void* stop_event);
 
 #ifdef __cplusplus

@@ -20,12 +20,17 @@ F32, BF16 = 0, 1
 FULL, REINDEX, FULL_SHARED = 0, 1, 2
 MAX_TOP_K = 4096
 KERNEL_QUANT, KERNEL_INDEX_SCAN, KERNEL_REINDEX_SCORE, KERNEL_ATTN, KERNEL_ATTN_COMBINE = 1, 2, 3, 4, 5
+KERNEL_QUANT_FP8, KERNEL_SWA_ATTN = 6, 7
+SWA_WINDOW = 128
 EXPORTED = (
     "csa2_quantize_kv_fp4",
     "csa2_index_topk",
     "csa2_index_topk_workspace_size",
     "csa2_sparse_attn",
     "csa2_sparse_attn_workspace_size",
+    "csa2_quantize_swa_fp8",
+    "csa2_sparse_attn_swa",
+    "csa2_sparse_attn_swa_workspace_size",
     "csa2_last_error",
     "csa2_profile_kernel_events",
 )
@@ -59,6 +64,13 @@ def lib():
         L.csa2_sparse_attn.restype = i32
         L.csa2_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32]
         L.csa2_sparse_attn_workspace_size.restype = sz
+        L.csa2_quantize_swa_fp8.argtypes = [P, i32, i64, i64, P, P, i64, P]
+        L.csa2_quantize_swa_fp8.restype = i32
+        L.csa2_sparse_attn_swa.argtypes = [i32, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P, ctypes.c_float, P, i32,
+                                           P, P, sz, P]
+        L.csa2_sparse_attn_swa.restype = i32
+        L.csa2_sparse_attn_swa_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.csa2_sparse_attn_swa_workspace_size.restype = sz
         L.csa2_last_error.argtypes = []
         L.csa2_last_error.restype = ctypes.c_char_p
         L.csa2_profile_kernel_events.argtypes = [i32, P, P]
@@ -145,6 +157,38 @@ def sparse_attn(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor
         R, _ptr(q), _dt(q), Hq, D, _ptr(kv_codes), _ptr(kv_scales), _ptr(row_kv_start), _ptr(idx),
         idx.shape[1], _ptr(row_visible), float(softmax_scale), _ptr(out), _dt(out), _ptr(lse), _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+def quantize_swa_fp8(x: torch.Tensor, win_codes: torch.Tensor, dst_rows: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """x [n, 512(+)] fp32/bf16 -> signed E4M3 rows of win_codes [cap, 512] u8."""
+    _contig(win_codes, dst_rows)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [n, C] with unit channel stride")
+    _check(lib().csa2_quantize_swa_fp8(_ptr(x), _dt(x), x.shape[0], x.stride(0), _ptr(dst_rows), _ptr(win_codes),
+                                       win_codes.shape[0], _stream(stream)))
+
+
+def sparse_attn_swa_workspace_size(n_rows: int, n_heads: int, q_dtype: int, top_k: int) -> int:
+    return int(lib().csa2_sparse_attn_swa_workspace_size(n_rows, n_heads, q_dtype, top_k))
+
+
+def sparse_attn_swa(q: torch.Tensor, win_codes: torch.Tensor, row_win_start: torch.Tensor,
+                    row_win_len: torch.Tensor, out: torch.Tensor, softmax_scale: float,
+                    kv_codes: Optional[torch.Tensor] = None, kv_scales: Optional[torch.Tensor] = None,
+                    row_kv_start: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                    row_visible: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Selected FP4 entries (idx; None = window only) joined with each row's FP8 window in one softmax."""
+    _contig(q, win_codes, row_win_start, row_win_len, out, kv_codes, kv_scales, row_kv_start, idx, row_visible, lse,
+            workspace)
+    R, Hq, D = q.shape
+    top_k = 0 if idx is None else idx.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().csa2_sparse_attn_swa(
+        R, _ptr(q), _dt(q), Hq, D, _ptr(kv_codes), _ptr(kv_scales), _ptr(row_kv_start), _ptr(idx), top_k,
+        _ptr(row_visible), _ptr(win_codes), _ptr(row_win_start), _ptr(row_win_len), float(softmax_scale), _ptr(out),
+        _dt(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def profile_kernel_events(kernel_id: int, start=None, stop=None) -> None:

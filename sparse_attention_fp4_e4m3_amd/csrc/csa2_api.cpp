@@ -42,7 +42,7 @@ extern "C" {
 const char* csa2_last_error(void) { return g_last_error.c_str(); }
 
 int32_t csa2_profile_kernel_events(int32_t kernel_id, void* start_event, void* stop_event) {
-  if (kernel_id < CSA2_KERNEL_QUANT || kernel_id > CSA2_KERNEL_ATTN_COMBINE)
+  if (kernel_id < CSA2_KERNEL_QUANT || kernel_id > CSA2_KERNEL_SWA_ATTN)
     return fail(CSA2_E_INVALID, "csa2_profile_kernel_events: unknown kernel id %d", kernel_id);
   g_events[kernel_id].start = static_cast<hipEvent_t>(start_event);
   g_events[kernel_id].stop = static_cast<hipEvent_t>(stop_event);
@@ -126,7 +126,7 @@ int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t
 
 size_t csa2_sparse_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t q_dtype, int32_t top_k) {
   if (n_rows <= 0 || n_heads <= 0 || n_heads % 16 || top_k <= 0 || !dtype_ok(q_dtype)) return 0;
-  return attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k);
+  return attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k, false);
 }
 
 int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
@@ -147,13 +147,69 @@ int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t
     return fail(CSA2_E_INVALID, "%s: null buffer", fn);
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(kv_codes, 16) || !aligned(kv_scales, 8))
     return fail(CSA2_E_INVALID, "%s: q/out/kv_codes must be 16-byte and kv_scales 8-byte aligned", fn);
-  const size_t need = attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k);
+  const size_t need = attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k, false);
   if (need && (!workspace || workspace_bytes < need))
     return fail(CSA2_E_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
   if (need && !aligned(workspace, 256)) return fail(CSA2_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
   return hip_status(launch_sparse_attn(n_rows, q, q_dtype, n_heads, kv_codes, kv_scales, row_kv_start, idx, top_k,
-                                       row_visible, softmax_scale, out, out_dtype, lse, workspace,
-                                       static_cast<hipStream_t>(stream)),
+                                       row_visible, nullptr, nullptr, nullptr, softmax_scale, out, out_dtype, lse,
+                                       workspace, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int32_t csa2_quantize_swa_fp8(const void* x, int32_t x_dtype, int64_t n_tokens, int64_t x_row_stride,
+                              const int64_t* dst_rows, uint8_t* win_codes, int64_t cap_rows, void* stream) {
+  const char* fn = "csa2_quantize_swa_fp8";
+  if (n_tokens < 0) return fail(CSA2_E_INVALID, "%s: n_tokens < 0", fn);
+  if (!dtype_ok(x_dtype)) return fail(CSA2_E_INVALID, "%s: x_dtype %d is not F32/BF16", fn, x_dtype);
+  if (n_tokens == 0) return CSA2_OK;
+  if (!x || !win_codes) return fail(CSA2_E_INVALID, "%s: null buffer", fn);
+  if (x_row_stride < kDim) return fail(CSA2_E_INVALID, "%s: x_row_stride %lld < 512", fn, (long long)x_row_stride);
+  if (!aligned(x, 16) || (x_row_stride * (int64_t)dtype_size(x_dtype)) % 16)
+    return fail(CSA2_E_INVALID, "%s: x rows must be 16-byte aligned", fn);
+  if (!aligned(win_codes, 16)) return fail(CSA2_E_INVALID, "%s: win_codes must be 16-byte aligned", fn);
+  if (cap_rows <= 0) return fail(CSA2_E_INVALID, "%s: cap_rows <= 0", fn);
+  if (!dst_rows && n_tokens > cap_rows)
+    return fail(CSA2_E_INVALID, "%s: n_tokens %lld > cap_rows %lld", fn, (long long)n_tokens, (long long)cap_rows);
+  return hip_status(launch_quantize_fp8(x, x_dtype, n_tokens, x_row_stride, dst_rows, win_codes, cap_rows,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t csa2_sparse_attn_swa_workspace_size(int32_t n_rows, int32_t n_heads, int32_t q_dtype, int32_t top_k) {
+  if (n_rows <= 0 || n_heads <= 0 || n_heads % 16 || top_k < 0 || !dtype_ok(q_dtype)) return 0;
+  return attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k, true);
+}
+
+int32_t csa2_sparse_attn_swa(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                             const uint8_t* kv_codes, const uint8_t* kv_scales, const int64_t* row_kv_start,
+                             const int32_t* idx, int32_t top_k, const int32_t* row_visible,
+                             const uint8_t* win_codes, const int64_t* row_win_start, const int32_t* row_win_len,
+                             float softmax_scale, void* out, int32_t out_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "csa2_sparse_attn_swa";
+  if (n_rows < 0) return fail(CSA2_E_INVALID, "%s: n_rows < 0", fn);
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return fail(CSA2_E_INVALID, "%s: dtype is not F32/BF16", fn);
+  if (head_dim != kDim) return fail(CSA2_E_UNSUPPORTED, "%s: head_dim %d (only 512 is built)", fn, head_dim);
+  if (n_heads < 16 || n_heads > 128 || n_heads % 16)
+    return fail(CSA2_E_INVALID, "%s: n_heads %d must be a multiple of 16 in 16..128", fn, n_heads);
+  if (top_k < 0) return fail(CSA2_E_INVALID, "%s: top_k %d < 0", fn, top_k);
+  if (!(softmax_scale == softmax_scale)) return fail(CSA2_E_INVALID, "%s: softmax_scale is NaN", fn);
+  if (n_rows == 0) return CSA2_OK;
+  if (!q || !out || !win_codes || !row_win_start || !row_win_len) return fail(CSA2_E_INVALID, "%s: null buffer", fn);
+  if (top_k > 0 && (!kv_codes || !kv_scales || !row_kv_start || !idx))
+    return fail(CSA2_E_INVALID, "%s: null cache or index buffer with top_k > 0", fn);
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(win_codes, 16))
+    return fail(CSA2_E_INVALID, "%s: q/out/win_codes must be 16-byte aligned", fn);
+  if (top_k > 0 && (!aligned(kv_codes, 16) || !aligned(kv_scales, 8)))
+    return fail(CSA2_E_INVALID, "%s: kv_codes must be 16-byte and kv_scales 8-byte aligned", fn);
+  const size_t need = attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k, true);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(CSA2_E_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+  if (need && !aligned(workspace, 256)) return fail(CSA2_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
+  return hip_status(launch_sparse_attn(n_rows, q, q_dtype, n_heads, kv_codes, kv_scales, row_kv_start, idx, top_k,
+                                       row_visible, win_codes, row_win_start, row_win_len, softmax_scale, out,
+                                       out_dtype, lse, workspace, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -43,10 +43,16 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
                              int32_t* out_idx, int pool_size, int32_t* out_pool, int32_t* out_pool_len,
                              void* ws, hipStream_t s);
 
-size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k);
+hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
+                               uint8_t* codes, int64_t cap, hipStream_t s);
 
+// window = true: one more partial slot per (row, head) for the local window
+size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window);
+
+// top_k may be 0 when a window is given (win != nullptr): the window alone is attended
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
                               const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
+                              const uint8_t* win, const int64_t* win_start, const int32_t* win_len,
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
 
 // ------------------------------------------------------------ device helpers

@@ -57,6 +57,7 @@ constexpr int kOStride = 516;        // fp32 per row of the epilogue reduction b
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;        // log2 headroom before the reference maximum moves
+constexpr int kWinMax = 128;         // local window entries per row
 
 __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ half2v bits_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
@@ -119,11 +120,14 @@ struct AttnArgs {
   void* out;
   int out_dtype;
   float* lse;
-  int splits;
+  int slots;             // partials per (row, head): key splits (+1 for the window); 1 = write out directly
   int keys_per_split;    // multiple of kStep
-  float* ws_o;           // [R, Hq, splits, 512] split outputs, normalized
-  float* ws_m;           // [R, Hq, splits] reference maxima (log2 units)
-  float* ws_l;           // [R, Hq, splits] sums
+  float* ws_o;           // [R, Hq, slots, 512] partial outputs, normalized
+  float* ws_m;           // [R, Hq, slots] reference maxima (log2 units)
+  float* ws_l;           // [R, Hq, slots] sums
+  const uint8_t* win;        // local window entries [*, 512] signed E4M3 bytes
+  const int64_t* win_start;  // [R] first window entry of each row
+  const int32_t* win_len;    // [R] window entries of each row (clamped to [0, kWinMax])
 };
 
 // byte offset of staged code row k.  Rows are padded to 272 bytes and each
@@ -535,9 +539,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
                       O[ht][4][i] + o1.x, O[ht][5][i] + o1.y, O[ht][6][i] + o1.z, O[ht][7][i] + o1.w};
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[t] *= inv;
-        if (a.splits > 1) {
+        if (a.slots > 1) {
           // streaming stores: the partials are read once, by the combine kernel
-          floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch);
+          floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.slots + split) * kDim + ch);
           __builtin_nontemporal_store(floatx4{v[0], v[1], v[2], v[3]}, dst);
           __builtin_nontemporal_store(floatx4{v[4], v[5], v[6], v[7]}, dst + 1);
         } else if (a.out_dtype == CSA2_F32) {
@@ -562,11 +566,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         const int h = 16 * ht + n16;
-        if (a.splits == 1) {
+        if (a.slots == 1) {
           if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
         } else {
-          a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
-          a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+          a.ws_m[(rowh + h) * a.slots + split] = mref[ht];
+          a.ws_l[(rowh + h) * a.slots + split] = lrun[ht];
         }
       }
     }
@@ -801,11 +805,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         const int h = 16 * ht + n16;
-        if (a.splits == 1) {
+        if (a.slots == 1) {
           if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
         } else {
-          a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
-          a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+          a.ws_m[(rowh + h) * a.slots + split] = mref[ht];
+          a.ws_l[(rowh + h) * a.slots + split] = lrun[ht];
         }
       }
     }
@@ -895,8 +899,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
         float v[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[t] = O[ht][t][i] * inv;
-        if (a.splits > 1) {
-          floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch);
+        if (a.slots > 1) {
+          floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.slots + split) * kDim + ch);
           __builtin_nontemporal_store(floatx4{v[0], v[1], v[2], v[3]}, dst);
           __builtin_nontemporal_store(floatx4{v[4], v[5], v[6], v[7]}, dst + 1);
         } else if (a.out_dtype == CSA2_F32) {
@@ -1168,8 +1172,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
       const float L = sm.lfin[h];
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       const float v0 = O[ht][0][i] * inv, v1 = O[ht][1][i] * inv, v2 = O[ht][2][i] * inv, v3 = O[ht][3][i] * inv;
-      if (a.splits > 1) {
-        floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.splits + split) * kDim + ch);
+      if (a.slots > 1) {
+        floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.slots + split) * kDim + ch);
         __builtin_nontemporal_store(floatx4{v0, v1, v2, v3}, dst);
       } else if (a.out_dtype == CSA2_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + ch) = make_float4(v0, v1, v2, v3);
@@ -1191,11 +1195,251 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
-      if (a.splits == 1) {
+      if (a.slots == 1) {
         if (a.lse) a.lse[rowh + h] = lrun[ht] > 0.0f ? (mref[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
       } else {
-        a.ws_m[(rowh + h) * a.splits + split] = mref[ht];
-        a.ws_l[(rowh + h) * a.splits + split] = lrun[ht];
+        a.ws_m[(rowh + h) * a.slots + split] = mref[ht];
+        a.ws_l[(rowh + h) * a.slots + split] = lrun[ht];
+      }
+    }
+  }
+}
+
+// ---- local sliding window.  A row's window (at most 128 entries of one
+// signed E4M3 byte per channel, K = V like a Main KV entry) is one step of
+// the loop above with no gather and no scales: a workgroup owns one (row,
+// group of 16*NHT heads); lane (w, n16, q4) loads bytes [128 q4, +128) of
+// window entry 16w + n16 into registers, converts them pairwise to fp16
+// (exact: every E4M3 value is an fp16 value) as the QK^T A operand, and
+// stages them in LDS for PV.  PV gives wave w channels [64w, 64w+64) as in
+// the 64-head kernel: a lane reads the 4 bytes at channel 64w + 4*n16 of 8
+// consecutive entries and transposes them with byte permutes so that each
+// fp16 pair holds two entries of one channel.  The result is a partial
+// (normalized output, maximum, sum) in the last slot, merged by the combine
+// with the key splits of the selected entries, or the output itself when
+// nothing else is attended.
+constexpr int kWStride = 520;  // bytes per staged window entry: entries 8 apart land 16 banks apart
+
+template <int NHT, bool SPLITQ>
+struct SmemSwa {
+  static constexpr int kQRows = 16 * NHT * (SPLITQ ? 2 : 1);
+  _Float16 q[kQRows * kQStride];
+  uint8_t wc[kWinMax * kWStride];
+  _Float16 p[16 * NHT * kPStride];
+  float red_max[kWaves][64];
+  float red_sum[kWaves][64];
+};
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+template <int NHT, bool SPLITQ, int QDT>
+__global__ __launch_bounds__(kThreads, 1) void k_swa_attn(AttnArgs a) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  using Sm = SmemSwa<NHT, SPLITQ>;
+  Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+  constexpr int HG = 16 * NHT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int r = blockIdx.x, hg = blockIdx.y;
+  const int h0 = hg * HG;
+  const int len = min(max(a.win_len[r], 0), kWinMax);
+  const int key = 16 * w + n16;  // this lane's entry in QK^T
+
+  u32x4 c[8];  // bytes [128 q4, +128) of entry `key`
+  if (key < len) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.win + (a.win_start[r] + key) * kDim + 128 * q4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = src[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // queries to LDS as fp16 (fp32 queries as hi + lo halves, rows HG.. the lo halves)
+  if (QDT == CSA2_BF16) {
+    constexpr int NP = HG * kDim / 8 / kThreads;
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
+    u32x4 v[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + kThreads * i;
+      v[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)(p / (kDim / 8)) * kDim + (p % (kDim / 8)) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + kThreads * i;
+      half8 hv;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        hv[2 * k] = (_Float16)__uint_as_float(v[i][k] << 16);
+        hv[2 * k + 1] = (_Float16)__uint_as_float(v[i][k] & 0xFFFF0000u);
+      }
+      *reinterpret_cast<half8*>(&sm.q[(p / (kDim / 8)) * kQStride + (p % (kDim / 8)) * 8]) = hv;
+    }
+  } else {
+    constexpr int NP = HG * kDim / 4 / kThreads;
+    const float* qf = static_cast<const float*>(a.q) + ((int64_t)r * a.Hq + h0) * kDim;
+    floatx4 v[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + kThreads * i;
+      v[i] = *reinterpret_cast<const floatx4*>(qf + (int64_t)(p / (kDim / 4)) * kDim + (p % (kDim / 4)) * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + kThreads * i;
+      const int h = p / (kDim / 4), c4 = (p % (kDim / 4)) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const _Float16 hi = (_Float16)v[i][k];
+        sm.q[h * kQStride + c4 + k] = hi;
+        if (SPLITQ) sm.q[(HG + h) * kQStride + c4 + k] = (_Float16)(v[i][k] - (float)hi);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sm.wc[key * kWStride + 128 * q4 + 16 * i]) = c[i];
+  __syncthreads();
+
+  // ---- QK^T: S^T[entry][head]; K-step ks covers channels 128*q4 + 8*ks .. +7 on both operands
+  constexpr int NQ = SPLITQ ? 2 : 1;
+  floatx4 S[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) S[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    const uint32_t w0 = c[ks >> 1][2 * (ks & 1)], w1 = c[ks >> 1][2 * (ks & 1) + 1];
+    const half8 av = cat4(e4m3x2_to_h2<false>(w0), e4m3x2_to_h2<true>(w0), e4m3x2_to_h2<false>(w1),
+                          e4m3x2_to_h2<true>(w1));
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+      for (int qh = 0; qh < NQ; ++qh) {
+        const half8 bq = *reinterpret_cast<const half8*>(&sm.q[(16 * (qh * NHT + ht) + n16) * kQStride + 128 * q4 + 8 * ks]);
+        S[ht] = mfma(av, bq, S[ht]);
+      }
+    }
+  }
+
+  // ---- softmax over the window: lane holds entries 16w + 4q4 + i of head 16ht + n16
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float z = (16 * w + 4 * q4 + i < len) ? S[ht][i] * a.c2 : -INFINITY;
+      S[ht][i] = z;
+      mx = fmaxf(mx, z);
+    }
+    mx = rows_max(mx);
+    if (q4 == 0) sm.red_max[w][16 * ht + n16] = mx;
+  }
+  __syncthreads();
+  float mrow[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int h = 16 * ht + n16;
+    float m = sm.red_max[0][h];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) m = fmaxf(m, sm.red_max[ww][h]);
+    mrow[ht] = m;
+    const float muse = (m == -INFINITY) ? 0.0f : m;
+    _Float16 pv[4];
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
+      sum += (float)pv[i];
+    }
+    *reinterpret_cast<u32x2*>(&sm.p[h * kPStride + 16 * w + 4 * q4]) =
+        u32x2{h2_bits(half2v{pv[0], pv[1]}), h2_bits(half2v{pv[2], pv[3]})};
+    sum = rows_sum(sum);
+    if (q4 == 0) sm.red_sum[w][h] = sum;
+  }
+  __syncthreads();
+
+  // ---- PV: wave w, channels 64w + 4*n16 + t (tile t), all window entries
+  floatx4 O[NHT][4];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[ht][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int cb = 64 * w + 4 * n16;
+  const int kk_end = (len + 31) >> 5;  // 32-entry K-steps holding a valid entry
+  for (int kk = 0; kk < kk_end; ++kk) {
+    const int e0 = 32 * kk + 8 * q4;
+    uint32_t W[8];  // channels cb .. cb+3 of entries e0 .. e0+7
+#pragma unroll
+    for (int k = 0; k < 8; ++k) W[k] = *reinterpret_cast<const uint32_t*>(&sm.wc[(e0 + k) * kWStride + cb]);
+    // 4x4 byte transposes: T[t] of a group of 4 entries holds channel t of each
+    uint32_t T[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t a01 = perm(W[4 * g + 1], W[4 * g], 0x05010400u), b01 = perm(W[4 * g + 1], W[4 * g], 0x07030602u);
+      const uint32_t a23 = perm(W[4 * g + 3], W[4 * g + 2], 0x05010400u),
+                     b23 = perm(W[4 * g + 3], W[4 * g + 2], 0x07030602u);
+      T[g][0] = perm(a23, a01, 0x05040100u);
+      T[g][1] = perm(a23, a01, 0x07060302u);
+      T[g][2] = perm(b23, b01, 0x05040100u);
+      T[g][3] = perm(b23, b01, 0x07060302u);
+    }
+    half8 av[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) av[ht] = *reinterpret_cast<const half8*>(&sm.p[(16 * ht + n16) * kPStride + e0]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const half8 b = cat4(e4m3x2_to_h2<false>(T[0][t]), e4m3x2_to_h2<true>(T[0][t]), e4m3x2_to_h2<false>(T[1][t]),
+                           e4m3x2_to_h2<true>(T[1][t]));
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) O[ht][t] = mfma(av[ht], b, O[ht][t]);
+    }
+  }
+
+  // ---- epilogue: the partial of the last slot, or the output when it is the only one
+  const int64_t rowh = (int64_t)r * a.Hq + h0;
+  const int slot = a.slots - 1;
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * ht + 4 * q4 + i;
+      float L = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) L += sm.red_sum[ww][h];
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      const float v0 = O[ht][0][i] * inv, v1 = O[ht][1][i] * inv, v2 = O[ht][2][i] * inv, v3 = O[ht][3][i] * inv;
+      if (a.slots > 1) {
+        floatx4* dst = reinterpret_cast<floatx4*>(a.ws_o + ((rowh + h) * a.slots + slot) * kDim + cb);
+        __builtin_nontemporal_store(floatx4{v0, v1, v2, v3}, dst);
+      } else if (a.out_dtype == CSA2_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (rowh + h) * kDim + cb) = make_float4(v0, v1, v2, v3);
+      } else {
+        const float vv[4] = {v0, v1, v2, v3};
+        uint32_t pk[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          uint32_t lo = __float_as_uint(vv[2 * k]), hi = __float_as_uint(vv[2 * k + 1]);
+          lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+          hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+          pk[k] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + (rowh + h) * kDim + cb) = make_uint2(pk[0], pk[1]);
+      }
+    }
+  }
+  if (w == 0 && q4 == 0) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      float L = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) L += sm.red_sum[ww][h];
+      if (a.slots == 1) {
+        if (a.lse) a.lse[rowh + h] = L > 0.0f ? (mrow[ht] + __log2f(L)) * kLn2 : -INFINITY;
+      } else {
+        a.ws_m[(rowh + h) * a.slots + slot] = mrow[ht];
+        a.ws_l[(rowh + h) * a.slots + slot] = L;
       }
     }
   }
@@ -1328,20 +1572,43 @@ hipError_t go(const Plan& p, int R, const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NHT, bool SPLITQ, int QDT>
+hipError_t go_swa(int R, int head_groups, const AttnArgs& a, hipStream_t s) {
+  auto kern = k_swa_attn<NHT, SPLITQ, QDT>;
+  const size_t lds = sizeof(SmemSwa<NHT, SPLITQ>);
+  static bool configured = false;
+  if (!configured) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    configured = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(R, head_groups), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+// partial slots per (row, head): the key splits of the selected entries
+// plus one for the window; 1 means the only kernel writes the output
+int attn_slots(int R, int Hq, int q_dtype, int top_k, bool window) {
+  const int splits = top_k > 0 ? plan(R, Hq, q_dtype, top_k).splits : 0;
+  return splits + (window ? 1 : 0);
+}
+
 }  // namespace
 
-size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k) {
-  const Plan p = plan(R, Hq, q_dtype, top_k);
-  if (p.splits <= 1) return 0;
-  const size_t n = (size_t)R * Hq * p.splits;
+size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window) {
+  const int slots = attn_slots(R, Hq, q_dtype, top_k, window);
+  if (slots <= 1) return 0;
+  const size_t n = (size_t)R * Hq * slots;
   return ((n * kDim * 4 + 255) & ~size_t(255)) + 2 * ((n * 4 + 255) & ~size_t(255));
 }
 
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
                               const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
+                              const uint8_t* win, const int64_t* win_start, const int32_t* win_len,
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s) {
   if (R == 0) return hipSuccess;
-  const Plan p = plan(R, Hq, q_dtype, top_k);
+  const bool window = win != nullptr;
+  const Plan p = top_k > 0 ? plan(R, Hq, q_dtype, top_k) : Plan{};
   AttnArgs a{};
   a.q = q;
   a.Hq = Hq;
@@ -1355,10 +1622,13 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
   a.out = out;
   a.out_dtype = out_dtype;
   a.lse = lse;
-  a.splits = p.splits;
+  a.slots = attn_slots(R, Hq, q_dtype, top_k, window);
   a.keys_per_split = p.keys_per_split;
-  if (p.splits > 1) {
-    const size_t n = (size_t)R * Hq * p.splits;
+  a.win = win;
+  a.win_start = win_start;
+  a.win_len = win_len;
+  if (a.slots > 1) {
+    const size_t n = (size_t)R * Hq * a.slots;
     char* b = static_cast<char*>(ws);
     a.ws_o = reinterpret_cast<float*>(b);
     b += (n * kDim * 4 + 255) & ~size_t(255);
@@ -1366,35 +1636,49 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
     b += (n * 4 + 255) & ~size_t(255);
     a.ws_l = reinterpret_cast<float*>(b);
   }
-  auto& ev = profile_events(CSA2_KERNEL_ATTN);
-  if (ev.start) (void)hipEventRecord(ev.start, s);
-  hipError_t e;
-  if (p.wide) {
-    const size_t lds = sizeof(SmemWide);
-    static bool configured = false;
-    if (!configured) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_sparse_attn_wide),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      configured = true;
+  hipError_t e = hipSuccess;
+  if (top_k > 0) {
+    auto& ev = profile_events(CSA2_KERNEL_ATTN);
+    if (ev.start) (void)hipEventRecord(ev.start, s);
+    if (p.wide) {
+      const size_t lds = sizeof(SmemWide);
+      static bool configured = false;
+      if (!configured) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_sparse_attn_wide),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        configured = true;
+      }
+      hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.splits, R, p.head_groups), dim3(kThreads), lds, s, a);
+      e = hipGetLastError();
+    } else if (q_dtype == CSA2_BF16) {
+      // splits of at least two steps take the pipelined kernel (its first and last
+      // iterations run one role only, which a single step cannot amortize)
+      const bool pipelined = p.keys_per_split >= 2 * kStep;
+      if (p.nht == 2) e = pipelined ? go_pp<2, 2>(p, R, a, s) : go<2, false, CSA2_BF16>(p, R, a, s);
+      else e = pipelined ? go_pp<1, 2>(p, R, a, s) : go<1, false, CSA2_BF16>(p, R, a, s);
+    } else {
+      e = go<1, true, CSA2_F32>(p, R, a, s);
     }
-    hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.splits, R, p.head_groups), dim3(kThreads), lds, s, a);
-    e = hipGetLastError();
-  } else if (q_dtype == CSA2_BF16) {
-    // splits of at least two steps take the pipelined kernel (its first and last
-    // iterations run one role only, which a single step cannot amortize)
-    const bool pipelined = p.keys_per_split >= 2 * kStep;
-    if (p.nht == 2) e = pipelined ? go_pp<2, 2>(p, R, a, s) : go<2, false, CSA2_BF16>(p, R, a, s);
-    else e = pipelined ? go_pp<1, 2>(p, R, a, s) : go<1, false, CSA2_BF16>(p, R, a, s);
-  } else {
-    e = go<1, true, CSA2_F32>(p, R, a, s);
+    if (ev.stop) (void)hipEventRecord(ev.stop, s);
+    if (e != hipSuccess) return e;
   }
-  if (ev.stop) (void)hipEventRecord(ev.stop, s);
-  if (e != hipSuccess) return e;
-  if (p.splits > 1) {
+  if (window) {
+    // 64-head workgroups when rows alone fill the chip (bf16 queries), else 16
+    const int tiles = Hq / 16;
+    const bool wide = q_dtype == CSA2_BF16 && tiles % 4 == 0 && (int64_t)R * (tiles / 4) >= 256;
+    auto& ew = profile_events(CSA2_KERNEL_SWA_ATTN);
+    if (ew.start) (void)hipEventRecord(ew.start, s);
+    if (wide) e = go_swa<4, false, CSA2_BF16>(R, tiles / 4, a, s);
+    else if (q_dtype == CSA2_BF16) e = go_swa<1, false, CSA2_BF16>(R, tiles, a, s);
+    else e = go_swa<1, true, CSA2_F32>(R, tiles, a, s);
+    if (ew.stop) (void)hipEventRecord(ew.stop, s);
+    if (e != hipSuccess) return e;
+  }
+  if (a.slots > 1) {
     auto& ec = profile_events(CSA2_KERNEL_ATTN_COMBINE);
     if (ec.start) (void)hipEventRecord(ec.start, s);
     hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((int64_t)R * Hq)), dim3(128), 0, s, a.ws_o, a.ws_m, a.ws_l,
-                       p.splits, out, out_dtype, lse);
+                       a.slots, out, out_dtype, lse);
     if (ec.stop) (void)hipEventRecord(ec.stop, s);
     e = hipGetLastError();
   }

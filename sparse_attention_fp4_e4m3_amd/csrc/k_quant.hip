@@ -1,4 +1,5 @@
-// k_quant.hip -- quantize-on-write of 512-channel KV latents to FP4.
+// k_quant.hip -- quantize-on-write of 512-channel KV latents to FP4, and of
+// local-window latents to FP8.
 //
 // Cache format of "FP4 cache entries, and why they're safe" (course brief
 // "DeepSeek-V4.1-Flash"): E2M1 elements, one E4M3 scale per 16 channels, no
@@ -93,7 +94,66 @@ __global__ __launch_bounds__(256) void k_quant_fp4(const void* __restrict__ x, i
   scales[dst * kGroups + g] = (uint8_t)sb;
 }
 
+// Local-window entries: one signed E4M3 byte per channel (the brief's
+// "FP4 cache entries, and why they're safe" keeps the local sliding-window
+// cache in FP8; no scale is named, so values are stored as they are):
+// nearest value, ties to the even code, |x| > 448 saturating to 448, the
+// sign bit copied from x (a negative value that rounds to zero gives 0x80).
+// Same thread layout as k_quant_fp4; each lane writes 16 bytes.
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant_fp8(const void* __restrict__ x, int64_t n, int64_t stride,
+                                                   const int64_t* __restrict__ dst_rows, uint8_t* __restrict__ codes,
+                                                   int64_t cap) {
+  const int64_t tok = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int g = threadIdx.x & 31;
+  if (tok >= n) return;
+  const int64_t dst = dst_rows ? dst_rows[tok] : tok;
+  if (dst < 0 || dst >= cap) return;
+  uint32_t u[16];  // fp32 bits of the lane's 16 channels
+  if (DT == CSA2_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + tok * stride + g * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 t = p[i];
+      u[4 * i] = t.x; u[4 * i + 1] = t.y; u[4 * i + 2] = t.z; u[4 * i + 3] = t.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + tok * stride + g * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 t = p[i];
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u[8 * i + 2 * k] = w[k] << 16;
+        u[8 * i + 2 * k + 1] = w[k] & 0xFFFF0000u;
+      }
+    }
+  }
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t b = e4m3_code(__uint_as_float(u[i] & 0x7FFFFFFFu)) | ((u[i] >> 24) & 0x80u);
+    out[i >> 2] |= b << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint4*>(codes + dst * kDim + g * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
+                               uint8_t* codes, int64_t cap, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(n, 8)), block(256);
+  auto& ev = profile_events(CSA2_KERNEL_QUANT_FP8);
+  if (ev.start) (void)hipEventRecord(ev.start, s);
+  if (x_dtype == CSA2_F32)
+    hipLaunchKernelGGL(k_quant_fp8<CSA2_F32>, grid, block, 0, s, x, n, stride, dst_rows, codes, cap);
+  else
+    hipLaunchKernelGGL(k_quant_fp8<CSA2_BF16>, grid, block, 0, s, x, n, stride, dst_rows, codes, cap);
+  if (ev.stop) (void)hipEventRecord(ev.stop, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
                            uint8_t* codes, uint8_t* scales, int64_t cap, hipStream_t s) {

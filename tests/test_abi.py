@@ -112,10 +112,44 @@ def test_sparse_attn_rejects_bad_arguments():
     assert _attn(L, R=0) == 0
 
 
+def _swa(L, **kw):
+    f = ctypes.c_void_p(0x10000)
+    a = dict(R=2, q=f, qd=1, H=64, D=512, codes=f, scales=f, start=f, idx=f, K=256, vis=None, win=f, ws0=f, wl=f,
+             scale=0.1, out=f, od=0, lse=None, ws=f, wsb=1 << 30)
+    a.update(kw)
+    return L.csa2_sparse_attn_swa(a["R"], a["q"], a["qd"], a["H"], a["D"], a["codes"], a["scales"], a["start"],
+                                  a["idx"], a["K"], a["vis"], a["win"], a["ws0"], a["wl"], a["scale"], a["out"],
+                                  a["od"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_window_calls_reject_bad_arguments():
+    L = _L()
+    f = ctypes.c_void_p(0x10000)
+    assert _swa(L, D=576) == -2 and "head_dim" in _err()
+    assert _swa(L, H=40) == -1 and _swa(L, K=-1) == -1
+    assert _swa(L, win=None) == -1 and "null" in _err()
+    assert _swa(L, wl=None) == -1 and _swa(L, ws0=None) == -1
+    assert _swa(L, idx=None) == -1 and "top_k" in _err()
+    assert _swa(L, win=ctypes.c_void_p(0x10008)) == -1 and "aligned" in _err()
+    assert _swa(L, ws=None, wsb=0) == -3
+    assert _swa(L, R=0) == 0
+    # window only: the cache and index arguments are not needed
+    assert L.csa2_sparse_attn_swa_workspace_size(2, 64, 1, 0) == 0  # one slot: written directly
+    assert L.csa2_sparse_attn_swa_workspace_size(2, 64, 1, 256) > 0
+    assert L.csa2_sparse_attn_swa_workspace_size(4096, 64, 1, 2048) > L.csa2_sparse_attn_workspace_size(4096, 64, 1, 2048)
+    assert L.csa2_quantize_swa_fp8(f, 7, 4, 512, None, f, 10, None) == -1 and "dtype" in _err()
+    assert L.csa2_quantize_swa_fp8(None, 0, 4, 512, None, f, 10, None) == -1 and "null" in _err()
+    assert L.csa2_quantize_swa_fp8(f, 0, 4, 100, None, f, 10, None) == -1 and "stride" in _err()
+    assert L.csa2_quantize_swa_fp8(f, 0, 40, 512, None, f, 10, None) == -1 and "cap_rows" in _err()
+    assert L.csa2_quantize_swa_fp8(f, 0, 4, 512, None, ctypes.c_void_p(0x10004), 10, None) == -1
+    assert L.csa2_quantize_swa_fp8(None, 0, 0, 512, None, None, 10, None) == 0
+
+
 def test_profile_hook_ids():
     L = _L()
     assert L.csa2_profile_kernel_events(99, None, None) == -1
     assert L.csa2_profile_kernel_events(2, None, None) == 0
+    assert L.csa2_profile_kernel_events(7, None, None) == 0 and L.csa2_profile_kernel_events(8, None, None) == -1
 
 
 def test_layer_mode_rules():
