@@ -16,6 +16,11 @@ measurement hook), and the CPU oracle timed on a bounded sample.
 The prefill workload (c4) times one 4,096-token chunk appended causally to a
 262,144-token cache: quantize-on-write of the chunk, the Full indexer and
 exact top-K for each of its rows, and sparse attention for each row.
+
+--swa adds the local branch to every layer: each layer keeps its own FP8
+window of the 128 most recent tokens (a ring of 128 rows per sequence in
+decode, the chunk's band in prefill), writes the step's tokens into it and
+attends over it joined with its selected entries in one softmax.
 """
 from __future__ import annotations
 
@@ -107,6 +112,51 @@ def build_prefill(w, device, chunk=65536):
     return cache, qs, iqs, new_kv, new_rows, (P0 + 1 + np.arange(T)).astype(np.int64)
 
 
+def build_windows(w, lens, device):
+    """Each layer's FP8 window, filled with the 128 tokens before the timed step's own.
+
+    Decode: a ring of 128 rows per sequence (row = position mod 128); the step
+    writes each sequence's newest token.  Prefill: rows i <-> positions
+    P0 - 127 + i; the step writes the chunk's T tokens at rows 127.., and
+    chunk row r attends over rows r .. r + 127.
+    Returns (windows, new_win per layer, new_win_rows)."""
+    import torch
+
+    from sparse_attention_fp4_e4m3_amd import Window, csa2
+
+    W = 128
+    wins, new = [], []
+    if w.is_prefill:
+        T = w.prefill_tokens
+        P0 = w.n - T
+        rows = torch.from_numpy(np.arange(W - 1, W - 1 + T, dtype=np.int64)).to(device)
+        for li in range(len(w.layers)):
+            codes = torch.empty(W - 1 + T, 512, dtype=torch.uint8, device=device)
+            csa2.quantize_swa_fp8(torch.from_numpy(gen.window_rows(w, li, 0, P0 - (W - 1), P0)).to(device),
+                                  codes[:W - 1])
+            wins.append(Window(codes, torch.arange(T, dtype=torch.int64, device=device),
+                               torch.full((T,), W, dtype=torch.int32, device=device)))
+            new.append(torch.from_numpy(gen.window_rows(w, li, 0, P0, w.n)).to(device))
+        torch.cuda.synchronize()
+        return wins, new, rows
+    B = len(lens)
+    ring = lambda b, t: b * W + t % W  # noqa: E731
+    rows = torch.from_numpy(np.array([ring(b, int(lens[b]) - 1) for b in range(B)], np.int64)).to(device)
+    for li in range(len(w.layers)):
+        codes = torch.zeros(B * W, 512, dtype=torch.uint8, device=device)
+        for b in range(B):
+            n = int(lens[b])
+            t0 = max(0, n - W)
+            dst = torch.from_numpy(np.array([ring(b, t) for t in range(t0, n)], np.int64)).to(device)
+            csa2.quantize_swa_fp8(torch.from_numpy(gen.window_rows(w, li, b, t0, n)).to(device), codes, dst)
+        wins.append(Window(codes, torch.from_numpy(np.arange(B, dtype=np.int64) * W).to(device),
+                           torch.from_numpy(np.minimum(lens, W).astype(np.int32)).to(device)))
+        new.append(torch.from_numpy(np.concatenate([gen.window_rows(w, li, b, int(lens[b]) - 1, int(lens[b]))
+                                                    for b in range(B)])).to(device))
+    torch.cuda.synchronize()
+    return wins, new, rows
+
+
 def to_dev(a, kind, device):
     import torch
 
@@ -176,9 +226,27 @@ def index_flops(w, lens):
     return 2.0 * float(np.sum(lens)) * w.H * 64
 
 
-def cpu_baseline_prefill(w, sample_rows):
+def oracle_window(w, li, b, t_end):
+    """Signed E4M3 codes of layer li's window ending before position t_end (at most 128 tokens)."""
+    import oracle
+
+    return oracle.e4m3_encode_signed(gen.window_rows(w, li, b, max(0, t_end - 128), t_end, threads=False))
+
+
+def oracle_attend(w, q, codes, scales, sel, nvis, win):
+    """The oracle's attention of one row, joined with its window when one is given."""
+    import oracle
+
+    if win is None:
+        return oracle.attention(q, codes, scales, sel, nvis, w.softmax_scale)
+    z = np.zeros(1, np.int64)
+    return oracle.attention_rows_swa(q[None], codes, scales, z, sel[None], np.array([nvis]), win, z,
+                                     np.array([win.shape[0]], np.int32), w.softmax_scale)
+
+
+def cpu_baseline_prefill(w, sample_rows, swa=False):
     """The CPU oracle on `sample_rows` rows of the prefill chunk: indexer scan over the row's visible
-    entries, exact top-K and attention."""
+    entries, exact top-K and attention (joined with the row's window under swa)."""
     import oracle
 
     T = w.prefill_tokens
@@ -189,11 +257,12 @@ def cpu_baseline_prefill(w, sample_rows):
     ik = gen.idx_k_rows(w, 0, 0, w.n)
     iq = gen.index_q(w, 0)
     q = gen.attn_q(w, 0)
+    wins = {r: oracle_window(w, 0, 0, P0 + r + 1) for r in rows} if swa else {}
     t0 = time.perf_counter()
     for r in rows:
         nvis = P0 + r + 1
         sel = oracle.topk(oracle.index_scores(iq[r], ik[:nvis]), w.K)
-        oracle.attention(q[r], codes, scales, sel, nvis, w.softmax_scale)
+        oracle_attend(w, q[r], codes, scales, sel, nvis, wins.get(r))
     dt = time.perf_counter() - t0
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%d of %d chunk rows (indexer scan over ~%d entries, top-K, attention each); %.1f s wall"
@@ -219,8 +288,9 @@ def traffic_from_profiles(workload, kernel_file):
 
 # ------------------------------------------------------------------ CPU oracle baseline
 
-def cpu_baseline(w, lens, sample_rows, reps):
-    """`reps` decode steps of the same chain for `sample_rows` sequences, run by the CPU oracle."""
+def cpu_baseline(w, lens, sample_rows, reps, swa=False):
+    """`reps` decode steps of the same chain for `sample_rows` sequences, run by the CPU oracle
+    (every layer joined with its window under swa)."""
     import oracle
 
     rows = list(range(min(sample_rows, w.B)))
@@ -233,6 +303,7 @@ def cpu_baseline(w, lens, sample_rows, reps):
     qs = [gen.attn_q(w, li, 0, len(rows)) for li in range(len(w.layers))]
     iqs = [gen.index_q(w, li, 0, len(rows)) if L.mode != "reuse" else None for li, L in enumerate(w.layers)]
     new_kv = [gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b])) for b in rows]
+    wins = {(li, b): oracle_window(w, li, b, int(lens[b])) for li in range(len(w.layers)) for b in rows} if swa else {}
     t0 = time.perf_counter()
     for b in [b for _ in range(reps) for b in rows]:
         (codes, scales), ik = caches[b]
@@ -246,7 +317,7 @@ def cpu_baseline(w, lens, sample_rows, reps):
                 sel, pool, _ = oracle.full_select(iqs[li][b], ik, n, w.K, L.pool_size)
             elif L.mode == "reindex":
                 sel = oracle.reindex_select(iqs[li][b], ik, pool, n, w.K)
-            oracle.attention(qs[li][b], codes, scales, sel, n, w.softmax_scale)
+            oracle_attend(w, qs[li][b], codes, scales, sel, n, wins.get((li, b)))
     dt = time.perf_counter() - t0
     return {"value": reps * len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%d of %d sequences x %d repetitions of one full decode step of the %d-layer chain (quantize "
@@ -326,6 +397,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=16)
     ap.add_argument("--cpu-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--swa", action="store_true",
+                    help="every layer also attends over its own 128-token FP8 window (local branch)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
     ap.add_argument("--event-kind", default="nofence", choices=["nofence", "torch"],
                     help="per-kernel timing events: created without a system fence, or torch's default")
@@ -356,11 +429,16 @@ def main():
                                                   for b in range(w.B)])).to(device)
         new_rows_t = torch.from_numpy(new_rows.astype(np.int64)).to(device)
     log("inputs built in %.1f s (%d cache rows)" % (time.time() - t, int(cache.kv_codes.shape[0])))
+    wins = new_win = new_win_rows = None
+    if args.swa:
+        wins, new_win, new_win_rows = build_windows(w, lens, device)
+        log("windows built: %d layers x %d rows" % (len(wins), int(wins[0].codes.shape[0])))
     chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.rows, w.Hq, w.H, w.K, cache.max_visible,
-                       qs[0].dtype, device, shared_segment=cache.shared_segment)
+                       qs[0].dtype, device, shared_segment=cache.shared_segment, swa=args.swa)
 
     def step():
-        chain.step(cache, qs, iqs, w.softmax_scale, new_kv=new_kv, new_kv_rows=new_rows_t)
+        chain.step(cache, qs, iqs, w.softmax_scale, new_kv=new_kv, new_kv_rows=new_rows_t, windows=wins,
+                   new_win=new_win, new_win_rows=new_win_rows)
 
     if args.calib_copy_mib:
         a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=device)
@@ -409,6 +487,9 @@ def main():
     n_launch = {"index_scan": 1, "quantize": 1,
                 "reindex_score": sum(L.mode == "reindex" for L in w.layers),
                 "attention": len(w.layers), "attention_combine": len(w.layers)}
+    if args.swa:
+        kernels.update({"swa_attention": csa2.KERNEL_SWA_ATTN, "quantize_fp8": csa2.KERNEL_QUANT_FP8})
+        n_launch.update({"swa_attention": len(w.layers), "quantize_fp8": len(w.layers)})
 
     def arm(kid):
         if args.event_kind == "torch":
@@ -434,6 +515,7 @@ def main():
         vals = [p[k][0].elapsed_time(p[k][1]) * 1e3 for p in pairs]
         per_kernel_us[k] = float(np.mean(vals))
 
+    wname = w.name + ("+swa" if args.swa else "")
     byt = algorithmic_bytes(w, lens)
     attn_flops = attention_flops(w)
     kern = {
@@ -445,13 +527,19 @@ def main():
         "attention_combine": {"avg_us": per_kernel_us["attention_combine"]},
         "quantize": {"avg_us": per_kernel_us["quantize"], "bytes": byt["quantize"]},
     }
+    if args.swa:
+        # the window: 128 entries x 512 B per row; QK^T and PV over them for every head
+        kern["swa_attention"] = {"avg_us": per_kernel_us["swa_attention"], "bytes": w.rows * 128 * 512,
+                                 "flops": 4.0 * w.rows * w.Hq * 128 * 512}
+        kern["quantize_fp8"] = {"avg_us": per_kernel_us["quantize_fp8"],
+                                "bytes": (w.prefill_tokens or w.B) * (512 * 4 + 512)}
     for k, v in kern.items():
         if "bytes" in v and v["avg_us"] > 0:
             v["GBps"] = v["bytes"] / (v["avg_us"] * 1e3)
             v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
         if "flops" in v and v["avg_us"] > 0:
             v["TFLOPs"] = v["flops"] / (v["avg_us"] * 1e6)
-            if k == "attention":
+            if k in ("attention", "swa_attention"):
                 v["mfma_frac"] = v["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
             else:
                 v["valu_fp32_frac"] = v["TFLOPs"] / VALU_F32_PEAK_TFLOPS
@@ -461,16 +549,16 @@ def main():
     if dominant == "attention":
         roof = {"kernel": attention_kernel_name(w), "bound": "mfma", "achieved": dk["TFLOPs"],
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": dk["mfma_frac"],
-                "traffic": traffic_from_profiles(w.name, "k_attn.hip")}
+                "traffic": traffic_from_profiles(wname, "k_attn.hip")}
     elif dominant == "index_scan" and w.is_prefill:
         # the chunk's rows share one key segment: the scores are a bf16 MFMA product (two passes)
         roof = {"kernel": "k_pf_pass", "bound": "mfma", "achieved": dk["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": dk["TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
-                "traffic": traffic_from_profiles(w.name, "k_index.hip")}
+                "traffic": traffic_from_profiles(wname, "k_index.hip")}
     else:
         roof = {"kernel": "k_scan_full" if dominant == "index_scan" else "k_score_pool", "bound": "hbm",
                 "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["hbm_frac"],
-                "traffic": traffic_from_profiles(w.name, "k_index.hip")}
+                "traffic": traffic_from_profiles(wname, "k_index.hip")}
 
     tokens_s = w.rows / (ms_step * 1e-3)
     res = {
@@ -486,19 +574,21 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: %s" % (w.name, w.description), "batch": w.B, "rows": w.rows,
+        "config": {"workload": "%s: %s" % (wname, w.description + (" + local 128-token FP8 window" if args.swa else "")), "batch": w.B, "rows": w.rows,
                    "ctx": int(lens.max()),
                    "layers": [L.mode for L in w.layers], "top_k": w.K, "q_heads": w.Hq, "indexer_heads": w.H,
                    "kv": "fp4 e2m1 + e4m3 scale per 16 ch (288 B/entry)",
                    "compute": "indexer fp32 fmaf; attention f16 MFMA, f32 accumulate", "parallelism": "single GPU",
-                   "launch": "eager" if graph is None else "hip graph replay of one step"},
+                   "launch": "eager" if graph is None else "hip graph replay of one step",
+                   "local_window": "128-token FP8 (E4M3) window per layer, joined in one softmax" if args.swa
+                   else "none"},
         "roofline": roof,
         "kernels": kern,
     }
     res["chain_hbm_GBps"] = byt["total"] / (ms_step * 1e-3) / 1e9
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = (cpu_baseline_prefill(w, max(args.cpu_rows, 128)) if w.is_prefill
-                               else cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps))
+        res["cpu_baseline"] = (cpu_baseline_prefill(w, max(args.cpu_rows, 128), args.swa) if w.is_prefill
+                               else cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps, args.swa))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

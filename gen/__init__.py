@@ -1,7 +1,7 @@
 """Seeded synthetic inputs shared by the CPU oracle and the GPU path.
 
 This package holds random-number plumbing only: it draws the raw values the
-method consumes (KV latents, indexer keys and queries, attention queries,
+method consumes (KV latents, local-window latents, indexer keys and queries, attention queries,
 sequence lengths) and rounds them to the storage dtype a workload names.  It
 contains none of the method's arithmetic (no quantization, scoring,
 selection or attention).
@@ -14,6 +14,7 @@ from .workloads import (  # noqa: F401
     bf16_round,
     bf16_bits,
     kv_rows,
+    window_rows,
     idx_k_rows,
     attn_q,
     index_q,

@@ -42,7 +42,7 @@ CHUNK = 4096  # tokens per generator chunk
 # stream tags of the seed sequence
 _T_KV, _T_IK, _T_WTOT_KV, _T_WTOT_IK, _T_WKV, _T_WIK = 1, 2, 3, 4, 5, 6
 _T_LEN, _T_OUTLIER = 7, 8
-_T_Q, _T_IQ = 100, 200
+_T_Q, _T_IQ, _T_WIN = 100, 200, 300
 
 _POOL = None
 
@@ -224,6 +224,22 @@ def kv_rows(w: Workload, b: int, t0: int, t1: int, threads: bool = True) -> np.n
 def idx_k_rows(w: Workload, b: int, t0: int, t1: int, threads: bool = True) -> np.ndarray:
     """Indexer keys of tokens [t0, t1) of sequence b: fp32 [t1-t0, 64] (bf16-exact if bf16)."""
     return _rows(w, _ik_chunk, b, t0, t1, D_I, threads)
+
+
+def _win_chunk(w: Workload, layer: int, b: int, chunk: int) -> np.ndarray:
+    x = _rng(w.seed, _T_WIN + layer, b, chunk).standard_normal((CHUNK, D), dtype=np.float32)
+    if w.outlier_channels:
+        x[:, _outlier_channels(w)] *= np.float32(w.outlier_gain)
+    return x
+
+
+def window_rows(w: Workload, layer: int, b: int, t0: int, t1: int, threads: bool = True) -> np.ndarray:
+    """Local sliding-window latents of one layer, tokens [t0, t1) of sequence b: fp32 [t1-t0, 512].
+
+    Each layer has its own window (its own hidden state), drawn like the
+    KV latents (N(0, 1), the same outlier channels) from its own stream.
+    """
+    return _rows(w, lambda w_, b_, c: _win_chunk(w_, layer, b_, c), b, t0, t1, D, threads)
 
 
 def attn_q(w: Workload, layer: int, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:

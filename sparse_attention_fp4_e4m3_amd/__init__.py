@@ -15,7 +15,10 @@ from .csa2 import (  # noqa: F401
     index_topk,
     index_topk_workspace_size,
     quantize_kv_fp4,
+    quantize_swa_fp8,
     sparse_attn,
+    sparse_attn_swa,
+    sparse_attn_swa_workspace_size,
     sparse_attn_workspace_size,
 )
-from .chain import Cache, LayerChain, LayerSpec, validate_modes  # noqa: F401
+from .chain import Cache, LayerChain, LayerSpec, Window, validate_modes  # noqa: F401

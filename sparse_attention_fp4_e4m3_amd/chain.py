@@ -10,7 +10,11 @@ Full because there is nothing to reuse yet).  Rules enforced here:
 * Reindex re-scores the candidate pool of the most recent Full layer with
   its own indexer query, so that Full layer must emit a pool;
 * Reuse takes the selection of the most recent Full or Reindex layer;
-* every layer attends with its own query.
+* every layer attends with its own query;
+* with local windows, every layer also attends over its own FP8 window of
+  the most recent tokens, joined to its selected entries in one softmax
+  ("The Paper" in the talk write-up; "Two attention paths in every layer"
+  in the course brief).
 
 The driver only sequences the three library calls on one stream; all
 arithmetic happens in libcsa2.so.
@@ -35,6 +39,14 @@ class Cache:
     row_visible: torch.Tensor   # [R] int32
     max_visible: int
     shared_segment: bool = False  # every row reads the segment at row_kv_start[0] (a prefill chunk)
+
+
+@dataclass
+class Window:
+    """One layer's local window cache (device tensors): FP8 entries and each row's window."""
+    codes: torch.Tensor         # [rows, 512] uint8, signed E4M3 per channel
+    row_start: torch.Tensor     # [R] int64 first window entry of each query row
+    row_len: torch.Tensor       # [R] int32 window entries of each query row (<= 128)
 
 
 @dataclass(frozen=True)
@@ -71,8 +83,9 @@ class LayerChain:
 
     def __init__(self, layers: Sequence[LayerSpec], n_rows: int, n_heads: int, idx_heads: int, top_k: int,
                  max_visible: int, q_dtype: torch.dtype, device="cuda", out_dtype=torch.float32,
-                 shared_segment: bool = False):
+                 shared_segment: bool = False, swa: bool = False):
         validate_modes(layers)
+        self.swa = swa
         self.layers = list(layers)
         self.full_mode = csa2.FULL_SHARED if shared_segment else csa2.FULL
         self.R, self.Hq, self.H, self.K = n_rows, n_heads, idx_heads, top_k
@@ -95,16 +108,23 @@ class LayerChain:
                 ws = max(ws, csa2.index_topk_workspace_size(csa2.REINDEX, n_rows, idx_heads, max_visible,
                                                             last_pool, top_k, 0))
         qdt = csa2.F32 if q_dtype == torch.float32 else csa2.BF16
-        aws = csa2.sparse_attn_workspace_size(n_rows, n_heads, qdt, top_k)
+        aws = (csa2.sparse_attn_swa_workspace_size if swa else csa2.sparse_attn_workspace_size)(n_rows, n_heads, qdt,
+                                                                                                top_k)
         self.ws_index = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(max(aws, 256), dtype=torch.uint8, device=dev)
         self.out = [torch.empty(n_rows, n_heads, 512, dtype=out_dtype, device=dev) for _ in self.layers]
         self.lse = [torch.empty(n_rows, n_heads, dtype=torch.float32, device=dev) for _ in self.layers]
 
     def step(self, cache: Cache, q: List[torch.Tensor], idx_q: List[Optional[torch.Tensor]], softmax_scale: float,
-             new_kv: Optional[torch.Tensor] = None, new_kv_rows: Optional[torch.Tensor] = None, stream=None):
+             new_kv: Optional[torch.Tensor] = None, new_kv_rows: Optional[torch.Tensor] = None,
+             windows: Optional[List[Window]] = None, new_win: Optional[List[torch.Tensor]] = None,
+             new_win_rows: Optional[torch.Tensor] = None, stream=None):
         """One pass of every layer.  q[l]: [R, Hq, 512]; idx_q[l]: [R, H, 64] for Full/Reindex layers.
-        new_kv/new_kv_rows: tokens the first Full layer writes into the cache before indexing."""
+        new_kv/new_kv_rows: tokens the first Full layer writes into the cache before indexing.
+        windows[l] (chains built with swa=True): layer l's window; new_win[l]/new_win_rows: the
+        tokens layer l writes into its window before attending."""
+        if self.swa != (windows is not None):
+            raise ValueError("windows must be given exactly when the chain was built with swa=True")
         last_full_pool = None
         last_sel = None
         for i, L in enumerate(self.layers):
@@ -123,7 +143,16 @@ class LayerChain:
                                 cache.max_visible, self.K, self.idx[i], self.ws_index, pool=pool, pool_len=plen,
                                 stream=stream)
                 last_sel = self.idx[i]
-            csa2.sparse_attn(q[i], cache.kv_codes, cache.kv_scales, cache.row_kv_start, last_sel, self.out[i],
-                             softmax_scale, row_visible=cache.row_visible, lse=self.lse[i], workspace=self.ws_attn,
-                             stream=stream)
+            if windows is None:
+                csa2.sparse_attn(q[i], cache.kv_codes, cache.kv_scales, cache.row_kv_start, last_sel, self.out[i],
+                                 softmax_scale, row_visible=cache.row_visible, lse=self.lse[i],
+                                 workspace=self.ws_attn, stream=stream)
+                continue
+            win = windows[i]
+            if new_win is not None:
+                csa2.quantize_swa_fp8(new_win[i], win.codes, new_win_rows, stream=stream)
+            csa2.sparse_attn_swa(q[i], win.codes, win.row_start, win.row_len, self.out[i], softmax_scale,
+                                 kv_codes=cache.kv_codes, kv_scales=cache.kv_scales, row_kv_start=cache.row_kv_start,
+                                 idx=last_sel, row_visible=cache.row_visible, lse=self.lse[i],
+                                 workspace=self.ws_attn, stream=stream)
         return self.out

@@ -8,7 +8,7 @@ import torch
 import gen
 import oracle
 from gpu_util import DEV, check_attention, dev, say
-from sparse_attention_fp4_e4m3_amd import Cache, LayerChain, LayerSpec, csa2
+from sparse_attention_fp4_e4m3_amd import Cache, LayerChain, LayerSpec, Window, csa2
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +20,10 @@ def _to_dev(a, kind):
 
 
 def _setup(w):
-    lens = gen.seq_lens(w)
+    return _setup_lens(w, gen.seq_lens(w))
+
+
+def _setup_lens(w, lens):
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
     raw = [gen.kv_rows(w, b, 0, int(lens[b])) for b in range(w.B)]
     ik = [gen.idx_k_rows(w, b, 0, int(lens[b])) for b in range(w.B)]
@@ -103,17 +106,71 @@ def test_long_decode_drift_scaled():
     say("max err %.3e" % _run_and_compare(w))
 
 
-def test_graph_replay_matches_eager():
+def _windows(w, lens):
+    """Each layer's ring of 128 window rows per sequence (row = position mod 128) holding the
+    sequence's last min(n, 128) tokens, written by the FP8 quantize call; plus the newest
+    token of every sequence per layer and its ring row (what a decode step writes)."""
+    wins, new = [], []
+    B = w.B
+    new_rows = dev(np.array([b * 128 + (int(lens[b]) - 1) % 128 for b in range(B)], np.int64))
+    for li in range(len(w.layers)):
+        codes = torch.zeros(B * 128, 512, dtype=torch.uint8, device=DEV)
+        for b in range(B):
+            n = int(lens[b])
+            t0 = max(0, n - 128)
+            dst = dev(np.array([b * 128 + t % 128 for t in range(t0, n)], np.int64))
+            csa2.quantize_swa_fp8(torch.from_numpy(gen.window_rows(w, li, b, t0, n)).to(DEV), codes, dst)
+        wins.append(Window(codes, dev(np.arange(B, dtype=np.int64) * 128), dev(np.minimum(lens, 128).astype(np.int32))))
+        new.append(torch.from_numpy(np.concatenate([gen.window_rows(w, li, b, int(lens[b]) - 1, int(lens[b]))
+                                                    for b in range(B)])).to(DEV))
+    return wins, new, new_rows
+
+
+def test_chain_with_local_windows_scaled():
+    """Every layer of the 128K chain's structure joined with its own FP8 window, at oracle size,
+    one layer's window shorter than 128 (a sequence of 100 tokens)."""
+    w = gen.get("c3").scaled(B=3, n=24001, K=512, layers=(gen.Layer("full", 2048), gen.Layer("reindex"),
+                                                         gen.Layer("reuse")), len_range=(100, 24001))
+    lens = gen.seq_lens(w)
+    lens[0] = 100  # first sequence: a window of 100 tokens
+    lens, starts, raw, ik, cache, qs, iqs = _setup_lens(w, lens)
+    wins, new_win, new_win_rows = _windows(w, lens)
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, cache.max_visible,
+                       qs[0].dtype, DEV, swa=True)
+    chain.step(cache, qs, iqs, w.softmax_scale, windows=wins, new_win=new_win, new_win_rows=new_win_rows)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b in range(w.B):
+        oc, os_, ref = _oracle_chain(w, lens, raw, ik, b)
+        n = int(lens[b])
+        for li, (sel, pool, o, lse) in enumerate(ref):
+            wc = oracle.e4m3_encode_signed(gen.window_rows(w, li, b, max(0, n - 128), n))
+            ring = wins[li].codes[b * 128:b * 128 + 128].cpu().numpy()
+            assert np.array_equal(ring[[t % 128 for t in range(max(0, n - 128), n)]], wc), "window codes"
+            z = np.zeros(1, np.int64)
+            o2, lse2 = oracle.attention_rows_swa(gen.attn_q(w, li, b, b + 1), oc, os_, z, sel[None], np.array([n]),
+                                                 wc, z, np.array([len(wc)], np.int32), w.softmax_scale)
+            worst = max(worst, check_attention(chain.out[li][b:b + 1], chain.lse[li][b:b + 1], o2, lse2,
+                                               "swa chain layer %d seq %d" % (li, b)))
+    say("max err %.3e" % worst)
+
+
+@pytest.mark.parametrize("swa", [False, True])
+def test_graph_replay_matches_eager(swa):
     w = gen.get("c3").scaled(B=4, n=30000, K=512, layers=(gen.Layer("full", 2048), gen.Layer("reindex"),
                                                          gen.Layer("reuse")))
     lens, starts, raw, ik, cache, qs, iqs = _setup(w)
     chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, cache.max_visible,
-                       qs[0].dtype, DEV)
+                       qs[0].dtype, DEV, swa=swa)
     new_rows = dev((starts + lens - 1).astype(np.int64))
     new_kv = torch.from_numpy(np.stack([r[-1] for r in raw])).to(DEV)
+    wins = new_win = new_win_rows = None
+    if swa:
+        wins, new_win, new_win_rows = _windows(w, lens)
 
     def step():
-        chain.step(cache, qs, iqs, w.softmax_scale, new_kv=new_kv, new_kv_rows=new_rows)
+        chain.step(cache, qs, iqs, w.softmax_scale, new_kv=new_kv, new_kv_rows=new_rows, windows=wins,
+                   new_win=new_win, new_win_rows=new_win_rows)
 
     step()
     torch.cuda.synchronize()
