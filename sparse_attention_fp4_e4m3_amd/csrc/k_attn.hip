@@ -58,6 +58,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;        // log2 headroom before the reference maximum moves
 constexpr int kWinMax = 128;         // local window entries per row
+constexpr int kWStride = 520;        // bytes per staged window entry: entries 8 apart land 16 banks apart
 
 __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ half2v bits_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
@@ -171,6 +172,11 @@ __device__ __forceinline__ float rows_sum(float x) {
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// byte permute: bytes of {hi:lo} picked by the four selector bytes (0..3 = lo, 4..7 = hi)
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
 struct Raw {
@@ -935,8 +941,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_pp(AttnArgs a) {
 // no key halves, each wave writes its own channels at the end.
 struct SmemWide {
   _Float16 q[64 * kQStride];
-  uint8_t cs[(kStep / 32) * kCsBlock];
-  _Float16 sct[kGroups * kScStride];
+  union {
+    struct {
+      uint8_t cs[(kStep / 32) * kCsBlock];
+      _Float16 sct[kGroups * kScStride];
+    } f;                            // FP4 steps: staged codes and scales
+    uint8_t wc[kWinMax * kWStride];  // the window step: staged FP8 entries
+  } u;
   _Float16 p[64 * kPStride];
   float red_max[kWaves][64];
   float red_sum[kWaves][64];
@@ -1053,11 +1064,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
     }
     lds_barrier();  // B1: maxima visible; every wave is past the previous PV
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&sm.cs[cs_off(myslot) + 64 * q4 + 16 * c]) = cur.c[c];
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&sm.u.f.cs[cs_off(myslot) + 64 * q4 + 16 * c]) = cur.c[c];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      sm.sct[(8 * q4 + 2 * g) * kScStride + myslot] = sc[g][0];
-      sm.sct[(8 * q4 + 2 * g + 1) * kScStride + myslot] = sc[g][1];
+      sm.u.f.sct[(8 * q4 + 2 * g) * kScStride + myslot] = sc[g][0];
+      sm.u.f.sct[(8 * q4 + 2 * g + 1) * kScStride + myslot] = sc[g][1];
     }
     float alpha[NHT];
 #pragma unroll
@@ -1120,8 +1131,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
       const int key0 = 32 * kk + 8 * q4;
       uint32_t W[8];  // the 4 code nibbles (channels 64w + 4*n16 .. +3) of each key
 #pragma unroll
-      for (int k = 0; k < 8; ++k) W[k] = *reinterpret_cast<const uint16_t*>(&sm.cs[cs_off(key0 + k) + cb]);
-      const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.sct[grp * kScStride + key0]);
+      for (int k = 0; k < 8; ++k) W[k] = *reinterpret_cast<const uint16_t*>(&sm.u.f.cs[cs_off(key0 + k) + cb]);
+      const u32x4 spw = *reinterpret_cast<const u32x4*>(&sm.u.f.sct[grp * kScStride + key0]);
       // bytes of E: channel 0 of keys (0,1), channel 2 of keys (0,1), channel 0 of keys (2,3),
       // channel 2 of keys (2,3) (first two key pairs; the second word the next two); D: channels 1, 3
       uint32_t E[2], D[2];
@@ -1154,6 +1165,134 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
   for (int st = 0; st < nsteps; st += 2) {
     step(st, bufA, vA, bufB, vB);
     if (st + 1 < nsteps) step(st + 1, bufB, vB, bufA, vA);
+  }
+
+  // ---- the row's local window as one more step (FP8 entries, no gather, no scales): lane
+  // loads bytes [128 q4, +128) of entry `myslot`, converts them for QK^T, stages them for PV
+  // (the staging area of the FP4 steps, free once every wave is past their PV), and PV
+  // transposes each lane's 4-byte channel pieces of 8 entries with byte permutes.
+  if (a.win) {
+    const int len = min(max(a.win_len[r], 0), kWinMax);
+    u32x4 c[8];
+    if (myslot < len) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.win + (a.win_start[r] + myslot) * kDim + 128 * q4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = src[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    floatx4 S[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) S[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const uint32_t w0 = c[ks >> 1][2 * (ks & 1)], w1 = c[ks >> 1][2 * (ks & 1) + 1];
+      const half8 av = cat4(e4m3x2_to_h2<false>(w0), e4m3x2_to_h2<true>(w0), e4m3x2_to_h2<false>(w1),
+                            e4m3x2_to_h2<true>(w1));
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+        S[ht] = mfma(av, *reinterpret_cast<const half8*>(&sm.q[(16 * ht + n16) * kQStride + 128 * q4 + 8 * ks]),
+                     S[ht]);
+    }
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float z = (16 * w + 4 * q4 + i < len) ? S[ht][i] * a.c2 : -INFINITY;
+        S[ht][i] = z;
+        mx = fmaxf(mx, z);
+      }
+      mx = rows_max(mx);
+      if (q4 == 0) sm.red_max[w][16 * ht + n16] = mx;
+    }
+    lds_barrier();  // maxima visible; every wave is past the last FP4 PV
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sm.u.wc[myslot * kWStride + 128 * q4 + 16 * i]) = c[i];
+    float alpha[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      float mstep = sm.red_max[0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) mstep = fmaxf(mstep, sm.red_max[ww][h]);
+      const float mnew = (mstep > mref[ht] + kLazy) ? mstep : mref[ht];
+      const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+      alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
+      mref[ht] = mnew;
+      _Float16 pv[4];
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
+        sum += (float)pv[i];
+      }
+      *reinterpret_cast<u32x2*>(&sm.p[h * kPStride + 16 * w + 4 * q4]) =
+          u32x2{h2_bits(half2v{pv[0], pv[1]}), h2_bits(half2v{pv[2], pv[3]})};
+      sum = rows_sum(sum);
+      if (q4 == 0) {
+        sm.red_sum[w][h] = sum;
+        if (w == 0) sm.alpha[h] = alpha[ht];
+      }
+    }
+    lds_barrier();  // probabilities, sums, alpha and staged entries visible
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = 16 * ht + n16;
+      float add = sm.red_sum[0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) add += sm.red_sum[ww][h];
+      lrun[ht] = lrun[ht] * alpha[ht] + add;
+    }
+    {
+      float al[NHT][4];
+      bool moved = false;
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          al[ht][i] = sm.alpha[16 * ht + 4 * q4 + i];
+          moved |= al[ht][i] != 1.0f;
+        }
+      if (__ballot(moved)) {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) O[ht][t][i] *= al[ht][i];
+      }
+    }
+    const int cw = 64 * w + 4 * n16;  // this lane's 4 PV channels
+    const int kk_end = (len + 31) >> 5;
+    for (int kk = 0; kk < kk_end; ++kk) {
+      const int e0 = 32 * kk + 8 * q4;
+      uint32_t W[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) W[k] = *reinterpret_cast<const uint32_t*>(&sm.u.wc[(e0 + k) * kWStride + cw]);
+      uint32_t T[2][4];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t a01 = perm(W[4 * g + 1], W[4 * g], 0x05010400u), b01 = perm(W[4 * g + 1], W[4 * g], 0x07030602u);
+        const uint32_t a23 = perm(W[4 * g + 3], W[4 * g + 2], 0x05010400u),
+                       b23 = perm(W[4 * g + 3], W[4 * g + 2], 0x07030602u);
+        T[g][0] = perm(a23, a01, 0x05040100u);
+        T[g][1] = perm(a23, a01, 0x07060302u);
+        T[g][2] = perm(b23, b01, 0x05040100u);
+        T[g][3] = perm(b23, b01, 0x07060302u);
+      }
+      half8 av[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) av[ht] = *reinterpret_cast<const half8*>(&sm.p[(16 * ht + n16) * kPStride + e0]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const half8 b = cat4(e4m3x2_to_h2<false>(T[0][t]), e4m3x2_to_h2<true>(T[0][t]), e4m3x2_to_h2<false>(T[1][t]),
+                             e4m3x2_to_h2<true>(T[1][t]));
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) O[ht][t] = mfma(av[ht], b, O[ht][t]);
+      }
+    }
   }
 
   // ---- epilogue: each wave writes its 64 channels of the 64 heads
@@ -1218,8 +1357,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
 // (normalized output, maximum, sum) in the last slot, merged by the combine
 // with the key splits of the selected entries, or the output itself when
 // nothing else is attended.
-constexpr int kWStride = 520;  // bytes per staged window entry: entries 8 apart land 16 banks apart
-
 template <int NHT, bool SPLITQ>
 struct SmemSwa {
   static constexpr int kQRows = 16 * NHT * (SPLITQ ? 2 : 1);
@@ -1229,10 +1366,6 @@ struct SmemSwa {
   float red_max[kWaves][64];
   float red_sum[kWaves][64];
 };
-
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
 
 template <int NHT, bool SPLITQ, int QDT>
 __global__ __launch_bounds__(kThreads, 1) void k_swa_attn(AttnArgs a) {
@@ -1587,10 +1720,12 @@ hipError_t go_swa(int R, int head_groups, const AttnArgs& a, hipStream_t s) {
 }
 
 // partial slots per (row, head): the key splits of the selected entries
-// plus one for the window; 1 means the only kernel writes the output
+// plus one for the window kernel (the 64-head kernel takes the window as one
+// more step of its own loop instead); 1 means the only kernel writes the output
 int attn_slots(int R, int Hq, int q_dtype, int top_k, bool window) {
-  const int splits = top_k > 0 ? plan(R, Hq, q_dtype, top_k).splits : 0;
-  return splits + (window ? 1 : 0);
+  if (top_k == 0) return 1;
+  const Plan p = plan(R, Hq, q_dtype, top_k);
+  return p.splits + (window && !p.wide ? 1 : 0);
 }
 
 }  // namespace
@@ -1662,7 +1797,7 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
     if (ev.stop) (void)hipEventRecord(ev.stop, s);
     if (e != hipSuccess) return e;
   }
-  if (window) {
+  if (window && !(top_k > 0 && p.wide)) {
     // 64-head workgroups when rows alone fill the chip (bf16 queries), else 16
     const int tiles = Hq / 16;
     const bool wide = q_dtype == CSA2_BF16 && tiles % 4 == 0 && (int64_t)R * (tiles / 4) >= 256;

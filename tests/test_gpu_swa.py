@@ -3,7 +3,8 @@
 Bit-exact: the FP8 (signed E4M3) window codes.  Attention with the window
 joined to the selected entries: within 2e-3 max relative error per row and
 head (normwise), lse within 1e-3, on every launch path (split-K partials
-of 16-head and pipelined workgroups, 64-head workgroups, window only).
+of 16-head and pipelined workgroups with a window kernel, 64-head
+workgroups that take the window as one more step, window only).
 Every call goes through the C ABI.
 """
 import numpy as np
@@ -97,7 +98,8 @@ def _run(q, qkind, oc, os_, wc, idx, vis, wstart, wlen, scale, out_dtype=torch.f
     (64, "bf16", 16, 2048, 9000, [128]),           # pipelined 16-head workgroups
     (64, "bf16", 32, 1500, 6000, [128, 100]),      # pipelined 32-head workgroups, ragged last split
     (32, "bf16", 5, 300, 3000, [64, 128, 5]),
-    (64, "bf16", 256, 300, 5000, [128, 127, 31]),  # 64-head workgroups for both branches
+    (64, "bf16", 256, 300, 5000, [128, 127, 31]),  # 64-head workgroups: the window as their last step
+    (128, "bf16", 160, 200, 3000, [128, 0, 96, 33]),  # 64-head workgroups, two per row
     (128, "bf16", 3, 0, 100, [128, 9, 0]),         # window only (the first, local-only layers)
     (32, "f32", 3, 0, 100, [128, 64, 1]),
 ])
