@@ -70,6 +70,9 @@ def _lib():
             "oracle_attention_row": (None, [P, i32, P, P, P, i32, i64, f64, P, P]),
             "oracle_attention_rows": (None, [i32, P, i32, P, P, P, P, i32, P, f64, P, P]),
             "oracle_e4m3_encode_signed": (ctypes.c_uint8, [ctypes.c_float]),
+            "oracle_e8m0_value": (f64, [ctypes.c_uint8]),
+            "oracle_mxfp4_quantize_rows": (None, [P, i64, i64, i32, P, P]),
+            "oracle_mxfp4_dequant_rows": (None, [P, P, i64, i32, P]),
             "oracle_e4m3_encode_signed_array": (None, [P, i64, P]),
             "oracle_attention_row_swa": (None, [P, i32, P, P, P, i32, i64, P, i64, i32, f64, P, P]),
             "oracle_attention_rows_swa": (None, [i32, P, i32, P, P, P, P, i32, P, P, P, P, f64, P, P]),
@@ -149,6 +152,30 @@ def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------- indexer
+
+def mxfp4_quantize(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """fp32 [n, dim] (dim a multiple of 32) -> OCP MXFP4 (codes u8 [n, dim/2], E8M0 scales u8 [n, dim/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n, dim = x.shape
+    codes = np.empty((n, dim // 2), dtype=np.uint8)
+    scales = np.empty((n, dim // 32), dtype=np.uint8)
+    _lib().oracle_mxfp4_quantize_rows(_p(x), n, dim, dim, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mxfp4_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 rows -> fp32 [n, dim] (exact)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    n, dim = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((n, dim), dtype=np.float32)
+    _lib().oracle_mxfp4_dequant_rows(_p(codes), _p(scales), n, dim, _p(out))
+    return out
+
+
+def e8m0_value(b: int) -> float:
+    return float(_lib().oracle_e8m0_value(b))
+
 
 def index_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
     """q fp32 [H, Dk], k fp32 [n, Dk] -> scores fp32 [n] (fixed fmaf order)."""

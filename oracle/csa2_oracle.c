@@ -287,6 +287,63 @@ int64_t oracle_hsi_pool(const float* scores, int64_t n, int32_t block, int32_t P
     return len;
 }
 
+/* ------------------------------------------------------ MXFP4 indexer keys */
+
+/* OCP MXFP4 (OCP Microscaling Formats v1.0, the FP4 E2M1 element type):
+ * blocks of 32 consecutive values share one E8M0 scale X = 2^(code - 127)
+ * ([Brief] "FP4 cache entries, and why they're safe" assumes indexer keys
+ * in this format, one 8-bit scale per 32 values).  Conversion as that
+ * specification gives it: X = 2^(floor(log2(max |v|)) - 2), 2 being the
+ * largest E2M1 exponent; each element = E2M1(v / X), nearest, ties to even,
+ * values past 6 clamped to 6, sign kept.  A block of zeros takes code 0.
+ * The scale code is clamped to 0..254 (255 is NaN). */
+static int mx_scale_code(float amax) {
+    int e, c;
+    if (!(amax > 0.0f)) return 0;
+    (void)frexp((double)amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+    c = (e - 1) - 2 + 127;
+    return c < 0 ? 0 : (c > 254 ? 254 : c);
+}
+
+double oracle_e8m0_value(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* rows of `dim` values (dim a multiple of 32, row stride `stride` floats) ->
+ * codes [n][dim/2] (low nibble = even channel) and scales [n][dim/32]. */
+void oracle_mxfp4_quantize_rows(const float* x, int64_t n, int64_t stride, int32_t dim, uint8_t* codes,
+                                uint8_t* scales) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r) {
+        const float* xr = x + r * stride;
+        int b, c;
+        for (b = 0; b < dim / 32; ++b) {
+            float amax = 0.0f, X;
+            int sc;
+            for (c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(xr[32 * b + c]));
+            sc = mx_scale_code(amax);
+            X = (float)oracle_e8m0_value((uint8_t)sc);
+            scales[r * (dim / 32) + b] = (uint8_t)sc;
+            for (c = 0; c < 32; c += 2) {
+                float q0 = xr[32 * b + c] / X, q1 = xr[32 * b + c + 1] / X;
+                codes[r * (dim / 2) + 16 * b + c / 2] =
+                    (uint8_t)(oracle_e2m1_encode(q0) | (oracle_e2m1_encode(q1) << 4));
+            }
+        }
+    }
+}
+
+/* value of channel c = E2M1(code_c) * E8M0(scale of block c/32), as fp32 (exact) */
+void oracle_mxfp4_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t n, int32_t dim, float* out) {
+    int64_t r;
+    int c;
+    for (r = 0; r < n; ++r)
+        for (c = 0; c < dim; ++c) {
+            uint8_t byte = codes[r * (dim / 2) + c / 2];
+            uint8_t code = (c & 1) ? (byte >> 4) : (byte & 15);
+            out[r * dim + c] = (float)(oracle_e2m1_value(code) * oracle_e8m0_value(scales[r * (dim / 32) + c / 32]));
+        }
+}
+
 /* ---------------------------------------------------------- attention */
 
 /* Softmax attention of Hq query heads over ns entries given as dequantized
