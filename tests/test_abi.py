@@ -136,7 +136,8 @@ def test_window_calls_reject_bad_arguments():
     # window only: the cache and index arguments are not needed
     assert L.csa2_sparse_attn_swa_workspace_size(2, 64, 1, 0) == 0  # one slot: written directly
     assert L.csa2_sparse_attn_swa_workspace_size(2, 64, 1, 256) > 0
-    assert L.csa2_sparse_attn_swa_workspace_size(4096, 64, 1, 2048) > L.csa2_sparse_attn_workspace_size(4096, 64, 1, 2048)
+    assert L.csa2_sparse_attn_swa_workspace_size(16, 64, 1, 2048) > L.csa2_sparse_attn_workspace_size(16, 64, 1, 2048)
+    assert L.csa2_sparse_attn_swa_workspace_size(4096, 64, 1, 2048) == 0  # 64-head workgroups: the window is a step
     assert L.csa2_quantize_swa_fp8(f, 7, 4, 512, None, f, 10, None) == -1 and "dtype" in _err()
     assert L.csa2_quantize_swa_fp8(None, 0, 4, 512, None, f, 10, None) == -1 and "null" in _err()
     assert L.csa2_quantize_swa_fp8(f, 0, 4, 100, None, f, 10, None) == -1 and "stride" in _err()
