@@ -54,6 +54,7 @@ extern "C" {
 /* element types */
 #define CSA2_F32 0
 #define CSA2_BF16 1
+#define CSA2_MXFP4 2 /* indexer keys only: OCP MXFP4, see csa2_quantize_idx_mxfp4 */
 
 /* indexer modes */
 #define CSA2_FULL 0
@@ -148,6 +149,50 @@ int32_t csa2_index_topk(int32_t mode, int32_t n_rows,
 
 size_t csa2_index_topk_workspace_size(int32_t mode, int32_t n_rows, int32_t n_heads, int32_t max_visible,
                                       int32_t pool_stride, int32_t top_k, int32_t pool_size);
+
+/*
+ * MXFP4 indexer keys.  The course brief "DeepSeek-V4.1-Flash" ("FP4 cache
+ * entries, and why they're safe") assumes the indexer keys are stored in
+ * OCP MXFP4: blocks of 32 values share one 8-bit power-of-two scale (E8M0,
+ * value 2^(b - 127)), elements are E2M1.  A 64-channel key is 32 code bytes
+ * + 2 scale bytes = 34 B, against 128 B in bf16.
+ *
+ * csa2_quantize_idx_mxfp4 writes keys in that format, converting as the OCP
+ * Microscaling specification does: per block of 32 channels,
+ *   X = 2^(floor(log2 max|x|) - 2) (E8M0 code clamped to 0..254; a block of
+ *   zeros gets code 0); code_c = E2M1(x_c / X) (fp32 division, nearest, ties
+ *   to even, |.| > 6 clamped to 6, sign kept).
+ * x            [n_tokens, x_row_stride] of x_dtype (CSA2_F32 or CSA2_BF16),
+ *              16-byte aligned rows; the first 64 values of a row are used;
+ *              values must be finite.
+ * dst_rows     [n_tokens] int64 destination rows or NULL (rows 0..n_tokens-1,
+ *              then n_tokens <= cap_rows); rows outside [0, cap_rows) are
+ *              skipped; repeated destinations in one call leave either token.
+ * k_codes      [cap_rows, 32] uint8 (byte i: channel 2i low nibble, 2i+1 high),
+ *              16-byte aligned.
+ * k_scales     [cap_rows, 2] uint8 E8M0 (block 0 = channels 0..31), 2-byte aligned.
+ *
+ * csa2_index_topk_mxfp4 is csa2_index_topk over such keys: each key value is
+ * the exact fp32 product E2M1(code) * 2^(b - 127), and the score is the
+ * same fixed-order fmaf chain, ReLU and head sum over those values; so the
+ * result equals csa2_index_topk over the dequantized keys bit for bit.
+ * CSA2_FULL_SHARED runs as CSA2_FULL over the shared segment (no MFMA pass).
+ * Arguments and errors as csa2_index_topk, with (idx_k, k_dtype) replaced by
+ * (idx_k_codes, idx_k_scales); the workspace size is
+ * csa2_index_topk_workspace_size's.
+ */
+int32_t csa2_quantize_idx_mxfp4(const void* x, int32_t x_dtype, int64_t n_tokens, int64_t x_row_stride,
+                                const int64_t* dst_rows, uint8_t* k_codes, uint8_t* k_scales, int64_t cap_rows,
+                                void* stream);
+
+int32_t csa2_index_topk_mxfp4(int32_t mode, int32_t n_rows,
+                              const void* idx_q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                              const uint8_t* idx_k_codes, const uint8_t* idx_k_scales,
+                              const int64_t* row_kv_start, const int32_t* row_visible, int32_t max_visible,
+                              const int32_t* pool, const int32_t* pool_len, int32_t pool_stride,
+                              int32_t top_k, int32_t* out_idx,
+                              int32_t pool_size, int32_t block_size, int32_t* out_pool, int32_t* out_pool_len,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Sparse attention over the selected entries ("The Paper" in the talk
@@ -263,6 +308,7 @@ const char* csa2_last_error(void);
 #define CSA2_KERNEL_ATTN_COMBINE 5
 #define CSA2_KERNEL_QUANT_FP8 6
 #define CSA2_KERNEL_SWA_ATTN 7
+#define CSA2_KERNEL_QUANT_MXFP4 8
 int32_t csa2_profile_kernel_events(int32_t kernel_id, void* start_event, void* stop_event);
 
 #ifdef __cplusplus

@@ -13,7 +13,9 @@ from .csa2 import (  # noqa: F401
     REINDEX,
     CSA2Error,
     index_topk,
+    index_topk_mxfp4,
     index_topk_workspace_size,
+    quantize_idx_mxfp4,
     quantize_kv_fp4,
     quantize_swa_fp8,
     sparse_attn,

@@ -16,11 +16,11 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
-F32, BF16 = 0, 1
+F32, BF16, MXFP4 = 0, 1, 2
 FULL, REINDEX, FULL_SHARED = 0, 1, 2
 MAX_TOP_K = 4096
 KERNEL_QUANT, KERNEL_INDEX_SCAN, KERNEL_REINDEX_SCORE, KERNEL_ATTN, KERNEL_ATTN_COMBINE = 1, 2, 3, 4, 5
-KERNEL_QUANT_FP8, KERNEL_SWA_ATTN = 6, 7
+KERNEL_QUANT_FP8, KERNEL_SWA_ATTN, KERNEL_QUANT_MXFP4 = 6, 7, 8
 SWA_WINDOW = 128
 EXPORTED = (
     "csa2_quantize_kv_fp4",
@@ -29,6 +29,8 @@ EXPORTED = (
     "csa2_sparse_attn",
     "csa2_sparse_attn_workspace_size",
     "csa2_quantize_swa_fp8",
+    "csa2_quantize_idx_mxfp4",
+    "csa2_index_topk_mxfp4",
     "csa2_sparse_attn_swa",
     "csa2_sparse_attn_swa_workspace_size",
     "csa2_last_error",
@@ -64,6 +66,11 @@ def lib():
         L.csa2_sparse_attn.restype = i32
         L.csa2_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32]
         L.csa2_sparse_attn_workspace_size.restype = sz
+        L.csa2_quantize_idx_mxfp4.argtypes = [P, i32, i64, i64, P, P, P, i64, P]
+        L.csa2_quantize_idx_mxfp4.restype = i32
+        L.csa2_index_topk_mxfp4.argtypes = [i32, i32, P, i32, i32, i32, P, P, P, P, i32, P, P, i32, i32, P, i32, i32,
+                                            P, P, P, sz, P]
+        L.csa2_index_topk_mxfp4.restype = i32
         L.csa2_quantize_swa_fp8.argtypes = [P, i32, i64, i64, P, P, i64, P]
         L.csa2_quantize_swa_fp8.restype = i32
         L.csa2_sparse_attn_swa.argtypes = [i32, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P, ctypes.c_float, P, i32,
@@ -138,6 +145,34 @@ def index_topk(mode: int, idx_q: torch.Tensor, idx_k: torch.Tensor, row_kv_start
         mode, R, _ptr(idx_q), _dt(idx_q), H, Dk, _ptr(idx_k), _dt(idx_k), _ptr(row_kv_start), _ptr(row_visible),
         int(max_visible), _ptr(pool), _ptr(pool_len), pool_stride, top_k, _ptr(out_idx), pool_size,
         8 if pool_size else 0, _ptr(out_pool), _ptr(out_pool_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def quantize_idx_mxfp4(x: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
+                       dst_rows: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Indexer keys x [n, 64(+)] fp32/bf16 -> OCP MXFP4 rows of k_codes [cap, 32] u8 / k_scales [cap, 2] u8."""
+    _contig(k_codes, k_scales, dst_rows)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [n, C] with unit channel stride")
+    _check(lib().csa2_quantize_idx_mxfp4(_ptr(x), _dt(x), x.shape[0], x.stride(0), _ptr(dst_rows), _ptr(k_codes),
+                                         _ptr(k_scales), k_codes.shape[0], _stream(stream)))
+
+
+def index_topk_mxfp4(mode: int, idx_q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
+                     row_kv_start: torch.Tensor, row_visible: torch.Tensor, max_visible: int, top_k: int,
+                     out_idx: torch.Tensor, workspace: torch.Tensor, pool: Optional[torch.Tensor] = None,
+                     pool_len: Optional[torch.Tensor] = None, pool_size: int = 0,
+                     out_pool: Optional[torch.Tensor] = None, out_pool_len: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """index_topk over MXFP4 indexer keys (k_codes [rows, 32], k_scales [rows, 2])."""
+    _contig(idx_q, k_codes, k_scales, row_kv_start, row_visible, out_idx, workspace, pool, pool_len, out_pool,
+            out_pool_len)
+    R, H, Dk = idx_q.shape
+    pool_stride = pool.shape[1] if pool is not None else 0
+    _check(lib().csa2_index_topk_mxfp4(
+        mode, R, _ptr(idx_q), _dt(idx_q), H, Dk, _ptr(k_codes), _ptr(k_scales), _ptr(row_kv_start),
+        _ptr(row_visible), int(max_visible), _ptr(pool), _ptr(pool_len), pool_stride, top_k, _ptr(out_idx),
+        pool_size, 8 if pool_size else 0, _ptr(out_pool), _ptr(out_pool_len), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 

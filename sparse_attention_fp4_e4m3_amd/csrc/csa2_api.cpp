@@ -10,9 +10,9 @@
 namespace csa2 {
 
 static thread_local std::string g_last_error;
-static ProfileEvents g_events[8];
+static ProfileEvents g_events[16];
 
-ProfileEvents& profile_events(int id) { return g_events[(id >= 0 && id < 8) ? id : 0]; }
+ProfileEvents& profile_events(int id) { return g_events[(id >= 0 && id < 16) ? id : 0]; }
 
 static int32_t fail(int32_t code, const char* fmt, ...) {
   char buf[512];
@@ -42,7 +42,7 @@ extern "C" {
 const char* csa2_last_error(void) { return g_last_error.c_str(); }
 
 int32_t csa2_profile_kernel_events(int32_t kernel_id, void* start_event, void* stop_event) {
-  if (kernel_id < CSA2_KERNEL_QUANT || kernel_id > CSA2_KERNEL_SWA_ATTN)
+  if (kernel_id < CSA2_KERNEL_QUANT || kernel_id > CSA2_KERNEL_QUANT_MXFP4)
     return fail(CSA2_E_INVALID, "csa2_profile_kernel_events: unknown kernel id %d", kernel_id);
   g_events[kernel_id].start = static_cast<hipEvent_t>(start_event);
   g_events[kernel_id].stop = static_cast<hipEvent_t>(stop_event);
@@ -78,17 +78,20 @@ size_t csa2_index_topk_workspace_size(int32_t mode, int32_t n_rows, int32_t n_he
                               pool_stride < 0 ? 0 : pool_stride, pool_size < 0 ? 0 : pool_size);
 }
 
-int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t q_dtype, int32_t n_heads,
-                        int32_t head_dim, const void* idx_k, int32_t k_dtype, const int64_t* row_kv_start,
-                        const int32_t* row_visible, int32_t max_visible, const int32_t* pool,
-                        const int32_t* pool_len, int32_t pool_stride, int32_t top_k, int32_t* out_idx,
-                        int32_t pool_size, int32_t block_size, int32_t* out_pool, int32_t* out_pool_len,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "csa2_index_topk";
+}  // extern "C"
+
+// one validation and dispatch for both key formats (fn names the caller)
+static int32_t index_topk(const char* fn, int32_t mode, int32_t n_rows, const void* idx_q, int32_t q_dtype,
+                          int32_t n_heads, int32_t head_dim, const void* idx_k, const uint8_t* idx_ks,
+                          int32_t k_dtype, const int64_t* row_kv_start, const int32_t* row_visible,
+                          int32_t max_visible, const int32_t* pool, const int32_t* pool_len, int32_t pool_stride,
+                          int32_t top_k, int32_t* out_idx, int32_t pool_size, int32_t block_size, int32_t* out_pool,
+                          int32_t* out_pool_len, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool mx = k_dtype == CSA2_MXFP4;
   if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_FULL_SHARED)
     return fail(CSA2_E_INVALID, "%s: unknown mode %d", fn, mode);
   if (n_rows < 0) return fail(CSA2_E_INVALID, "%s: n_rows < 0", fn);
-  if (!dtype_ok(q_dtype) || !dtype_ok(k_dtype)) return fail(CSA2_E_INVALID, "%s: dtype is not F32/BF16", fn);
+  if (!dtype_ok(q_dtype) || !(mx || dtype_ok(k_dtype))) return fail(CSA2_E_INVALID, "%s: dtype is not F32/BF16", fn);
   if (head_dim != kIdxDim) return fail(CSA2_E_UNSUPPORTED, "%s: head_dim %d (only 64 is built)", fn, head_dim);
   if (n_heads < 1 || n_heads > 32) return fail(CSA2_E_UNSUPPORTED, "%s: n_heads %d outside 1..32", fn, n_heads);
   if (top_k < 1 || top_k > CSA2_MAX_TOP_K) return fail(CSA2_E_INVALID, "%s: top_k %d outside 1..%d", fn, top_k,
@@ -99,9 +102,10 @@ int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t
   if (mode == CSA2_REINDEX && pool_stride > 65536)
     return fail(CSA2_E_UNSUPPORTED, "%s: pool_stride %d above 65536", fn, pool_stride);
   if (n_rows == 0) return CSA2_OK;
-  if (!idx_q || !idx_k || !row_kv_start || !row_visible || !out_idx)
+  if (!idx_q || !idx_k || (mx && !idx_ks) || !row_kv_start || !row_visible || !out_idx)
     return fail(CSA2_E_INVALID, "%s: null buffer", fn);
   if (!aligned(idx_k, 16)) return fail(CSA2_E_INVALID, "%s: idx_k must be 16-byte aligned", fn);
+  if (mx && !aligned(idx_ks, 2)) return fail(CSA2_E_INVALID, "%s: idx_k_scales must be 2-byte aligned", fn);
   if (mode == CSA2_REINDEX) {
     if (!pool) return fail(CSA2_E_INVALID, "%s: REINDEX needs a pool", fn);
     if (pool_stride < 1) return fail(CSA2_E_INVALID, "%s: REINDEX needs pool_stride >= 1", fn);
@@ -117,10 +121,57 @@ int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t
   if (!workspace || workspace_bytes < need)
     return fail(CSA2_E_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(CSA2_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
-  return hip_status(launch_index_topk(mode, n_rows, idx_q, q_dtype, n_heads, idx_k, k_dtype, row_kv_start,
+  return hip_status(launch_index_topk(mode, n_rows, idx_q, q_dtype, n_heads, idx_k, idx_ks, k_dtype, row_kv_start,
                                       row_visible, max_visible, pool, pool_len, pool_stride, top_k, out_idx,
                                       mode == CSA2_FULL ? pool_size : 0, out_pool, out_pool_len, workspace,
                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+extern "C" {
+
+int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t q_dtype, int32_t n_heads,
+                        int32_t head_dim, const void* idx_k, int32_t k_dtype, const int64_t* row_kv_start,
+                        const int32_t* row_visible, int32_t max_visible, const int32_t* pool,
+                        const int32_t* pool_len, int32_t pool_stride, int32_t top_k, int32_t* out_idx,
+                        int32_t pool_size, int32_t block_size, int32_t* out_pool, int32_t* out_pool_len,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (k_dtype == CSA2_MXFP4)
+    return fail(CSA2_E_INVALID, "csa2_index_topk: MXFP4 keys go through csa2_index_topk_mxfp4");
+  return index_topk("csa2_index_topk", mode, n_rows, idx_q, q_dtype, n_heads, head_dim, idx_k, nullptr, k_dtype,
+                    row_kv_start, row_visible, max_visible, pool, pool_len, pool_stride, top_k, out_idx, pool_size,
+                    block_size, out_pool, out_pool_len, workspace, workspace_bytes, stream);
+}
+
+int32_t csa2_index_topk_mxfp4(int32_t mode, int32_t n_rows, const void* idx_q, int32_t q_dtype, int32_t n_heads,
+                              int32_t head_dim, const uint8_t* idx_k_codes, const uint8_t* idx_k_scales,
+                              const int64_t* row_kv_start, const int32_t* row_visible, int32_t max_visible,
+                              const int32_t* pool, const int32_t* pool_len, int32_t pool_stride, int32_t top_k,
+                              int32_t* out_idx, int32_t pool_size, int32_t block_size, int32_t* out_pool,
+                              int32_t* out_pool_len, void* workspace, size_t workspace_bytes, void* stream) {
+  return index_topk("csa2_index_topk_mxfp4", mode, n_rows, idx_q, q_dtype, n_heads, head_dim, idx_k_codes,
+                    idx_k_scales, CSA2_MXFP4, row_kv_start, row_visible, max_visible, pool, pool_len, pool_stride,
+                    top_k, out_idx, pool_size, block_size, out_pool, out_pool_len, workspace, workspace_bytes, stream);
+}
+
+int32_t csa2_quantize_idx_mxfp4(const void* x, int32_t x_dtype, int64_t n_tokens, int64_t x_row_stride,
+                                const int64_t* dst_rows, uint8_t* k_codes, uint8_t* k_scales, int64_t cap_rows,
+                                void* stream) {
+  const char* fn = "csa2_quantize_idx_mxfp4";
+  if (n_tokens < 0) return fail(CSA2_E_INVALID, "%s: n_tokens < 0", fn);
+  if (!dtype_ok(x_dtype)) return fail(CSA2_E_INVALID, "%s: x_dtype %d is not F32/BF16", fn, x_dtype);
+  if (n_tokens == 0) return CSA2_OK;
+  if (!x || !k_codes || !k_scales) return fail(CSA2_E_INVALID, "%s: null buffer", fn);
+  if (x_row_stride < kIdxDim) return fail(CSA2_E_INVALID, "%s: x_row_stride %lld < 64", fn, (long long)x_row_stride);
+  if (!aligned(x, 16) || (x_row_stride * (int64_t)dtype_size(x_dtype)) % 16)
+    return fail(CSA2_E_INVALID, "%s: x rows must be 16-byte aligned", fn);
+  if (!aligned(k_codes, 16) || !aligned(k_scales, 2))
+    return fail(CSA2_E_INVALID, "%s: k_codes must be 16-byte and k_scales 2-byte aligned", fn);
+  if (cap_rows <= 0) return fail(CSA2_E_INVALID, "%s: cap_rows <= 0", fn);
+  if (!dst_rows && n_tokens > cap_rows)
+    return fail(CSA2_E_INVALID, "%s: n_tokens %lld > cap_rows %lld", fn, (long long)n_tokens, (long long)cap_rows);
+  return hip_status(launch_quantize_mxfp4(x, x_dtype, n_tokens, x_row_stride, dst_rows, k_codes, k_scales, cap_rows,
+                                          static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -37,11 +37,16 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t n, int64_t stride
 size_t topk_workspace_bytes(int mode, int R, int H, int max_visible, int pool_stride, int pool_size);
 int topk_max_visible();
 
-hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k, int k_dtype,
+// k_dtype CSA2_MXFP4: idx_k = codes [rows][32], idx_ks = E8M0 scales [rows][2]; else idx_ks unused
+hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k,
+                             const uint8_t* idx_ks, int k_dtype,
                              const int64_t* row_start, const int32_t* row_visible, int max_visible,
                              const int32_t* pool, const int32_t* pool_len, int pool_stride, int top_k,
                              int32_t* out_idx, int pool_size, int32_t* out_pool, int32_t* out_pool_len,
                              void* ws, hipStream_t s);
+
+hipError_t launch_quantize_mxfp4(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
+                                 uint8_t* codes, uint8_t* scales, int64_t cap, hipStream_t s);
 
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
                                uint8_t* codes, int64_t cap, hipStream_t s);

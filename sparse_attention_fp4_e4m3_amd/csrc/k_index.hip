@@ -52,14 +52,20 @@ constexpr int kMaxHeads = 32;
 // loaded with fully coalesced 16-byte pieces, staged in the wave's own LDS
 // area and read back one row per lane, so no workgroup barrier is needed
 // between tiles and the waves of a workgroup drift freely.
+//
+// MXFP4 keys (32 code bytes + 2 E8M0 scale bytes per key, in two arrays) are
+// not staged: each lane loads its own key's 32 bytes (two 16-byte loads; the
+// wave's two loads cover 2 KiB of consecutive rows) and its 2 scale bytes,
+// and widens the codes to fp32 itself (exact: E2M1 value times a power of two).
 template <int KDT>
 struct KeyTile {
-  static constexpr int kBytes = KDT == CSA2_BF16 ? 128 : 256;  // one indexer key row
+  static constexpr bool kMx = KDT == CSA2_MXFP4;
+  static constexpr int kBytes = KDT == CSA2_BF16 ? 128 : (kMx ? 32 : 256);  // one indexer key row (codes)
   static constexpr int kKeys = 64;                             // keys per wave tile
   static constexpr int kStride = kBytes + 16;                  // padded LDS row
   static constexpr int kPieces = kBytes / 16;                  // 16-byte pieces per row
-  static constexpr int kPerLane = kKeys * kPieces / 64;        // 8 (bf16) or 16 (fp32)
-  static constexpr int kWaveBytes = kKeys * kStride;           // LDS per wave
+  static constexpr int kPerLane = kKeys * kPieces / 64;        // 8 (bf16), 16 (fp32) or 2 (MXFP4, own key)
+  static constexpr int kWaveBytes = kMx ? 0 : kKeys * kStride;  // LDS per wave
 };
 constexpr int kWavesPerWG = kThreads / 64;
 constexpr int kWGKeys = kWavesPerWG * 64;  // keys per workgroup tile (one wave tile per wave)
@@ -243,6 +249,7 @@ __global__ __launch_bounds__(256) void k_zero(uint32_t* __restrict__ x, int64_t 
 struct ScoreArgs {
   int H;
   const void* idx_k;
+  const uint8_t* idx_ks;      // MXFP4 keys: E8M0 scales [rows][2]
   const int64_t* row_start;
   const int32_t* row_visible;
   int max_visible;
@@ -263,8 +270,14 @@ struct ScoreArgs {
 template <int KDT>
 struct Staged {
   u32x4 v[KeyTile<KDT>::kPerLane];
+  uint32_t sc;  // MXFP4: the two scale bytes of this lane's key
   int32_t pos;  // Reindex: the entry position of this lane's own slot (-1: none)
 };
+
+// E8M0 byte -> 2^(b - 127) as fp32 (b = 0: the subnormal 2^-127); the codec never writes 255
+__device__ __forceinline__ float e8m0_f(uint32_t b) {
+  return __uint_as_float(b ? (b << 23) : 0x00400000u);
+}
 
 // First-digit histograms are kept as packed 16-bit counters (two bins per
 // word): a workgroup scores at most 255 x 256 entries, so no counter overflows.
@@ -329,6 +342,21 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
   // discarded below; the loaded values are not inspected here, so the loads
   // of the next tile stay in flight while the current one is scored.
   auto load_tile = [&](int64_t base, Staged<KDT>& st) {
+    if constexpr (T::kMx) {
+      // own key: slot base + lane (Full: clamped to the last visible entry; Reindex: its pool entry, else row 0)
+      int64_t row;
+      if (!REINDEX) {
+        row = rs + std::min<int64_t>(base + lane, (int64_t)vis - 1);
+      } else {
+        st.pos = (int32_t)position(base + lane);
+        row = st.pos >= 0 ? rs + st.pos : 0;
+      }
+      const u32x4* pc = reinterpret_cast<const u32x4*>(kbase + row * 32);
+      st.v[0] = __builtin_nontemporal_load(pc);
+      st.v[1] = __builtin_nontemporal_load(pc + 1);
+      st.sc = *reinterpret_cast<const uint16_t*>(a.idx_ks + row * 2);
+      return;
+    }
     if (!REINDEX) {
       // Full: 32-bit offsets into the row's key segment (at most 2^21 entries of 256 bytes)
       const uint8_t* kseg = kbase + rs * T::kBytes;
@@ -369,11 +397,18 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
   auto score_tile = [&](int j, Staged<KDT>& st) {
     const int64_t base = tile_base(j);
     const int32_t own = st.pos;  // (st is refilled with the next tile below)
-    // (the LDS operations of one wave execute in order: the previous tile's reads are done)
+    u32x4 mc[2] = {st.v[0], st.v[T::kPerLane > 1 ? 1 : 0]};  // MXFP4: this key's codes, kept in registers
+    float mx0 = 0.0f, mx1 = 0.0f;                             // MXFP4: the two block scales
+    if constexpr (T::kMx) {
+      mx0 = e8m0_f(st.sc & 0xFFu);
+      mx1 = e8m0_f(st.sc >> 8);
+    } else {
+      // (the LDS operations of one wave execute in order: the previous tile's reads are done)
 #pragma unroll
-    for (int i = 0; i < T::kPerLane; ++i) {
-      const int id = lane + 64 * i;
-      *reinterpret_cast<u32x4*>(tile + (id / T::kPieces) * T::kStride + (id % T::kPieces) * 16) = st.v[i];
+      for (int i = 0; i < T::kPerLane; ++i) {
+        const int id = lane + 64 * i;
+        *reinterpret_cast<u32x4*>(tile + (id / T::kPieces) * T::kStride + (id % T::kPieces) * 16) = st.v[i];
+      }
     }
     if (j + kWavesPerWG < nwt) load_tile(tile_base(j + kWavesPerWG), st);
 
@@ -382,10 +417,20 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
 #pragma unroll
     for (int h = 0; h < NACC; ++h) acc[h] = 0.0f;
     const uint8_t* row = tile + lane * T::kStride;
-#pragma unroll 2
+#pragma unroll(T::kMx ? 16 : 2)  // MXFP4: full, so the code words stay in registers
     for (int c4 = 0; c4 < 16; ++c4) {
       float kv[4];
-      if (KDT == CSA2_BF16) {
+      if constexpr (T::kMx) {
+        // channels 4 c4 .. +3: code bytes 2 c4, 2 c4 + 1 (low nibble first), block c4 / 8
+        const uint32_t wd = mc[c4 >> 3][(c4 >> 1) & 3] >> (16 * (c4 & 1));  // its two bytes, low half
+        const float X = c4 < 8 ? mx0 : mx1;
+        const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 0);
+        const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 1);
+        kv[0] = __fmul_rn(lo[0], X);
+        kv[1] = __fmul_rn(lo[1], X);
+        kv[2] = __fmul_rn(hi[0], X);
+        kv[3] = __fmul_rn(hi[1], X);
+      } else if (KDT == CSA2_BF16) {
         const u32x2 w = *reinterpret_cast<const u32x2*>(row + c4 * 8);
         kv[0] = __uint_as_float(w[0] << 16);
         kv[1] = __uint_as_float(w[0] & 0xFFFF0000u);
@@ -1361,7 +1406,8 @@ namespace {
 
 // the exact path: scan (Full: every visible entry; Reindex: the pool), then
 // the exact selection; row_mask restricts it to flagged rows
-void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H, const void* idx_k, int k_dtype,
+void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H, const void* idx_k,
+               const uint8_t* idx_ks, int k_dtype,
                const int64_t* row_start, const int32_t* row_visible, int max_visible, const int32_t* pool,
                const int32_t* pool_len, int pool_stride, int top_k, int32_t* out_idx, int pool_size,
                int32_t* out_pool, int32_t* out_pool_len, const uint32_t* row_mask, float* scores,
@@ -1379,6 +1425,7 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     ScoreArgs sa{};
     sa.H = H;
     sa.idx_k = idx_k;
+    sa.idx_ks = idx_ks;
     sa.row_start = row_start;
     sa.row_visible = row_visible;
     sa.max_visible = max_visible;
@@ -1405,7 +1452,12 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
     if (record && ev.start) (void)hipEventRecord(ev.start, s);
     const bool qbf = q_dtype == CSA2_BF16;
-    if (k_dtype == CSA2_BF16) {
+    if (k_dtype == CSA2_MXFP4) {
+      if (!full && qbf) dispatch_heads<CSA2_MXFP4, true, false, CSA2_BF16>(H, sa, idx_q, grid, s);
+      else if (!full) dispatch_heads<CSA2_MXFP4, true, false, CSA2_F32>(H, sa, idx_q, grid, s);
+      else if (pool_on) dispatch_heads<CSA2_MXFP4, false, true, CSA2_F32>(H, sa, L.qf, grid, s);
+      else dispatch_heads<CSA2_MXFP4, false, false, CSA2_F32>(H, sa, L.qf, grid, s);
+    } else if (k_dtype == CSA2_BF16) {
       if (!full && qbf) dispatch_heads<CSA2_BF16, true, false, CSA2_BF16>(H, sa, idx_q, grid, s);
       else if (!full) dispatch_heads<CSA2_BF16, true, false, CSA2_F32>(H, sa, idx_q, grid, s);
       else if (pool_on) dispatch_heads<CSA2_BF16, false, true, CSA2_F32>(H, sa, L.qf, grid, s);
@@ -1482,7 +1534,8 @@ bool topk_uses_prefill_path(int mode, int q_dtype, int k_dtype, int H, int pool_
          (H == 4 || H == 8 || H == 16);
 }
 
-hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k, int k_dtype,
+hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k,
+                             const uint8_t* idx_ks, int k_dtype,
                              const int64_t* row_start, const int32_t* row_visible, int max_visible,
                              const int32_t* pool, const int32_t* pool_len, int pool_stride, int top_k,
                              int32_t* out_idx, int pool_size, int32_t* out_pool, int32_t* out_pool_len, void* ws,
@@ -1491,7 +1544,7 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   const int emode = shared ? CSA2_FULL : mode;
   Layout L = layout(ws, mode, R, H, max_visible, pool_stride, pool_size);
   if (!topk_uses_prefill_path(mode, q_dtype, k_dtype, H, pool_size)) {
-    run_exact(L, emode, shared, R, q_dtype, H, idx_k, k_dtype, row_start, row_visible, max_visible, pool, pool_len,
+    run_exact(L, emode, shared, R, q_dtype, H, idx_k, idx_ks, k_dtype, row_start, row_visible, max_visible, pool, pool_len,
               pool_stride, top_k, out_idx, pool_size, out_pool, out_pool_len, nullptr, L.scores, L.n_pad, false, true,
               idx_q, s);
     return hipGetLastError();
@@ -1566,10 +1619,10 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   if (ev.stop) (void)hipEventRecord(ev.stop, s);
   hipLaunchKernelGGL(k_pf_compact, dim3((unsigned)R), dim3(256), 0, s, p);
   // exact scores of the candidates and the exact selection among them (Reindex over the candidate lists)
-  run_exact(L, CSA2_REINDEX, true, R, q_dtype, H, idx_k, k_dtype, row_start, row_visible, max_visible, L.cand,
+  run_exact(L, CSA2_REINDEX, true, R, q_dtype, H, idx_k, nullptr, k_dtype, row_start, row_visible, max_visible, L.cand,
             L.ccnt, kPfCap, top_k, out_idx, 0, nullptr, nullptr, nullptr, L.cscore, kPfCap, true, true, idx_q, s);
   // rows whose candidates overflowed: the exact full scan and selection, for those rows only
-  run_exact(L, CSA2_FULL, true, R, q_dtype, H, idx_k, k_dtype, row_start, row_visible, max_visible, nullptr,
+  run_exact(L, CSA2_FULL, true, R, q_dtype, H, idx_k, nullptr, k_dtype, row_start, row_visible, max_visible, nullptr,
             nullptr, 0, top_k, out_idx, 0, nullptr, nullptr, L.over, L.scores, L.n_pad, true, false, idx_q, s);
   return hipGetLastError();
 }

@@ -1,5 +1,5 @@
-// k_quant.hip -- quantize-on-write of 512-channel KV latents to FP4, and of
-// local-window latents to FP8.
+// k_quant.hip -- quantize-on-write of 512-channel KV latents to FP4, of
+// local-window latents to FP8, and of indexer keys to MXFP4.
 //
 // Cache format of "FP4 cache entries, and why they're safe" (course brief
 // "DeepSeek-V4.1-Flash"): E2M1 elements, one E4M3 scale per 16 channels, no
@@ -139,7 +139,70 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const void* __restrict__ x, i
   *reinterpret_cast<uint4*>(codes + dst * kDim + g * 16) = make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// Indexer keys in OCP MXFP4 (64 channels = two blocks of 32 sharing an E8M0
+// scale each), converted as the OCP Microscaling specification gives it:
+// X = 2^(floor(log2 amax) - 2) -- for a normal amax with biased exponent E
+// that is E8M0 code E - 2; a zero or subnormal amax gives code 0 -- then
+// E2M1(x / X) with the FP4 element rounding above.  One thread per block of
+// 32 channels writes 16 code bytes and 1 scale byte.
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ x, int64_t n, int64_t stride,
+                                                  const int64_t* __restrict__ dst_rows, uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales, int64_t cap) {
+  const int64_t tok = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 1;
+  const int blk = threadIdx.x & 1;
+  if (tok >= n) return;
+  const int64_t dst = dst_rows ? dst_rows[tok] : tok;
+  if (dst < 0 || dst >= cap) return;
+  float v[32];
+  if (DT == CSA2_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + tok * stride + blk * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 t = p[i];
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + tok * stride + blk * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 t = p[i];
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+        v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  const uint32_t sb = (uint32_t)max(e - 2, 0);
+  const float X = __uint_as_float(sb ? (sb << 23) : 0x00400000u);
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) out[i >> 3] |= e2m1_code(__fdiv_rn(v[i], X)) << (4 * (i & 7));
+  *reinterpret_cast<uint4*>(codes + dst * 32 + blk * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  scales[dst * 2 + blk] = (uint8_t)sb;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_mxfp4(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
+                                 uint8_t* codes, uint8_t* scales, int64_t cap, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(n, 128)), block(256);
+  auto& ev = profile_events(CSA2_KERNEL_QUANT_MXFP4);
+  if (ev.start) (void)hipEventRecord(ev.start, s);
+  if (x_dtype == CSA2_F32)
+    hipLaunchKernelGGL(k_quant_mx<CSA2_F32>, grid, block, 0, s, x, n, stride, dst_rows, codes, scales, cap);
+  else
+    hipLaunchKernelGGL(k_quant_mx<CSA2_BF16>, grid, block, 0, s, x, n, stride, dst_rows, codes, scales, cap);
+  if (ev.stop) (void)hipEventRecord(ev.stop, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
                                uint8_t* codes, int64_t cap, hipStream_t s) {

@@ -146,11 +146,35 @@ def test_window_calls_reject_bad_arguments():
     assert L.csa2_quantize_swa_fp8(None, 0, 0, 512, None, None, 10, None) == 0
 
 
+def test_mxfp4_calls_reject_bad_arguments():
+    L = _L()
+    f = ctypes.c_void_p(0x10000)
+    assert L.csa2_quantize_idx_mxfp4(f, 7, 4, 64, None, f, f, 10, None) == -1 and "dtype" in _err()
+    assert L.csa2_quantize_idx_mxfp4(f, 0, 4, 64, None, f, None, 10, None) == -1 and "null" in _err()
+    assert L.csa2_quantize_idx_mxfp4(f, 0, 4, 32, None, f, f, 10, None) == -1 and "stride" in _err()
+    assert L.csa2_quantize_idx_mxfp4(f, 0, 40, 64, None, f, f, 10, None) == -1 and "cap_rows" in _err()
+    assert L.csa2_quantize_idx_mxfp4(f, 0, 4, 64, None, ctypes.c_void_p(0x10008), f, 10, None) == -1
+    assert L.csa2_quantize_idx_mxfp4(None, 0, 0, 64, None, None, None, 10, None) == 0
+    args = [0, 2, f, 1, 8, 64, f, f, f, f, 1000, None, None, 0, 64, f, 0, 0, None, None, f, 1 << 30, None]
+    bad = list(args)
+    bad[7] = None  # scales
+    assert L.csa2_index_topk_mxfp4(*bad) == -1 and "null" in _err()
+    bad = list(args)
+    bad[7] = ctypes.c_void_p(0x10001)
+    assert L.csa2_index_topk_mxfp4(*bad) == -1 and "aligned" in _err()
+    bad = list(args)
+    bad[5] = 128
+    assert L.csa2_index_topk_mxfp4(*bad) == -2
+    # MXFP4 keys are not accepted by the two-format call
+    assert L.csa2_index_topk(0, 2, f, 1, 8, 64, f, 2, f, f, 1000, None, None, 0, 64, f, 0, 0, None, None, f,
+                             1 << 30, None) == -1 and "mxfp4" in _err()
+
+
 def test_profile_hook_ids():
     L = _L()
     assert L.csa2_profile_kernel_events(99, None, None) == -1
     assert L.csa2_profile_kernel_events(2, None, None) == 0
-    assert L.csa2_profile_kernel_events(7, None, None) == 0 and L.csa2_profile_kernel_events(8, None, None) == -1
+    assert L.csa2_profile_kernel_events(8, None, None) == 0 and L.csa2_profile_kernel_events(9, None, None) == -1
 
 
 def test_layer_mode_rules():
