@@ -17,6 +17,9 @@ The prefill workload (c4) times one 4,096-token chunk appended causally to a
 262,144-token cache: quantize-on-write of the chunk, the Full indexer and
 exact top-K for each of its rows, and sparse attention for each row.
 
+--idx-mxfp4 stores the indexer keys in OCP MXFP4 (34 B per 64-channel key
+instead of 128 B of bf16), quantized on the GPU from the same generated keys.
+
 --swa adds the local branch to every layer: each layer keeps its own FP8
 window of the 128 most recent tokens (a ring of 128 rows per sequence in
 decode, the chunk's band in prefill), writes the step's tokens into it and
@@ -51,8 +54,8 @@ def log(msg):
 
 # ------------------------------------------------------------------ setup
 
-def build_cache(w, lens, device, chunk=65536):
-    """Quantize every sequence's KV into one packed FP4 cache on the GPU."""
+def build_cache(w, lens, device, chunk=65536, mxfp4=False):
+    """Quantize every sequence's KV into one packed FP4 cache on the GPU (indexer keys in MXFP4 if asked)."""
     import torch
 
     from sparse_attention_fp4_e4m3_amd import Cache, csa2
@@ -63,6 +66,8 @@ def build_cache(w, lens, device, chunk=65536):
     scales = torch.empty(rows, 32, dtype=torch.uint8, device=device)
     kdt = torch.bfloat16 if w.idx_dtype == "bf16" else torch.float32
     idx_k = torch.empty(rows, 64, dtype=kdt, device=device)
+    ik_codes = torch.empty(rows, 32, dtype=torch.uint8, device=device) if mxfp4 else None
+    ik_scales = torch.empty(rows, 2, dtype=torch.uint8, device=device) if mxfp4 else None
     for b in range(len(lens)):
         for t0 in range(0, int(lens[b]), chunk):
             t1 = min(int(lens[b]), t0 + chunk)
@@ -75,7 +80,15 @@ def build_cache(w, lens, device, chunk=65536):
             else:
                 ik = torch.from_numpy(ik)
             idx_k[r0:r0 + (t1 - t0)] = ik.to(device)
+            if mxfp4:
+                csa2.quantize_idx_mxfp4(idx_k[r0:r0 + (t1 - t0)], ik_codes[r0:r0 + (t1 - t0)],
+                                        ik_scales[r0:r0 + (t1 - t0)])
         torch.cuda.synchronize()
+    if mxfp4:
+        del idx_k
+        return Cache(codes, scales, ik_codes, torch.from_numpy(starts).to(device),
+                     torch.from_numpy(lens.astype(np.int32)).to(device), int(lens.max()),
+                     idx_k_scales=ik_scales), starts
     return Cache(codes, scales, idx_k, torch.from_numpy(starts).to(device),
                  torch.from_numpy(lens.astype(np.int32)).to(device), int(lens.max())), starts
 
@@ -175,24 +188,26 @@ def layer_inputs(w, device):
 
 # ------------------------------------------------------------------ accounting
 
-def algorithmic_bytes(w, lens):
+def algorithmic_bytes(w, lens, mxfp4=False):
     """Bytes the method must move per step (one decode token per sequence, or one prefill chunk), by kernel family."""
     R, K = w.rows, w.K
     qb = 2 if w.q_dtype == "bf16" else 4
     kb = 2 if w.idx_dtype == "bf16" else 4
+    if mxfp4:
+        kb = 34 / 64  # 32 code bytes + 2 E8M0 scale bytes per 64-channel key
     out = {"quantize": R * (512 * 4 + KV_ROW_BYTES)}
     if w.is_prefill:
         # the chunk's rows share one key segment: each key and each query is read once
         out["index_scan"] = int(lens.max()) * 64 * kb + R * w.H * 64 * qb
     else:
-        out["index_scan"] = int(lens.sum()) * 64 * kb
+        out["index_scan"] = int(int(lens.sum()) * 64 * kb)
     pool = 0
     reindex = 0
     for L in w.layers:
         if L.mode == "full":
             pool = L.pool_size
         elif L.mode == "reindex":
-            reindex += R * pool * 64 * kb
+            reindex += int(R * pool * 64 * kb)
     out["reindex_score"] = reindex
     per_attn = R * (K * KV_ROW_BYTES + K * 4 + w.Hq * 512 * qb + w.Hq * 512 * 4)
     out["attention_per_layer"] = per_attn
@@ -288,7 +303,7 @@ def traffic_from_profiles(workload, kernel_file):
 
 # ------------------------------------------------------------------ CPU oracle baseline
 
-def cpu_baseline(w, lens, sample_rows, reps, swa=False):
+def cpu_baseline(w, lens, sample_rows, reps, swa=False, mxfp4=False):
     """`reps` decode steps of the same chain for `sample_rows` sequences, run by the CPU oracle
     (every layer joined with its window under swa)."""
     import oracle
@@ -298,7 +313,10 @@ def cpu_baseline(w, lens, sample_rows, reps, swa=False):
     caches = {}
     for b in rows:
         x = gen.kv_rows(w, b, 0, int(lens[b]))
-        caches[b] = (oracle.quantize(x), gen.idx_k_rows(w, b, 0, int(lens[b])))
+        ik = gen.idx_k_rows(w, b, 0, int(lens[b]))
+        if mxfp4:  # the keys the GPU scores: MXFP4, dequantized exactly
+            ik = oracle.mxfp4_dequant(*oracle.mxfp4_quantize(ik))
+        caches[b] = (oracle.quantize(x), ik)
         del x
     qs = [gen.attn_q(w, li, 0, len(rows)) for li in range(len(w.layers))]
     iqs = [gen.index_q(w, li, 0, len(rows)) if L.mode != "reuse" else None for li, L in enumerate(w.layers)]
@@ -397,6 +415,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=16)
     ap.add_argument("--cpu-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--idx-mxfp4", action="store_true",
+                    help="indexer keys stored in OCP MXFP4 (decode workloads)")
     ap.add_argument("--swa", action="store_true",
                     help="every layer also attends over its own 128-token FP8 window (local branch)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
@@ -416,13 +436,17 @@ def main():
 
     device = torch.device("cuda:0")
     w = gen.get(args.workload)
+    if args.idx_mxfp4 and w.is_prefill:
+        print("bench.py: --idx-mxfp4 is built for the decode workloads (the prefill chunk's MFMA indexer reads "
+              "bf16 keys)", file=sys.stderr)
+        sys.exit(2)
     log("workload %s: %s" % (w.name, w.description))
     t = time.time()
     if w.is_prefill:
         cache, qs, iqs, new_kv, new_rows_t, lens = build_prefill(w, device)
     else:
         lens = gen.seq_lens(w)
-        cache, _ = build_cache(w, lens, device)
+        cache, _ = build_cache(w, lens, device, mxfp4=args.idx_mxfp4)
         qs, iqs = layer_inputs(w, device)
         new_rows = np.concatenate([[0], np.cumsum(lens)[:-1]]) + lens - 1
         new_kv = torch.from_numpy(np.concatenate([gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b]))
@@ -515,8 +539,8 @@ def main():
         vals = [p[k][0].elapsed_time(p[k][1]) * 1e3 for p in pairs]
         per_kernel_us[k] = float(np.mean(vals))
 
-    wname = w.name + ("+swa" if args.swa else "")
-    byt = algorithmic_bytes(w, lens)
+    wname = w.name + ("+swa" if args.swa else "") + ("+mxfp4idx" if args.idx_mxfp4 else "")
+    byt = algorithmic_bytes(w, lens, args.idx_mxfp4)
     attn_flops = attention_flops(w)
     kern = {
         "index_scan": {"avg_us": per_kernel_us["index_scan"], "bytes": byt["index_scan"], "flops": index_flops(w, lens)},
@@ -574,7 +598,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: %s" % (wname, w.description + (" + local 128-token FP8 window" if args.swa else "")), "batch": w.B, "rows": w.rows,
+        "config": {"workload": "%s: %s" % (wname, w.description + (" + local 128-token FP8 window" if args.swa else "")
+                                                        + (" + MXFP4 indexer keys" if args.idx_mxfp4 else "")), "batch": w.B, "rows": w.rows,
                    "ctx": int(lens.max()),
                    "layers": [L.mode for L in w.layers], "top_k": w.K, "q_heads": w.Hq, "indexer_heads": w.H,
                    "kv": "fp4 e2m1 + e4m3 scale per 16 ch (288 B/entry)",
@@ -588,7 +613,7 @@ def main():
     res["chain_hbm_GBps"] = byt["total"] / (ms_step * 1e-3) / 1e9
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_prefill(w, max(args.cpu_rows, 128), args.swa) if w.is_prefill
-                               else cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps, args.swa))
+                               else cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps, args.swa, args.idx_mxfp4))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

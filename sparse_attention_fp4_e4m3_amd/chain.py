@@ -34,11 +34,12 @@ class Cache:
     """A packed FP4 cache and its indexer keys (device tensors)."""
     kv_codes: torch.Tensor      # [rows, 256] uint8
     kv_scales: torch.Tensor     # [rows, 32] uint8
-    idx_k: torch.Tensor         # [rows, 64] bf16 / fp32
+    idx_k: torch.Tensor         # [rows, 64] bf16 / fp32, or MXFP4 codes [rows, 32] uint8
     row_kv_start: torch.Tensor  # [R] int64
     row_visible: torch.Tensor   # [R] int32
     max_visible: int
     shared_segment: bool = False  # every row reads the segment at row_kv_start[0] (a prefill chunk)
+    idx_k_scales: Optional[torch.Tensor] = None  # [rows, 2] uint8 E8M0: the indexer keys are MXFP4
 
 
 @dataclass
@@ -127,21 +128,26 @@ class LayerChain:
             raise ValueError("windows must be given exactly when the chain was built with swa=True")
         last_full_pool = None
         last_sel = None
+        if cache.idx_k_scales is not None:
+            def topk(mode, iq, out, **kw):
+                csa2.index_topk_mxfp4(mode, iq, cache.idx_k, cache.idx_k_scales, cache.row_kv_start,
+                                      cache.row_visible, cache.max_visible, self.K, out, self.ws_index,
+                                      stream=stream, **kw)
+        else:
+            def topk(mode, iq, out, **kw):
+                csa2.index_topk(mode, iq, cache.idx_k, cache.row_kv_start, cache.row_visible, cache.max_visible,
+                                self.K, out, self.ws_index, stream=stream, **kw)
         for i, L in enumerate(self.layers):
             if L.mode == "full":
                 if new_kv is not None and i == 0:
                     csa2.quantize_kv_fp4(new_kv, cache.kv_codes, cache.kv_scales, new_kv_rows, stream=stream)
                 pool, plen = self.pool.get(i, (None, None))
-                csa2.index_topk(self.full_mode, idx_q[i], cache.idx_k, cache.row_kv_start, cache.row_visible,
-                                cache.max_visible, self.K, self.idx[i], self.ws_index, pool_size=L.pool_size,
-                                out_pool=pool, out_pool_len=plen, stream=stream)
+                topk(self.full_mode, idx_q[i], self.idx[i], pool_size=L.pool_size, out_pool=pool, out_pool_len=plen)
                 last_full_pool = (pool, plen)
                 last_sel = self.idx[i]
             elif L.mode == "reindex":
                 pool, plen = last_full_pool
-                csa2.index_topk(csa2.REINDEX, idx_q[i], cache.idx_k, cache.row_kv_start, cache.row_visible,
-                                cache.max_visible, self.K, self.idx[i], self.ws_index, pool=pool, pool_len=plen,
-                                stream=stream)
+                topk(csa2.REINDEX, idx_q[i], self.idx[i], pool=pool, pool_len=plen)
                 last_sel = self.idx[i]
             if windows is None:
                 csa2.sparse_attn(q[i], cache.kv_codes, cache.kv_scales, cache.row_kv_start, last_sel, self.out[i],

@@ -155,6 +155,33 @@ def test_chain_with_local_windows_scaled():
     say("max err %.3e" % worst)
 
 
+def test_chain_with_mxfp4_indexer_keys_scaled():
+    """The 128K chain's structure with MXFP4 indexer keys written by the library: every selection
+    equals the oracle's over the dequantized keys."""
+    w = gen.get("c3").scaled(B=3, n=24001, K=512, layers=(gen.Layer("full", 2048), gen.Layer("reindex"),
+                                                         gen.Layer("reindex"), gen.Layer("reuse")))
+    lens, starts, raw, ik, cache, qs, iqs = _setup(w)
+    kc = torch.empty(cache.idx_k.shape[0], 32, dtype=torch.uint8, device=DEV)
+    ks = torch.empty(cache.idx_k.shape[0], 2, dtype=torch.uint8, device=DEV)
+    csa2.quantize_idx_mxfp4(cache.idx_k, kc, ks)
+    mx = Cache(cache.kv_codes, cache.kv_scales, kc, cache.row_kv_start, cache.row_visible, cache.max_visible,
+               idx_k_scales=ks)
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, mx.max_visible,
+                       qs[0].dtype, DEV)
+    chain.step(mx, qs, iqs, w.softmax_scale)
+    torch.cuda.synchronize()
+    ikh = [oracle.mxfp4_dequant(*oracle.mxfp4_quantize(k)) for k in ik]
+    worst = 0.0
+    for b in range(w.B):
+        oc, os_, ref = _oracle_chain(w, lens, raw, ikh, b)
+        for li, (sel, pool, o, lse) in enumerate(ref):
+            if w.layers[li].mode != "reuse":
+                assert np.array_equal(chain.idx[li][b].cpu().numpy(), sel), "indices, layer %d seq %d" % (li, b)
+            worst = max(worst, check_attention(chain.out[li][b:b + 1], chain.lse[li][b:b + 1], o[None], lse[None],
+                                               "mxfp4 chain layer %d seq %d" % (li, b)))
+    say("max err %.3e" % worst)
+
+
 @pytest.mark.parametrize("swa", [False, True])
 def test_graph_replay_matches_eager(swa):
     w = gen.get("c3").scaled(B=4, n=30000, K=512, layers=(gen.Layer("full", 2048), gen.Layer("reindex"),
