@@ -20,6 +20,10 @@ exact top-K for each of its rows, and sparse attention for each row.
 --idx-mxfp4 stores the indexer keys in OCP MXFP4 (34 B per 64-channel key
 instead of 128 B of bf16), quantized on the GPU from the same generated keys.
 
+--workload c3v checks 5 draft tokens per sequence of the 128K chain in one pass
+(speculative verification): the 5 drafts are the last 5 cached tokens, written
+by the step, and draft i of a sequence sees the cache up to itself (80 rows).
+
 --swa adds the local branch to every layer: each layer keeps its own FP8
 window of the 128 most recent tokens (a ring of 128 rows per sequence in
 decode, the chunk's band in prefill), writes the step's tokens into it and
@@ -238,7 +242,7 @@ def attention_flops(w):
 
 def index_flops(w, lens):
     """fp32 multiply-adds of the indexer scan: every visible entry, every indexer head, 64 channels."""
-    return 2.0 * float(np.sum(lens)) * w.H * 64
+    return 2.0 * float(np.sum(lens)) * w.H * 64 * w.verify
 
 
 def oracle_window(w, li, b, t_end):
@@ -309,6 +313,7 @@ def cpu_baseline(w, lens, sample_rows, reps, swa=False, mxfp4=False):
     import oracle
 
     rows = list(range(min(sample_rows, w.B)))
+    V = w.verify
     log("cpu baseline: preparing oracle cache for %d sequences" % len(rows))
     caches = {}
     for b in rows:
@@ -318,29 +323,31 @@ def cpu_baseline(w, lens, sample_rows, reps, swa=False, mxfp4=False):
             ik = oracle.mxfp4_dequant(*oracle.mxfp4_quantize(ik))
         caches[b] = (oracle.quantize(x), ik)
         del x
-    qs = [gen.attn_q(w, li, 0, len(rows)) for li in range(len(w.layers))]
-    iqs = [gen.index_q(w, li, 0, len(rows)) if L.mode != "reuse" else None for li, L in enumerate(w.layers)]
-    new_kv = [gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b])) for b in rows]
+    qs = [gen.attn_q(w, li, 0, len(rows) * V) for li in range(len(w.layers))]
+    iqs = [gen.index_q(w, li, 0, len(rows) * V) if L.mode != "reuse" else None for li, L in enumerate(w.layers)]
+    new_kv = [gen.kv_rows(w, b, int(lens[b]) - V, int(lens[b])) for b in rows]
     wins = {(li, b): oracle_window(w, li, b, int(lens[b])) for li in range(len(w.layers)) for b in rows} if swa else {}
     t0 = time.perf_counter()
     for b in [b for _ in range(reps) for b in rows]:
         (codes, scales), ik = caches[b]
-        n = int(lens[b])
-        c1, s1 = oracle.quantize(new_kv[b])  # the newest token, written by the first Full layer
-        codes[n - 1], scales[n - 1] = c1[0], s1[0]
-        pool = None
-        sel = None
-        for li, L in enumerate(w.layers):
-            if L.mode == "full":
-                sel, pool, _ = oracle.full_select(iqs[li][b], ik, n, w.K, L.pool_size)
-            elif L.mode == "reindex":
-                sel = oracle.reindex_select(iqs[li][b], ik, pool, n, w.K)
-            oracle_attend(w, qs[li][b], codes, scales, sel, n, wins.get((li, b)))
+        c1, s1 = oracle.quantize(new_kv[b])  # the newest token(s), written by the first Full layer
+        codes[int(lens[b]) - V:int(lens[b])], scales[int(lens[b]) - V:int(lens[b])] = c1, s1
+        for i in range(V):  # query row (b, i) sees the cache up to its own token
+            n = int(lens[b]) - V + 1 + i
+            r = b * V + i
+            pool = None
+            sel = None
+            for li, L in enumerate(w.layers):
+                if L.mode == "full":
+                    sel, pool, _ = oracle.full_select(iqs[li][r], ik, n, w.K, L.pool_size)
+                elif L.mode == "reindex":
+                    sel = oracle.reindex_select(iqs[li][r], ik, pool, n, w.K)
+                oracle_attend(w, qs[li][r], codes, scales, sel, n, wins.get((li, b)))
     dt = time.perf_counter() - t0
-    return {"value": reps * len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d sequences x %d repetitions of one full decode step of the %d-layer chain (quantize "
-                      "newest token, indexer scan over %d tokens, top-K, pool, Reindex, attention per layer); "
-                      "%.1f s wall" % (len(rows), w.B, reps, len(w.layers), int(lens[0]), dt)}
+    return {"value": reps * len(rows) * V / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d sequences x %d query rows x %d repetitions of one full decode step of the %d-layer "
+                      "chain (quantize newest token(s), indexer scan over %d tokens, top-K, pool, Reindex, attention "
+                      "per layer); %.1f s wall" % (len(rows), w.B, V, reps, len(w.layers), int(lens[0]), dt)}
 
 
 # ------------------------------------------------------------------ HIP events without a system fence
@@ -411,7 +418,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5", "c4"])
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5", "c4", "c3v"])
     ap.add_argument("--cpu-rows", type=int, default=16)
     ap.add_argument("--cpu-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -436,6 +443,9 @@ def main():
 
     device = torch.device("cuda:0")
     w = gen.get(args.workload)
+    if args.swa and w.verify > 1:
+        print("bench.py: --swa is built for one query row per sequence", file=sys.stderr)
+        sys.exit(2)
     if args.idx_mxfp4 and w.is_prefill:
         print("bench.py: --idx-mxfp4 is built for the decode workloads (the prefill chunk's MFMA indexer reads "
               "bf16 keys)", file=sys.stderr)
@@ -448,10 +458,16 @@ def main():
         lens = gen.seq_lens(w)
         cache, _ = build_cache(w, lens, device, mxfp4=args.idx_mxfp4)
         qs, iqs = layer_inputs(w, device)
-        new_rows = np.concatenate([[0], np.cumsum(lens)[:-1]]) + lens - 1
-        new_kv = torch.from_numpy(np.concatenate([gen.kv_rows(w, b, int(lens[b]) - 1, int(lens[b]))
+        V = w.verify  # the last V tokens of each sequence are (re)written by the step; row (b, i) sees up to draft i
+        starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+        new_rows = np.concatenate([starts[b] + np.arange(int(lens[b]) - V, int(lens[b])) for b in range(w.B)])
+        new_kv = torch.from_numpy(np.concatenate([gen.kv_rows(w, b, int(lens[b]) - V, int(lens[b]))
                                                   for b in range(w.B)])).to(device)
         new_rows_t = torch.from_numpy(new_rows.astype(np.int64)).to(device)
+        if V > 1:
+            cache.row_kv_start = torch.from_numpy(np.repeat(starts, V).astype(np.int64)).to(device)
+            cache.row_visible = torch.from_numpy(np.concatenate([int(lens[b]) - V + 1 + np.arange(V)
+                                                                 for b in range(w.B)]).astype(np.int32)).to(device)
     log("inputs built in %.1f s (%d cache rows)" % (time.time() - t, int(cache.kv_codes.shape[0])))
     wins = new_win = new_win_rows = None
     if args.swa:

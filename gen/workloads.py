@@ -97,6 +97,7 @@ class Workload:
     outlier_gain: float = 1.0
     drift_sigma: float = 0.0
     prefill_tokens: int = 0  # >0: prefill chunk of this many new tokens at the end
+    verify: int = 1  # decode query rows per sequence: the last `verify` cached tokens are drafts, checked in one pass
     block: int = 8  # HSI block size
 
     @property
@@ -109,8 +110,8 @@ class Workload:
 
     @property
     def rows(self) -> int:
-        """Query rows per layer: sequences for decode, chunk tokens for prefill."""
-        return self.prefill_tokens if self.is_prefill else self.B
+        """Query rows per layer: sequences (x draft rows) for decode, chunk tokens for prefill."""
+        return self.prefill_tokens if self.is_prefill else self.B * self.verify
 
     def scaled(self, **kw) -> "Workload":
         """The same distributions at other sizes (for oracle-sized parity runs)."""
@@ -137,6 +138,12 @@ WORKLOADS = {
         name="c4", description="prefill 4096 tokens onto 256K cached (n=266240), causal top-2048",
         B=1, n=262144 + 4096, Hq=64, q_dtype="bf16", q_std=1.0, H=8, idx_dtype="bf16",
         K=2048, seed=3, layers=(Layer("full"),), prefill_tokens=4096),
+    "c3v": Workload(
+        name="c3v", description="the 128K chain checking 5 draft tokens per sequence in one pass: 80 query rows",
+        B=16, n=131072, Hq=64, q_dtype="bf16", q_std=1.0, H=8, idx_dtype="bf16",
+        K=2048, seed=2, verify=5,
+        layers=(Layer("full", 8192), Layer("reindex"), Layer("reindex"),
+                Layer("reuse"), Layer("reuse"), Layer("reuse"))),
     "c5": Workload(
         name="c5", description="long decode at 1M, B=4, drifting keys: Full(pool 16384), Reindex, Reuse",
         B=4, n=1048576, Hq=64, q_dtype="bf16", q_std=1.0, H=8, idx_dtype="bf16",

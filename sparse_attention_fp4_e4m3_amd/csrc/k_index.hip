@@ -15,8 +15,9 @@
 //   k_score     Full: every visible entry; Reindex: the pool entries.  Key
 //               rows are staged through LDS with fully coalesced 16-byte
 //               loads (the next tile prefetched into registers), queries
-//               reach every lane through scalar loads, each thread runs the H
-//               fmaf chains of one key.  Full also writes the 8-entry block maxima and
+//               reach every lane through scalar loads (Full over bf16 / fp32
+//               keys) or broadcast LDS loads of a once-staged copy (Reindex,
+//               MXFP4 keys), each thread runs the H fmaf chains of one key.  Full also writes the 8-entry block maxima and
 //               builds the first radix histogram (12 bits) of scores and
 //               block maxima in the same pass.  HBM-bound on the key rows.
 //   k_collect   (Full) every wave compacts, in position order, the entries
@@ -263,6 +264,8 @@ struct ScoreArgs {
   uint32_t* hist_s;           // [R][kD1]
   uint32_t* hist_b;           // [R][kD1]
   int tiles_per_wg;
+  int n_rows;                 // rows of the grid
+  int n_ranges;               // key ranges (of tiles_per_wg tiles) per row
   const uint32_t* row_mask;   // [R] nonzero = score this row; null = every row
   int shared_start;           // every row reads the segment at row_start[0]
 };
@@ -305,15 +308,24 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
   uint8_t* tile = smem + wv * T::kWaveBytes;                                       // this wave's rows
   uint32_t* h1 = reinterpret_cast<uint32_t*>(smem + kWavesPerWG * T::kWaveBytes);  // kD1/2 packed
   uint32_t* hb = h1 + kD1 / 2;                                                     // kD1/2 packed (POOL)
+  // queries [quad][head][4]: after the histograms (Full), or where they would start (Reindex has none)
+  float* sq = reinterpret_cast<float*>(REINDEX ? h1 : hb + (POOL ? kD1 / 2 : 0));
 
   const int H = HC > 0 ? HC : a.H;
-  const int r = blockIdx.y;
+  // XCD-aware order: workgroups are handed to the 8 XCDs round-robin by id, so ids
+  // 8 s + x (x = id % 8) run on XCD x.  Tile range t of every row is placed on XCD t % 8 in
+  // consecutive slots (row fastest): rows that read the same keys (draft rows of one
+  // sequence, a chunk's rows) meet them in that XCD's L2 at about the same time.
+  const int wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
+  const int r = slot % a.n_rows;
+  const int trange = (slot / a.n_rows) * 8 + xcd;
+  if (trange >= a.n_ranges) return;
   if (a.row_mask && !a.row_mask[r]) return;
   const int vis = clampv(a.row_visible[r], a.max_visible);
   int plen = 0;
   if (REINDEX) plen = a.pool_len ? clampv(a.pool_len[r], a.pool_stride) : a.pool_stride;
   const int n = REINDEX ? plen : vis;  // slots scored: Reindex, the pool's valid length
-  const int64_t base0 = (int64_t)blockIdx.x * a.tiles_per_wg * kWGKeys;
+  const int64_t base0 = (int64_t)trange * a.tiles_per_wg * kWGKeys;
   if (base0 >= n) return;
   const int ntiles = (int)std::min<int64_t>(a.tiles_per_wg, ceil_div(n - base0, kWGKeys));
   if (!REINDEX) {
@@ -321,8 +333,26 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
       h1[b] = 0u;
       if (POOL) hb[b] = 0u;
     }
-    __syncthreads();
   }
+  // Reindex and MXFP4 keys: the row's queries to LDS as fp32 in [channel quad][head][4] order (Full: the
+  // prepared block, already in that order; Reindex: the caller's [head][64] queries, bf16 widened): every
+  // lane reads a quad's H x 4 values as same-address (broadcast) LDS loads, which the compiler issues
+  // ahead of their use.  Full over bf16 / fp32 keys, whose key rows already come from LDS, keeps scalar
+  // loads of the prepared block (measured: LDS queries there halve its rate).
+  constexpr bool kLdsQ = REINDEX || T::kMx;
+  for (int i = threadIdx.x; kLdsQ && i < H * kIdxDim; i += kThreads) {
+    float v;
+    if constexpr (REINDEX) {
+      const int h = i / kIdxDim, c = i % kIdxDim;
+      const int64_t at = ((int64_t)r * H + h) * kIdxDim + c;
+      v = QDT == CSA2_BF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(qsrc)[at] << 16)
+                           : static_cast<const float*>(qsrc)[at];
+      sq[((c >> 2) * H + h) * 4 + (c & 3)] = v;
+    } else {
+      sq[i] = static_cast<const float*>(qsrc)[(int64_t)r * H * kIdxDim + i];
+    }
+  }
+  __syncthreads();
   const int64_t rs = a.row_start[a.shared_start ? 0 : r];
   const uint8_t* kbase = static_cast<const uint8_t*>(a.idx_k);
   float* srow = a.scores + (int64_t)r * a.n_pad;
@@ -441,31 +471,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
 #pragma unroll
         for (int e = 0; e < 4; ++e) kv[e] = __uint_as_float(w[e]);
       }
-      // the H x 4 query values of this channel quad are wave-uniform: scalar loads
-      if constexpr (REINDEX) {
-#pragma unroll
-        for (int h = 0; h < NACC; ++h) {
-          if (HC > 0 || h < H) {
-            float qv[4];
-            if constexpr (QDT == CSA2_BF16) {
-              const uint32_t* qp = static_cast<const uint32_t*>(qsrc) + ((int64_t)r * H + h) * (kIdxDim / 2) + 2 * c4;
-              const uint32_t w0 = qp[0], w1 = qp[1];
-              qv[0] = __uint_as_float(w0 << 16);
-              qv[1] = __uint_as_float(w0 & 0xFFFF0000u);
-              qv[2] = __uint_as_float(w1 << 16);
-              qv[3] = __uint_as_float(w1 & 0xFFFF0000u);
-            } else {
-              const float* qp = static_cast<const float*>(qsrc) + ((int64_t)r * H + h) * kIdxDim + 4 * c4;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) qv[e] = qp[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[h] = __builtin_fmaf(qv[e], kv[e], acc[h]);
-          }
-        }
-        continue;
-      }
-      const float* qrow = static_cast<const float*>(qsrc) + (int64_t)r * H * kIdxDim + c4 * H * 4;
+      // the H x 4 query values of this channel quad: broadcast LDS loads
+      const float* qrow = kLdsQ ? sq + c4 * H * 4 : static_cast<const float*>(qsrc) + (int64_t)r * H * kIdxDim + c4 * H * 4;
       if constexpr (HC > 0) {
 #pragma unroll
         for (int h = 0; h < HC; ++h) {
@@ -1376,7 +1383,8 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
 template <int KDT, int HC, bool REINDEX, bool POOL, int QDT>
 void launch_score(const ScoreArgs& sa, const void* qsrc, dim3 grid, hipStream_t s) {
   using T = KeyTile<KDT>;
-  const size_t lds = (size_t)kWavesPerWG * T::kWaveBytes + (REINDEX ? 0 : (size_t)kD1 / 2 * 4 * (POOL ? 2 : 1));
+  const size_t lds = (size_t)kWavesPerWG * T::kWaveBytes + (REINDEX ? 0 : (size_t)kD1 / 2 * 4 * (POOL ? 2 : 1)) +
+                     ((REINDEX || T::kMx) ? (size_t)(HC > 0 ? HC : kMaxHeads) * kIdxDim * 4 : 0);
   auto kern = k_score<KDT, HC, REINDEX, POOL, QDT>;
   static bool configured = false;
   if (!configured) {
@@ -1448,7 +1456,9 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     const int64_t tiles = ceil_div(n, (int64_t)kWGKeys);
     sa.tiles_per_wg =
         (int)std::min<int64_t>(255, ceil_div(tiles, std::max<int64_t>(1, ceil_div((int64_t)kScanSlots, R))));
-    const dim3 grid((unsigned)ceil_div(tiles, (int64_t)sa.tiles_per_wg), (unsigned)R);
+    sa.n_rows = R;
+    sa.n_ranges = (int)ceil_div(tiles, (int64_t)sa.tiles_per_wg);
+    const dim3 grid((unsigned)(round_up(sa.n_ranges, 8) * R));
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
     if (record && ev.start) (void)hipEventRecord(ev.start, s);
     const bool qbf = q_dtype == CSA2_BF16;

@@ -155,6 +155,42 @@ def test_chain_with_local_windows_scaled():
     say("max err %.3e" % worst)
 
 
+def test_verification_rows_scaled():
+    """Checking 5 draft tokens per sequence in one pass (the 5-row verification workload at oracle
+    size): rows (b, 0..4) share sequence b's cache and see it up to their own draft; the step
+    writes the drafts' KV first."""
+    w = gen.get("c3v").scaled(B=2, n=20000, K=512, layers=(gen.Layer("full", 2048), gen.Layer("reindex"),
+                                                           gen.Layer("reuse")))
+    V = w.verify
+    lens, starts, raw, ik, cache, qs, iqs = _setup(w)
+    cache.row_kv_start = dev(np.repeat(starts, V).astype(np.int64))
+    vis = np.concatenate([lens[b] - V + 1 + np.arange(V) for b in range(w.B)]).astype(np.int32)
+    cache.row_visible = dev(vis)
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.rows, w.Hq, w.H, w.K, cache.max_visible,
+                       qs[0].dtype, DEV)
+    new_rows = dev(np.concatenate([starts[b] + np.arange(lens[b] - V, lens[b]) for b in range(w.B)]).astype(np.int64))
+    new_kv = torch.from_numpy(np.concatenate([r[-V:] for r in raw])).to(DEV)
+    chain.step(cache, qs, iqs, w.softmax_scale, new_kv=new_kv, new_kv_rows=new_rows)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b in range(w.B):
+        oc, os_ = oracle.quantize(raw[b])
+        for i in range(V):
+            r, n = b * V + i, int(vis[b * V + i])
+            pool = sel = None
+            for li, L in enumerate(w.layers):
+                if L.mode == "full":
+                    sel, pool, _ = oracle.full_select(gen.index_q(w, li, r, r + 1)[0], ik[b], n, w.K, L.pool_size)
+                elif L.mode == "reindex":
+                    sel = oracle.reindex_select(gen.index_q(w, li, r, r + 1)[0], ik[b], pool, n, w.K)
+                if L.mode != "reuse":
+                    assert np.array_equal(chain.idx[li][r].cpu().numpy(), sel), "indices, layer %d row %d" % (li, r)
+                o, lse = oracle.attention(gen.attn_q(w, li, r, r + 1)[0], oc, os_, sel, n, w.softmax_scale)
+                worst = max(worst, check_attention(chain.out[li][r:r + 1], chain.lse[li][r:r + 1], o[None],
+                                                   lse[None], "verify layer %d row %d" % (li, r)))
+    say("max err %.3e" % worst)
+
+
 def test_chain_with_mxfp4_indexer_keys_scaled():
     """The 128K chain's structure with MXFP4 indexer keys written by the library: every selection
     equals the oracle's over the dequantized keys."""
