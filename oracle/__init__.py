@@ -262,6 +262,18 @@ def attention_rows_swa(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, row
     return o, lse
 
 
+def visible_entries(t: int, m: int) -> int:
+    """Cache entries a query at token position t sees when each entry folds m tokens: the entries
+    whose whole block of m tokens lies at or before t (the brief's encoder layers compress m = 2
+    tokens per entry, "The global branch" / mode layout).  Counted one block at a time."""
+    n = 0
+    e = 0
+    while m * e + (m - 1) <= t:
+        n += 1
+        e += 1
+    return n
+
+
 # ------------------------------------------------------------------- modes
 
 def full_select(idx_q: np.ndarray, idx_k: np.ndarray, visible: int, K: int,

@@ -23,4 +23,4 @@ from .csa2 import (  # noqa: F401
     sparse_attn_swa_workspace_size,
     sparse_attn_workspace_size,
 )
-from .chain import Cache, LayerChain, LayerSpec, Window, validate_modes  # noqa: F401
+from .chain import Cache, LayerChain, LayerSpec, Window, compressed_visible, validate_modes  # noqa: F401

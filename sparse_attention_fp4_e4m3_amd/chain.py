@@ -56,6 +56,16 @@ class LayerSpec:
     pool_size: int = 0          # Full only
 
 
+def compressed_visible(positions, m: int):
+    """Entries a query at token position t may attend when each cache entry folds m consecutive
+    tokens (entry e covers tokens m*e .. m*e + m - 1): only complete blocks, so (t + 1) // m.
+    m = 1 gives t + 1 (every token up to and including the query's own).  Works on ints, numpy
+    arrays and torch tensors; the result is what row_visible takes."""
+    if m < 1:
+        raise ValueError("m must be >= 1")
+    return (positions + 1) // m
+
+
 def validate_modes(layers: Sequence[LayerSpec]) -> None:
     have_full = have_pool = have_sel = False
     for i, L in enumerate(layers):

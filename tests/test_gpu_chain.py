@@ -256,3 +256,35 @@ def test_graph_replay_matches_eager(swa):
         got = chain.out + chain.lse + [i for i in chain.idx if i is not None]
         for a, b in zip(got, eager):
             assert torch.equal(a, b), "replay %d differs from eager" % rep
+
+
+def test_compressed_entries_visibility_in_a_chunk():
+    """Encoder-style entries that fold m = 2 tokens: chunk token t (rows of one shared segment) may
+    attend only complete blocks, row_visible = (t + 1) // 2.  Selection and attention against the
+    oracle at those visible counts."""
+    from sparse_attention_fp4_e4m3_amd import compressed_visible
+    T, P0, H, Hq, K = 64, 8001, 8, 64, 256
+    nc = (P0 + T) // 2
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((nc, 512)).astype(np.float32)
+    k = gen.bf16_round(rng.standard_normal((nc, 64)).astype(np.float32))
+    oc, os_ = oracle.quantize(x)
+    vis = compressed_visible(P0 + np.arange(T), 2).astype(np.int32)
+    assert vis.min() == (P0 + 1) // 2 and vis.max() == nc
+    cache = Cache(dev(oc), dev(os_), _to_dev(k, "bf16"), dev(np.zeros(T, np.int64)), dev(vis), nc,
+                  shared_segment=True)
+    q = gen.bf16_round(rng.standard_normal((T, Hq, 512)).astype(np.float32))
+    iq = gen.bf16_round(rng.standard_normal((T, H, 64)).astype(np.float32))
+    chain = LayerChain([LayerSpec("full")], T, Hq, H, K, nc, torch.bfloat16, DEV, shared_segment=True)
+    chain.step(cache, [_to_dev(q, "bf16")], [_to_dev(iq, "bf16")], 1 / np.sqrt(512))
+    torch.cuda.synchronize()
+    got = chain.idx[0].cpu().numpy()
+    worst = 0.0
+    for r in [0, 1, 2, 31, 62, 63]:
+        sel, _, _ = oracle.full_select(iq[r], k, int(vis[r]), K)
+        assert np.array_equal(got[r], sel), "row %d" % r
+        assert got[r].max() < vis[r]
+        o, lse = oracle.attention(q[r], oc, os_, sel, int(vis[r]), 1 / np.sqrt(512))
+        worst = max(worst, check_attention(chain.out[0][r:r + 1], chain.lse[0][r:r + 1], o[None], lse[None],
+                                           "m=2 row %d" % r))
+    say("max err %.3e" % worst)

@@ -145,3 +145,20 @@ def test_reindex_equals_brute_force_on_pool():
     got = oracle.reindex_select(q, k, pool, visible, K)
     cand = pool[(pool >= 0) & (pool < visible)]
     assert np.array_equal(got, _brute_topk(s_all[cand], K, cand))
+
+
+def test_compressed_visibility_counts_only_complete_blocks():
+    """m tokens per entry (encoder layers fold m = 2): a query sees only the entries whose whole
+    block lies at or before it.  Pinned by the block count itself (brute force over tokens), by
+    m = 1 reducing to the causal t + 1, and by the library helper on arrays."""
+    import numpy as np
+    from sparse_attention_fp4_e4m3_amd import compressed_visible
+    for m in (1, 2, 3, 4):
+        for t in range(0, 50):
+            complete = sum(1 for e in range(t + 1) if all(m * e + k <= t for k in range(m)))
+            assert oracle.visible_entries(t, m) == complete
+            assert compressed_visible(t, m) == complete
+    assert all(oracle.visible_entries(t, 1) == t + 1 for t in range(100))
+    assert [oracle.visible_entries(t, 2) for t in range(6)] == [0, 1, 1, 2, 2, 3]
+    pos = np.arange(262144, 262144 + 4096)
+    assert np.array_equal(compressed_visible(pos, 2), np.array([oracle.visible_entries(int(t), 2) for t in pos]))
