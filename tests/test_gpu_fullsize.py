@@ -5,7 +5,8 @@ For every sampled sequence the oracle regenerates the raw inputs from the
 seeded generators and computes, on its own: FP4 codes of every entry the
 check touches, the Full indexer scores over the whole visible context, the
 top-K, the hierarchical pool, Reindex selections and the attention of every
-layer.  Indices, pools and codes must match bit for bit; attention outputs
+layer (joined with the layer's FP8 window, over MXFP4 indexer keys, or for
+every draft row of a sequence, in the corresponding variants).  Indices, pools and codes must match bit for bit; attention outputs
 within 2e-3 (row-normwise per head).
 """
 import numpy as np
@@ -21,31 +22,44 @@ from sparse_attention_fp4_e4m3_amd import Cache, LayerChain, LayerSpec, csa2
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
 
-def _chain_fullsize(name, sample):
+def _chain_fullsize(name, sample, swa=False, mxfp4=False):
+    """The named decode workload at full size, as the benchmark runs it (optionally with every
+    layer's FP8 window, or with MXFP4 indexer keys), checked on the sampled sequences (every
+    draft row of a sequence for the verification workload)."""
     w = gen.get(name)
+    V = w.verify
     lens = gen.seq_lens(w)
     say("%s: building the FP4 cache (%d entries)" % (name, int(lens.sum())))
-    cache, starts = bench.build_cache(w, lens, DEV)
+    cache, starts = bench.build_cache(w, lens, DEV, mxfp4=mxfp4)
+    vis_rows = np.concatenate([lens[b] - V + 1 + np.arange(V) for b in range(w.B)]).astype(np.int32)
+    if V > 1:
+        cache.row_kv_start = dev(np.repeat(starts, V).astype(np.int64))
+        cache.row_visible = dev(vis_rows)
     qs, iqs = bench.layer_inputs(w, DEV)
-    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.B, w.Hq, w.H, w.K, cache.max_visible,
-                       qs[0].dtype, DEV)
-    chain.step(cache, qs, iqs, w.softmax_scale)
+    wins = bench.build_windows(w, lens, DEV)[0] if swa else None
+    chain = LayerChain([LayerSpec(L.mode, L.pool_size) for L in w.layers], w.rows, w.Hq, w.H, w.K, cache.max_visible,
+                       qs[0].dtype, DEV, swa=swa)
+    chain.step(cache, qs, iqs, w.softmax_scale, windows=wins)
     torch.cuda.synchronize()
     for b in sample:
         n, s0 = int(lens[b]), int(starts[b])
         say("%s: oracle for sequence %d (n=%d)" % (name, b, n))
         ik = gen.idx_k_rows(w, b, 0, n)
+        if mxfp4:  # the keys the GPU scores: MXFP4 of the same values, dequantized exactly
+            ik = oracle.mxfp4_dequant(*oracle.mxfp4_quantize(ik))
         raw = gen.kv_rows(w, b, 0, n)
-        pool = sel = None
         touched = set()
-        ref = []
-        for li, L in enumerate(w.layers):
-            if L.mode == "full":
-                sel, pool, plen = oracle.full_select(gen.index_q(w, li, b, b + 1)[0], ik, n, w.K, L.pool_size)
-            elif L.mode == "reindex":
-                sel = oracle.reindex_select(gen.index_q(w, li, b, b + 1)[0], ik, pool, n, w.K)
-            ref.append((sel.copy(), None if pool is None else pool.copy()))
-            touched.update(int(j) for j in sel if j >= 0)
+        ref = {}
+        for i in range(V):
+            r, nv = b * V + i, int(vis_rows[b * V + i])
+            pool = sel = None
+            for li, L in enumerate(w.layers):
+                if L.mode == "full":
+                    sel, pool, plen = oracle.full_select(gen.index_q(w, li, r, r + 1)[0], ik, nv, w.K, L.pool_size)
+                elif L.mode == "reindex":
+                    sel = oracle.reindex_select(gen.index_q(w, li, r, r + 1)[0], ik, pool, nv, w.K)
+                ref[r, li] = (sel.copy(), None if pool is None else pool.copy(), nv)
+                touched.update(int(j) for j in sel if j >= 0)
         rng = np.random.default_rng(b)
         rows = np.array(sorted(touched | set(rng.integers(0, n, 2000).tolist()) | {0, n - 1}), np.int64)
         oc_rows, os_rows = oracle.quantize(raw[rows])
@@ -56,17 +70,25 @@ def _chain_fullsize(name, sample):
         oc = np.zeros((n, 256), np.uint8)
         os_ = np.zeros((n, 32), np.uint8)
         oc[rows], os_[rows] = oc_rows, os_rows
-        for li, L in enumerate(w.layers):
-            sel, pool = ref[li]
+        for (r, li), (sel, pool, nv) in sorted(ref.items()):
+            L = w.layers[li]
             if L.mode != "reuse":
-                got = chain.idx[li][b].cpu().numpy()
-                assert np.array_equal(got, sel), "indices differ: layer %d sequence %d" % (li, b)
+                got = chain.idx[li][r].cpu().numpy()
+                assert np.array_equal(got, sel), "indices differ: layer %d row %d" % (li, r)
             if L.mode == "full" and L.pool_size:
                 gp, gl = chain.pool[li]
-                assert np.array_equal(gp[b].cpu().numpy(), pool), "pool differs: sequence %d" % b
-            o, lse = oracle.attention(gen.attn_q(w, li, b, b + 1)[0], oc, os_, sel, n, w.softmax_scale)
-            check_attention(chain.out[li][b:b + 1], chain.lse[li][b:b + 1], o[None], lse[None],
-                            "%s layer %d (%s) seq %d" % (name, li, L.mode, b))
+                assert np.array_equal(gp[r].cpu().numpy(), pool), "pool differs: row %d" % r
+            q = gen.attn_q(w, li, r, r + 1)
+            if swa:
+                wc = oracle.e4m3_encode_signed(gen.window_rows(w, li, b, max(0, n - 128), n))
+                z = np.zeros(1, np.int64)
+                o, lse = oracle.attention_rows_swa(q, oc, os_, z, sel[None], np.array([nv]), wc, z,
+                                                   np.array([len(wc)], np.int32), w.softmax_scale)
+                o, lse = o[0], lse[0]
+            else:
+                o, lse = oracle.attention(q[0], oc, os_, sel, nv, w.softmax_scale)
+            check_attention(chain.out[li][r:r + 1], chain.lse[li][r:r + 1], o[None], lse[None],
+                            "%s layer %d (%s) row %d" % (name, li, L.mode, r))
 
 
 def test_decode_full_32x_32k_64k():
@@ -75,6 +97,18 @@ def test_decode_full_32x_32k_64k():
 
 def test_chain_128k_batch16():
     _chain_fullsize("c3", sample=[0, 9])
+
+
+def test_chain_128k_batch16_with_local_windows():
+    _chain_fullsize("c3", sample=[0, 9], swa=True)
+
+
+def test_chain_128k_batch16_mxfp4_indexer_keys():
+    _chain_fullsize("c3", sample=[0, 9], mxfp4=True)
+
+
+def test_chain_128k_verification_5_draft_rows():
+    _chain_fullsize("c3v", sample=[3])
 
 
 def test_long_decode_1m_batch4():
