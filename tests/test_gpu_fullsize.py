@@ -116,7 +116,8 @@ def test_long_decode_1m_batch4():
 
 
 def test_prefill_4096_on_256k():
-    """4096 new tokens appended causally to 262,144 cached: row r sees [0, 262144 + r]."""
+    """4096 new tokens appended causally to 262,144 cached: row r sees [0, 262144 + r]; then the same
+    attention joined with each row's 128-token FP8 window."""
     w = gen.get("c4")
     T = w.prefill_tokens
     P0 = w.n - T
@@ -163,6 +164,30 @@ def test_prefill_4096_on_256k():
         oc[rows], os_[rows] = oc_rows, os_rows
         o, l = oracle.attention(gen.attn_q(w, 0, r, r + 1)[0], oc, os_, sel, nvis, w.softmax_scale)
         check_attention(out[r:r + 1], lse[r:r + 1], o[None], l[None], "c4 row %d" % r)
+    # the same chunk with the local windows joined (the benchmark's --swa configuration): each row's
+    # 128-token FP8 window ends at its own position; the chunk's window rows are written first
+    wins, new_win, new_win_rows = bench.build_windows(w, lens, DEV)
+    csa2.quantize_swa_fp8(new_win[0], wins[0].codes, new_win_rows)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    aws = torch.empty(max(256, csa2.sparse_attn_swa_workspace_size(T, w.Hq, csa2.BF16, w.K)), dtype=torch.uint8,
+                      device=DEV)
+    csa2.sparse_attn_swa(q, wins[0].codes, wins[0].row_start, wins[0].row_len, out2, w.softmax_scale,
+                         kv_codes=codes, kv_scales=scales, row_kv_start=starts, idx=idx, row_visible=vis, lse=lse2,
+                         workspace=aws)
+    torch.cuda.synchronize()
+    for r in [0, 1, 2048, T - 1]:
+        nvis = P0 + r + 1
+        sel = idx[r].cpu().numpy()
+        rows = np.array(sorted(set(int(j) for j in sel if j >= 0)), np.int64)
+        oc = np.zeros((w.n, 256), np.uint8)
+        os_ = np.zeros((w.n, 32), np.uint8)
+        oc[rows], os_[rows] = oracle.quantize(raw[rows])
+        wc = oracle.e4m3_encode_signed(gen.window_rows(w, 0, 0, nvis - 128, nvis))
+        z = np.zeros(1, np.int64)
+        o, l = oracle.attention_rows_swa(gen.attn_q(w, 0, r, r + 1), oc, os_, z, sel[None], np.array([nvis]), wc, z,
+                                         np.array([128], np.int32), w.softmax_scale)
+        check_attention(out2[r:r + 1], lse2[r:r + 1], o, l, "c4 window row %d" % r)
     # causality: no row selects a position it cannot see
     idx_np = idx.cpu().numpy()
     limit = (P0 + np.arange(T))[:, None]
