@@ -264,8 +264,6 @@ struct ScoreArgs {
   uint32_t* hist_s;           // [R][kD1]
   uint32_t* hist_b;           // [R][kD1]
   int tiles_per_wg;
-  int n_rows;                 // rows of the grid
-  int n_ranges;               // key ranges (of tiles_per_wg tiles) per row
   const uint32_t* row_mask;   // [R] nonzero = score this row; null = every row
   int shared_start;           // every row reads the segment at row_start[0]
 };
@@ -312,14 +310,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
   float* sq = reinterpret_cast<float*>(REINDEX ? h1 : hb + (POOL ? kD1 / 2 : 0));
 
   const int H = HC > 0 ? HC : a.H;
-  // XCD-aware order: workgroups are handed to the 8 XCDs round-robin by id, so ids
-  // 8 s + x (x = id % 8) run on XCD x.  Tile range t of every row is placed on XCD t % 8 in
-  // consecutive slots (row fastest): rows that read the same keys (draft rows of one
-  // sequence, a chunk's rows) meet them in that XCD's L2 at about the same time.
-  const int wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
-  const int r = slot % a.n_rows;
-  const int trange = (slot / a.n_rows) * 8 + xcd;
-  if (trange >= a.n_ranges) return;
+  const int r = blockIdx.y, trange = blockIdx.x;
   if (a.row_mask && !a.row_mask[r]) return;
   const int vis = clampv(a.row_visible[r], a.max_visible);
   int plen = 0;
@@ -1456,9 +1447,7 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     const int64_t tiles = ceil_div(n, (int64_t)kWGKeys);
     sa.tiles_per_wg =
         (int)std::min<int64_t>(255, ceil_div(tiles, std::max<int64_t>(1, ceil_div((int64_t)kScanSlots, R))));
-    sa.n_rows = R;
-    sa.n_ranges = (int)ceil_div(tiles, (int64_t)sa.tiles_per_wg);
-    const dim3 grid((unsigned)(round_up(sa.n_ranges, 8) * R));
+    const dim3 grid((unsigned)ceil_div(tiles, (int64_t)sa.tiles_per_wg), (unsigned)R);
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
     if (record && ev.start) (void)hipEventRecord(ev.start, s);
     const bool qbf = q_dtype == CSA2_BF16;
