@@ -528,8 +528,12 @@ def main():
                 "reindex_score": sum(L.mode == "reindex" for L in w.layers),
                 "attention": len(w.layers), "attention_combine": len(w.layers)}
     if args.swa:
-        kernels.update({"swa_attention": csa2.KERNEL_SWA_ATTN, "quantize_fp8": csa2.KERNEL_QUANT_FP8})
-        n_launch.update({"swa_attention": len(w.layers), "quantize_fp8": len(w.layers)})
+        # decode writes each row's window token inside the attention call; a prefill chunk writes first
+        kernels["swa_attention"] = csa2.KERNEL_SWA_ATTN
+        n_launch["swa_attention"] = len(w.layers)
+        if w.is_prefill:
+            kernels["quantize_fp8"] = csa2.KERNEL_QUANT_FP8
+            n_launch["quantize_fp8"] = len(w.layers)
 
     def arm(kid):
         if args.event_kind == "torch":
@@ -571,8 +575,8 @@ def main():
         # the window: 128 entries x 512 B per row; QK^T and PV over them for every head
         kern["swa_attention"] = {"avg_us": per_kernel_us["swa_attention"], "bytes": w.rows * 128 * 512,
                                  "flops": 4.0 * w.rows * w.Hq * 128 * 512}
-        kern["quantize_fp8"] = {"avg_us": per_kernel_us["quantize_fp8"],
-                                "bytes": (w.prefill_tokens or w.B) * (512 * 4 + 512)}
+        if w.is_prefill:
+            kern["quantize_fp8"] = {"avg_us": per_kernel_us["quantize_fp8"], "bytes": w.prefill_tokens * (512 * 4 + 512)}
     for k, v in kern.items():
         if "bytes" in v and v["avg_us"] > 0:
             v["GBps"] = v["bytes"] / (v["avg_us"] * 1e3)

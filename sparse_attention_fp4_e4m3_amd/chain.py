@@ -165,10 +165,14 @@ class LayerChain:
                                  workspace=self.ws_attn, stream=stream)
                 continue
             win = windows[i]
-            if new_win is not None:
+            # one window per row (decode): the attention call writes each row's token itself; a
+            # chunk's rows share overlapping windows, so its tokens are written first
+            fused = new_win is not None and not cache.shared_segment
+            if new_win is not None and not fused:
                 csa2.quantize_swa_fp8(new_win[i], win.codes, new_win_rows, stream=stream)
             csa2.sparse_attn_swa(q[i], win.codes, win.row_start, win.row_len, self.out[i], softmax_scale,
                                  kv_codes=cache.kv_codes, kv_scales=cache.kv_scales, row_kv_start=cache.row_kv_start,
                                  idx=last_sel, row_visible=cache.row_visible, lse=self.lse[i],
-                                 workspace=self.ws_attn, stream=stream)
+                                 workspace=self.ws_attn, new_x=new_win[i] if fused else None,
+                                 new_rows=new_win_rows if fused else None, stream=stream)
         return self.out

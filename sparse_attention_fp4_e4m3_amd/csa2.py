@@ -73,8 +73,8 @@ def lib():
         L.csa2_index_topk_mxfp4.restype = i32
         L.csa2_quantize_swa_fp8.argtypes = [P, i32, i64, i64, P, P, i64, P]
         L.csa2_quantize_swa_fp8.restype = i32
-        L.csa2_sparse_attn_swa.argtypes = [i32, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P, ctypes.c_float, P, i32,
-                                           P, P, sz, P]
+        L.csa2_sparse_attn_swa.argtypes = [i32, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, i32, i64, P,
+                                           ctypes.c_float, P, i32, P, P, sz, P]
         L.csa2_sparse_attn_swa.restype = i32
         L.csa2_sparse_attn_swa_workspace_size.argtypes = [i32, i32, i32, i32]
         L.csa2_sparse_attn_swa_workspace_size.restype = sz
@@ -213,16 +213,22 @@ def sparse_attn_swa(q: torch.Tensor, win_codes: torch.Tensor, row_win_start: tor
                     kv_codes: Optional[torch.Tensor] = None, kv_scales: Optional[torch.Tensor] = None,
                     row_kv_start: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
                     row_visible: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Selected FP4 entries (idx; None = window only) joined with each row's FP8 window in one softmax."""
+                    workspace: Optional[torch.Tensor] = None, new_x: Optional[torch.Tensor] = None,
+                    new_rows: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Selected FP4 entries (idx; None = window only) joined with each row's FP8 window in one softmax;
+    new_x [R, 512(+)] / new_rows [R]: each row's newest token, written into its window by the same call."""
     _contig(q, win_codes, row_win_start, row_win_len, out, kv_codes, kv_scales, row_kv_start, idx, row_visible, lse,
-            workspace)
+            workspace, new_rows)
+    if new_x is not None and (new_x.dim() != 2 or new_x.stride(1) != 1):
+        raise ValueError("new_x must be [R, C] with unit channel stride")
     R, Hq, D = q.shape
     top_k = 0 if idx is None else idx.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().csa2_sparse_attn_swa(
         R, _ptr(q), _dt(q), Hq, D, _ptr(kv_codes), _ptr(kv_scales), _ptr(row_kv_start), _ptr(idx), top_k,
-        _ptr(row_visible), _ptr(win_codes), _ptr(row_win_start), _ptr(row_win_len), float(softmax_scale), _ptr(out),
+        _ptr(row_visible), _ptr(win_codes), _ptr(row_win_start), _ptr(row_win_len), _ptr(new_x),
+        _dt(new_x) if new_x is not None else 0, new_x.stride(0) if new_x is not None else 0, _ptr(new_rows),
+        float(softmax_scale), _ptr(out),
         _dt(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 

@@ -203,7 +203,8 @@ int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t
     return fail(CSA2_E_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
   if (need && !aligned(workspace, 256)) return fail(CSA2_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
   return hip_status(launch_sparse_attn(n_rows, q, q_dtype, n_heads, kv_codes, kv_scales, row_kv_start, idx, top_k,
-                                       row_visible, nullptr, nullptr, nullptr, softmax_scale, out, out_dtype, lse,
+                                       row_visible, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, softmax_scale,
+                                       out, out_dtype, lse,
                                        workspace, static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -236,6 +237,7 @@ int32_t csa2_sparse_attn_swa(int32_t n_rows, const void* q, int32_t q_dtype, int
                              const uint8_t* kv_codes, const uint8_t* kv_scales, const int64_t* row_kv_start,
                              const int32_t* idx, int32_t top_k, const int32_t* row_visible,
                              const uint8_t* win_codes, const int64_t* row_win_start, const int32_t* row_win_len,
+                             const void* new_x, int32_t new_x_dtype, int64_t new_x_stride, const int64_t* new_rows,
                              float softmax_scale, void* out, int32_t out_dtype, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream) {
   const char* fn = "csa2_sparse_attn_swa";
@@ -254,13 +256,21 @@ int32_t csa2_sparse_attn_swa(int32_t n_rows, const void* q, int32_t q_dtype, int
     return fail(CSA2_E_INVALID, "%s: q/out/win_codes must be 16-byte aligned", fn);
   if (top_k > 0 && (!aligned(kv_codes, 16) || !aligned(kv_scales, 8)))
     return fail(CSA2_E_INVALID, "%s: kv_codes must be 16-byte and kv_scales 8-byte aligned", fn);
+  if (new_x) {
+    if (!dtype_ok(new_x_dtype)) return fail(CSA2_E_INVALID, "%s: new_x_dtype %d is not F32/BF16", fn, new_x_dtype);
+    if (!new_rows) return fail(CSA2_E_INVALID, "%s: new_x without new_rows", fn);
+    if (new_x_stride < kDim) return fail(CSA2_E_INVALID, "%s: new_x_stride %lld < 512", fn, (long long)new_x_stride);
+    if (!aligned(new_x, 16) || (new_x_stride * (int64_t)dtype_size(new_x_dtype)) % 16)
+      return fail(CSA2_E_INVALID, "%s: new_x rows must be 16-byte aligned", fn);
+  }
   const size_t need = attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k, true);
   if (need && (!workspace || workspace_bytes < need))
     return fail(CSA2_E_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
   if (need && !aligned(workspace, 256)) return fail(CSA2_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
   return hip_status(launch_sparse_attn(n_rows, q, q_dtype, n_heads, kv_codes, kv_scales, row_kv_start, idx, top_k,
-                                       row_visible, win_codes, row_win_start, row_win_len, softmax_scale, out,
-                                       out_dtype, lse, workspace, static_cast<hipStream_t>(stream)),
+                                       row_visible, win_codes, row_win_start, row_win_len, new_x, new_x_dtype,
+                                       new_x_stride, new_rows, softmax_scale, out, out_dtype, lse, workspace,
+                                       static_cast<hipStream_t>(stream)),
                     fn);
 }
 

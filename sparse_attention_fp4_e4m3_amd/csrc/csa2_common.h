@@ -58,6 +58,7 @@ size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window);
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
                               const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
                               const uint8_t* win, const int64_t* win_start, const int32_t* win_len,
+                              const void* new_x, int new_x_dtype, int64_t new_x_stride, const int64_t* new_rows,
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
 
 // ------------------------------------------------------------ device helpers
@@ -68,6 +69,22 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
 // Use it only where the data exchanged through the barrier lives in LDS.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// nearest E4M3 (E4M3FN) code of v >= 0, ties to even, saturating at 448
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  if (!(v > 0.0f)) return 0u;
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9 (scaling by 512 is exact)
+    return (uint32_t)__float2int_rn(v * 512.0f);
+  }
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t e = (u >> 23) - 120u;  // rebias 127 -> 7
+  const uint32_t man = u & 0x7FFFFFu;
+  const uint32_t keep = man >> 20, rest = man & 0xFFFFFu;
+  uint32_t code = (e << 3) | keep;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) code += 1u;  // carries into the exponent
+  return code;
 }
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -129,7 +129,40 @@ struct AttnArgs {
   const uint8_t* win;        // local window entries [*, 512] signed E4M3 bytes
   const int64_t* win_start;  // [R] first window entry of each row
   const int32_t* win_len;    // [R] window entries of each row (clamped to [0, kWinMax])
+  const void* new_x;         // optional: row r's newest token [R][new_x_stride] of new_x_dtype ...
+  int new_x_dtype;
+  int64_t new_x_stride;
+  const int64_t* new_rows;   // ... written to window row new_rows[r] (< 0: none) by this call
 };
+
+// Row r's newest window token, written by the attention call itself (one launch
+// fewer per layer in decode, where every row has its own window).  Before a
+// workgroup barrier every thread encodes one channel of x[r] as signed E4M3 (as
+// the FP8 quantize call does) into a 512-byte LDS row, and workgroups of head
+// group 0 store it to the window; after the barrier the 4 lanes (q4 = 0..3) of
+// the entry slot the token occupies in the row's window take their 128 bytes
+// from LDS in place of the ones they loaded, which may predate the write.
+__device__ __forceinline__ void encode_fresh(const AttnArgs& a, int r, int hg, uint8_t* fresh) {
+  const int64_t dst = a.new_rows[r];
+  if (dst < 0) return;
+  const int t = threadIdx.x;  // one channel per thread (512 threads)
+  const uint32_t u = a.new_x_dtype == CSA2_F32
+                         ? __float_as_uint(static_cast<const float*>(a.new_x)[r * a.new_x_stride + t])
+                         : (uint32_t)static_cast<const uint16_t*>(a.new_x)[r * a.new_x_stride + t] << 16;
+  const uint8_t b = (uint8_t)(e4m3_code(__uint_as_float(u & 0x7FFFFFFFu)) | ((u >> 24) & 0x80u));
+  fresh[t] = b;
+  if (hg == 0) const_cast<uint8_t*>(a.win)[dst * kDim + t] = b;
+}
+
+// after the barrier: true if this lane's entry is the fresh one (its c[] now holds it)
+__device__ __forceinline__ bool take_fresh(const AttnArgs& a, int r, int key, int len, int q4, const uint8_t* fresh,
+                                           u32x4 (&c)[8]) {
+  const int64_t dst = a.new_rows[r];
+  if (dst < 0 || dst - a.win_start[r] != key || key >= len) return false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = *reinterpret_cast<const u32x4*>(fresh + 128 * q4 + 16 * i);
+  return true;
+}
 
 // byte offset of staged code row k.  Rows are padded to 272 bytes and each
 // group of 8 rows inside a 32-row block is shifted by another 64 bytes, so
@@ -953,6 +986,7 @@ struct SmemWide {
   float red_sum[kWaves][64];
   float alpha[64];
   float lfin[64];
+  uint8_t fresh[kDim];  // the row's newest window token, when the call writes it
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
@@ -1182,6 +1216,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) c[i] = u32x4{0u, 0u, 0u, 0u};
     }
+    if (a.new_x) {
+      encode_fresh(a, r, hg, sm.fresh);
+      lds_barrier();
+      (void)take_fresh(a, r, myslot, len, q4, sm.fresh, c);
+    }
     floatx4 S[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) S[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1365,6 +1404,7 @@ struct SmemSwa {
   _Float16 p[16 * NHT * kPStride];
   float red_max[kWaves][64];
   float red_sum[kWaves][64];
+  uint8_t fresh[kDim];  // the row's newest window token, when the call writes it
 };
 
 template <int NHT, bool SPLITQ, int QDT>
@@ -1389,6 +1429,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_swa_attn(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) c[i] = u32x4{0u, 0u, 0u, 0u};
   }
+  if (a.new_x) encode_fresh(a, r, hg, sm.fresh);
   // queries to LDS as fp16 (fp32 queries as hi + lo halves, rows HG.. the lo halves)
   if (QDT == CSA2_BF16) {
     constexpr int NP = HG * kDim / 8 / kThreads;
@@ -1434,6 +1475,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_swa_attn(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sm.wc[key * kWStride + 128 * q4 + 16 * i]) = c[i];
   __syncthreads();
+  // the fresh entry replaces the loaded one in registers and in its staged row (read by PV after the
+  // softmax barrier)
+  if (a.new_x && take_fresh(a, r, key, len, q4, sm.fresh, c)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sm.wc[key * kWStride + 128 * q4 + 16 * i]) = c[i];
+  }
 
   // ---- QK^T: S^T[entry][head]; K-step ks covers channels 128*q4 + 8*ks .. +7 on both operands
   constexpr int NQ = SPLITQ ? 2 : 1;
@@ -1740,6 +1787,7 @@ size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window) 
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
                               const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
                               const uint8_t* win, const int64_t* win_start, const int32_t* win_len,
+                              const void* new_x, int new_x_dtype, int64_t new_x_stride, const int64_t* new_rows,
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s) {
   if (R == 0) return hipSuccess;
   const bool window = win != nullptr;
@@ -1762,6 +1810,10 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
   a.win = win;
   a.win_start = win_start;
   a.win_len = win_len;
+  a.new_x = new_x;
+  a.new_x_dtype = new_x_dtype;
+  a.new_x_stride = new_x_stride;
+  a.new_rows = new_rows;
   if (a.slots > 1) {
     const size_t n = (size_t)R * Hq * a.slots;
     char* b = static_cast<char*>(ws);

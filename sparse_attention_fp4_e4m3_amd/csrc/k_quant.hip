@@ -17,22 +17,6 @@
 namespace csa2 {
 namespace {
 
-// nearest E4M3 (E4M3FN) code of v >= 0, ties to even, saturating at 448
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  if (!(v > 0.0f)) return 0u;
-  if (v >= 448.0f) return 0x7Eu;
-  if (v < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9 (scaling by 512 is exact)
-    return (uint32_t)__float2int_rn(v * 512.0f);
-  }
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t e = (u >> 23) - 120u;  // rebias 127 -> 7
-  const uint32_t man = u & 0x7FFFFFu;
-  const uint32_t keep = man >> 20, rest = man & 0xFFFFFu;
-  uint32_t code = (e << 3) | keep;
-  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) code += 1u;  // carries into the exponent
-  return code;
-}
-
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, m = b & 7u;
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;

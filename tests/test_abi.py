@@ -115,11 +115,11 @@ def test_sparse_attn_rejects_bad_arguments():
 def _swa(L, **kw):
     f = ctypes.c_void_p(0x10000)
     a = dict(R=2, q=f, qd=1, H=64, D=512, codes=f, scales=f, start=f, idx=f, K=256, vis=None, win=f, ws0=f, wl=f,
-             scale=0.1, out=f, od=0, lse=None, ws=f, wsb=1 << 30)
+             nx=None, nxd=0, nxs=0, nr=None, scale=0.1, out=f, od=0, lse=None, ws=f, wsb=1 << 30)
     a.update(kw)
     return L.csa2_sparse_attn_swa(a["R"], a["q"], a["qd"], a["H"], a["D"], a["codes"], a["scales"], a["start"],
-                                  a["idx"], a["K"], a["vis"], a["win"], a["ws0"], a["wl"], a["scale"], a["out"],
-                                  a["od"], a["lse"], a["ws"], a["wsb"], None)
+                                  a["idx"], a["K"], a["vis"], a["win"], a["ws0"], a["wl"], a["nx"], a["nxd"], a["nxs"],
+                                  a["nr"], a["scale"], a["out"], a["od"], a["lse"], a["ws"], a["wsb"], None)
 
 
 def test_window_calls_reject_bad_arguments():
@@ -133,6 +133,10 @@ def test_window_calls_reject_bad_arguments():
     assert _swa(L, win=ctypes.c_void_p(0x10008)) == -1 and "aligned" in _err()
     assert _swa(L, ws=None, wsb=0) == -3
     assert _swa(L, R=0) == 0
+    assert _swa(L, nx=f, nxd=5, nxs=512, nr=f) == -1 and "new_x_dtype" in _err()
+    assert _swa(L, nx=f, nxd=0, nxs=512, nr=None) == -1 and "new_rows" in _err()
+    assert _swa(L, nx=f, nxd=0, nxs=100, nr=f) == -1 and "stride" in _err()
+    assert _swa(L, nx=ctypes.c_void_p(0x10004), nxd=0, nxs=512, nr=f) == -1 and "aligned" in _err()
     # window only: the cache and index arguments are not needed
     assert L.csa2_sparse_attn_swa_workspace_size(2, 64, 1, 0) == 0  # one slot: written directly
     assert L.csa2_sparse_attn_swa_workspace_size(2, 64, 1, 256) > 0

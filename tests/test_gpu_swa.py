@@ -163,3 +163,52 @@ def test_decode_ring_window_after_quantize():
     ro, rl = oracle.attention_rows_swa(q, oc, os_, np.zeros(B, np.int64), idx, vis.astype(np.int64), wc, wst, wlen,
                                        0.044)
     check_attention(out, lse, ro, rl, "decode ring window")
+
+
+@pytest.mark.parametrize("R,Hq,K", [(4, 64, 2048), (256, 64, 300), (3, 32, 0)])
+def test_window_write_inside_the_attention_call(R, Hq, K):
+    """The attention call writing each row's newest token itself (decode rings) gives the same
+    window bytes and the same outputs, bit for bit, as the FP8 quantize call followed by the
+    attention call: on the split path, the 64-head path and window only; a token landing outside
+    its row's window and a row with no token (-1) included."""
+    n = 3000
+    rng = np.random.default_rng(R + K)
+    oc, os_ = oracle.quantize(rng.standard_normal((n, 512)).astype(np.float32))
+    q = bf16_round(rng.standard_normal((R, Hq, 512)).astype(np.float32))
+    idx = np.stack([rng.permutation(n)[:K] for _ in range(R)]).astype(np.int32) if K else np.zeros((R, 0), np.int32)
+    vis = np.full(R, n, np.int32)
+    wstart = np.arange(R, dtype=np.int64) * 128
+    wlen = np.resize(np.array([128, 77, 1, 128], np.int32), R)
+    ring0 = oracle.e4m3_encode_signed(rng.standard_normal((R * 128, 512)).astype(np.float32))
+    new_rows = wstart + rng.integers(0, 128, R)
+    new_rows[0] = wstart[0] + 5
+    if R > 1:
+        new_rows[1] = wstart[1] + 100  # past its 77-entry window: written, not attended
+    if R > 2:
+        new_rows[2] = -1
+    x = rng.standard_normal((R, 512)).astype(np.float32) * 3
+    kw = {}
+    if K:
+        kw = dict(kv_codes=dev(oc), kv_scales=dev(os_), row_kv_start=dev(np.zeros(R, np.int64)), idx=dev(idx),
+                  row_visible=dev(vis))
+    ws = torch.empty(max(256, csa2.sparse_attn_swa_workspace_size(R, Hq, csa2.BF16, K)), dtype=torch.uint8,
+                     device=DEV)
+    outs = []
+    rings = []
+    for fused in (False, True):
+        ring = dev(ring0)
+        out = torch.empty(R, Hq, 512, dtype=torch.float32, device=DEV)
+        lse = torch.empty(R, Hq, dtype=torch.float32, device=DEV)
+        if not fused:
+            sel = new_rows >= 0
+            csa2.quantize_swa_fp8(dev(x[sel]), ring, dev(new_rows[sel]))
+        csa2.sparse_attn_swa(dev_bf16(q), ring, dev(wstart), dev(wlen), out, 0.044, lse=lse, workspace=ws,
+                             new_x=dev(x) if fused else None, new_rows=dev(new_rows) if fused else None, **kw)
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+        rings.append(ring.cpu().numpy())
+    assert np.array_equal(rings[0], rings[1]), "window bytes differ"
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), "outputs differ"
+    ro, rl = oracle.attention_rows_swa(q, oc, os_, np.zeros(R, np.int64), idx, vis.astype(np.int64), rings[0],
+                                       wstart, wlen, 0.044)
+    check_attention(outs[1][0], outs[1][1], ro, rl, "fused window write R=%d K=%d" % (R, K))
