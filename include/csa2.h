@@ -14,13 +14,19 @@
  *             -> csa2_sparse_attn
  *   Reuse   : csa2_sparse_attn(idx = last Full/Reindex selection)
  *
+ * Variants: csa2_sparse_attn_swa joins each layer's local FP8 window to the
+ * selection (csa2_quantize_swa_fp8 writes window entries);
+ * csa2_index_topk_mxfp4 scores MXFP4 indexer keys (csa2_quantize_idx_mxfp4
+ * writes them).
+ *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
  *     every buffer (inputs, outputs, workspace); the library never allocates,
  *     frees, synchronizes or copies to the host.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Work is enqueued on it and the call returns without waiting.
- *   - Inputs are read-only.  Outputs are overwritten in full, padding too.
+ *   - Inputs are read-only (except win_codes, when csa2_sparse_attn_swa is
+ *     given new_x).  Outputs are overwritten in full, padding too.
  *   - Return value: CSA2_OK (0) or a negative status.  Only host-visible
  *     arguments are checked; device data are never read by the host.
  *     Data-dependent conditions are defined behaviour, not errors: an index
