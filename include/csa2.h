@@ -283,7 +283,8 @@ int32_t csa2_quantize_swa_fp8(const void* x, int32_t x_dtype, int64_t n_tokens, 
  * Arguments as for csa2_sparse_attn, plus:
  * top_k        0..CSA2_MAX_TOP_K; with 0, kv_codes, kv_scales, row_kv_start,
  *              idx and row_visible are not read and may be NULL.
- * win_codes    window entries written by csa2_quantize_swa_fp8, 16-byte aligned.
+ * win_codes    window entries written by csa2_quantize_swa_fp8, 16-byte aligned;
+ *              read only, unless new_x is given.
  * row_win_start [n_rows] int64;  row_win_len [n_rows] int32.
  * new_x        optional (NULL: none): [n_rows, new_x_stride] of new_x_dtype
  *              (CSA2_F32 or CSA2_BF16), 16-byte aligned rows.  Row r's token
@@ -300,7 +301,7 @@ int32_t csa2_quantize_swa_fp8(const void* x, int32_t x_dtype, int64_t n_tokens, 
 int32_t csa2_sparse_attn_swa(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
                              const uint8_t* kv_codes, const uint8_t* kv_scales, const int64_t* row_kv_start,
                              const int32_t* idx, int32_t top_k, const int32_t* row_visible,
-                             const uint8_t* win_codes, const int64_t* row_win_start, const int32_t* row_win_len,
+                             uint8_t* win_codes, const int64_t* row_win_start, const int32_t* row_win_len,
                              const void* new_x, int32_t new_x_dtype, int64_t new_x_stride, const int64_t* new_rows,
                              float softmax_scale, void* out, int32_t out_dtype, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream);

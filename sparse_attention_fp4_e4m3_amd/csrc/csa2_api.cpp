@@ -236,7 +236,7 @@ size_t csa2_sparse_attn_swa_workspace_size(int32_t n_rows, int32_t n_heads, int3
 int32_t csa2_sparse_attn_swa(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
                              const uint8_t* kv_codes, const uint8_t* kv_scales, const int64_t* row_kv_start,
                              const int32_t* idx, int32_t top_k, const int32_t* row_visible,
-                             const uint8_t* win_codes, const int64_t* row_win_start, const int32_t* row_win_len,
+                             uint8_t* win_codes, const int64_t* row_win_start, const int32_t* row_win_len,
                              const void* new_x, int32_t new_x_dtype, int64_t new_x_stride, const int64_t* new_rows,
                              float softmax_scale, void* out, int32_t out_dtype, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream) {

@@ -57,7 +57,7 @@ size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window);
 // top_k may be 0 when a window is given (win != nullptr): the window alone is attended
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
                               const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
-                              const uint8_t* win, const int64_t* win_start, const int32_t* win_len,
+                              uint8_t* win, const int64_t* win_start, const int32_t* win_len,
                               const void* new_x, int new_x_dtype, int64_t new_x_stride, const int64_t* new_rows,
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
 

@@ -126,7 +126,7 @@ struct AttnArgs {
   float* ws_o;           // [R, Hq, slots, 512] partial outputs, normalized
   float* ws_m;           // [R, Hq, slots] reference maxima (log2 units)
   float* ws_l;           // [R, Hq, slots] sums
-  const uint8_t* win;        // local window entries [*, 512] signed E4M3 bytes
+  uint8_t* win;              // local window entries [*, 512] signed E4M3 bytes (written only with new_x)
   const int64_t* win_start;  // [R] first window entry of each row
   const int32_t* win_len;    // [R] window entries of each row (clamped to [0, kWinMax])
   const void* new_x;         // optional: row r's newest token [R][new_x_stride] of new_x_dtype ...
@@ -151,7 +151,7 @@ __device__ __forceinline__ void encode_fresh(const AttnArgs& a, int r, int hg, u
                          : (uint32_t)static_cast<const uint16_t*>(a.new_x)[r * a.new_x_stride + t] << 16;
   const uint8_t b = (uint8_t)(e4m3_code(__uint_as_float(u & 0x7FFFFFFFu)) | ((u >> 24) & 0x80u));
   fresh[t] = b;
-  if (hg == 0) const_cast<uint8_t*>(a.win)[dst * kDim + t] = b;
+  if (hg == 0) a.win[dst * kDim + t] = b;
 }
 
 // after the barrier: true if this lane's entry is the fresh one (its c[] now holds it)
@@ -1786,7 +1786,7 @@ size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window) 
 
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
                               const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
-                              const uint8_t* win, const int64_t* win_start, const int32_t* win_len,
+                              uint8_t* win, const int64_t* win_start, const int32_t* win_len,
                               const void* new_x, int new_x_dtype, int64_t new_x_stride, const int64_t* new_rows,
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s) {
   if (R == 0) return hipSuccess;
