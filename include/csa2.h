@@ -289,7 +289,8 @@ int32_t csa2_quantize_swa_fp8(const void* x, int32_t x_dtype, int64_t n_tokens, 
  * new_x        optional (NULL: none): [n_rows, new_x_stride] of new_x_dtype
  *              (CSA2_F32 or CSA2_BF16), 16-byte aligned rows.  Row r's token
  *              new_x[r] is written, as csa2_quantize_swa_fp8 writes it, to
- *              window row new_rows[r] (skipped if negative) by this call, and
+ *              window row new_rows[r] (skipped if negative; a non-negative
+ *              value must be a row of win_codes) by this call, and
  *              row r attends over it if that row lies in its window: the
  *              decode step's newest token, without a separate write call.
  *              Precondition: no new row of the call lies in another row's
