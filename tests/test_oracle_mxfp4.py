@@ -85,3 +85,14 @@ def test_layout_low_nibble_is_the_even_channel():
     assert scales.tolist() == [[127, 125]]   # block maxima 6 (2^0) and 1 (2^-2)
     assert codes[0, 0] == (0x7 | (0x9 << 4))  # 6 -> code 7, -0.5 -> code 9
     assert codes[0, 16] == (0x0 | (0x6 << 4))  # channel 33: 1.0 / 2^-2 = 4 -> code 6, high nibble
+
+
+def test_hand_worked_block():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_block_example.txt")
+    rec = {l.split()[0]: l.split()[1:] for l in open(path) if l.strip() and not l.startswith("#")}
+    x = np.zeros((1, 64), np.float32)
+    x[0, :32] = np.arange(32) / 4.0
+    codes, scales = oracle.mxfp4_quantize(x)
+    assert scales[0].tolist() == [int(s) for s in rec["scales"]]
+    assert codes[0].tolist() == [int(b, 16) for b in rec["codes"]]

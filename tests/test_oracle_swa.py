@@ -155,3 +155,12 @@ def test_nothing_to_attend_gives_zero_and_minus_inf():
     z = np.zeros(1, np.int64)
     o, lse = oracle.attention_rows_swa(q, codes, scales, z, idx, visible, win_codes, z, np.zeros(1, np.int32), 0.04)
     assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_signed_e4m3_hand_worked_examples():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "e4m3_signed_examples.txt")
+    rows = [l.split()[:2] for l in open(path) if l.strip() and not l.startswith("#")]
+    v = np.array([float(a) for a, _ in rows], np.float32)
+    want = np.array([int(b, 16) for _, b in rows], np.uint8)
+    assert np.array_equal(oracle.e4m3_encode_signed(v), want)
