@@ -131,3 +131,19 @@ def test_reindex_over_mxfp4_keys_and_shared_segment():
     for r in [0, 1, 50, T - 1]:
         sel, _, _ = oracle.full_select(qs[r], kh[:vis[r]], vis[r], K)
         assert np.array_equal(got3[r], sel), "shared row %d" % r
+
+
+@pytest.mark.parametrize("kind,H", [("f32", 4), ("bf16", 16), ("f32", 3)])
+def test_reindex_over_mxfp4_keys_query_types_and_head_counts(kind, H):
+    lens, P, K = [12000, 5003], 1024, 256
+    R = len(lens)
+    q, kc, ks, kh, starts = _inputs(300 + H, R, H, lens, kind)
+    q2 = np.random.default_rng(301 + H).standard_normal((R, H, 64)).astype(np.float32)
+    if kind == "bf16":
+        q2 = bf16_round(q2)
+    _, pool, plen = _run(csa2.FULL, q, kind, kc, ks, starts, lens, K, pool_size=P)
+    idx2, _, _ = _run(csa2.REINDEX, q2, kind, kc, ks, starts, lens, K, pool=pool, pool_len=plen)
+    gpool, got = pool.cpu().numpy(), idx2.cpu().numpy()
+    for r in range(R):
+        want = oracle.reindex_select(q2[r], kh[starts[r]:starts[r] + lens[r]], gpool[r], lens[r], K)
+        assert np.array_equal(got[r], want), "row %d" % r

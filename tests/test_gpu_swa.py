@@ -212,3 +212,17 @@ def test_window_write_inside_the_attention_call(R, Hq, K):
     ro, rl = oracle.attention_rows_swa(q, oc, os_, np.zeros(R, np.int64), idx, vis.astype(np.int64), rings[0],
                                        wstart, wlen, 0.044)
     check_attention(outs[1][0], outs[1][1], ro, rl, "fused window write R=%d K=%d" % (R, K))
+
+
+@pytest.mark.parametrize("R,Hq,K,out_dtype", [(256, 64, 300, torch.bfloat16), (4, 64, 2048, torch.bfloat16)])
+def test_window_attention_bf16_output_matches_fp32_rounded(R, Hq, K, out_dtype):
+    """bf16 outputs are the fp32 results rounded to nearest even, on the 64-head path (window as a
+    step) and the split path (window partial + combine); the fp32 results meet the attention bar
+    (bf16 rounding alone is up to 2^-9 relative, so the bar applies before it)."""
+    q, oc, os_, wc, idx, vis, wstart, wlen = _window_case(900 + R, R, Hq, "bf16", K, 6000, [128, 64, 1])
+    a, la = _run(q, "bf16", oc, os_, wc, idx, vis, wstart, wlen, 0.044)
+    b, lb = _run(q, "bf16", oc, os_, wc, idx, vis, wstart, wlen, 0.044, out_dtype=out_dtype)
+    assert torch.equal(b, a.to(torch.bfloat16)) and torch.equal(la, lb)
+    ro, rl = oracle.attention_rows_swa(q, oc, os_, np.zeros(R, np.int64), idx, vis.astype(np.int64), wc, wstart,
+                                       wlen, 0.044)
+    check_attention(a, la, ro, rl, "swa fp32 out R=%d" % R)
