@@ -35,3 +35,22 @@ def test_drift_is_a_random_walk():
     m = x.reshape(-1, 1024, 64).mean(1)
     d = np.diff(m, axis=0)
     assert 0.5 < d.std() / (0.01 * np.sqrt(1024)) < 1.6
+
+
+def test_benchmark_accounting_of_the_variants():
+    """Algorithmic bytes per step: bf16 keys 128 B, MXFP4 keys 34 B per scanned entry; the
+    verification workload scans each sequence's keys once and attends 5 rows per sequence."""
+    import bench
+    w = gen.get("c3")
+    lens = gen.seq_lens(w)
+    b = bench.algorithmic_bytes(w, lens)
+    m = bench.algorithmic_bytes(w, lens, mxfp4=True)
+    assert b["index_scan"] == int(lens.sum()) * 128
+    assert m["index_scan"] == int(lens.sum()) * 34
+    assert b["reindex_score"] == 2 * 16 * 8192 * 128 and m["reindex_score"] == 2 * 16 * 8192 * 34
+    assert b["attention_per_layer"] == 16 * (2048 * 288 + 2048 * 4 + 64 * 512 * 2 + 64 * 512 * 4)
+    v = gen.get("c3v")
+    bv = bench.algorithmic_bytes(v, gen.seq_lens(v))
+    assert v.rows == 80 and bv["index_scan"] == b["index_scan"]
+    assert bv["attention_per_layer"] == 5 * b["attention_per_layer"]
+    assert bench.index_flops(v, gen.seq_lens(v)) == 5 * bench.index_flops(w, lens)
