@@ -97,7 +97,7 @@ def build_cache(w, lens, device, chunk=65536, mxfp4=False):
                  torch.from_numpy(lens.astype(np.int32)).to(device), int(lens.max())), starts
 
 
-def build_prefill(w, device, chunk=65536):
+def build_prefill(w, device, chunk=65536, mxfp4=False):
     """The prefill workload: a cache of n - T tokens plus the chunk's own T rows.
 
     Row r of the chunk sits at cache position P0 + r and sees positions
@@ -122,6 +122,13 @@ def build_prefill(w, device, chunk=65536):
     starts = torch.zeros(T, dtype=torch.int64, device=device)
     vis = torch.from_numpy((P0 + 1 + np.arange(T)).astype(np.int32)).to(device)
     cache = Cache(codes, scales, idx_k, starts, vis, w.n, shared_segment=True)
+    if mxfp4:
+        kc = torch.empty(w.n, 32, dtype=torch.uint8, device=device)
+        ks = torch.empty(w.n, 2, dtype=torch.uint8, device=device)
+        csa2.quantize_idx_mxfp4(idx_k, kc, ks)
+        torch.cuda.synchronize()
+        cache = Cache(codes, scales, kc, starts, vis, w.n, shared_segment=True, idx_k_scales=ks)
+        del idx_k
     qs = [to_dev(gen.attn_q(w, 0), w.q_dtype, device)]
     iqs = [to_dev(gen.index_q(w, 0), w.idx_dtype, device)]
     new_kv = torch.from_numpy(gen.kv_rows(w, 0, P0, w.n)).to(device)
@@ -263,7 +270,7 @@ def oracle_attend(w, q, codes, scales, sel, nvis, win):
                                      np.array([win.shape[0]], np.int32), w.softmax_scale)
 
 
-def cpu_baseline_prefill(w, sample_rows, swa=False):
+def cpu_baseline_prefill(w, sample_rows, swa=False, mxfp4=False):
     """The CPU oracle on `sample_rows` rows of the prefill chunk: indexer scan over the row's visible
     entries, exact top-K and attention (joined with the row's window under swa)."""
     import oracle
@@ -274,6 +281,8 @@ def cpu_baseline_prefill(w, sample_rows, swa=False):
     log("cpu baseline: preparing the oracle cache (%d entries)" % w.n)
     codes, scales = oracle.quantize(gen.kv_rows(w, 0, 0, w.n))
     ik = gen.idx_k_rows(w, 0, 0, w.n)
+    if mxfp4:  # the keys the GPU scores: MXFP4, dequantized exactly
+        ik = oracle.mxfp4_dequant(*oracle.mxfp4_quantize(ik))
     iq = gen.index_q(w, 0)
     q = gen.attn_q(w, 0)
     wins = {r: oracle_window(w, 0, 0, P0 + r + 1) for r in rows} if swa else {}
@@ -446,14 +455,10 @@ def main():
     if args.swa and w.verify > 1:
         print("bench.py: --swa is built for one query row per sequence", file=sys.stderr)
         sys.exit(2)
-    if args.idx_mxfp4 and w.is_prefill:
-        print("bench.py: --idx-mxfp4 is built for the decode workloads (the prefill chunk's MFMA indexer reads "
-              "bf16 keys)", file=sys.stderr)
-        sys.exit(2)
     log("workload %s: %s" % (w.name, w.description))
     t = time.time()
     if w.is_prefill:
-        cache, qs, iqs, new_kv, new_rows_t, lens = build_prefill(w, device)
+        cache, qs, iqs, new_kv, new_rows_t, lens = build_prefill(w, device, mxfp4=args.idx_mxfp4)
     else:
         lens = gen.seq_lens(w)
         cache, _ = build_cache(w, lens, device, mxfp4=args.idx_mxfp4)
@@ -632,7 +637,7 @@ def main():
     }
     res["chain_hbm_GBps"] = byt["total"] / (ms_step * 1e-3) / 1e9
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = (cpu_baseline_prefill(w, max(args.cpu_rows, 128), args.swa) if w.is_prefill
+        res["cpu_baseline"] = (cpu_baseline_prefill(w, max(args.cpu_rows, 128), args.swa, args.idx_mxfp4) if w.is_prefill
                                else cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps, args.swa, args.idx_mxfp4))
     else:
         res["cpu_baseline"] = None

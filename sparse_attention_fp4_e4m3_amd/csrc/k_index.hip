@@ -932,7 +932,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 struct PfArgs {
   const uint16_t* q;          // [R][H][64] bf16 indexer queries
-  const uint8_t* k;           // indexer keys, bf16 rows of 128 bytes
+  const uint8_t* k;           // indexer keys: bf16 rows of 128 bytes, or MXFP4 codes (32 bytes per key)
+  const uint8_t* ks;          // MXFP4 keys: E8M0 scales [rows][2] (null: bf16 keys)
   const int64_t* row_start;   // segment start = row_start[0]
   const int32_t* row_visible; // [R]
   int max_visible;
@@ -965,16 +966,39 @@ __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   float nrm = 0.0f;
   if (i < a.max_visible) {
-    const u32x4* row = reinterpret_cast<const u32x4*>(a.k + (seg + i) * 128);
     float ss = 0.0f;
+    if (a.ks) {  // MXFP4: the exact values E2M1(code) * 2^(scale - 127)
+      const u32x4* row = reinterpret_cast<const u32x4*>(a.k + (seg + i) * 32);
+      const uint32_t sc = *reinterpret_cast<const uint16_t*>(a.ks + (seg + i) * 2);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const u32x4 v = row[p];
+      for (int b = 0; b < 2; ++b) {
+        const u32x4 v = row[b];
+        const float X = e8m0_f(b ? sc >> 8 : sc & 0xFFu);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xFFFF0000u);
-        ss = __builtin_fmaf(lo, lo, ss);
-        ss = __builtin_fmaf(hi, hi, ss);
+        for (int e = 0; e < 4; ++e) {
+          const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[e], 1.0f, 0);
+          const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[e], 1.0f, 1);
+          const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[e], 1.0f, 2);
+          const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[e], 1.0f, 3);
+          const float x[8] = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float y = __fmul_rn(x[k], X);
+            ss = __builtin_fmaf(y, y, ss);
+          }
+        }
+      }
+    } else {
+      const u32x4* row = reinterpret_cast<const u32x4*>(a.k + (seg + i) * 128);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const u32x4 v = row[p];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xFFFF0000u);
+          ss = __builtin_fmaf(lo, lo, ss);
+          ss = __builtin_fmaf(hi, hi, ss);
+        }
       }
     }
     nrm = __fsqrt_rn(ss) * 1.00001f;
@@ -1017,7 +1041,8 @@ __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
 // for key lane%16 in every tile, and each lane sums its row's H ReLU'd heads
 // by itself: every (row, key) score lives in exactly one lane.  In MODE 1 a
 // step yields one whole bitmap word per row, stored directly.
-template <int MODE, int H>
+// MX: MXFP4 keys, widened to the bf16 B operand in registers (exact: an E2M1 value times a power of two).
+template <int MODE, int H, bool MX>
 __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
   constexpr int kPfRows = pf_rows<H>();
   static_assert(H % 4 == 0 && kPfRows % 4 == 0, "heads and rows in fours");
@@ -1092,15 +1117,50 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
     u32x4 b[2][2];  // [tile][k step]
     float kn[2];
   };
-  const uint8_t* kseg = a.k + seg * 128;  // uniform base: loads take a 32-bit lane offset
+  const uint8_t* kseg = a.k + seg * (MX ? 32 : 128);  // uniform base: loads take a 32-bit lane offset
   auto load_step = [&](int p, Step& st) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t j = (uint32_t)min(kbeg + 32 * p * sample + 16 * tt + n16, klim - 1);
-      const uint32_t off = j * 128u + 16u * (uint32_t)g;
-      st.b[tt][0] = *reinterpret_cast<const u32x4*>(kseg + off);
-      st.b[tt][1] = *reinterpret_cast<const u32x4*>(kseg + off + 64u);
-      st.kn[tt] = MODE == 1 ? a.knorm[j] : 0.0f;
+      if constexpr (MX) {
+        // channels 8g .. 8g+7 (block 0) and 32+8g .. (block 1): one code word each; bf16 values
+        // packed as the loaded bf16 rows are (low half = even channel)
+        const uint32_t c0 = *reinterpret_cast<const uint32_t*>(kseg + j * 32u + 4u * (uint32_t)g);
+        const uint32_t c1 = *reinterpret_cast<const uint32_t*>(kseg + j * 32u + 16u + 4u * (uint32_t)g);
+        st.b[tt][0] = u32x4{c0, 0u, 0u, 0u};
+        st.b[tt][1] = u32x4{c1, 0u, 0u, 0u};
+        st.kn[tt] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(a.ks + (seg + j) * 2));  // scales
+        if (MODE == 1) st.b[tt][0][1] = __float_as_uint(a.knorm[j]);
+      } else {
+        const uint32_t off = j * 128u + 16u * (uint32_t)g;
+        st.b[tt][0] = *reinterpret_cast<const u32x4*>(kseg + off);
+        st.b[tt][1] = *reinterpret_cast<const u32x4*>(kseg + off + 64u);
+        st.kn[tt] = MODE == 1 ? a.knorm[j] : 0.0f;
+      }
+    }
+  };
+  // MXFP4: the loaded code words and scales -> the bf16 B operand and the key norm (in place)
+  auto widen = [&](Step& st) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint32_t sc = __float_as_uint(st.kn[tt]);
+        const float kn = MODE == 1 ? __uint_as_float(st.b[tt][0][1]) : 0.0f;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const uint32_t c = st.b[tt][blk][0];
+          const float X = e8m0_f(blk ? sc >> 8 : sc & 0xFFu);
+          // exact in bf16: each fp32 product has at most 2 significant bits, so its top half is it
+          auto pk = [&](auto v) {
+            return (__float_as_uint(__fmul_rn(v[0], X)) >> 16) | (__float_as_uint(__fmul_rn(v[1], X)) & 0xFFFF0000u);
+          };
+          st.b[tt][blk] = u32x4{pk(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)),
+                                pk(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1)),
+                                pk(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2)),
+                                pk(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3))};
+        }
+        st.kn[tt] = kn;
+      }
     }
   };
   // the products of one step: every (row group, key tile, head tile) accumulator
@@ -1139,6 +1199,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
     load_step(min(p + 8, nsteps - 1), ahead);  // clamped: always in bounds
     const int j0 = kbeg + 32 * p * sample;
     floatx4 acc[NG][2][TG];
+    widen(cur);
     products(cur, acc);
 #pragma unroll
     for (int rg = 0; rg < NG; ++rg) {
@@ -1504,33 +1565,33 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
   hipLaunchKernelGGL(k_finalize, dim3((unsigned)R, (unsigned)a.nseries), dim3(kFinThreads), lds, s, a);
 }
 
-template <int H>
+template <int H, bool MX>
 void launch_pf_pass(int mode, const PfArgs& p, int R, int max_visible, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(R, pf_rows<H>()), mode == 0 ? 1u : (unsigned)ceil_div(max_visible, kPfRange));
   const size_t lds = mode == 0 ? (size_t)pf_rows<H>() * kD1 / 2 * 4 : 0;
   static bool configured[2] = {false, false};
   if (mode == 0) {
     if (!configured[0]) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pf_pass<0, H>),
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pf_pass<0, H, MX>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       configured[0] = true;
     }
-    hipLaunchKernelGGL((k_pf_pass<0, H>), grid, dim3(256), lds, s, p);
+    hipLaunchKernelGGL((k_pf_pass<0, H, MX>), grid, dim3(256), lds, s, p);
   } else {
     if (!configured[1]) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pf_pass<1, H>),
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pf_pass<1, H, MX>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       configured[1] = true;
     }
-    hipLaunchKernelGGL((k_pf_pass<1, H>), grid, dim3(256), lds, s, p);
+    hipLaunchKernelGGL((k_pf_pass<1, H, MX>), grid, dim3(256), lds, s, p);
   }
 }
 
 }  // namespace
 
 bool topk_uses_prefill_path(int mode, int q_dtype, int k_dtype, int H, int pool_size) {
-  return mode == CSA2_FULL_SHARED && pool_size == 0 && q_dtype == CSA2_BF16 && k_dtype == CSA2_BF16 &&
-         (H == 4 || H == 8 || H == 16);
+  return mode == CSA2_FULL_SHARED && pool_size == 0 && q_dtype == CSA2_BF16 &&
+         (k_dtype == CSA2_BF16 || k_dtype == CSA2_MXFP4) && (H == 4 || H == 8 || H == 16);
 }
 
 hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, int H, const void* idx_k,
@@ -1552,6 +1613,7 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   PfArgs p{};
   p.q = static_cast<const uint16_t*>(idx_q);
   p.k = static_cast<const uint8_t*>(idx_k);
+  p.ks = k_dtype == CSA2_MXFP4 ? idx_ks : nullptr;
   p.row_start = row_start;
   p.row_visible = row_visible;
   p.max_visible = max_visible;
@@ -1590,9 +1652,15 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   auto& ev = profile_events(CSA2_KERNEL_INDEX_SCAN);
   if (ev.start) (void)hipEventRecord(ev.start, s);
   auto pass = [&](int mode, const PfArgs& pa) {
-    if (H == 4) launch_pf_pass<4>(mode, pa, R, max_visible, s);
-    else if (H == 8) launch_pf_pass<8>(mode, pa, R, max_visible, s);
-    else launch_pf_pass<16>(mode, pa, R, max_visible, s);
+    if (pa.ks) {
+      if (H == 4) launch_pf_pass<4, true>(mode, pa, R, max_visible, s);
+      else if (H == 8) launch_pf_pass<8, true>(mode, pa, R, max_visible, s);
+      else launch_pf_pass<16, true>(mode, pa, R, max_visible, s);
+    } else {
+      if (H == 4) launch_pf_pass<4, false>(mode, pa, R, max_visible, s);
+      else if (H == 8) launch_pf_pass<8, false>(mode, pa, R, max_visible, s);
+      else launch_pf_pass<16, false>(mode, pa, R, max_visible, s);
+    }
   };
   // 1. a provisional bound per row from a 1/kPfSample sample of the keys, with headroom
   PfArgs ps = p;
@@ -1618,10 +1686,10 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   if (ev.stop) (void)hipEventRecord(ev.stop, s);
   hipLaunchKernelGGL(k_pf_compact, dim3((unsigned)R), dim3(256), 0, s, p);
   // exact scores of the candidates and the exact selection among them (Reindex over the candidate lists)
-  run_exact(L, CSA2_REINDEX, true, R, q_dtype, H, idx_k, nullptr, k_dtype, row_start, row_visible, max_visible, L.cand,
+  run_exact(L, CSA2_REINDEX, true, R, q_dtype, H, idx_k, idx_ks, k_dtype, row_start, row_visible, max_visible, L.cand,
             L.ccnt, kPfCap, top_k, out_idx, 0, nullptr, nullptr, nullptr, L.cscore, kPfCap, true, true, idx_q, s);
   // rows whose candidates overflowed: the exact full scan and selection, for those rows only
-  run_exact(L, CSA2_FULL, true, R, q_dtype, H, idx_k, nullptr, k_dtype, row_start, row_visible, max_visible, nullptr,
+  run_exact(L, CSA2_FULL, true, R, q_dtype, H, idx_k, idx_ks, k_dtype, row_start, row_visible, max_visible, nullptr,
             nullptr, 0, top_k, out_idx, 0, nullptr, nullptr, L.over, L.scores, L.n_pad, true, false, idx_q, s);
   return hipGetLastError();
 }

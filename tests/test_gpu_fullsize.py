@@ -188,6 +188,22 @@ def test_prefill_4096_on_256k():
         o, l = oracle.attention_rows_swa(gen.attn_q(w, 0, r, r + 1), oc, os_, z, sel[None], np.array([nvis]), wc, z,
                                          np.array([128], np.int32), w.softmax_scale)
         check_attention(out2[r:r + 1], lse2[r:r + 1], o, l, "c4 window row %d" % r)
+    # the same chunk's selection over MXFP4 indexer keys (MFMA passes on the widened keys, exact
+    # rescoring on the dequantized ones), against the oracle over the dequantized keys
+    kc = torch.empty(w.n, 32, dtype=torch.uint8, device=DEV)
+    kscl = torch.empty(w.n, 2, dtype=torch.uint8, device=DEV)
+    csa2.quantize_idx_mxfp4(idx_k, kc, kscl)
+    ws = torch.empty(csa2.index_topk_workspace_size(csa2.FULL_SHARED, T, w.H, w.n, 0, w.K, 0), dtype=torch.uint8,
+                     device=DEV)
+    idx_mx = torch.empty(T, w.K, dtype=torch.int32, device=DEV)
+    csa2.index_topk_mxfp4(csa2.FULL_SHARED, iq, kc, kscl, starts, vis, w.n, w.K, idx_mx, ws)
+    torch.cuda.synchronize()
+    del ws
+    ikh = oracle.mxfp4_dequant(*oracle.mxfp4_quantize(ik_all))
+    for r in [0, 1, 777, 2048, T - 1]:
+        nvis = P0 + r + 1
+        sel = oracle.topk(oracle.index_scores(gen.index_q(w, 0, r, r + 1)[0], ikh[:nvis]), w.K)
+        assert np.array_equal(idx_mx[r].cpu().numpy(), sel), "MXFP4 indices differ, row %d" % r
     # causality: no row selects a position it cannot see
     idx_np = idx.cpu().numpy()
     limit = (P0 + np.arange(T))[:, None]
