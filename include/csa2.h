@@ -182,7 +182,8 @@ size_t csa2_index_topk_workspace_size(int32_t mode, int32_t n_rows, int32_t n_he
  * the exact fp32 product E2M1(code) * 2^(b - 127), and the score is the
  * same fixed-order fmaf chain, ReLU and head sum over those values; so the
  * result equals csa2_index_topk over the dequantized keys bit for bit.
- * CSA2_FULL_SHARED runs as CSA2_FULL over the shared segment (no MFMA pass).
+ * CSA2_FULL_SHARED takes the MFMA passes (on the keys widened to bf16, which is
+ * exact) and the exact rescoring, as with bf16 keys.
  * Arguments and errors as csa2_index_topk, with (idx_k, k_dtype) replaced by
  * (idx_k_codes, idx_k_scales); the workspace size is
  * csa2_index_topk_workspace_size's.
