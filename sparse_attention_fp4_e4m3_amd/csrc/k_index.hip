@@ -1150,14 +1150,12 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
         for (int blk = 0; blk < 2; ++blk) {
           const uint32_t c = st.b[tt][blk][0];
           const float X = e8m0_f(blk ? sc >> 8 : sc & 0xFFu);
-          // exact in bf16: each fp32 product has at most 2 significant bits, so its top half is it
-          auto pk = [&](auto v) {
-            return (__float_as_uint(__fmul_rn(v[0], X)) >> 16) | (__float_as_uint(__fmul_rn(v[1], X)) & 0xFFFF0000u);
-          };
-          st.b[tt][blk] = u32x4{pk(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)),
-                                pk(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1)),
-                                pk(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2)),
-                                pk(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3))};
+          // the power-of-two scale applied by the conversion itself (exact: an E2M1 value times 2^k)
+          auto pk = [](auto v) { return __builtin_bit_cast(uint32_t, v); };
+          st.b[tt][blk] = u32x4{pk(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, X, 0)),
+                                pk(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, X, 1)),
+                                pk(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, X, 2)),
+                                pk(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, X, 3))};
         }
         st.kn[tt] = kn;
       }
