@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["csa2_api.cpp", "k_quant.hip", "k_index.hip", "k_attn.hip"]
+SOURCES = ["csa2_api.cpp", "k_quant.hip", "k_index.hip", "k_attn.hip", "k_attn_dec.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

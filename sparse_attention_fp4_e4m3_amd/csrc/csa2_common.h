@@ -54,6 +54,13 @@ hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, int64_t st
 // window = true: one more partial slot per (row, head) for the local window
 size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window);
 
+// decode attention with 32-head workgroups (bf16 queries, no window) and the merge of its key splits
+bool attn_dec_applies(int R, int Hq, int q_dtype, int top_k, bool window);
+size_t attn_dec_workspace_bytes(int R, int Hq, int top_k);
+hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, const uint8_t* scales,
+                           const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
+                           float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
+
 // top_k may be 0 when a window is given (win != nullptr): the window alone is attended
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
                               const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,

@@ -1778,6 +1778,7 @@ int attn_slots(int R, int Hq, int q_dtype, int top_k, bool window) {
 }  // namespace
 
 size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window) {
+  if (attn_dec_applies(R, Hq, q_dtype, top_k, window)) return attn_dec_workspace_bytes(R, Hq, top_k);
   const int slots = attn_slots(R, Hq, q_dtype, top_k, window);
   if (slots <= 1) return 0;
   const size_t n = (size_t)R * Hq * slots;
@@ -1791,6 +1792,9 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s) {
   if (R == 0) return hipSuccess;
   const bool window = win != nullptr;
+  if (attn_dec_applies(R, Hq, q_dtype, top_k, window))
+    return launch_attn_dec(R, q, Hq, codes, scales, row_start, idx, top_k, row_visible, softmax_scale, out, out_dtype,
+                           lse, ws, s);
   const Plan p = top_k > 0 ? plan(R, Hq, q_dtype, top_k) : Plan{};
   AttnArgs a{};
   a.q = q;

@@ -61,7 +61,7 @@ def index_topk(mode, idx_q, idx_k, starts, vis, max_visible, K, pool=None, pool_
 def attention(q, codes, scales, starts, idx, scale, vis=None, out_dtype=torch.float32):
     R, Hq, _ = q.shape
     qdt = csa2.F32 if q.dtype == torch.float32 else csa2.BF16
-    ws = torch.empty(max(256, csa2.sparse_attn_workspace_size(R, Hq, qdt, idx.shape[1])), dtype=torch.uint8,
+    ws = torch.zeros(max(256, csa2.sparse_attn_workspace_size(R, Hq, qdt, idx.shape[1])), dtype=torch.uint8,
                      device=DEV)
     out = torch.empty(R, Hq, 512, dtype=out_dtype, device=DEV)
     lse = torch.empty(R, Hq, dtype=torch.float32, device=DEV)

@@ -107,7 +107,7 @@ def test_sparse_attn_rejects_bad_arguments():
     assert _attn(L, qd=3) == -1 and _attn(L, od=9) == -1
     assert _attn(L, q=None) == -1 and "null" in _err()
     assert _attn(L, q=ctypes.c_void_p(0x10008)) == -1 and "aligned" in _err()
-    assert _attn(L, ws=None, wsb=0) == -3
+    assert _attn(L, K=2048, ws=None, wsb=0) == -3  # split keys need partials
     assert _attn(L, scale=float("nan")) == -1
     assert _attn(L, R=0) == 0
 

@@ -145,7 +145,7 @@ def test_prefill_4096_on_256k():
     del ws
     out = torch.empty(T, w.Hq, 512, dtype=torch.float32, device=DEV)
     lse = torch.empty(T, w.Hq, dtype=torch.float32, device=DEV)
-    aws = torch.empty(max(256, csa2.sparse_attn_workspace_size(T, w.Hq, csa2.BF16, w.K)), dtype=torch.uint8,
+    aws = torch.zeros(max(256, csa2.sparse_attn_workspace_size(T, w.Hq, csa2.BF16, w.K)), dtype=torch.uint8,
                       device=DEV)
     csa2.sparse_attn(q, codes, scales, starts, idx, out, w.softmax_scale, row_visible=vis, lse=lse, workspace=aws)
     torch.cuda.synchronize()
@@ -170,7 +170,7 @@ def test_prefill_4096_on_256k():
     csa2.quantize_swa_fp8(new_win[0], wins[0].codes, new_win_rows)
     out2 = torch.empty_like(out)
     lse2 = torch.empty_like(lse)
-    aws = torch.empty(max(256, csa2.sparse_attn_swa_workspace_size(T, w.Hq, csa2.BF16, w.K)), dtype=torch.uint8,
+    aws = torch.zeros(max(256, csa2.sparse_attn_swa_workspace_size(T, w.Hq, csa2.BF16, w.K)), dtype=torch.uint8,
                       device=DEV)
     csa2.sparse_attn_swa(q, wins[0].codes, wins[0].row_start, wins[0].row_len, out2, w.softmax_scale,
                          kv_codes=codes, kv_scales=scales, row_kv_start=starts, idx=idx, row_visible=vis, lse=lse2,

@@ -81,7 +81,7 @@ def _run(q, qkind, oc, os_, wc, idx, vis, wstart, wlen, scale, out_dtype=torch.f
     R, Hq, _ = q.shape
     K = idx.shape[1]
     qdt = csa2.F32 if qkind == "f32" else csa2.BF16
-    ws = torch.empty(max(256, csa2.sparse_attn_swa_workspace_size(R, Hq, qdt, K)), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(256, csa2.sparse_attn_swa_workspace_size(R, Hq, qdt, K)), dtype=torch.uint8, device=DEV)
     out = torch.empty(R, Hq, 512, dtype=out_dtype, device=DEV)
     lse = torch.empty(R, Hq, dtype=torch.float32, device=DEV)
     kw = {}
@@ -191,7 +191,7 @@ def test_window_write_inside_the_attention_call(R, Hq, K):
     if K:
         kw = dict(kv_codes=dev(oc), kv_scales=dev(os_), row_kv_start=dev(np.zeros(R, np.int64)), idx=dev(idx),
                   row_visible=dev(vis))
-    ws = torch.empty(max(256, csa2.sparse_attn_swa_workspace_size(R, Hq, csa2.BF16, K)), dtype=torch.uint8,
+    ws = torch.zeros(max(256, csa2.sparse_attn_swa_workspace_size(R, Hq, csa2.BF16, K)), dtype=torch.uint8,
                      device=DEV)
     outs = []
     rings = []
