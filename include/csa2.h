@@ -136,6 +136,10 @@ int32_t csa2_quantize_kv_fp4(const void* x, int32_t x_dtype, int64_t n_tokens, i
  *
  * idx_q        [n_rows, n_heads, head_dim] of q_dtype.
  * idx_k        [cache rows, head_dim] of k_dtype; row_kv_start[r] + j.
+ * k_heads      indexer keys per entry: 1, one key shared by the n_heads query
+ *              heads (the only layout built: the brief's per-entry byte count
+ *              of the indexer cache holds one key vector per entry); any other
+ *              value returns CSA2_E_UNSUPPORTED.
  * row_kv_start [n_rows] int64;  row_visible [n_rows] int32.
  * max_visible  host-side upper bound of row_visible (sizes grids and
  *              workspace); larger row_visible values are clamped to it.
@@ -146,7 +150,7 @@ int32_t csa2_quantize_kv_fp4(const void* x, int32_t x_dtype, int64_t n_tokens, i
  */
 int32_t csa2_index_topk(int32_t mode, int32_t n_rows,
                         const void* idx_q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
-                        const void* idx_k, int32_t k_dtype,
+                        const void* idx_k, int32_t k_dtype, int32_t k_heads,
                         const int64_t* row_kv_start, const int32_t* row_visible, int32_t max_visible,
                         const int32_t* pool, const int32_t* pool_len, int32_t pool_stride,
                         int32_t top_k, int32_t* out_idx,
@@ -194,7 +198,7 @@ int32_t csa2_quantize_idx_mxfp4(const void* x, int32_t x_dtype, int64_t n_tokens
 
 int32_t csa2_index_topk_mxfp4(int32_t mode, int32_t n_rows,
                               const void* idx_q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
-                              const uint8_t* idx_k_codes, const uint8_t* idx_k_scales,
+                              const uint8_t* idx_k_codes, const uint8_t* idx_k_scales, int32_t k_heads,
                               const int64_t* row_kv_start, const int32_t* row_visible, int32_t max_visible,
                               const int32_t* pool, const int32_t* pool_len, int32_t pool_stride,
                               int32_t top_k, int32_t* out_idx,
@@ -213,9 +217,18 @@ int32_t csa2_index_topk_mxfp4(int32_t mode, int32_t n_rows,
  * S empty: out = 0, lse = -inf.  Duplicate indices count as often as listed.
  *
  * q            [n_rows, n_heads, 512] of q_dtype (CSA2_F32 or CSA2_BF16);
- *              16-byte aligned.  bf16 values are used exactly; fp32 values
- *              are split into two fp16 halves (about 22 significant bits).
- *              |q| must stay below 65504.
+ *              16-byte aligned.  The products run in fp16 on the matrix
+ *              cores.  bf16 queries: decode launches (bf16, no window,
+ *              n_heads a multiple of 32, n_rows * n_heads / 32 <= 256, and
+ *              not n_rows * n_heads / 64 >= 256) first scale each head by
+ *              the power of two that puts its largest |q| in [2^14, 2^15)
+ *              (undone in the logit scale), so every finite value at least
+ *              2^-28 of its head's largest is used exactly; other launches
+ *              use a bf16 value exactly when 2^-14 <= |q| < 65520 (the fp16
+ *              normal range): smaller values lose low bits (below 2^-24 they
+ *              count as 0) and larger ones overflow.  fp32 queries are split
+ *              into two fp16 halves (about 22 significant bits in the fp16
+ *              normal range) and must stay below 65504 in magnitude.
  * n_heads      a multiple of 16, at most 128; head_dim must be 512.
  * kv_codes/kv_scales  the cache written by csa2_quantize_kv_fp4.
  * idx          [n_rows, top_k] int32 positions (e.g. out_idx of the indexer).
@@ -309,6 +322,20 @@ int32_t csa2_sparse_attn_swa(int32_t n_rows, const void* q, int32_t q_dtype, int
                              void* workspace, size_t workspace_bytes, void* stream);
 
 size_t csa2_sparse_attn_swa_workspace_size(int32_t n_rows, int32_t n_heads, int32_t q_dtype, int32_t top_k);
+
+/*
+ * Visible entries of layers whose cache entries fold m consecutive tokens
+ * ("The global branch: compress, index, select" in the course brief: the
+ * encoder layers compress m = 2 tokens into one entry, the decoder's keep
+ * m = 1).  Entry e covers tokens m*e .. m*e + m - 1, and a query at token
+ * position t sees only entries whose whole block lies at or before t:
+ *   row_visible[r] = (token_pos[r] + 1) / tokens_per_entry   (0 if token_pos[r] < 0),
+ * computed on the device, ready for the row_visible argument of the calls above.
+ * token_pos    [n_rows] int64 (device).   row_visible  [n_rows] int32 (device), written.
+ * Errors: CSA2_E_INVALID for null buffers, n_rows < 0 or tokens_per_entry < 1.
+ */
+int32_t csa2_visible_entries(const int64_t* token_pos, int32_t tokens_per_entry, int32_t n_rows,
+                             int32_t* row_visible, void* stream);
 
 /* Thread-local description of the last non-zero status of this thread. */
 const char* csa2_last_error(void);

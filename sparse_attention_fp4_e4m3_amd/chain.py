@@ -56,14 +56,12 @@ class LayerSpec:
     pool_size: int = 0          # Full only
 
 
-def compressed_visible(positions, m: int):
-    """Entries a query at token position t may attend when each cache entry folds m consecutive
-    tokens (entry e covers tokens m*e .. m*e + m - 1): only complete blocks, so (t + 1) // m.
-    m = 1 gives t + 1 (every token up to and including the query's own).  Works on ints, numpy
-    arrays and torch tensors; the result is what row_visible takes."""
-    if m < 1:
-        raise ValueError("m must be >= 1")
-    return (positions + 1) // m
+def compressed_visible(token_pos: torch.Tensor, m: int, stream=None) -> torch.Tensor:
+    """row_visible for query rows at token positions token_pos ([R] int64, device) when each cache
+    entry folds m consecutive tokens: the library counts the complete blocks on the device."""
+    out = torch.empty(token_pos.shape, dtype=torch.int32, device=token_pos.device)
+    csa2.visible_entries(token_pos, m, out, stream=stream)
+    return out
 
 
 def validate_modes(layers: Sequence[LayerSpec]) -> None:

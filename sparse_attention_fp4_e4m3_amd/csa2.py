@@ -33,6 +33,7 @@ EXPORTED = (
     "csa2_index_topk_mxfp4",
     "csa2_sparse_attn_swa",
     "csa2_sparse_attn_swa_workspace_size",
+    "csa2_visible_entries",
     "csa2_last_error",
     "csa2_profile_kernel_events",
 )
@@ -57,8 +58,8 @@ def lib():
         P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.csa2_quantize_kv_fp4.argtypes = [P, i32, i64, i64, P, P, P, i64, P]
         L.csa2_quantize_kv_fp4.restype = i32
-        L.csa2_index_topk.argtypes = [i32, i32, P, i32, i32, i32, P, i32, P, P, i32, P, P, i32, i32, P, i32, i32,
-                                      P, P, P, sz, P]
+        L.csa2_index_topk.argtypes = [i32, i32, P, i32, i32, i32, P, i32, i32, P, P, i32, P, P, i32, i32, P, i32,
+                                      i32, P, P, P, sz, P]
         L.csa2_index_topk.restype = i32
         L.csa2_index_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.csa2_index_topk_workspace_size.restype = sz
@@ -68,8 +69,8 @@ def lib():
         L.csa2_sparse_attn_workspace_size.restype = sz
         L.csa2_quantize_idx_mxfp4.argtypes = [P, i32, i64, i64, P, P, P, i64, P]
         L.csa2_quantize_idx_mxfp4.restype = i32
-        L.csa2_index_topk_mxfp4.argtypes = [i32, i32, P, i32, i32, i32, P, P, P, P, i32, P, P, i32, i32, P, i32, i32,
-                                            P, P, P, sz, P]
+        L.csa2_index_topk_mxfp4.argtypes = [i32, i32, P, i32, i32, i32, P, P, i32, P, P, i32, P, P, i32, i32, P,
+                                            i32, i32, P, P, P, sz, P]
         L.csa2_index_topk_mxfp4.restype = i32
         L.csa2_quantize_swa_fp8.argtypes = [P, i32, i64, i64, P, P, i64, P]
         L.csa2_quantize_swa_fp8.restype = i32
@@ -78,6 +79,8 @@ def lib():
         L.csa2_sparse_attn_swa.restype = i32
         L.csa2_sparse_attn_swa_workspace_size.argtypes = [i32, i32, i32, i32]
         L.csa2_sparse_attn_swa_workspace_size.restype = sz
+        L.csa2_visible_entries.argtypes = [P, i32, i32, P, P]
+        L.csa2_visible_entries.restype = i32
         L.csa2_last_error.argtypes = []
         L.csa2_last_error.restype = ctypes.c_char_p
         L.csa2_profile_kernel_events.argtypes = [i32, P, P]
@@ -142,7 +145,7 @@ def index_topk(mode: int, idx_q: torch.Tensor, idx_k: torch.Tensor, row_kv_start
     R, H, Dk = idx_q.shape
     pool_stride = pool.shape[1] if pool is not None else 0
     _check(lib().csa2_index_topk(
-        mode, R, _ptr(idx_q), _dt(idx_q), H, Dk, _ptr(idx_k), _dt(idx_k), _ptr(row_kv_start), _ptr(row_visible),
+        mode, R, _ptr(idx_q), _dt(idx_q), H, Dk, _ptr(idx_k), _dt(idx_k), 1, _ptr(row_kv_start), _ptr(row_visible),
         int(max_visible), _ptr(pool), _ptr(pool_len), pool_stride, top_k, _ptr(out_idx), pool_size,
         8 if pool_size else 0, _ptr(out_pool), _ptr(out_pool_len), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -170,7 +173,7 @@ def index_topk_mxfp4(mode: int, idx_q: torch.Tensor, k_codes: torch.Tensor, k_sc
     R, H, Dk = idx_q.shape
     pool_stride = pool.shape[1] if pool is not None else 0
     _check(lib().csa2_index_topk_mxfp4(
-        mode, R, _ptr(idx_q), _dt(idx_q), H, Dk, _ptr(k_codes), _ptr(k_scales), _ptr(row_kv_start),
+        mode, R, _ptr(idx_q), _dt(idx_q), H, Dk, _ptr(k_codes), _ptr(k_scales), 1, _ptr(row_kv_start),
         _ptr(row_visible), int(max_visible), _ptr(pool), _ptr(pool_len), pool_stride, top_k, _ptr(out_idx),
         pool_size, 8 if pool_size else 0, _ptr(out_pool), _ptr(out_pool_len), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -230,6 +233,17 @@ def sparse_attn_swa(q: torch.Tensor, win_codes: torch.Tensor, row_win_start: tor
         _dt(new_x) if new_x is not None else 0, new_x.stride(0) if new_x is not None else 0, _ptr(new_rows),
         float(softmax_scale), _ptr(out),
         _dt(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def visible_entries(token_pos: torch.Tensor, tokens_per_entry: int, row_visible: torch.Tensor,
+                    stream=None) -> None:
+    """row_visible [R] int32 <- entries visible at token positions token_pos [R] int64 when each
+    entry folds tokens_per_entry tokens (computed by the library on the device)."""
+    _contig(token_pos, row_visible)
+    if token_pos.dtype != torch.int64 or row_visible.dtype != torch.int32 or token_pos.shape != row_visible.shape:
+        raise ValueError("token_pos must be int64 and row_visible int32 of the same shape")
+    _check(lib().csa2_visible_entries(_ptr(token_pos), int(tokens_per_entry), token_pos.numel(), _ptr(row_visible),
+                                      _stream(stream)))
 
 
 def profile_kernel_events(kernel_id: int, start=None, stop=None) -> None:

@@ -83,7 +83,7 @@ size_t csa2_index_topk_workspace_size(int32_t mode, int32_t n_rows, int32_t n_he
 // one validation and dispatch for both key formats (fn names the caller)
 static int32_t index_topk(const char* fn, int32_t mode, int32_t n_rows, const void* idx_q, int32_t q_dtype,
                           int32_t n_heads, int32_t head_dim, const void* idx_k, const uint8_t* idx_ks,
-                          int32_t k_dtype, const int64_t* row_kv_start, const int32_t* row_visible,
+                          int32_t k_dtype, int32_t k_heads, const int64_t* row_kv_start, const int32_t* row_visible,
                           int32_t max_visible, const int32_t* pool, const int32_t* pool_len, int32_t pool_stride,
                           int32_t top_k, int32_t* out_idx, int32_t pool_size, int32_t block_size, int32_t* out_pool,
                           int32_t* out_pool_len, void* workspace, size_t workspace_bytes, void* stream) {
@@ -93,6 +93,8 @@ static int32_t index_topk(const char* fn, int32_t mode, int32_t n_rows, const vo
   if (n_rows < 0) return fail(CSA2_E_INVALID, "%s: n_rows < 0", fn);
   if (!dtype_ok(q_dtype) || !(mx || dtype_ok(k_dtype))) return fail(CSA2_E_INVALID, "%s: dtype is not F32/BF16", fn);
   if (head_dim != kIdxDim) return fail(CSA2_E_UNSUPPORTED, "%s: head_dim %d (only 64 is built)", fn, head_dim);
+  if (k_heads != 1)
+    return fail(CSA2_E_UNSUPPORTED, "%s: k_heads %d (only one key shared by the query heads is built)", fn, k_heads);
   if (n_heads < 1 || n_heads > 32) return fail(CSA2_E_UNSUPPORTED, "%s: n_heads %d outside 1..32", fn, n_heads);
   if (top_k < 1 || top_k > CSA2_MAX_TOP_K) return fail(CSA2_E_INVALID, "%s: top_k %d outside 1..%d", fn, top_k,
                                                        CSA2_MAX_TOP_K);
@@ -123,7 +125,7 @@ static int32_t index_topk(const char* fn, int32_t mode, int32_t n_rows, const vo
   if (!aligned(workspace, 256)) return fail(CSA2_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
   return hip_status(launch_index_topk(mode, n_rows, idx_q, q_dtype, n_heads, idx_k, idx_ks, k_dtype, row_kv_start,
                                       row_visible, max_visible, pool, pool_len, pool_stride, top_k, out_idx,
-                                      mode == CSA2_FULL ? pool_size : 0, out_pool, out_pool_len, workspace,
+                                      mode != CSA2_REINDEX ? pool_size : 0, out_pool, out_pool_len, workspace,
                                       static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -131,7 +133,8 @@ static int32_t index_topk(const char* fn, int32_t mode, int32_t n_rows, const vo
 extern "C" {
 
 int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t q_dtype, int32_t n_heads,
-                        int32_t head_dim, const void* idx_k, int32_t k_dtype, const int64_t* row_kv_start,
+                        int32_t head_dim, const void* idx_k, int32_t k_dtype, int32_t k_heads,
+                        const int64_t* row_kv_start,
                         const int32_t* row_visible, int32_t max_visible, const int32_t* pool,
                         const int32_t* pool_len, int32_t pool_stride, int32_t top_k, int32_t* out_idx,
                         int32_t pool_size, int32_t block_size, int32_t* out_pool, int32_t* out_pool_len,
@@ -139,18 +142,18 @@ int32_t csa2_index_topk(int32_t mode, int32_t n_rows, const void* idx_q, int32_t
   if (k_dtype == CSA2_MXFP4)
     return fail(CSA2_E_INVALID, "csa2_index_topk: MXFP4 keys go through csa2_index_topk_mxfp4");
   return index_topk("csa2_index_topk", mode, n_rows, idx_q, q_dtype, n_heads, head_dim, idx_k, nullptr, k_dtype,
-                    row_kv_start, row_visible, max_visible, pool, pool_len, pool_stride, top_k, out_idx, pool_size,
+                    k_heads, row_kv_start, row_visible, max_visible, pool, pool_len, pool_stride, top_k, out_idx, pool_size,
                     block_size, out_pool, out_pool_len, workspace, workspace_bytes, stream);
 }
 
 int32_t csa2_index_topk_mxfp4(int32_t mode, int32_t n_rows, const void* idx_q, int32_t q_dtype, int32_t n_heads,
                               int32_t head_dim, const uint8_t* idx_k_codes, const uint8_t* idx_k_scales,
-                              const int64_t* row_kv_start, const int32_t* row_visible, int32_t max_visible,
+                              int32_t k_heads, const int64_t* row_kv_start, const int32_t* row_visible, int32_t max_visible,
                               const int32_t* pool, const int32_t* pool_len, int32_t pool_stride, int32_t top_k,
                               int32_t* out_idx, int32_t pool_size, int32_t block_size, int32_t* out_pool,
                               int32_t* out_pool_len, void* workspace, size_t workspace_bytes, void* stream) {
   return index_topk("csa2_index_topk_mxfp4", mode, n_rows, idx_q, q_dtype, n_heads, head_dim, idx_k_codes,
-                    idx_k_scales, CSA2_MXFP4, row_kv_start, row_visible, max_visible, pool, pool_len, pool_stride,
+                    idx_k_scales, CSA2_MXFP4, k_heads, row_kv_start, row_visible, max_visible, pool, pool_len, pool_stride,
                     top_k, out_idx, pool_size, block_size, out_pool, out_pool_len, workspace, workspace_bytes, stream);
 }
 
@@ -172,6 +175,17 @@ int32_t csa2_quantize_idx_mxfp4(const void* x, int32_t x_dtype, int64_t n_tokens
     return fail(CSA2_E_INVALID, "%s: n_tokens %lld > cap_rows %lld", fn, (long long)n_tokens, (long long)cap_rows);
   return hip_status(launch_quantize_mxfp4(x, x_dtype, n_tokens, x_row_stride, dst_rows, k_codes, k_scales, cap_rows,
                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int32_t csa2_visible_entries(const int64_t* token_pos, int32_t tokens_per_entry, int32_t n_rows,
+                             int32_t* row_visible, void* stream) {
+  const char* fn = "csa2_visible_entries";
+  if (n_rows < 0) return fail(CSA2_E_INVALID, "%s: n_rows < 0", fn);
+  if (tokens_per_entry < 1) return fail(CSA2_E_INVALID, "%s: tokens_per_entry %d < 1", fn, tokens_per_entry);
+  if (n_rows == 0) return CSA2_OK;
+  if (!token_pos || !row_visible) return fail(CSA2_E_INVALID, "%s: null buffer", fn);
+  return hip_status(launch_visible(token_pos, tokens_per_entry, n_rows, row_visible, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -48,6 +48,9 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
 hipError_t launch_quantize_mxfp4(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
                                  uint8_t* codes, uint8_t* scales, int64_t cap, hipStream_t s);
 
+// row_visible of query rows at token positions pos when each entry folds m tokens
+hipError_t launch_visible(const int64_t* pos, int m, int n, int32_t* vis, hipStream_t s);
+
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
                                uint8_t* codes, int64_t cap, hipStream_t s);
 

@@ -172,7 +172,27 @@ __global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ x, in
   scales[dst * 2 + blk] = (uint8_t)sb;
 }
 
+// Visible entries of query rows when each cache entry folds m consecutive
+// tokens (entry e covers tokens m*e .. m*e + m - 1; "The global branch" in the
+// course brief: the encoder layers compress m = 2 tokens per entry): a query
+// at token position t sees the entries whose whole block lies at or before t,
+// (t + 1) / m of them; t < 0 sees none.
+__global__ __launch_bounds__(256) void k_visible(const int64_t* __restrict__ pos, int m, int n,
+                                                 int32_t* __restrict__ vis) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t t = pos[i];
+  const int64_t e = t < 0 ? 0 : (t + 1) / m;
+  vis[i] = (int32_t)(e > 0x7FFFFFFF ? 0x7FFFFFFF : e);
+}
+
 }  // namespace
+
+hipError_t launch_visible(const int64_t* pos, int m, int n, int32_t* vis, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_visible, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, pos, m, n, vis);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_mxfp4(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
                                  uint8_t* codes, uint8_t* scales, int64_t cap, hipStream_t s) {

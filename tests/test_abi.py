@@ -54,10 +54,11 @@ def test_quantize_rejects_bad_arguments():
 
 def _topk(L, **kw):
     f = ctypes.c_void_p(0x10000)
-    a = dict(mode=0, n_rows=2, q=f, qd=1, H=8, D=64, k=f, kd=1, start=f, vis=f, maxv=1000, pool=None, plen=None,
-             pstride=0, K=256, out=f, P=0, blk=0, opool=None, oplen=None, ws=f, wsb=1 << 30)
+    a = dict(mode=0, n_rows=2, q=f, qd=1, H=8, D=64, k=f, kd=1, kh=1, start=f, vis=f, maxv=1000, pool=None,
+             plen=None, pstride=0, K=256, out=f, P=0, blk=0, opool=None, oplen=None, ws=f, wsb=1 << 30)
     a.update(kw)
-    return L.csa2_index_topk(a["mode"], a["n_rows"], a["q"], a["qd"], a["H"], a["D"], a["k"], a["kd"], a["start"],
+    return L.csa2_index_topk(a["mode"], a["n_rows"], a["q"], a["qd"], a["H"], a["D"], a["k"], a["kd"], a["kh"],
+                             a["start"],
                              a["vis"], a["maxv"], a["pool"], a["plen"], a["pstride"], a["K"], a["out"], a["P"],
                              a["blk"], a["opool"], a["oplen"], a["ws"], a["wsb"], None)
 
@@ -76,6 +77,18 @@ def test_index_topk_rejects_bad_arguments():
     assert _topk(L, wsb=16) == -3 and "workspace" in _err()
     assert _topk(L, ws=None) == -3
     assert _topk(L, n_rows=0) == 0
+    # one key shared by the query heads is the only key layout built
+    assert _topk(L, kh=8) == -2 and "k_heads" in _err()
+    assert _topk(L, kh=0) == -2
+
+
+def test_visible_entries_rejects_bad_arguments():
+    L = _L()
+    f = ctypes.c_void_p(0x10000)
+    assert L.csa2_visible_entries(f, 0, 4, f, None) == -1 and "tokens_per_entry" in _err()
+    assert L.csa2_visible_entries(None, 2, 4, f, None) == -1 and "null" in _err()
+    assert L.csa2_visible_entries(f, 2, -1, f, None) == -1
+    assert L.csa2_visible_entries(None, 2, 0, None, None) == 0  # nothing to do
 
 
 def test_workspace_sizes_grow_with_the_problem():
@@ -159,7 +172,7 @@ def test_mxfp4_calls_reject_bad_arguments():
     assert L.csa2_quantize_idx_mxfp4(f, 0, 40, 64, None, f, f, 10, None) == -1 and "cap_rows" in _err()
     assert L.csa2_quantize_idx_mxfp4(f, 0, 4, 64, None, ctypes.c_void_p(0x10008), f, 10, None) == -1
     assert L.csa2_quantize_idx_mxfp4(None, 0, 0, 64, None, None, None, 10, None) == 0
-    args = [0, 2, f, 1, 8, 64, f, f, f, f, 1000, None, None, 0, 64, f, 0, 0, None, None, f, 1 << 30, None]
+    args = [0, 2, f, 1, 8, 64, f, f, 1, f, f, 1000, None, None, 0, 64, f, 0, 0, None, None, f, 1 << 30, None]
     bad = list(args)
     bad[7] = None  # scales
     assert L.csa2_index_topk_mxfp4(*bad) == -1 and "null" in _err()
@@ -170,8 +183,11 @@ def test_mxfp4_calls_reject_bad_arguments():
     bad[5] = 128
     assert L.csa2_index_topk_mxfp4(*bad) == -2
     # MXFP4 keys are not accepted by the two-format call
-    assert L.csa2_index_topk(0, 2, f, 1, 8, 64, f, 2, f, f, 1000, None, None, 0, 64, f, 0, 0, None, None, f,
+    assert L.csa2_index_topk(0, 2, f, 1, 8, 64, f, 2, 1, f, f, 1000, None, None, 0, 64, f, 0, 0, None, None, f,
                              1 << 30, None) == -1 and "mxfp4" in _err()
+    bad = list(args)
+    bad[8] = 2  # k_heads
+    assert L.csa2_index_topk_mxfp4(*bad) == -2 and "k_heads" in _err()
 
 
 def test_profile_hook_ids():

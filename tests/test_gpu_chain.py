@@ -269,9 +269,12 @@ def test_compressed_entries_visibility_in_a_chunk():
     x = rng.standard_normal((nc, 512)).astype(np.float32)
     k = gen.bf16_round(rng.standard_normal((nc, 64)).astype(np.float32))
     oc, os_ = oracle.quantize(x)
-    vis = compressed_visible(P0 + np.arange(T), 2).astype(np.int32)
+    # the library's visible counts (device) against the oracle's, counted block by block
+    vis_gpu = compressed_visible(dev((P0 + np.arange(T)).astype(np.int64)), 2)
+    vis = np.array([oracle.visible_entries(P0 + r, 2) for r in range(T)], np.int32)
+    assert np.array_equal(vis_gpu.cpu().numpy(), vis)
     assert vis.min() == (P0 + 1) // 2 and vis.max() == nc
-    cache = Cache(dev(oc), dev(os_), _to_dev(k, "bf16"), dev(np.zeros(T, np.int64)), dev(vis), nc,
+    cache = Cache(dev(oc), dev(os_), _to_dev(k, "bf16"), dev(np.zeros(T, np.int64)), vis_gpu, nc,
                   shared_segment=True)
     q = gen.bf16_round(rng.standard_normal((T, Hq, 512)).astype(np.float32))
     iq = gen.bf16_round(rng.standard_normal((T, H, 64)).astype(np.float32))

@@ -22,10 +22,11 @@ from sparse_attention_fp4_e4m3_amd import Cache, LayerChain, LayerSpec, csa2
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
 
-def _chain_fullsize(name, sample, swa=False, mxfp4=False):
+def _chain_fullsize(name, sample, swa=False, mxfp4=False, select_all=False):
     """The named decode workload at full size, as the benchmark runs it (optionally with every
     layer's FP8 window, or with MXFP4 indexer keys), checked on the sampled sequences (every
-    draft row of a sequence for the verification workload)."""
+    draft row of a sequence for the verification workload).  select_all: the indices and pools
+    of every selecting layer are also checked for every other sequence."""
     w = gen.get(name)
     V = w.verify
     lens = gen.seq_lens(w)
@@ -41,6 +42,28 @@ def _chain_fullsize(name, sample, swa=False, mxfp4=False):
                        qs[0].dtype, DEV, swa=swa)
     chain.step(cache, qs, iqs, w.softmax_scale, windows=wins)
     torch.cuda.synchronize()
+    if select_all:
+        for b in range(w.B):
+            if b in sample:
+                continue  # checked in full below
+            n = int(lens[b])
+            ik = gen.idx_k_rows(w, b, 0, n)
+            if mxfp4:
+                ik = oracle.mxfp4_dequant(*oracle.mxfp4_quantize(ik))
+            for i in range(V):
+                r, nv = b * V + i, int(vis_rows[b * V + i])
+                pool = None
+                for li, L in enumerate(w.layers):
+                    if L.mode == "full":
+                        sel, pool, _ = oracle.full_select(gen.index_q(w, li, r, r + 1)[0], ik, nv, w.K, L.pool_size)
+                        if L.pool_size:
+                            assert np.array_equal(chain.pool[li][0][r].cpu().numpy(), pool), "pool differs: row %d" % r
+                    elif L.mode == "reindex":
+                        sel = oracle.reindex_select(gen.index_q(w, li, r, r + 1)[0], ik, pool, nv, w.K)
+                    else:
+                        continue
+                    assert np.array_equal(chain.idx[li][r].cpu().numpy(), sel), "indices differ: layer %d row %d" % (li, r)
+            say("%s: sequence %d selections exact" % (name, b))
     for b in sample:
         n, s0 = int(lens[b]), int(starts[b])
         say("%s: oracle for sequence %d (n=%d)" % (name, b, n))
@@ -96,7 +119,7 @@ def test_decode_full_32x_32k_64k():
 
 
 def test_chain_128k_batch16():
-    _chain_fullsize("c3", sample=[0, 9])
+    _chain_fullsize("c3", sample=[0, 9], select_all=True)
 
 
 def test_chain_128k_batch16_with_local_windows():
@@ -112,7 +135,7 @@ def test_chain_128k_verification_5_draft_rows():
 
 
 def test_long_decode_1m_batch4():
-    _chain_fullsize("c5", sample=[2])
+    _chain_fullsize("c5", sample=[0, 1, 2, 3])
 
 
 def test_prefill_4096_on_256k():
@@ -150,7 +173,10 @@ def test_prefill_4096_on_256k():
     csa2.sparse_attn(q, codes, scales, starts, idx, out, w.softmax_scale, row_visible=vis, lse=lse, workspace=aws)
     torch.cuda.synchronize()
     raw = gen.kv_rows(w, 0, 0, w.n)
-    for r in [0, 1, 777, 2048, T - 1]:
+    # 64 rows spread over the chunk plus the edges.  None of this workload's rows takes the
+    # certification-failure or candidate-overflow fallbacks; test_gpu_prefill.py forces both.
+    sample_rows = sorted(set(np.linspace(0, T - 1, 64).astype(int).tolist()) | {0, 1, 777, 2048, T - 1})
+    for r in sample_rows:
         say("c4: oracle for query row %d (sees %d entries)" % (r, P0 + r + 1))
         nvis = P0 + r + 1
         sel = oracle.topk(oracle.index_scores(gen.index_q(w, 0, r, r + 1)[0], ik_all[:nvis]), w.K)
@@ -200,7 +226,7 @@ def test_prefill_4096_on_256k():
     torch.cuda.synchronize()
     del ws
     ikh = oracle.mxfp4_dequant(*oracle.mxfp4_quantize(ik_all))
-    for r in [0, 1, 777, 2048, T - 1]:
+    for r in sample_rows[::4]:
         nvis = P0 + r + 1
         sel = oracle.topk(oracle.index_scores(gen.index_q(w, 0, r, r + 1)[0], ikh[:nvis]), w.K)
         assert np.array_equal(idx_mx[r].cpu().numpy(), sel), "MXFP4 indices differ, row %d" % r

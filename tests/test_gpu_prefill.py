@@ -127,3 +127,31 @@ def test_shared_bound_holds_on_low_norm_sample():
     q = bf16_round(rng.standard_normal((T, H, 64), dtype=np.float32))
     idx = _run_shared(ik, q, P0, K)
     _check_rows(idx, ik, q, P0, K, range(T))
+
+
+def test_shared_with_pool_equals_full_and_feeds_reindex():
+    """CSA2_FULL_SHARED asked for a pool returns exactly what CSA2_FULL returns (indices, pool, pool
+    length), and a Reindex layer over that pool matches the oracle ("The hierarchical indexer" in the
+    course brief: blocks of 8 ranked by their best member, members rescored by a later layer)."""
+    P0, T, H, K, P = 6000, 40, 8, 256, 1024
+    ik, q = _chunk(P0, T, H, seed=71)
+    q2 = bf16_round(np.random.default_rng(72).standard_normal((T, H, 64), dtype=np.float32))
+    n = ik.shape[0]
+    starts = dev(np.zeros(T, np.int64))
+    vis_np = (P0 + 1 + np.arange(T)).astype(np.int32)
+    vis = dev(vis_np)
+    kk = dev_bf16(ik)
+    i_s, p_s, l_s = index_topk(csa2.FULL_SHARED, dev_bf16(q), kk, starts, vis, n, K, pool_size=P)
+    i_f, p_f, l_f = index_topk(csa2.FULL, dev_bf16(q), kk, starts, vis, n, K, pool_size=P)
+    torch.cuda.synchronize()
+    assert torch.equal(i_s, i_f) and torch.equal(p_s, p_f) and torch.equal(l_s, l_f)
+    i_r, _, _ = index_topk(csa2.REINDEX, dev_bf16(q2), kk, starts, vis, n, K, pool=p_s, pool_len=l_s)
+    torch.cuda.synchronize()
+    idx, pool, plen, ridx = i_s.cpu().numpy(), p_s.cpu().numpy(), l_s.cpu().numpy(), i_r.cpu().numpy()
+    for r in range(T):
+        sel, opool, olen = oracle.full_select(q[r], ik[:vis_np[r]], int(vis_np[r]), K, P)
+        assert np.array_equal(idx[r], sel), "row %d: indices differ" % r
+        assert np.array_equal(pool[r], opool) and plen[r] == olen, "row %d: pool differs" % r
+        want = oracle.reindex_select(q2[r], ik, opool, int(vis_np[r]), K)
+        assert np.array_equal(ridx[r], want), "row %d: Reindex over the shared pool differs" % r
+    say("shared segment with pool: %d rows, pool and Reindex exact" % T)
