@@ -39,10 +39,6 @@
 
 #include "csa2_common.h"
 
-#ifndef CSA2_HW_CVT
-#define CSA2_HW_CVT 1
-#endif
-
 namespace csa2 {
 namespace {
 
@@ -66,38 +62,13 @@ __device__ __forceinline__ half2v bits_h2(uint32_t u) { return __builtin_bit_cas
 // two E2M1 codes (byte SEL of w: low nibble first) -> two fp16 values
 template <int SEL>
 __device__ __forceinline__ half2v fp4x2_to_h2(uint32_t w) {
-#if CSA2_HW_CVT
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
-#else
-  const uint32_t b = (w >> (8 * SEL)) & 0xFFu;
-  uint32_t out = 0;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t c = (b >> (4 * k)) & 15u, mag = c & 7u;
-    uint32_t bits = mag < 2u ? (mag ? 0x3800u : 0u) : ((((mag >> 1) + 14u) << 10) | ((mag & 1u) << 9));
-    bits |= (c & 8u) << 12;
-    out |= bits << (16 * k);
-  }
-  return bits_h2(out);
-#endif
 }
 
 // two E4M3 bytes (half SEL of w) -> two fp16 values
 template <bool SEL>
 __device__ __forceinline__ half2v e4m3x2_to_h2(uint32_t w) {
-#if CSA2_HW_CVT
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL);
-#else
-  uint32_t out = 0;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t b = (w >> (16 * (SEL ? 1 : 0) + 8 * k)) & 0xFFu;
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-    out |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v) << (16 * k);
-  }
-  return bits_h2(out);
-#endif
 }
 
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {

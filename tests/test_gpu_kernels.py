@@ -308,6 +308,39 @@ def test_attention_all_selected_equals_dense_and_edge_rows(R):
     assert np.array_equal(o[3], np.broadcast_to(xh[17].astype(np.float32), o[3].shape))
 
 
+@pytest.mark.parametrize("Hq,qkind,R", [(64, "bf16", 4), (16, "f32", 2)])
+def test_attention_error_bound_under_cancellation(Hq, qkind, R):
+    """Entries in +/- pairs with nearly equal logits: the output is a small difference of large values
+    (max|o| well below max|x_hat|), where a relative bound on max|o| would not follow from the
+    arithmetic.  What does follow: probabilities rounded to fp16 (2^-11 relative, the row sum adds the
+    same rounded values) move the normalized weights by at most about 2^-10 of themselves, and split
+    partials stored in fp16 add 2^-11 of their size, so |o - o_exact| <= (2^-10 + 2^-11) max |x_hat|
+    per channel over the selected entries; checked here with 2e-3."""
+    rng = np.random.default_rng(60 + Hq)
+    half = 512
+    x = rng.standard_normal((half, 512)).astype(np.float32)
+    x = np.concatenate([x, -x])  # quantization is sign-symmetric: the pairs dequantize to exact negatives
+    oc, os_ = oracle.quantize(x)
+    xh = oracle.dequant(oc, os_)
+    assert np.array_equal(xh[half:], -xh[:half])
+    n = x.shape[0]
+    q = rng.standard_normal((R, Hq, 512)).astype(np.float32) * 2e-4
+    if qkind == "bf16":
+        q = bf16_round(q)
+    idx = np.stack([rng.permutation(n) for _ in range(R)]).astype(np.int32)
+    starts = np.zeros(R, np.int64)
+    out, lse = attention(as_dtype(q, qkind), dev(oc), dev(os_), dev(starts), dev(idx), 0.0441941738)
+    ro, rl = oracle.attention_rows(q, oc, os_, starts, idx, np.full(R, n, np.int64), 0.0441941738)
+    o = out.cpu().numpy().astype(np.float64)
+    xmax = np.abs(xh).max()
+    assert np.abs(ro).max() < 0.05 * xmax  # heavy cancellation in the reference itself
+    err = np.abs(o - ro).max()
+    say("cancellation Hq=%d %s: max|o_ref| %.3g, max|x_hat| %.3g, max abs err %.3g (%.2e of max|x_hat|)"
+        % (Hq, qkind, np.abs(ro).max(), xmax, err, err / xmax))
+    assert err <= 2e-3 * xmax
+    assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-3
+
+
 def test_attention_deterministic_and_bf16_output():
     n, R, Hq, K = 20000, 16, 64, 2048
     rng = np.random.default_rng(4)
