@@ -228,19 +228,25 @@ def algorithmic_bytes(w, lens, mxfp4=False):
 
 
 def attention_kernel_name(w):
-    """Name of the attention kernel the library's launch plan picks for this workload (a label
-    for the report): 64-head workgroups when rows x 64-head groups fill 256 workgroups; else 16
-    heads per workgroup for at most 64 row x 16-head tiles, 32 otherwise, and the pipelined
-    kernel when a key split holds two or more 128-key steps."""
-    tiles = w.Hq // 16
-    if w.q_dtype != "bf16":
-        return "k_sparse_attn"
-    if tiles % 4 == 0 and w.rows * (tiles // 4) >= 256:
-        return "k_sparse_attn_wide"
-    nht = 2 if tiles % 2 == 0 and w.rows * tiles > 64 else 1
-    splits = min(max(1, -(-w.K // 128)), max(1, -(-256 // (w.rows * (tiles // nht)))))
-    kps = -(-(-(-w.K // splits)) // 128) * 128
-    return "k_attn_pp<%d, 2>" % nht if kps >= 256 else "k_sparse_attn"
+    """Name and source file of the attention kernel the library's launch plan picks for this
+    workload (a label for the report).  bf16 queries without a window: 64-head workgroups when
+    rows x 64-head groups fill 256 workgroups, else 32-head decode workgroups (k_attn_dec, whose
+    key splits are merged by workgroups of the same launch) for up to 256 row x 32-head pairs."""
+    if w.q_dtype == "bf16" and w.Hq % 32 == 0:
+        if (w.Hq // 16) % 4 == 0 and w.rows * (w.Hq // 64) >= 256:
+            return "k_sparse_attn_wide", "k_attn.hip"
+        if w.rows * (w.Hq // 32) <= 256:
+            return "k_attn_dec<%s>" % ("true" if dec_keys_per_split(w) > 256 else "false"), "k_attn_dec.hip"
+    return "k_sparse_attn", "k_attn.hip"
+
+
+def dec_keys_per_split(w):
+    """Keys per workgroup of the decode attention: splits so that about 256 workgroups run, at most
+    one per 256-key chunk and at most 8."""
+    pairs = w.rows * (w.Hq // 32)
+    chunks = -(-w.K // 256)
+    s = min(chunks, 8, max(1, -(-256 // pairs)))
+    return -(-(-(-w.K // s)) // 256) * 256
 
 
 def attention_flops(w):
@@ -550,19 +556,27 @@ def main():
         csa2.profile_kernel_events(kid, s, e)
         return s, e
 
+    def mark():
+        if args.event_kind == "torch":
+            m = torch.cuda.Event(enable_timing=True)
+            m.record()
+            return m
+        return HipEvent()  # recorded on creation
+
     pairs = []
     torch.cuda.synchronize()
     for _ in range(args.steps):
         armed = {k: arm(kid) for k, kid in kernels.items()}
+        begin = mark()  # a kernel whose stop event precedes this one was not launched in the step
         step()
-        pairs.append(armed)
+        pairs.append((begin, armed))
     torch.cuda.synchronize()
     for kid in kernels.values():
         csa2.profile_kernel_events(kid, None, None)
     per_kernel_us = {}
     for k in kernels:
-        vals = [p[k][0].elapsed_time(p[k][1]) * 1e3 for p in pairs]
-        per_kernel_us[k] = float(np.mean(vals))
+        vals = [a[k][0].elapsed_time(a[k][1]) * 1e3 for b, a in pairs if b.elapsed_time(a[k][1]) > 0]
+        per_kernel_us[k] = float(np.mean(vals)) if vals else None
 
     wname = w.name + ("+swa" if args.swa else "") + ("+mxfp4idx" if args.idx_mxfp4 else "")
     byt = algorithmic_bytes(w, lens, args.idx_mxfp4)
@@ -576,6 +590,8 @@ def main():
         "attention_combine": {"avg_us": per_kernel_us["attention_combine"]},
         "quantize": {"avg_us": per_kernel_us["quantize"], "bytes": byt["quantize"]},
     }
+    if per_kernel_us["attention_combine"] is None:
+        del kern["attention_combine"]  # the split merge runs inside the attention launch
     if args.swa:
         # the window: 128 entries x 512 B per row; QK^T and PV over them for every head
         kern["swa_attention"] = {"avg_us": per_kernel_us["swa_attention"], "bytes": w.rows * 128 * 512,
@@ -583,6 +599,8 @@ def main():
         if w.is_prefill:
             kern["quantize_fp8"] = {"avg_us": per_kernel_us["quantize_fp8"], "bytes": w.prefill_tokens * (512 * 4 + 512)}
     for k, v in kern.items():
+        if v["avg_us"] is None:
+            raise RuntimeError("kernel %s was not launched by the step" % k)
         if "bytes" in v and v["avg_us"] > 0:
             v["GBps"] = v["bytes"] / (v["avg_us"] * 1e3)
             v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
@@ -596,9 +614,10 @@ def main():
     dominant = max(["index_scan", "attention", "reindex_score"], key=lambda k: kern[k]["per_step_us"])
     dk = kern[dominant]
     if dominant == "attention":
-        roof = {"kernel": attention_kernel_name(w), "bound": "mfma", "achieved": dk["TFLOPs"],
+        kname, ksrc = attention_kernel_name(w)
+        roof = {"kernel": kname, "bound": "mfma", "achieved": dk["TFLOPs"],
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": dk["mfma_frac"],
-                "traffic": traffic_from_profiles(wname, "k_attn.hip")}
+                "traffic": traffic_from_profiles(wname, ksrc)}
     elif dominant == "index_scan" and w.is_prefill:
         # the chunk's rows share one key segment: the scores are a bf16 MFMA product (two passes)
         roof = {"kernel": "k_pf_pass", "bound": "mfma", "achieved": dk["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,

@@ -236,7 +236,12 @@ int32_t csa2_index_topk_mxfp4(int32_t mode, int32_t n_rows,
  * out          [n_rows, n_heads, 512] of out_dtype (CSA2_F32 or CSA2_BF16).
  * lse          [n_rows, n_heads] fp32 or NULL.
  * workspace    csa2_sparse_attn_workspace_size(...) bytes (may be 0 when
- *              that function returns 0), 256-byte aligned.
+ *              that function returns 0), 256-byte aligned.  Its first 4 KiB
+ *              hold counters through which the workgroups of a key-split
+ *              launch hand their partials to the workgroups that merge them:
+ *              they must be zero when a workspace is first used (allocate it
+ *              zero-filled) and every call leaves them zero again, so only
+ *              other writers of that memory need to restore them.
  * Results are deterministic: the same inputs give the same bits.
  */
 int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
@@ -310,7 +315,8 @@ int32_t csa2_quantize_swa_fp8(const void* x, int32_t x_dtype, int64_t n_tokens, 
  *              Precondition: no new row of the call lies in another row's
  *              window (true for one ring per sequence; a prefill chunk, whose
  *              windows overlap, writes first with csa2_quantize_swa_fp8).
- * workspace    csa2_sparse_attn_swa_workspace_size(...) bytes, 256-byte aligned.
+ * workspace    csa2_sparse_attn_swa_workspace_size(...) bytes, 256-byte aligned,
+ *              first 4 KiB zero as for csa2_sparse_attn.
  * Results are deterministic.
  */
 int32_t csa2_sparse_attn_swa(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,

@@ -120,7 +120,7 @@ class LayerChain:
         aws = (csa2.sparse_attn_swa_workspace_size if swa else csa2.sparse_attn_workspace_size)(n_rows, n_heads, qdt,
                                                                                                 top_k)
         self.ws_index = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
-        self.ws_attn = torch.empty(max(aws, 256), dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.zeros(max(aws, 256), dtype=torch.uint8, device=dev)  # split-merge counters start at 0
         self.out = [torch.empty(n_rows, n_heads, 512, dtype=out_dtype, device=dev) for _ in self.layers]
         self.lse = [torch.empty(n_rows, n_heads, dtype=torch.float32, device=dev) for _ in self.layers]
 

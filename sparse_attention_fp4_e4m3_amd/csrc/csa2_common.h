@@ -54,6 +54,11 @@ hipError_t launch_visible(const int64_t* pos, int m, int n, int32_t* vis, hipStr
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, int64_t stride, const int64_t* dst_rows,
                                uint8_t* codes, int64_t cap, hipStream_t s);
 
+// Attention workspace: the first kAttnCounterBytes hold the arrival counters of
+// split launches that merge their own partials; they are zero before the first
+// call and every call leaves them zero.  Split partials follow them.
+constexpr size_t kAttnCounterBytes = 4096;
+
 // window = true: one more partial slot per (row, head) for the local window
 size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window);
 

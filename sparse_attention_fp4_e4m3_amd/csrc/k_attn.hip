@@ -1753,7 +1753,7 @@ size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window) 
   const int slots = attn_slots(R, Hq, q_dtype, top_k, window);
   if (slots <= 1) return 0;
   const size_t n = (size_t)R * Hq * slots;
-  return ((n * kDim * 4 + 255) & ~size_t(255)) + 2 * ((n * 4 + 255) & ~size_t(255));
+  return kAttnCounterBytes + ((n * kDim * 4 + 255) & ~size_t(255)) + 2 * ((n * 4 + 255) & ~size_t(255));
 }
 
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,
@@ -1791,7 +1791,7 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
   a.new_rows = new_rows;
   if (a.slots > 1) {
     const size_t n = (size_t)R * Hq * a.slots;
-    char* b = static_cast<char*>(ws);
+    char* b = static_cast<char*>(ws) + kAttnCounterBytes;
     a.ws_o = reinterpret_cast<float*>(b);
     b += (n * kDim * 4 + 255) & ~size_t(255);
     a.ws_m = reinterpret_cast<float*>(b);

@@ -54,6 +54,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplits = 8;   // key splits per (row, head group)
 constexpr int kMaxPairs = 256;  // (row, 32-head group) pairs; more rows take the 64-head prefill kernel
+static_assert(kMaxPairs * 16 <= (int)kAttnCounterBytes, "arrival and done counters of every pair");
+constexpr int kMergeParts = 4;  // merge workgroups per pair: one 16-byte piece of every attention lane each
+constexpr int kSpinMax = 1 << 21;  // bounded wait of a merge workgroup (about 100 ms at 128 clocks per poll)
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
@@ -76,6 +79,9 @@ struct DecArgs {
   int xcd_map;              // 1: the S splits of a (row, head group) share blockIdx.x % 8
   _Float16* ws_o;           // [pairs][S][wave][piece 4][lane][8] normalized partials in accumulator order
   float* ws_ml;             // [pairs][32 heads][S][2] (max in log2 units, sum)
+  uint64_t* counters;       // [pairs][2]: attention arrivals, merge parts done (zero between calls); null:
+                            // the merge runs as a launch of its own
+  int nattn;                // attention workgroups (pairs x S); higher blockIdx.x are merge workgroups
 };
 
 struct __align__(16) SmemDec {
@@ -91,6 +97,9 @@ struct __align__(16) SmemDec {
   float c2h[kHG];
   float alpha[kHG];
   float ifin[kHG];
+  float om[16][kMaxSplits];  // merge workgroups: weights of the splits of their 16 heads
+  float2 mls[16 * kMaxSplits];
+  int flag;
 };
 
 __device__ __forceinline__ uint32_t h2u(half2v h) { return __builtin_bit_cast(uint32_t, h); }
@@ -171,6 +180,105 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
 __device__ __forceinline__ float h_lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu)); }
 __device__ __forceinline__ float h_hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
 
+// A merge workgroup: merges piece pc (tile pc >> 1, accumulator rows 8*(pc&1) .. +7: 16 heads x 256
+// channels) of the S partials of one (row, head group) once their S attention workgroups have
+// arrived.  Merge workgroups have higher blockIdx.x than every attention workgroup, so each starts only
+// once every attention workgroup has been placed on a CU, and it waits for its pair by polling the
+// arrival counter (bounded: past kSpinMax polls it writes NaN).  The S attention workgroups and the merge
+// workgroups of a pair share blockIdx.x % 8, hence one XCC and one L2: workgroups are dispatched to the
+// XCCs round-robin in blockIdx order, though not always from XCC 0 (graph launches start elsewhere).
+// Each arrival adds 1 to the count and 1 to a 4-bit field of its XCC, and a merge workgroup proceeds only
+// when the field of its own XCC holds all S arrivals (else NaN): the partials, stored before each arrival
+// is counted, are then in its L2 and are read back past this CU's L1 (agent-scope loads).  The last merge
+// workgroup of a pair to finish resets both counters for the next call.
+__device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7u; }
+
+__device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
+  const int j = (int)blockIdx.x - a.nattn;
+  const int jx = j >> 3, x = j & 7;
+  const int pair = 8 * (jx / kMergeParts) + x, pc = jx % kMergeParts;
+  const int S = a.splits;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h2 = lane >> 5, l32 = lane & 31, tt = pc >> 1, jj = pc & 1;
+  const int nhg = a.Hq / kHG;
+  const int r = pair / nhg, h0 = (pair % nhg) * kHG;
+  if (tid == 0) {
+    uint64_t c = 0;
+    int it = 0;
+    for (; it < kSpinMax; ++it) {
+      c = __hip_atomic_load(&a.counters[2 * pair], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int)(c & 255u) >= S) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    sm.flag = (it < kSpinMax && (int)((c >> (8 + 4 * xcc_id())) & 15u) == S) ? 1 : 0;
+  }
+  __syncthreads();
+  const bool ok = sm.flag != 0;
+  // piece pc of (split s, wave w, lane): 16 bytes each, all splits in flight, read from L2 (sc0)
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.ws_o, 0, 0x7FFFFFFF, 0x00020000);
+  u32x4 v[kMaxSplits];
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+    const uint32_t off = (uint32_t)((((((size_t)pair * S + (s2 < S ? s2 : 0)) * 8 + w) * 4 + pc) * 64 + lane) * 16);
+    v[s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off, 0, 16);
+  }
+  // weights of the splits of heads 16*jj .. +15, in fixed split order
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(a.ws_ml, 0, 0x7FFFFFFF, 0x00020000);
+  if (tid < 16 * S) {
+    const uint32_t e = (uint32_t)(((size_t)pair * kHG + 16 * jj + tid / S) * S + tid % S);
+    const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, (int)(8u * e), 0, 16);
+    sm.mls[tid] = make_float2(__uint_as_float(m2[0]), __uint_as_float(m2[1]));
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, sm.mls[tid * S + s2].x);
+    float wg[kMaxSplits], L = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+      wg[s2] = (s2 < S && M != -INFINITY) ? __builtin_amdgcn_exp2f(sm.mls[tid * S + s2].x - M) * sm.mls[tid * S + s2].y
+                                          : 0.0f;
+      L += wg[s2];
+    }
+    const float iL = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) sm.om[tid][s2] = wg[s2] * iL;
+    if (a.lse && tt == 0)
+      a.lse[(int64_t)r * a.Hq + h0 + 16 * jj + tid] = !ok ? __builtin_nanf("") : L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  // rows i = 8*jj + e of this lane: head 8*(i/4) + 4*h2 + i%4 (= 16*jj + local head), channel 64w + 32tt + l32
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+    if (s2 >= S) break;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e0 = 2 * k, e1 = 2 * k + 1;  // local heads 8*(e/4) + 4*h2 + e%4
+      acc[e0] += sm.om[8 * (e0 >> 2) + 4 * h2 + (e0 & 3)][s2] * h_lo(v[s2][k]);
+      acc[e1] += sm.om[8 * (e1 >> 2) + 4 * h2 + (e1 & 3)][s2] * h_hi(v[s2][k]);
+    }
+  }
+  const int64_t ob = ((int64_t)r * a.Hq + h0 + 16 * jj) * kDim + 64 * w + 32 * tt + l32;
+  const float bad = __builtin_nanf("");
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t o = ob + (int64_t)(8 * (e >> 2) + 4 * h2 + (e & 3)) * kDim;
+    const float val = ok ? acc[e] : bad;
+    if (a.out_dtype == CSA2_F32) static_cast<float*>(a.out)[o] = val;
+    else static_cast<uint16_t*>(a.out)[o] = (uint16_t)bf16_rne(val);
+  }
+  // every merge workgroup of the pair has seen all S arrivals once the last one gets here
+  if (tid == 0) {
+    const uint64_t d = __hip_atomic_fetch_add(&a.counters[2 * pair + 1], uint64_t(1), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (d == kMergeParts - 1) {
+      __hip_atomic_store(&a.counters[2 * pair], uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.counters[2 * pair + 1], uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // MULTI: splits of more than one chunk (the next chunk's rows are gathered
 // into registers while the current one is processed)
 template <bool MULTI>
@@ -180,6 +288,10 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
 
+  if (a.counters && (int)blockIdx.x >= a.nattn) {
+    merge_part(a, sm);
+    return;
+  }
   // (pair, split): with xcd_map the S splits of one (row, head group) run on
   // one XCD (workgroups are dispatched round-robin over the 8 XCDs), so its
   // queries are read from HBM once and then hit that XCD's L2
@@ -464,10 +576,18 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         pk[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[t][i] * inv[i])) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[t][i + 1] * inv[i + 1])) << 16);
       }
-      __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]}, po + 64 * (2 * t + j));
+      if (a.counters) po[64 * (2 * t + j)] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      else __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]}, po + 64 * (2 * t + j));
     }
   if (w == 0 && lane < 32)
     *reinterpret_cast<float2*>(a.ws_ml + (((size_t)pair * kHG + lane) * S + split) * 2) = make_float2(m_run, l_run);
+  if (!a.counters) return;
+  // arrival, once this workgroup's stores have reached L2: the count and this XCC's field
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    __hip_atomic_fetch_add(&a.counters[2 * pair], uint64_t(1) | (uint64_t(1) << (8 + 4 * xcc_id())),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The merge of the key splits: one workgroup of 256 threads per (row, head
@@ -574,7 +694,7 @@ size_t attn_dec_workspace_bytes(int R, int Hq, int top_k) {
   const DecPlan p = dec_plan(R, Hq, top_k);
   if (p.splits <= 1) return 0;
   const size_t n = (size_t)p.pairs * p.splits;
-  return round_up(n * kHG * 512 * 2, 256) + round_up(n * kHG * 8, 256);
+  return kAttnCounterBytes + round_up(n * kHG * 512 * 2, 256) + round_up(n * kHG * 8, 256);
 }
 
 hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, const uint8_t* scales,
@@ -597,10 +717,17 @@ hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, c
   a.splits = p.splits;
   a.kps = p.kps;
   a.xcd_map = p.xcd ? 1 : 0;
+  a.nattn = p.pairs * p.splits;
+  int nmerge = 0;
   if (p.splits > 1) {
     const size_t n = (size_t)p.pairs * p.splits;
-    a.ws_o = static_cast<_Float16*>(ws);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(n * kHG * 512 * 2, 256));
+    char* b = static_cast<char*>(ws);
+    if (p.xcd) {
+      a.counters = reinterpret_cast<uint64_t*>(b);
+      nmerge = kMergeParts * p.pairs;
+    }
+    a.ws_o = reinterpret_cast<_Float16*>(b + kAttnCounterBytes);
+    a.ws_ml = reinterpret_cast<float*>(b + kAttnCounterBytes + round_up(n * kHG * 512 * 2, 256));
   }
   const bool multi = p.kps > kChunk;
   auto kern = multi ? k_attn_dec<true> : k_attn_dec<false>;
@@ -612,10 +739,10 @@ hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, c
   }
   auto& ev = profile_events(CSA2_KERNEL_ATTN);
   if (ev.start) (void)hipEventRecord(ev.start, s);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(p.pairs * p.splits)), dim3(kT), sizeof(SmemDec), s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.nattn + nmerge)), dim3(kT), sizeof(SmemDec), s, a);
   if (ev.stop) (void)hipEventRecord(ev.stop, s);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits <= 1) return e;
+  if (e != hipSuccess || p.splits <= 1 || a.counters) return e;
   auto& ec = profile_events(CSA2_KERNEL_ATTN_COMBINE);
   if (ec.start) (void)hipEventRecord(ec.start, s);
   hipLaunchKernelGGL(k_dec_combine, dim3((unsigned)(p.pairs * 8)), dim3(256), 0, s, a);

@@ -341,6 +341,31 @@ def test_attention_error_bound_under_cancellation(Hq, qkind, R):
     assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-3
 
 
+def test_attention_split_merge_shares_one_workspace():
+    """Split launches hand their partials to merge workgroups through counters at the start of the
+    workspace: one zero-filled workspace serves calls of several shapes in a row (the merge inside the
+    launch for 8k (row, 32-head) pairs, a separate merge launch otherwise), each call matches the
+    oracle and leaves the counters zero."""
+    n = 6000
+    rng = np.random.default_rng(12)
+    x = _cache(12, n)
+    oc, os_ = oracle.quantize(x)
+    codes, scales = dev(oc), dev(os_)
+    shapes = [(16, 64, 2048), (32, 64, 2048), (3, 64, 2048), (4, 64, 1024), (16, 64, 2048)]
+    need = max(csa2.sparse_attn_workspace_size(R, Hq, csa2.BF16, K) for R, Hq, K in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for i, (R, Hq, K) in enumerate(shapes):
+        q = bf16_round(rng.standard_normal((R, Hq, 512)).astype(np.float32))
+        idx = np.stack([rng.permutation(n)[:K] for _ in range(R)]).astype(np.int32)
+        starts = np.zeros(R, np.int64)
+        out = torch.empty(R, Hq, 512, dtype=torch.float32, device=DEV)
+        lse = torch.empty(R, Hq, dtype=torch.float32, device=DEV)
+        csa2.sparse_attn(dev_bf16(q), codes, scales, dev(starts), dev(idx), out, 0.0441941738, lse=lse, workspace=ws)
+        ro, rl = oracle.attention_rows(q, oc, os_, starts, idx, np.full(R, n, np.int64), 0.0441941738)
+        check_attention(out, lse, ro, rl, "shared workspace call %d R=%d K=%d" % (i, R, K))
+        assert int(ws[:4096].count_nonzero()) == 0, "call %d left split-merge counters set" % i
+
+
 def test_attention_deterministic_and_bf16_output():
     n, R, Hq, K = 20000, 16, 64, 2048
     rng = np.random.default_rng(4)
