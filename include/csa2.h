@@ -253,6 +253,33 @@ int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t
 size_t csa2_sparse_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t q_dtype, int32_t top_k);
 
 /*
+ * csa2_sparse_attn without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation.  Arguments, results and errors are those of
+ * csa2_sparse_attn (the same kernels run); the split partials and merge
+ * counters live instead in one array of CSA2_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every device it runs on until the process ends.
+ *   - A call whose csa2_sparse_attn_workspace_size(...) exceeds
+ *     CSA2_NOALLOC_SCRATCH_BYTES (16 MiB) returns CSA2_E_WORKSPACE and
+ *     launches nothing.  Nearly every shape fits; the largest workspaces
+ *     (up to about 16.1 MiB) come with 129..255 row x 32-head pairs at
+ *     top_k above 2048, for example 255 rows of 32 heads at top_k 4096.
+ *   - Every call on a device uses that device's one array: calls that may
+ *     overlap on one device (other streams, other threads) race and must be
+ *     ordered by the caller.  The array keeps the last call's partials; the
+ *     counters in its first 4 KiB are cleared on the device's first call
+ *     (a kernel on `stream`) and every call leaves them zero.
+ *   - The call allocates nothing, neither device nor host memory.  The first
+ *     call on a device looks up the array's device address
+ *     (hipGetSymbolAddress) and is best made once before any capture.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int32_t csa2_sparse_attn_noalloc(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                                 const uint8_t* kv_codes, const uint8_t* kv_scales, const int64_t* row_kv_start,
+                                 const int32_t* idx, int32_t top_k, const int32_t* row_visible, float softmax_scale,
+                                 void* out, int32_t out_dtype, float* lse, void* stream);
+
+/*
  * Local sliding-window branch.  Every CSA2 layer also runs exact sliding-
  * window attention over the 128 most recent tokens with its own window
  * cache, kept in FP8, and the selected Main KV entries are joined to that

@@ -19,6 +19,7 @@ from .csa2 import (  # noqa: F401
     quantize_kv_fp4,
     quantize_swa_fp8,
     sparse_attn,
+    sparse_attn_noalloc,
     sparse_attn_swa,
     sparse_attn_swa_workspace_size,
     sparse_attn_workspace_size,

@@ -28,6 +28,7 @@ EXPORTED = (
     "csa2_index_topk_workspace_size",
     "csa2_sparse_attn",
     "csa2_sparse_attn_workspace_size",
+    "csa2_sparse_attn_noalloc",
     "csa2_quantize_swa_fp8",
     "csa2_quantize_idx_mxfp4",
     "csa2_index_topk_mxfp4",
@@ -67,6 +68,9 @@ def lib():
         L.csa2_sparse_attn.restype = i32
         L.csa2_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32]
         L.csa2_sparse_attn_workspace_size.restype = sz
+        L.csa2_sparse_attn_noalloc.argtypes = [i32, P, i32, i32, i32, P, P, P, P, i32, P, ctypes.c_float, P, i32, P,
+                                               P]
+        L.csa2_sparse_attn_noalloc.restype = i32
         L.csa2_quantize_idx_mxfp4.argtypes = [P, i32, i64, i64, P, P, P, i64, P]
         L.csa2_quantize_idx_mxfp4.restype = i32
         L.csa2_index_topk_mxfp4.argtypes = [i32, i32, P, i32, i32, i32, P, P, i32, P, P, i32, P, P, i32, i32, P,
@@ -195,6 +199,19 @@ def sparse_attn(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor
         R, _ptr(q), _dt(q), Hq, D, _ptr(kv_codes), _ptr(kv_scales), _ptr(row_kv_start), _ptr(idx),
         idx.shape[1], _ptr(row_visible), float(softmax_scale), _ptr(out), _dt(out), _ptr(lse), _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+def sparse_attn_noalloc(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor, row_kv_start: torch.Tensor,
+                        idx: torch.Tensor, out: torch.Tensor, softmax_scale: float,
+                        row_visible: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """sparse_attn with the library's own scratch instead of a workspace (nothing is allocated;
+    calls on one device share that scratch and must not overlap)."""
+    _contig(q, kv_codes, kv_scales, row_kv_start, idx, out, row_visible, lse)
+    R, Hq, D = q.shape
+    _check(lib().csa2_sparse_attn_noalloc(
+        R, _ptr(q), _dt(q), Hq, D, _ptr(kv_codes), _ptr(kv_scales), _ptr(row_kv_start), _ptr(idx),
+        idx.shape[1], _ptr(row_visible), float(softmax_scale), _ptr(out), _dt(out), _ptr(lse), _stream(stream)))
 
 
 def quantize_swa_fp8(x: torch.Tensor, win_codes: torch.Tensor, dst_rows: Optional[torch.Tensor] = None,

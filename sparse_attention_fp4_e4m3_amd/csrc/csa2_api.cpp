@@ -3,6 +3,7 @@
 // no call synchronizes, allocates or copies.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "csa2_common.h"
@@ -30,8 +31,73 @@ static int32_t hip_status(hipError_t e, const char* what) {
 }
 
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ------------------------------------------------------- the library's scratch
+// csa2_sparse_attn_noalloc keeps the split partials and merge counters of its
+// launches in this array instead of a caller's workspace.  On the host the
+// array's name stands for a host-side shadow, not device memory: host code
+// takes the device address from hipGetSymbolAddress, once per device, and
+// passes only that address to kernels.
+constexpr size_t kStaticScratchBytes = CSA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+__global__ void k_clear_u64(uint64_t* p, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0;
+}
+
+// Device address of the current device's scratch, looked up on the first call
+// on that device, which also clears the merge counters on stream s (the array
+// starts zero-filled and every call leaves the counters zero).
+static int32_t static_scratch(const char* fn, hipStream_t s, void** out);
 static bool dtype_ok(int32_t d) { return d == CSA2_F32 || d == CSA2_BF16; }
 static size_t dtype_size(int32_t d) { return d == CSA2_F32 ? 4 : 2; }
+
+static int32_t static_scratch(const char* fn, hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CSA2_E_UNSUPPORTED, "%s: device %d (the library keeps scratch for devices 0..%d)", fn, dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(CSA2_E_HIP, "%s: hipGetSymbolAddress(scratch) gave a null address", fn);
+    constexpr int n = (int)(kAttnCounterBytes / 8);
+    hipLaunchKernelGGL(k_clear_u64, dim3((n + 255) / 256), dim3(256), 0, s, static_cast<uint64_t*>(p), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
+
+// checks shared by csa2_sparse_attn and csa2_sparse_attn_noalloc (all but the workspace)
+static int32_t sparse_attn_args(const char* fn, int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads,
+                                int32_t head_dim, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                const int64_t* row_kv_start, const int32_t* idx, int32_t top_k, float softmax_scale,
+                                const void* out, int32_t out_dtype) {
+  if (n_rows < 0) return fail(CSA2_E_INVALID, "%s: n_rows < 0", fn);
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return fail(CSA2_E_INVALID, "%s: dtype is not F32/BF16", fn);
+  if (head_dim != kDim) return fail(CSA2_E_UNSUPPORTED, "%s: head_dim %d (only 512 is built)", fn, head_dim);
+  if (n_heads < 16 || n_heads > 128 || n_heads % 16)
+    return fail(CSA2_E_INVALID, "%s: n_heads %d must be a multiple of 16 in 16..128", fn, n_heads);
+  if (top_k < 1) return fail(CSA2_E_INVALID, "%s: top_k %d < 1", fn, top_k);
+  if (!(softmax_scale == softmax_scale)) return fail(CSA2_E_INVALID, "%s: softmax_scale is NaN", fn);
+  if (n_rows == 0) return CSA2_OK;
+  if (!q || !kv_codes || !kv_scales || !row_kv_start || !idx || !out)
+    return fail(CSA2_E_INVALID, "%s: null buffer", fn);
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(kv_codes, 16) || !aligned(kv_scales, 8))
+    return fail(CSA2_E_INVALID, "%s: q/out/kv_codes must be 16-byte and kv_scales 8-byte aligned", fn);
+  return CSA2_OK;
+}
 
 }  // namespace csa2
 
@@ -200,18 +266,9 @@ int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t
                          void* out, int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes,
                          void* stream) {
   const char* fn = "csa2_sparse_attn";
-  if (n_rows < 0) return fail(CSA2_E_INVALID, "%s: n_rows < 0", fn);
-  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return fail(CSA2_E_INVALID, "%s: dtype is not F32/BF16", fn);
-  if (head_dim != kDim) return fail(CSA2_E_UNSUPPORTED, "%s: head_dim %d (only 512 is built)", fn, head_dim);
-  if (n_heads < 16 || n_heads > 128 || n_heads % 16)
-    return fail(CSA2_E_INVALID, "%s: n_heads %d must be a multiple of 16 in 16..128", fn, n_heads);
-  if (top_k < 1) return fail(CSA2_E_INVALID, "%s: top_k %d < 1", fn, top_k);
-  if (!(softmax_scale == softmax_scale)) return fail(CSA2_E_INVALID, "%s: softmax_scale is NaN", fn);
-  if (n_rows == 0) return CSA2_OK;
-  if (!q || !kv_codes || !kv_scales || !row_kv_start || !idx || !out)
-    return fail(CSA2_E_INVALID, "%s: null buffer", fn);
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(kv_codes, 16) || !aligned(kv_scales, 8))
-    return fail(CSA2_E_INVALID, "%s: q/out/kv_codes must be 16-byte and kv_scales 8-byte aligned", fn);
+  const int32_t rc = sparse_attn_args(fn, n_rows, q, q_dtype, n_heads, head_dim, kv_codes, kv_scales, row_kv_start,
+                                      idx, top_k, softmax_scale, out, out_dtype);
+  if (rc != CSA2_OK || n_rows == 0) return rc;
   const size_t need = attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k, false);
   if (need && (!workspace || workspace_bytes < need))
     return fail(CSA2_E_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
@@ -220,6 +277,30 @@ int32_t csa2_sparse_attn(int32_t n_rows, const void* q, int32_t q_dtype, int32_t
                                        row_visible, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, softmax_scale,
                                        out, out_dtype, lse,
                                        workspace, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int32_t csa2_sparse_attn_noalloc(int32_t n_rows, const void* q, int32_t q_dtype, int32_t n_heads, int32_t head_dim,
+                                 const uint8_t* kv_codes, const uint8_t* kv_scales, const int64_t* row_kv_start,
+                                 const int32_t* idx, int32_t top_k, const int32_t* row_visible, float softmax_scale,
+                                 void* out, int32_t out_dtype, float* lse, void* stream) {
+  const char* fn = "csa2_sparse_attn_noalloc";
+  const int32_t rc = sparse_attn_args(fn, n_rows, q, q_dtype, n_heads, head_dim, kv_codes, kv_scales, row_kv_start,
+                                      idx, top_k, softmax_scale, out, out_dtype);
+  if (rc != CSA2_OK || n_rows == 0) return rc;
+  const size_t need = attn_workspace_bytes(n_rows, n_heads, q_dtype, top_k, false);
+  if (need > kStaticScratchBytes)
+    return fail(CSA2_E_WORKSPACE, "%s: the call needs %zu bytes of scratch, more than the %zu the library holds "
+                "(csa2_sparse_attn takes a workspace of any size)", fn, need, kStaticScratchBytes);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need) {
+    const int32_t r2 = static_scratch(fn, s, &ws);
+    if (r2 != CSA2_OK) return r2;
+  }
+  return hip_status(launch_sparse_attn(n_rows, q, q_dtype, n_heads, kv_codes, kv_scales, row_kv_start, idx, top_k,
+                                       row_visible, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, softmax_scale,
+                                       out, out_dtype, lse, ws, s),
                     fn);
 }
 
