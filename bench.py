@@ -9,7 +9,12 @@ are seeded synthetic data (gen/) resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s over the timed steps, the roofline of the
 dominant kernel (HIP events on the launch stream via the library's
-measurement hook), and the CPU oracle timed on a bounded sample.
+measurement hook), and the CPU oracle timed on a bounded sample (all host
+threads, and one thread on a smaller sample).  The timed steps replay back to
+back (warm caches); `cold_cache` repeats the per-kernel event pass with a
+1 GiB write before every step, so that nothing of the step stays in the
+256 MB MALL or the L2s.  `dtype` names the arithmetic: fp16 MFMA with fp32
+accumulation in the attention, fp32 fused multiply-adds in the indexer.
 
     python bench.py [--steps K] [--warmup W] [--workload c3|c2|c5|c4] [--gpus 1]
 
@@ -292,15 +297,29 @@ def cpu_baseline_prefill(w, sample_rows, swa=False, mxfp4=False):
     iq = gen.index_q(w, 0)
     q = gen.attn_q(w, 0)
     wins = {r: oracle_window(w, 0, 0, P0 + r + 1) for r in rows} if swa else {}
-    t0 = time.perf_counter()
-    for r in rows:
-        nvis = P0 + r + 1
-        sel = oracle.topk(oracle.index_scores(iq[r], ik[:nvis]), w.K)
-        oracle_attend(w, q[r], codes, scales, sel, nvis, wins.get(r))
-    dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d chunk rows (indexer scan over ~%d entries, top-K, attention each); %.1f s wall"
-                      % (len(rows), T, P0, dt)}
+    def run(rs):
+        t0 = time.perf_counter()
+        for r in rs:
+            nvis = P0 + r + 1
+            sel = oracle.topk(oracle.index_scores(iq[r], ik[:nvis]), w.K)
+            oracle_attend(w, q[r], codes, scales, sel, nvis, wins.get(r))
+        return time.perf_counter() - t0
+
+    cores = oracle.num_threads()
+    dt = run(rows)
+    res = {"value": len(rows) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": "%d of %d chunk rows (indexer scan over ~%d entries, top-K, attention each); %.1f s wall"
+                     % (len(rows), T, P0, dt)}
+    one = rows[::max(1, len(rows) // 8)][:8]
+    oracle.set_num_threads(1)
+    try:
+        dt1 = run(one)
+    finally:
+        oracle.set_num_threads(cores)
+    res["single_thread"] = {"value": len(one) / dt1, "unit": "tokens/s", "cores": 1,
+                            "sample": "%d of the same chunk rows; %.1f s wall" % (len(one), dt1)}
+    res["cpu_model"] = cpu_model()
+    return res
 
 
 def traffic_from_profiles(workload, kernel_file):
@@ -342,27 +361,66 @@ def cpu_baseline(w, lens, sample_rows, reps, swa=False, mxfp4=False):
     iqs = [gen.index_q(w, li, 0, len(rows) * V) if L.mode != "reuse" else None for li, L in enumerate(w.layers)]
     new_kv = [gen.kv_rows(w, b, int(lens[b]) - V, int(lens[b])) for b in rows]
     wins = {(li, b): oracle_window(w, li, b, int(lens[b])) for li in range(len(w.layers)) for b in rows} if swa else {}
-    t0 = time.perf_counter()
-    for b in [b for _ in range(reps) for b in rows]:
-        (codes, scales), ik = caches[b]
-        c1, s1 = oracle.quantize(new_kv[b])  # the newest token(s), written by the first Full layer
-        codes[int(lens[b]) - V:int(lens[b])], scales[int(lens[b]) - V:int(lens[b])] = c1, s1
-        for i in range(V):  # query row (b, i) sees the cache up to its own token
-            n = int(lens[b]) - V + 1 + i
-            r = b * V + i
-            pool = None
-            sel = None
-            for li, L in enumerate(w.layers):
-                if L.mode == "full":
-                    sel, pool, _ = oracle.full_select(iqs[li][r], ik, n, w.K, L.pool_size)
-                elif L.mode == "reindex":
-                    sel = oracle.reindex_select(iqs[li][r], ik, pool, n, w.K)
-                oracle_attend(w, qs[li][r], codes, scales, sel, n, wins.get((li, b)))
-    dt = time.perf_counter() - t0
-    return {"value": reps * len(rows) * V / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d sequences x %d query rows x %d repetitions of one full decode step of the %d-layer "
-                      "chain (quantize newest token(s), indexer scan over %d tokens, top-K, pool, Reindex, attention "
-                      "per layer); %.1f s wall" % (len(rows), w.B, V, reps, len(w.layers), int(lens[0]), dt)}
+    def run(seqs, nrep):
+        t0 = time.perf_counter()
+        for b in [b for _ in range(nrep) for b in seqs]:
+            (codes, scales), ik = caches[b]
+            c1, s1 = oracle.quantize(new_kv[b])  # the newest token(s), written by the first Full layer
+            codes[int(lens[b]) - V:int(lens[b])], scales[int(lens[b]) - V:int(lens[b])] = c1, s1
+            for i in range(V):  # query row (b, i) sees the cache up to its own token
+                n = int(lens[b]) - V + 1 + i
+                r = b * V + i
+                pool = None
+                sel = None
+                for li, L in enumerate(w.layers):
+                    if L.mode == "full":
+                        sel, pool, _ = oracle.full_select(iqs[li][r], ik, n, w.K, L.pool_size)
+                    elif L.mode == "reindex":
+                        sel = oracle.reindex_select(iqs[li][r], ik, pool, n, w.K)
+                    oracle_attend(w, qs[li][r], codes, scales, sel, n, wins.get((li, b)))
+        return time.perf_counter() - t0
+
+    what = ("one full decode step of the %d-layer chain (quantize newest token(s), indexer scan over %d tokens, "
+            "top-K, pool, Reindex, attention per layer)" % (len(w.layers), int(lens[0])))
+    cores = oracle.num_threads()
+    dt = run(rows, reps)
+    res = {"value": reps * len(rows) * V / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": "%d of %d sequences x %d query rows x %d repetitions of %s; %.1f s wall"
+                     % (len(rows), w.B, V, reps, what, dt)}
+    # the same oracle on one thread, over a smaller sample of the same steps
+    one = rows[:min(2, len(rows))]
+    oracle.set_num_threads(1)
+    try:
+        dt1 = run(one, 1)
+    finally:
+        oracle.set_num_threads(cores)
+    res["single_thread"] = {"value": len(one) * V / dt1, "unit": "tokens/s", "cores": 1,
+                            "sample": "%d of %d sequences x %d query rows x 1 repetition of the same step; %.1f s wall"
+                                      % (len(one), w.B, V, dt1)}
+    res["cpu_model"] = cpu_model()
+    return res
+
+
+def cpu_model():
+    """The host CPU: lscpu's model name and counts, else /proc/cpuinfo's model name."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        f = dict(line.split(":", 1) for line in out.splitlines() if ":" in line)
+        f = {k.strip(): v.strip() for k, v in f.items()}
+        if "Model name" in f:
+            return "%s; %s CPUs, %s threads per core, %s sockets" % (
+                f["Model name"], f.get("CPU(s)", "?"), f.get("Thread(s) per core", "?"), f.get("Socket(s)", "?"))
+    except Exception:
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
 
 
 # ------------------------------------------------------------------ HIP events without a system fence
@@ -563,20 +621,49 @@ def main():
             return m
         return HipEvent()  # recorded on creation
 
-    pairs = []
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        armed = {k: arm(kid) for k, kid in kernels.items()}
-        begin = mark()  # a kernel whose stop event precedes this one was not launched in the step
-        step()
-        pairs.append((begin, armed))
-    torch.cuda.synchronize()
+    def event_pass(flush=None):
+        """Eager steps with every kernel bracketed by events; flush: a tensor written by a fill kernel
+        before each step (cold caches).  Returns per-kernel mean us (None: never launched)."""
+        pairs = []
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if flush is not None:
+                flush.fill_(1 + (i % 250))
+            armed = {k: arm(kid) for k, kid in kernels.items()}
+            begin = mark()  # a kernel whose stop event precedes this one was not launched in the step
+            step()
+            pairs.append((begin, armed))
+        torch.cuda.synchronize()
+        us = {}
+        for k in kernels:
+            vals = [a[k][0].elapsed_time(a[k][1]) * 1e3 for b, a in pairs if b.elapsed_time(a[k][1]) > 0]
+            us[k] = float(np.mean(vals)) if vals else None
+        return us
+
+    def step_times(flush=None):
+        """Mean time of one step (a graph replay, else eager) between events around it, each step
+        after a fill kernel over `flush` when given; the fill gives the host time to queue the step."""
+        spans = []
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if flush is not None:
+                flush.fill_(1 + (i % 250))
+            b = mark()
+            run()
+            spans.append((b, mark()))
+        torch.cuda.synchronize()
+        return float(np.mean([b.elapsed_time(e) for b, e in spans]))
+
+    per_kernel_us = event_pass()
+    # cold caches: a 1 GiB write before every step evicts the 256 MB MALL and the L2s, so the step's
+    # cache, queries and indices come from HBM
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+    cold_us = event_pass(flush)
     for kid in kernels.values():
         csa2.profile_kernel_events(kid, None, None)
-    per_kernel_us = {}
-    for k in kernels:
-        vals = [a[k][0].elapsed_time(a[k][1]) * 1e3 for b, a in pairs if b.elapsed_time(a[k][1]) > 0]
-        per_kernel_us[k] = float(np.mean(vals)) if vals else None
+    cold_ms = step_times(flush)
+    del flush
+    warm_ms = step_times(torch.empty(1 << 20, dtype=torch.uint8, device=device))  # same spacing, no eviction
 
     wname = w.name + ("+swa" if args.swa else "") + ("+mxfp4idx" if args.idx_mxfp4 else "")
     byt = algorithmic_bytes(w, lens, args.idx_mxfp4)
@@ -640,7 +727,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16-mfma+f32",
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (wname, w.description + (" + local 128-token FP8 window" if args.swa else "")
                                                         + (" + MXFP4 indexer keys" if args.idx_mxfp4 else "")), "batch": w.B, "rows": w.rows,
@@ -655,6 +742,11 @@ def main():
         "kernels": kern,
     }
     res["chain_hbm_GBps"] = byt["total"] / (ms_step * 1e-3) / 1e9
+    res["cold_cache"] = {
+        "flush": "1 GiB written by a fill kernel before each step (warm: 1 MiB)",
+        "ms_per_step": cold_ms, "warm_ms_per_step": warm_ms, "tokens_per_s": w.rows / (cold_ms * 1e-3),
+        "kernels_avg_us": {k: v for k, v in cold_us.items() if v is not None},
+        "warm_kernels_avg_us": {k: v for k, v in per_kernel_us.items() if v is not None}}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_prefill(w, max(args.cpu_rows, 128), args.swa, args.idx_mxfp4) if w.is_prefill
                                else cpu_baseline(w, lens, args.cpu_rows, args.cpu_reps, args.swa, args.idx_mxfp4))

@@ -77,6 +77,7 @@ def _lib():
             "oracle_attention_row_swa": (None, [P, i32, P, P, P, i32, i64, P, i64, i32, f64, P, P]),
             "oracle_attention_rows_swa": (None, [i32, P, i32, P, P, P, P, i32, P, P, P, P, f64, P, P]),
             "oracle_num_threads": (i32, []),
+            "oracle_set_num_threads": (None, [i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -92,6 +93,11 @@ def _p(a: Optional[np.ndarray]):
 
 def num_threads() -> int:
     return int(_lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only)."""
+    _lib().oracle_set_num_threads(int(n))
 
 
 # ------------------------------------------------------------------ codecs

@@ -477,3 +477,13 @@ int32_t oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* threads of the parallel loops above (timing only: results do not depend on it) */
+void oracle_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

@@ -77,6 +77,8 @@ struct DecArgs {
   int splits;               // S
   int kps;                  // keys per split (multiple of kChunk)
   int xcd_map;              // 1: the S splits of a (row, head group) share blockIdx.x % 8
+  int grp;                  // xcd_map: consecutive pairs that share an XCD (a row's head groups, which
+                            // gather the same entries, when rows come in multiples of 8; else 1)
   _Float16* ws_o;           // [pairs][S][wave][piece 4][lane][8] normalized partials in accumulator order
   float* ws_ml;             // [pairs][32 heads][S][2] (max in log2 units, sum)
   uint64_t* counters;       // [pairs][2]: attention arrivals, merge parts done (zero between calls); null:
@@ -191,12 +193,16 @@ __device__ __forceinline__ float h_hi(uint32_t u) { return (float)__builtin_bit_
 // when the field of its own XCC holds all S arrivals (else NaN): the partials, stored before each arrival
 // is counted, are then in its L2 and are read back past this CU's L1 (agent-scope loads).  The last merge
 // workgroup of a pair to finish resets both counters for the next call.
+// Pair of the t-th (pair, ...) slot of XCD x: XCD x holds the groups of grp consecutive pairs numbered
+// x, x + 8, x + 16, ...
+__device__ __forceinline__ int xcd_pair(int t, int x, int grp) { return (8 * (t / grp) + x) * grp + t % grp; }
+
 __device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7u; }
 
 __device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
   const int j = (int)blockIdx.x - a.nattn;
   const int jx = j >> 3, x = j & 7;
-  const int pair = 8 * (jx / kMergeParts) + x, pc = jx % kMergeParts;
+  const int pair = xcd_pair(jx / kMergeParts, x, a.grp), pc = jx % kMergeParts;
   const int S = a.splits;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h2 = lane >> 5, l32 = lane & 31, tt = pc >> 1, jj = pc & 1;
@@ -294,14 +300,16 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
   // (pair, split): with xcd_map the S splits of one (row, head group) run on
   // one XCD (workgroups are dispatched round-robin over the 8 XCDs), so its
-  // queries are read from HBM once and then hit that XCD's L2
+  // queries are read from HBM once and then hit that XCD's L2; with grp > 1
+  // the other head groups of the row are there too, and the entries they
+  // gather as well come from that L2
   const int S = a.splits;
   const int L = blockIdx.x;
   int pair, split;
   if (a.xcd_map) {
     const int jx = L >> 3;
     split = jx % S;
-    pair = 8 * (jx / S) + (L & 7);
+    pair = xcd_pair(jx / S, L & 7, a.grp);
   } else {
     split = L % S;
     pair = L / S;
@@ -717,6 +725,7 @@ hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, c
   a.splits = p.splits;
   a.kps = p.kps;
   a.xcd_map = p.xcd ? 1 : 0;
+  a.grp = R % 8 == 0 ? Hq / kHG : 1;
   a.nattn = p.pairs * p.splits;
   int nmerge = 0;
   if (p.splits > 1) {
