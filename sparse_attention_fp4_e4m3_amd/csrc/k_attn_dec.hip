@@ -99,8 +99,7 @@ struct __align__(16) SmemDec {
   float c2h[kHG];
   float alpha[kHG];
   float ifin[kHG];
-  float om[16][kMaxSplits];  // merge workgroups: weights of the splits of their 16 heads
-  float2 mls[16 * kMaxSplits];
+  __align__(16) float om[16][kMaxSplits];  // merge workgroups: weights of the splits of their 16 heads
   int flag;
 };
 
@@ -218,51 +217,63 @@ __device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
     }
     sm.flag = (it < kSpinMax && (int)((c >> (8 + 4 * xcc_id())) & 15u) == S) ? 1 : 0;
   }
-  __syncthreads();
+  lds_barrier();
   const bool ok = sm.flag != 0;
-  // piece pc of (split s, wave w, lane): 16 bytes each, all splits in flight, read from L2 (sc0)
+  // threads 0..15: the (max, sum) pairs of head 16*jj + tid, issued first (they are needed first);
+  // then every thread's piece pc of (split s, wave w, lane): 16 bytes each, all in flight, from L2
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(a.ws_ml, 0, 0x7FFFFFFF, 0x00020000);
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.ws_o, 0, 0x7FFFFFFF, 0x00020000);
+  u32x2 ml[kMaxSplits];
+  if (tid < 16) {
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+      const uint32_t e = (uint32_t)(((size_t)pair * kHG + 16 * jj + tid) * S + (s2 < S ? s2 : 0));
+      ml[s2] = __builtin_amdgcn_raw_buffer_load_b64(rm, (int)(8u * e), 0, 16);
+    }
+  }
   u32x4 v[kMaxSplits];
 #pragma unroll
   for (int s2 = 0; s2 < kMaxSplits; ++s2) {
     const uint32_t off = (uint32_t)((((((size_t)pair * S + (s2 < S ? s2 : 0)) * 8 + w) * 4 + pc) * 64 + lane) * 16);
     v[s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off, 0, 16);
   }
-  // weights of the splits of heads 16*jj .. +15, in fixed split order
-  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(a.ws_ml, 0, 0x7FFFFFFF, 0x00020000);
-  if (tid < 16 * S) {
-    const uint32_t e = (uint32_t)(((size_t)pair * kHG + 16 * jj + tid / S) * S + tid % S);
-    const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, (int)(8u * e), 0, 16);
-    sm.mls[tid] = make_float2(__uint_as_float(m2[0]), __uint_as_float(m2[1]));
-  }
-  __syncthreads();
+  // weights of the splits of each head, in fixed split order
   if (tid < 16) {
     float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, sm.mls[tid * S + s2].x);
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2)
+      if (s2 < S) M = fmaxf(M, __uint_as_float(ml[s2][0]));
     float wg[kMaxSplits], L = 0.0f;
 #pragma unroll
     for (int s2 = 0; s2 < kMaxSplits; ++s2) {
-      wg[s2] = (s2 < S && M != -INFINITY) ? __builtin_amdgcn_exp2f(sm.mls[tid * S + s2].x - M) * sm.mls[tid * S + s2].y
-                                          : 0.0f;
+      wg[s2] = (s2 < S && M != -INFINITY)
+                   ? __builtin_amdgcn_exp2f(__uint_as_float(ml[s2][0]) - M) * __uint_as_float(ml[s2][1])
+                   : 0.0f;
       L += wg[s2];
     }
     const float iL = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-    for (int s2 = 0; s2 < kMaxSplits; ++s2) sm.om[tid][s2] = wg[s2] * iL;
+    *reinterpret_cast<floatx4*>(&sm.om[tid][0]) = floatx4{wg[0] * iL, wg[1] * iL, wg[2] * iL, wg[3] * iL};
+    *reinterpret_cast<floatx4*>(&sm.om[tid][4]) = floatx4{wg[4] * iL, wg[5] * iL, wg[6] * iL, wg[7] * iL};
     if (a.lse && tt == 0)
       a.lse[(int64_t)r * a.Hq + h0 + 16 * jj + tid] = !ok ? __builtin_nanf("") : L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
   }
-  __syncthreads();
+  lds_barrier();  // (the piece loads stay in flight)
   // rows i = 8*jj + e of this lane: head 8*(i/4) + 4*h2 + i%4 (= 16*jj + local head), channel 64w + 32tt + l32
+  floatx4 wv[8][2];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int hl = 8 * (e >> 2) + 4 * h2 + (e & 3);
+    wv[e][0] = *reinterpret_cast<const floatx4*>(&sm.om[hl][0]);
+    wv[e][1] = *reinterpret_cast<const floatx4*>(&sm.om[hl][4]);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s2 = 0; s2 < kMaxSplits; ++s2) {
     if (s2 >= S) break;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int e0 = 2 * k, e1 = 2 * k + 1;  // local heads 8*(e/4) + 4*h2 + e%4
-      acc[e0] += sm.om[8 * (e0 >> 2) + 4 * h2 + (e0 & 3)][s2] * h_lo(v[s2][k]);
-      acc[e1] += sm.om[8 * (e1 >> 2) + 4 * h2 + (e1 & 3)][s2] * h_hi(v[s2][k]);
+      acc[2 * k] += wv[2 * k][s2 >> 2][s2 & 3] * h_lo(v[s2][k]);
+      acc[2 * k + 1] += wv[2 * k + 1][s2 >> 2][s2 & 3] * h_hi(v[s2][k]);
     }
   }
   const int64_t ob = ((int64_t)r * a.Hq + h0 + 16 * jj) * kDim + 64 * w + 32 * tt + l32;
