@@ -679,6 +679,8 @@ def main():
     }
     if per_kernel_us["attention_combine"] is None:
         del kern["attention_combine"]  # the split merge runs inside the attention launch
+    if n_launch["reindex_score"] == 0:
+        del kern["reindex_score"]  # a chain without Reindex layers
     if args.swa:
         # the window: 128 entries x 512 B per row; QK^T and PV over them for every head
         kern["swa_attention"] = {"avg_us": per_kernel_us["swa_attention"], "bytes": w.rows * 128 * 512,
@@ -698,7 +700,8 @@ def main():
             else:
                 v["valu_fp32_frac"] = v["TFLOPs"] / VALU_F32_PEAK_TFLOPS
         v["per_step_us"] = v["avg_us"] * n_launch.get(k, 1)
-    dominant = max(["index_scan", "attention", "reindex_score"], key=lambda k: kern[k]["per_step_us"])
+    dominant = max([k for k in ("index_scan", "attention", "reindex_score") if k in kern],
+                   key=lambda k: kern[k]["per_step_us"])
     dk = kern[dominant]
     if dominant == "attention":
         kname, ksrc = attention_kernel_name(w)
