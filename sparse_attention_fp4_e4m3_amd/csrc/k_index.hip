@@ -204,9 +204,9 @@ __device__ __forceinline__ int find_bin_wave(const uint32_t* h, uint32_t K, uint
       lds[17] = run;
     }
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t bin = lds[16], ab = lds[17], tot = lds[18];
-  __syncthreads();
+  lds_barrier();
   *total = tot;
   *above = (bin == 0xFFFFFFFFu) ? tot : ab;
   return (bin == 0xFFFFFFFFu) ? -1 : (int)bin;
@@ -596,11 +596,11 @@ __device__ __forceinline__ uint32_t fin_gather(const Series& S, int r, bool full
     // Reindex: the first-digit histogram of the row's valid scores, counted here
     // in the candidate area (written only after find_bin has read it)
     for (int b = threadIdx.x; b < kD1; b += NT) lkey[b] = 0u;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < MAXCH; ++j)
       if (!(kr[j] >> 31)) atomicAdd(&lkey[kr[j] >> kS1], 1u);
-    __syncthreads();
+    lds_barrier();
     uint32_t total0;
     b0 = find_bin_wave<kD1>(lkey, (uint32_t)S.K, &above0, &total0, red);
   }
@@ -652,8 +652,31 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
   int nsub = 0;
   const uint32_t* sk;
   const int32_t* sp;
+  // Full with at most kSpec slices per wave: wave w owns slices [s_lo, s_hi) of the row's candidate
+  // lists (k_collect wrote slice s's candidates, in position order, from offset s * kSub), and the
+  // first 64 candidates of each are loaded before the slice counts have arrived
+  constexpr int kSpec = 16;
+  int s_lo = 0, s_hi = 0;
+  bool by_slice = false;
+  uint32_t kr[kSpec];
+  int32_t pr[kSpec];
   if (full) {
     nsub = (n + kSub - 1) / kSub;
+    sk = reinterpret_cast<const uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride;
+    sp = S.cand_pos + (int64_t)r * 2 * S.stride;
+    const int spw = (nsub + NW - 1) / NW;
+    by_slice = spw <= kSpec;
+    s_lo = min(nsub, wave * spw);
+    s_hi = min(nsub, s_lo + spw);
+    if (by_slice) {
+#pragma unroll
+      for (int j = 0; j < kSpec; ++j) {
+        const int sl = s_lo + j;
+        const int64_t at = sl < s_hi ? (int64_t)sl * kSub + lane : 0;
+        kr[j] = sk[at];
+        pr[j] = sp[at];
+      }
+    }
     const uint32_t c_first = ((int)threadIdx.x < nsub) ? S.counts[(int64_t)r * S.nsub + threadIdx.x] : 0u;
     b0 = (int)S.thr[2 * r];
     above0 = S.thr[2 * r + 1];
@@ -667,10 +690,8 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
       carry += tot;
     }
     if (threadIdx.x == 0) pre[nsub] = carry;
-    __syncthreads();
+    lds_barrier();
     M = pre[nsub];
-    sk = reinterpret_cast<const uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride;
-    sp = S.cand_pos + (int64_t)r * 2 * S.stride;
   } else {
     // the row is split by its pool capacity when that fits, so the candidate
     // loads need not wait for the pool length (slots past it are masked);
@@ -680,11 +701,34 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
     sp = a.pool + (int64_t)r * a.pool_stride;
   }
   const uint32_t per_w = ((M + NW - 1) / NW + 63u) & ~63u;
-  const uint32_t w0 = min(M, (uint32_t)wave * per_w), w1 = min(M, w0 + per_w);
+  uint32_t w0 = min(M, (uint32_t)wave * per_w);
+  const uint32_t w1 = min(M, w0 + per_w);
   const uint32_t* keys;
   const int32_t* posr;
   uint32_t cend;  // this wave works on [w0, cend) of keys/posr
-  if (M <= (uint32_t)kFinCap) {
+  if (by_slice && M <= (uint32_t)kFinCap) {
+    // candidate c of the row's order sits at LDS slot c: the wave's run is [pre[s_lo], pre[s_hi]);
+    // every collected candidate reaches the threshold bin, so all are kept
+#pragma unroll
+    for (int j = 0; j < kSpec; ++j) {
+      const int sl = s_lo + j;
+      if (sl < s_hi) {
+        const uint32_t base = pre[sl], cs = pre[sl + 1] - base;
+        if ((uint32_t)lane < cs) {
+          lkey[base + lane] = kr[j];
+          lpos[base + lane] = pr[j];
+        }
+        for (uint32_t c = 64u + lane; c < cs; c += 64u) {  // slices of more than 64 candidates
+          lkey[base + c] = sk[(int64_t)sl * kSub + c];
+          lpos[base + c] = sp[(int64_t)sl * kSub + c];
+        }
+      }
+    }
+    keys = lkey;
+    posr = lpos;
+    w0 = pre[s_lo];
+    cend = pre[s_hi];
+  } else if (M <= (uint32_t)kFinCap) {
     const int nchmax = (int)(per_w / 64u);  // uniform
     const uint32_t nv = full ? M : (uint32_t)n;  // Reindex: the valid slots
     uint32_t sw;
@@ -744,7 +788,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
         const uint32_t key = keys[c];
         if (!(key >> 31) && (key >> shift_hi) == prefix) atomicAdd(&h[(key >> sh) & (nb - 1)], 1u);
       }
-      __syncthreads();
+      lds_barrier();
       uint32_t above, total;
       const int b = lev == 1 ? find_bin_wave<kD2>(hist2, K, &above, &total, red)
                              : find_bin_wave<kD3>(hist, K, &above, &total, red);
@@ -770,7 +814,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
     red[wave] = gt;
     red[NW + wave] = eq;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t gt_before = 0, eq_before = 0, tot_gt = 0;
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) {
@@ -779,7 +823,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
     eq_before += ww < wave ? e : 0u;
     tot_gt += g;
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t nsel = all ? tot_gt : (uint32_t)S.K;
   uint32_t out = gt_before + (all ? 0u : min(eq_before, need));
   uint32_t ties = eq_before;
@@ -815,9 +859,9 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
     for (int i = (int)nsel + threadIdx.x; i < S.K; i += NT) o[i] = -1;
   } else {
     if (threadIdx.x == 0) red[0] = 0u;
-    __syncthreads();
+    lds_barrier();
     if (last_block_kept) red[0] = 1u;
-    __syncthreads();
+    lds_barrier();
     // the partial last block is the highest block, hence the last one written
     int plen = (int)nsel * kBlock;
     if (red[0] && (vis % kBlock) != 0) plen -= kBlock - (vis % kBlock);
