@@ -999,21 +999,54 @@ struct PfArgs {
   int32_t* cand;              // [R][kPfCap] candidate positions, ascending
   int32_t* ccnt;              // [R] candidates (0 on overflow)
   uint32_t* over;             // [R] 1 = overflow: exact fallback
+  uint32_t* hist2;            // [R][kD1] the failed rows' histograms (zeroed by k_pf_certify)
+  uint32_t* xhist;            // [R][kD1] the exact path's first-digit histograms (zeroed for overflow rows)
 };
 
 // max(x, +0) as one integer max: negative floats (sign bit set, -0 included) compare below 0
 __device__ __forceinline__ float relu0(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // norms: one thread per key of the shared segment, then one per (row, head) query
+// Key norms (MXFP4: one thread per key; bf16: eight lanes per key, 16 coalesced bytes each, summed
+// across the eight lanes; the order of the sum does not matter for the bound: 64 terms of rounding
+// stay far below the 1e-5 margin the norm is widened by) over a grid-stride loop, their maximum (one
+// atomic per workgroup), and each row's sum of query-head norms (one thread per row and head).
 __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
+  __shared__ uint32_t wmax[4];
   const int64_t seg = a.row_start[0];
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  float nrm = 0.0f;
-  if (i < a.max_visible) {
-    float ss = 0.0f;
-    if (a.ks) {  // MXFP4: the exact values E2M1(code) * 2^(scale - 127)
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t m = 0u;  // largest norm seen (non-negative floats order like their bits)
+  if (!a.ks) {
+    const int64_t nthreads = ((int64_t)a.max_visible * 8 + 63) & ~int64_t(63);  // whole waves
+    for (int64_t t = t0; t < nthreads; t += stride) {
+      const int64_t i = t >> 3;
+      const int part = (int)(t & 7);
+      float ss = 0.0f;
+      if (i < a.max_visible) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(a.k + (seg + i) * 128)[part];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xFFFF0000u);
+          ss = __builtin_fmaf(lo, lo, ss);
+          ss = __builtin_fmaf(hi, hi, ss);
+        }
+      }
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      if (i < a.max_visible) {
+        const float nrm = __fsqrt_rn(ss) * 1.00001f;
+        if (part == 0) a.knorm[i] = nrm;
+        m = max(m, __float_as_uint(nrm));
+      }
+    }
+  } else {
+    for (int64_t i = t0; i < a.max_visible; i += stride) {
+      // MXFP4: the exact values E2M1(code) * 2^(scale - 127)
       const u32x4* row = reinterpret_cast<const u32x4*>(a.k + (seg + i) * 32);
       const uint32_t sc = *reinterpret_cast<const uint16_t*>(a.ks + (seg + i) * 2);
+      float ss = 0.0f;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const u32x4 v = row[b];
@@ -1032,32 +1065,24 @@ __global__ __launch_bounds__(256) void k_pf_norms(PfArgs a, int H) {
           }
         }
       }
-    } else {
-      const u32x4* row = reinterpret_cast<const u32x4*>(a.k + (seg + i) * 128);
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const u32x4 v = row[p];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xFFFF0000u);
-          ss = __builtin_fmaf(lo, lo, ss);
-          ss = __builtin_fmaf(hi, hi, ss);
-        }
-      }
+      const float nrm = __fsqrt_rn(ss) * 1.00001f;
+      a.knorm[i] = nrm;
+      m = max(m, __float_as_uint(nrm));
     }
-    nrm = __fsqrt_rn(ss) * 1.00001f;
-    a.knorm[i] = nrm;
   }
-  // the wave's largest norm, then one atomic per wave (non-negative floats order like their bits)
-  uint32_t m = __float_as_uint(nrm);
   m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
   m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
   m = max(m, (uint32_t)__shfl_xor((int)m, 8, 64));
   m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
   m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
   m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
-  if ((threadIdx.x & 63) == 0 && m) atomicMax(a.kmax, m);
-  if (i < (int64_t)a.R * H) {
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t b = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (b) atomicMax(a.kmax, b);
+  }
+  for (int64_t i = t0; i < (int64_t)a.R * H; i += stride) {
     const u32x4* row = reinterpret_cast<const u32x4*>(a.q + i * 64);
     float ss = 0.0f;
 #pragma unroll
@@ -1327,10 +1352,17 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a, int H, int sampled)
   }
 }
 
-// per row: the provisional bound holds if at least K entries reach it
+// per row: the provisional bound holds if at least K entries reach it; a row that fails gets its
+// second approximate histogram zeroed here, before the pass that fills it
 __global__ __launch_bounds__(256) void k_pf_certify(PfArgs a) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r < a.R) a.failed[r] = a.nhi[r] < (uint32_t)a.K ? 1u : 0u;
+  if (r >= a.R) return;
+  const bool fail = a.nhi[r] < (uint32_t)a.K;
+  a.failed[r] = fail ? 1u : 0u;
+  if (fail) {
+    u32x4* h = reinterpret_cast<u32x4*>(a.hist2 + (int64_t)r * kD1);
+    for (int i = 0; i < kD1 / 4; ++i) h[i] = u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
 // per row: candidate bitmap -> ascending positions (or the overflow flag).
@@ -1376,10 +1408,14 @@ __global__ __launch_bounds__(256) void k_pf_compact(PfArgs a) {
       }
     }
   }
+  const bool overflow = total > (uint32_t)kPfCap;
   if (threadIdx.x == 0) {
-    const bool overflow = total > (uint32_t)kPfCap;
     a.ccnt[r] = overflow ? 0 : (int32_t)total;
     a.over[r] = overflow ? 1u : 0u;
+  }
+  if (overflow) {  // this row takes the exact full scan, whose first-digit histogram starts at zero
+    u32x4* h = reinterpret_cast<u32x4*>(a.xhist + (int64_t)r * kD1);
+    for (int i = threadIdx.x; i < kD1 / 4; i += 256) h[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -1676,21 +1712,23 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   p.cand = L.cand;
   p.ccnt = L.ccnt;
   p.over = L.over;
+  p.hist2 = L.phist2;
+  p.xhist = L.hist;
   {
-    // one pass zeroes every histogram and accumulator: the exact path's (fallback), the approximate
-    // histograms, the query-norm sums and the key-norm maximum (they are contiguous in the layout)
+    // the queries for the exact path (fallback rows); the approximate histogram, the certification
+    // counts and the key-norm maximum zeroed; the exact path's histograms of rows that overflow are
+    // zeroed by k_pf_compact, the second approximate histogram of rows that fail by k_pf_certify
     const int64_t nq = (int64_t)R * H * kIdxDim;
-    const int64_t nhist = (int64_t)R * kD1 * 2;
-    hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(std::max(nq, nhist), 256))),
-                       dim3(256), 0, s, idx_q, q_dtype, R, H, L.qf, L.hist, nhist);
+    hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(nq, 256))), dim3(256), 0, s, idx_q,
+                       q_dtype, R, H, L.qf, L.hist, (int64_t)0);
     hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>(2048, ceil_div((int64_t)R * kD1, 256))), dim3(256),
-                       0, s, L.phist, (int64_t)R * kD1, L.phist2, (int64_t)R * kD1, L.nhi, (int64_t)R, L.kmax);
+                       0, s, L.phist, (int64_t)R * kD1, L.nhi, (int64_t)R, L.nhi, (int64_t)0, L.kmax);
     hipLaunchKernelGGL(k_zero, dim3((unsigned)ceil_div((int64_t)R, 256)), dim3(256), 0, s,
                        reinterpret_cast<uint32_t*>(L.qn), (int64_t)R, L.failed, (int64_t)0, L.failed, (int64_t)0,
                        nullptr);
   }
-  const int64_t nn = std::max<int64_t>((int64_t)max_visible, (int64_t)R * H);
-  hipLaunchKernelGGL(k_pf_norms, dim3((unsigned)ceil_div(nn, 256)), dim3(256), 0, s, p, H);
+  const int64_t nn = std::max<int64_t>((int64_t)max_visible * (k_dtype == CSA2_MXFP4 ? 1 : 8), (int64_t)R * H);
+  hipLaunchKernelGGL(k_pf_norms, dim3((unsigned)std::min<int64_t>(1024, ceil_div(nn, 256))), dim3(256), 0, s, p, H);
   auto& ev = profile_events(CSA2_KERNEL_INDEX_SCAN);
   if (ev.start) (void)hipEventRecord(ev.start, s);
   auto pass = [&](int mode, const PfArgs& pa) {
