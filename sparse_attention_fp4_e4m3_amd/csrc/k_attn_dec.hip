@@ -282,8 +282,8 @@ __device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
   for (int e = 0; e < 8; ++e) {
     const int64_t o = ob + (int64_t)(8 * (e >> 2) + 4 * h2 + (e & 3)) * kDim;
     const float val = ok ? acc[e] : bad;
-    if (a.out_dtype == CSA2_F32) static_cast<float*>(a.out)[o] = val;
-    else static_cast<uint16_t*>(a.out)[o] = (uint16_t)bf16_rne(val);
+    if (a.out_dtype == CSA2_F32) __builtin_nontemporal_store(val, static_cast<float*>(a.out) + o);
+    else __builtin_nontemporal_store((uint16_t)bf16_rne(val), static_cast<uint16_t*>(a.out) + o);
   }
   // every merge workgroup of the pair has seen all S arrivals once the last one gets here
   if (tid == 0) {
@@ -595,8 +595,9 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         pk[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[t][i] * inv[i])) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[t][i + 1] * inv[i + 1])) << 16);
       }
-      if (a.counters) po[64 * (2 * t + j)] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-      else __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]}, po + 64 * (2 * t + j));
+      // streaming stores: the partials are read once, by the merge, and a kernel ending with 8 MB of
+      // them dirty in L2 would first write them back
+      __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]}, po + 64 * (2 * t + j));
     }
   if (w == 0 && lane < 32)
     *reinterpret_cast<float2*>(a.ws_ml + (((size_t)pair * kHG + lane) * S + split) * 2) = make_float2(m_run, l_run);
