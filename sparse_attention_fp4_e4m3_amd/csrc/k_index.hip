@@ -703,10 +703,113 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
   const uint32_t per_w = ((M + NW - 1) / NW + 63u) & ~63u;
   uint32_t w0 = min(M, (uint32_t)wave * per_w);
   const uint32_t w1 = min(M, w0 + per_w);
-  const uint32_t* keys;
-  const int32_t* posr;
-  uint32_t cend;  // this wave works on [w0, cend) of keys/posr
-  if (by_slice && M <= (uint32_t)kFinCap) {
+  // The threshold digits and the ordered compaction over this wave's run [w0, cend) of keys/posr,
+  // instantiated once for candidates in LDS and once for candidates in global memory: a pointer that
+  // could be either would turn every access into a flat one, whose waits also cover the global stores
+  // in flight.
+  auto phases = [&](const uint32_t* keys, const int32_t* posr, const uint32_t cend) {
+    // ---- exact threshold: digits 2 and 3 among the candidates of the first digit's bin
+    uint32_t need = 0;
+    uint32_t prefix = 0;
+    const bool all = b0 < 0;  // fewer than K valid entries: every valid candidate is selected
+    if (!all) {
+      uint32_t K = (uint32_t)S.K - above0;
+      prefix = (uint32_t)b0;
+      int shift_hi = kS1;
+  #pragma unroll 1
+      for (int lev = 1; lev < 3; ++lev) {
+        const int sh = lev == 1 ? kS2 : 0;
+        const int nb = lev == 1 ? kD2 : kD3;
+        uint32_t* h = lev == 1 ? hist2 : hist;
+  #pragma unroll 4
+        for (uint32_t c = w0 + lane; c < cend; c += 64) {
+          const uint32_t key = keys[c];
+          if (!(key >> 31) && (key >> shift_hi) == prefix) atomicAdd(&h[(key >> sh) & (nb - 1)], 1u);
+        }
+        lds_barrier();
+        uint32_t above, total;
+        const int b = lev == 1 ? find_bin_wave<kD2>(hist2, K, &above, &total, red)
+                               : find_bin_wave<kD3>(hist, K, &above, &total, red);
+        prefix = (prefix << (shift_hi - sh)) | (uint32_t)b;
+        shift_hi = sh;
+        K -= above;
+      }
+      need = K;  // ties at T to take, in candidate order
+    }
+    const uint32_t T = prefix;  // the full 31-bit key of the K-th largest
+
+    // ---- ordered compaction over each wave's run, 64 candidates at a time
+    auto is_gt = [&](uint32_t key) { return !(key >> 31) && (all || key > T); };
+    auto is_eq = [&](uint32_t key) { return !(key >> 31) && !all && key == T; };
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t c0 = w0; c0 < cend; c0 += 64) {
+      const uint32_t c = c0 + lane;
+      const uint32_t key = c < cend ? keys[c] : 0x80000000u;
+      gt += (uint32_t)__popcll(__ballot(is_gt(key)));
+      eq += (uint32_t)__popcll(__ballot(is_eq(key)));
+    }
+    if (lane == 0) {
+      red[wave] = gt;
+      red[NW + wave] = eq;
+    }
+    lds_barrier();
+    uint32_t gt_before = 0, eq_before = 0, tot_gt = 0;
+  #pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const uint32_t g = red[ww], e = red[NW + ww];
+      gt_before += ww < wave ? g : 0u;
+      eq_before += ww < wave ? e : 0u;
+      tot_gt += g;
+    }
+    lds_barrier();
+    const uint32_t nsel = all ? tot_gt : (uint32_t)S.K;
+    uint32_t out = gt_before + (all ? 0u : min(eq_before, need));
+    uint32_t ties = eq_before;
+    bool last_block_kept = false;
+    for (uint32_t c0 = w0; c0 < cend; c0 += 64) {
+      const uint32_t c = c0 + lane;
+      const uint32_t key = c < cend ? keys[c] : 0x80000000u;
+      const bool e = is_eq(key);
+      const unsigned long long me = __ballot(e);
+      const uint32_t rank =
+          ties + __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+      const bool sel = is_gt(key) || (e && rank < need);
+      const unsigned long long ms = __ballot(sel);
+      const uint32_t at =
+          out + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
+      if (sel && at < nsel) {
+        const int32_t pos = posr[c];
+        if (series == 0) {
+          a.out_idx[(int64_t)r * S.K + at] = pos;
+        } else {
+          int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)at * kBlock;
+  #pragma unroll
+          for (int m = 0; m < kBlock; ++m) o[m] = (pos * kBlock + m < vis) ? pos * kBlock + m : -1;
+          if (pos == n - 1) last_block_kept = true;
+        }
+      }
+      out += (uint32_t)__popcll(ms);
+      ties += (uint32_t)__popcll(me);
+    }
+    // ---- padding and pool length
+    if (series == 0) {
+      int32_t* o = a.out_idx + (int64_t)r * S.K;
+      for (int i = (int)nsel + threadIdx.x; i < S.K; i += NT) o[i] = -1;
+    } else {
+      if (threadIdx.x == 0) red[0] = 0u;
+      lds_barrier();
+      if (last_block_kept) red[0] = 1u;
+      lds_barrier();
+      // the partial last block is the highest block, hence the last one written
+      int plen = (int)nsel * kBlock;
+      if (red[0] && (vis % kBlock) != 0) plen -= kBlock - (vis % kBlock);
+      int32_t* o = a.out_pool + (int64_t)r * a.pool_size;
+      for (int i = (int)nsel * kBlock + threadIdx.x; i < a.pool_size; i += NT) o[i] = -1;
+      if (threadIdx.x == 0) a.out_pool_len[r] = plen;
+    }
+  };
+  if (M <= (uint32_t)kFinCap) {
+  if (by_slice) {
     // candidate c of the row's order sits at LDS slot c: the wave's run is [pre[s_lo], pre[s_hi]);
     // every collected candidate reaches the threshold bin, so all are kept
 #pragma unroll
@@ -724,11 +827,9 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
         }
       }
     }
-    keys = lkey;
-    posr = lpos;
     w0 = pre[s_lo];
-    cend = pre[s_hi];
-  } else if (M <= (uint32_t)kFinCap) {
+    phases(lkey, lpos, pre[s_hi]);
+  } else {
     const int nchmax = (int)(per_w / 64u);  // uniform
     const uint32_t nv = full ? M : (uint32_t)n;  // Reindex: the valid slots
     uint32_t sw;
@@ -737,10 +838,11 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
     else if (nchmax <= 8) sw = fin_gather<NT, 8>(S, r, full, nsub, pre, sk, sp, w0, w1, nv, b0, above0, red, lkey, lpos);
     else sw = fin_gather<NT, 16>(S, r, full, nsub, pre, sk, sp, w0, w1, nv, b0, above0, red, lkey, lpos);
     // (each wave reads back only its own run; LDS operations of a wave execute in order)
-    keys = lkey;
-    posr = lpos;
-    cend = w0 + sw;
+    phases(lkey, lpos, w0 + sw);
+  }
   } else {
+    const uint32_t* gk;
+    const int32_t* gp;
     if (full) {
       uint32_t* dk = reinterpret_cast<uint32_t*>(S.cand_key) + (int64_t)r * 2 * S.stride + S.stride;
       int32_t* dp = S.cand_pos + (int64_t)r * 2 * S.stride + S.stride;
@@ -751,8 +853,8 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
         dp[c] = sp[at];
       }
       __syncthreads();
-      keys = dk;
-      posr = dp;
+      gk = dk;
+      gp = dp;
     } else {
       // Reindex beyond the LDS capacity: the first-digit histogram from the scores in place
       for (int b = threadIdx.x; b < kD1; b += NT) lkey[b] = 0u;
@@ -764,110 +866,10 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
       __syncthreads();
       uint32_t total0;
       b0 = find_bin_wave<kD1>(lkey, (uint32_t)S.K, &above0, &total0, red);
-      keys = sk;
-      posr = sp;
+      gk = sk;
+      gp = sp;
     }
-    cend = w1;
-  }
-
-  // ---- exact threshold: digits 2 and 3 among the candidates of the first digit's bin
-  uint32_t need = 0;
-  uint32_t prefix = 0;
-  const bool all = b0 < 0;  // fewer than K valid entries: every valid candidate is selected
-  if (!all) {
-    uint32_t K = (uint32_t)S.K - above0;
-    prefix = (uint32_t)b0;
-    int shift_hi = kS1;
-#pragma unroll 1
-    for (int lev = 1; lev < 3; ++lev) {
-      const int sh = lev == 1 ? kS2 : 0;
-      const int nb = lev == 1 ? kD2 : kD3;
-      uint32_t* h = lev == 1 ? hist2 : hist;
-#pragma unroll 4
-      for (uint32_t c = w0 + lane; c < cend; c += 64) {
-        const uint32_t key = keys[c];
-        if (!(key >> 31) && (key >> shift_hi) == prefix) atomicAdd(&h[(key >> sh) & (nb - 1)], 1u);
-      }
-      lds_barrier();
-      uint32_t above, total;
-      const int b = lev == 1 ? find_bin_wave<kD2>(hist2, K, &above, &total, red)
-                             : find_bin_wave<kD3>(hist, K, &above, &total, red);
-      prefix = (prefix << (shift_hi - sh)) | (uint32_t)b;
-      shift_hi = sh;
-      K -= above;
-    }
-    need = K;  // ties at T to take, in candidate order
-  }
-  const uint32_t T = prefix;  // the full 31-bit key of the K-th largest
-
-  // ---- ordered compaction over each wave's run, 64 candidates at a time
-  auto is_gt = [&](uint32_t key) { return !(key >> 31) && (all || key > T); };
-  auto is_eq = [&](uint32_t key) { return !(key >> 31) && !all && key == T; };
-  uint32_t gt = 0, eq = 0;
-  for (uint32_t c0 = w0; c0 < cend; c0 += 64) {
-    const uint32_t c = c0 + lane;
-    const uint32_t key = c < cend ? keys[c] : 0x80000000u;
-    gt += (uint32_t)__popcll(__ballot(is_gt(key)));
-    eq += (uint32_t)__popcll(__ballot(is_eq(key)));
-  }
-  if (lane == 0) {
-    red[wave] = gt;
-    red[NW + wave] = eq;
-  }
-  lds_barrier();
-  uint32_t gt_before = 0, eq_before = 0, tot_gt = 0;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) {
-    const uint32_t g = red[ww], e = red[NW + ww];
-    gt_before += ww < wave ? g : 0u;
-    eq_before += ww < wave ? e : 0u;
-    tot_gt += g;
-  }
-  lds_barrier();
-  const uint32_t nsel = all ? tot_gt : (uint32_t)S.K;
-  uint32_t out = gt_before + (all ? 0u : min(eq_before, need));
-  uint32_t ties = eq_before;
-  bool last_block_kept = false;
-  for (uint32_t c0 = w0; c0 < cend; c0 += 64) {
-    const uint32_t c = c0 + lane;
-    const uint32_t key = c < cend ? keys[c] : 0x80000000u;
-    const bool e = is_eq(key);
-    const unsigned long long me = __ballot(e);
-    const uint32_t rank =
-        ties + __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
-    const bool sel = is_gt(key) || (e && rank < need);
-    const unsigned long long ms = __ballot(sel);
-    const uint32_t at =
-        out + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
-    if (sel && at < nsel) {
-      const int32_t pos = posr[c];
-      if (series == 0) {
-        a.out_idx[(int64_t)r * S.K + at] = pos;
-      } else {
-        int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)at * kBlock;
-#pragma unroll
-        for (int m = 0; m < kBlock; ++m) o[m] = (pos * kBlock + m < vis) ? pos * kBlock + m : -1;
-        if (pos == n - 1) last_block_kept = true;
-      }
-    }
-    out += (uint32_t)__popcll(ms);
-    ties += (uint32_t)__popcll(me);
-  }
-  // ---- padding and pool length
-  if (series == 0) {
-    int32_t* o = a.out_idx + (int64_t)r * S.K;
-    for (int i = (int)nsel + threadIdx.x; i < S.K; i += NT) o[i] = -1;
-  } else {
-    if (threadIdx.x == 0) red[0] = 0u;
-    lds_barrier();
-    if (last_block_kept) red[0] = 1u;
-    lds_barrier();
-    // the partial last block is the highest block, hence the last one written
-    int plen = (int)nsel * kBlock;
-    if (red[0] && (vis % kBlock) != 0) plen -= kBlock - (vis % kBlock);
-    int32_t* o = a.out_pool + (int64_t)r * a.pool_size;
-    for (int i = (int)nsel * kBlock + threadIdx.x; i < a.pool_size; i += NT) o[i] = -1;
-    if (threadIdx.x == 0) a.out_pool_len[r] = plen;
+    phases(gk, gp, w1);
   }
 }
 
