@@ -341,6 +341,34 @@ def test_attention_error_bound_under_cancellation(Hq, qkind, R):
     assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-3
 
 
+@pytest.mark.parametrize("R,Hq,exps", [
+    # decode kernel (16 rows x 64 heads): each head's queries are scaled by a power of two into fp16,
+    # so heads far below and above the fp16 range are used exactly
+    (16, 64, (-40, -24, -14, -3, 0, 3, 20, 60)),
+    # 64-head kernel (256 rows): bf16 converts to fp16 unscaled, exact for 2^-14 <= |q| < 65520
+    (256, 64, (-12, -6, -3, 0, 2, 4, 6, 8)),
+])
+def test_attention_bf16_query_magnitudes(R, Hq, exps):
+    """Heads whose bf16 queries sit at very different magnitudes (head h scaled by 2^exps[h % 8],
+    the softmax scale chosen so that the largest logits stay near 10): outputs and lse against the
+    oracle, which works on the exact bf16 values."""
+    n, K = 3000, 512
+    rng = np.random.default_rng(91 + R)
+    x = _cache(91, n)
+    oc, os_ = oracle.quantize(x)
+    q = rng.standard_normal((R, Hq, 512)).astype(np.float32)
+    e = np.array([exps[h % len(exps)] for h in range(Hq)], np.float64)
+    q = bf16_round((q * np.exp2(e)[None, :, None]).astype(np.float32))
+    idx = np.stack([rng.permutation(n)[:K] for _ in range(R)]).astype(np.int32)
+    starts = np.zeros(R, np.int64)
+    # one softmax scale per call: the heads' logits differ by their magnitude, which is the point
+    scale = float(2.0 ** -(max(exps) + 4))
+    out, lse = attention(dev_bf16(q), dev(oc), dev(os_), dev(starts), dev(idx), scale)
+    ro, rl = oracle.attention_rows(q, oc, os_, starts, idx, np.full(R, n, np.int64), scale)
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    check_attention(out, lse, ro, rl, "bf16 query magnitudes R=%d exps=%s" % (R, exps))
+
+
 def test_attention_split_merge_shares_one_workspace():
     """Split launches hand their partials to merge workgroups through counters at the start of the
     workspace: one zero-filled workspace serves calls of several shapes in a row (the merge inside the
