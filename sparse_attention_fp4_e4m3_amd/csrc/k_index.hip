@@ -633,8 +633,8 @@ __device__ __forceinline__ uint32_t fin_gather(const Series& S, int r, bool full
 // Two more digits give the exact K-th largest key T; the ordered compaction
 // then writes positions ascending, taking ties at T in candidate order
 // (= ascending position), and pads with -1.
-template <int NT>
-__device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r, uint32_t* hist, uint32_t* hist2,
+template <int NT, int series>
+__device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* hist, uint32_t* hist2,
                                              uint32_t* pre,
                              uint32_t* red, uint32_t* lkey, int32_t* lpos) {
   constexpr int NW = NT / 64;
@@ -768,7 +768,9 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
     bool last_block_kept = false;
     for (uint32_t c0 = w0; c0 < cend; c0 += 64) {
       const uint32_t c = c0 + lane;
-      const uint32_t key = c < cend ? keys[c] : 0x80000000u;
+      const bool in = c < cend;
+      const uint32_t key = in ? keys[c] : 0x80000000u;
+      const int32_t pos = posr[in ? c : w0];  // (read with the key: one wait for both)
       const bool e = is_eq(key);
       const unsigned long long me = __ballot(e);
       const uint32_t rank =
@@ -778,8 +780,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
       const uint32_t at =
           out + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
       if (sel && at < nsel) {
-        const int32_t pos = posr[c];
-        if (series == 0) {
+        if constexpr (series == 0) {
           a.out_idx[(int64_t)r * S.K + at] = pos;
         } else {
           int32_t* o = a.out_pool + (int64_t)r * a.pool_size + (int64_t)at * kBlock;
@@ -792,7 +793,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int series, int r
       ties += (uint32_t)__popcll(me);
     }
     // ---- padding and pool length
-    if (series == 0) {
+    if constexpr (series == 0) {
       int32_t* o = a.out_idx + (int64_t)r * S.K;
       for (int i = (int)nsel + threadIdx.x; i < S.K; i += NT) o[i] = -1;
     } else {
@@ -938,7 +939,9 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
   int32_t* lpos = reinterpret_cast<int32_t*>(lkey + kFinCap);
   if ((int)blockIdx.y >= a.nseries) return;
   if (a.row_mask && !a.row_mask[blockIdx.x]) return;
-  finalize_row<kFinThreads>(a, blockIdx.y, blockIdx.x, hist, hist2, pre, red, lkey, lpos);
+  // one instantiation per series (entries, blocks), so neither carries the other's branches
+  if (blockIdx.y == 0) finalize_row<kFinThreads, 0>(a, blockIdx.x, hist, hist2, pre, red, lkey, lpos);
+  else finalize_row<kFinThreads, 1>(a, blockIdx.x, hist, hist2, pre, red, lkey, lpos);
 }
 
 // ------------------------------------------------------------ prefill: approximate MFMA passes
