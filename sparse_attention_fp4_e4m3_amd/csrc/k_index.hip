@@ -88,14 +88,16 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
   return x;
 }
 
-// Exclusive prefix sum over the block; *total = the block sum.  lds >= NT/64 words.
-template <int NT>
+// Exclusive prefix sum over the block; *total = the block sum.  lds >= NT/64 words.  LDS_ONLY: the
+// barriers wait for LDS operations only, so global loads in flight stay in flight.
+template <int NT, bool LDS_ONLY = false>
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* lds, uint32_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_sum(v);
   if (lane == 63) lds[wave] = x;
-  __syncthreads();
+  if (LDS_ONLY) lds_barrier();
+  else __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -103,7 +105,8 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* lds, ui
     before += (w < wave) ? t : 0u;
     tot += t;
   }
-  __syncthreads();
+  if (LDS_ONLY) lds_barrier();
+  else __syncthreads();
   *total = tot;
   return before + x - v;
 }
@@ -668,6 +671,8 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
     by_slice = spw <= kSpec;
     s_lo = min(nsub, wave * spw);
     s_hi = min(nsub, s_lo + spw);
+    // the slice counts first: the prefix sums wait for them alone, the candidate loads stay in flight
+    const uint32_t c_first = ((int)threadIdx.x < nsub) ? S.counts[(int64_t)r * S.nsub + threadIdx.x] : 0u;
     if (by_slice) {
 #pragma unroll
       for (int j = 0; j < kSpec; ++j) {
@@ -677,7 +682,6 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
         pr[j] = sp[at];
       }
     }
-    const uint32_t c_first = ((int)threadIdx.x < nsub) ? S.counts[(int64_t)r * S.nsub + threadIdx.x] : 0u;
     b0 = (int)S.thr[2 * r];
     above0 = S.thr[2 * r + 1];
     uint32_t carry = 0;
@@ -685,7 +689,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
       const int s = s0 + threadIdx.x;
       const uint32_t c = s0 == 0 ? c_first : ((s < nsub) ? S.counts[(int64_t)r * S.nsub + s] : 0u);
       uint32_t tot;
-      const uint32_t ex = block_excl_sum<NT>(c, red, &tot);
+      const uint32_t ex = block_excl_sum<NT, true>(c, red, &tot);
       if (s < nsub) pre[s] = carry + ex;
       carry += tot;
     }
