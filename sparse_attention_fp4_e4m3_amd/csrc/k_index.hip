@@ -684,18 +684,24 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
     }
     b0 = (int)S.thr[2 * r];
     above0 = S.thr[2 * r + 1];
+    // pre[1027] (past the largest slice count's prefix) flags a slice of more than 64 candidates
+    if (threadIdx.x == 0) pre[1027] = 0u;
     uint32_t carry = 0;
     for (int s0 = 0; s0 < nsub; s0 += NT) {
       const int s = s0 + threadIdx.x;
       const uint32_t c = s0 == 0 ? c_first : ((s < nsub) ? S.counts[(int64_t)r * S.nsub + s] : 0u);
       uint32_t tot;
-      const uint32_t ex = block_excl_sum<NT, true>(c, red, &tot);
+      const uint32_t ex = block_excl_sum<NT, true>(c, red, &tot);  // (its barriers order the flag's reset)
       if (s < nsub) pre[s] = carry + ex;
+      if (c > 64u) pre[1027] = 1u;
       carry += tot;
     }
     if (threadIdx.x == 0) pre[nsub] = carry;
     lds_barrier();
     M = pre[nsub];
+    // candidates clustered in position (a slice of more than 64) leave the early loads short:
+    // the row is then split evenly over the waves instead
+    by_slice = by_slice && pre[1027] == 0u;
   } else {
     // the row is split by its pool capacity when that fits, so the candidate
     // loads need not wait for the pool length (slots past it are masked);
@@ -711,7 +717,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
   // instantiated once for candidates in LDS and once for candidates in global memory: a pointer that
   // could be either would turn every access into a flat one, whose waits also cover the global stores
   // in flight.
-  auto phases = [&](const uint32_t* keys, const int32_t* posr, const uint32_t cend) {
+  auto phases = [&](const uint32_t* keys, const int32_t* posr, const uint32_t cend, auto in_lds) {
     // ---- exact threshold: digits 2 and 3 among the candidates of the first digit's bin
     uint32_t need = 0;
     uint32_t prefix = 0;
@@ -774,7 +780,10 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
       const uint32_t c = c0 + lane;
       const bool in = c < cend;
       const uint32_t key = in ? keys[c] : 0x80000000u;
-      const int32_t pos = posr[in ? c : w0];  // (read with the key: one wait for both)
+      // in LDS the position is read with the key (one wait for both); in global memory only for the
+      // selected candidates
+      int32_t pos = 0;
+      if constexpr (decltype(in_lds)::value) pos = posr[in ? c : w0];
       const bool e = is_eq(key);
       const unsigned long long me = __ballot(e);
       const uint32_t rank =
@@ -784,6 +793,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
       const uint32_t at =
           out + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
       if (sel && at < nsel) {
+        if constexpr (!decltype(in_lds)::value) pos = posr[c];
         if constexpr (series == 0) {
           a.out_idx[(int64_t)r * S.K + at] = pos;
         } else {
@@ -826,14 +836,10 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
           lkey[base + lane] = kr[j];
           lpos[base + lane] = pr[j];
         }
-        for (uint32_t c = 64u + lane; c < cs; c += 64u) {  // slices of more than 64 candidates
-          lkey[base + c] = sk[(int64_t)sl * kSub + c];
-          lpos[base + c] = sp[(int64_t)sl * kSub + c];
-        }
       }
     }
     w0 = pre[s_lo];
-    phases(lkey, lpos, pre[s_hi]);
+    phases(lkey, lpos, pre[s_hi], std::true_type{});
   } else {
     const int nchmax = (int)(per_w / 64u);  // uniform
     const uint32_t nv = full ? M : (uint32_t)n;  // Reindex: the valid slots
@@ -843,7 +849,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
     else if (nchmax <= 8) sw = fin_gather<NT, 8>(S, r, full, nsub, pre, sk, sp, w0, w1, nv, b0, above0, red, lkey, lpos);
     else sw = fin_gather<NT, 16>(S, r, full, nsub, pre, sk, sp, w0, w1, nv, b0, above0, red, lkey, lpos);
     // (each wave reads back only its own run; LDS operations of a wave execute in order)
-    phases(lkey, lpos, w0 + sw);
+    phases(lkey, lpos, w0 + sw, std::true_type{});
   }
   } else {
     const uint32_t* gk;
@@ -874,7 +880,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
       gk = sk;
       gp = sp;
     }
-    phases(gk, gp, w1);
+    phases(gk, gp, w1, std::false_type{});
   }
 }
 
