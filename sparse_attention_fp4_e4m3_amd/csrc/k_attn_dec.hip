@@ -81,8 +81,9 @@ struct DecArgs {
                             // gather the same entries, when rows come in multiples of 8; else 1)
   _Float16* ws_o;           // [pairs][S][wave][piece 4][lane][8] normalized partials in accumulator order
   float* ws_ml;             // [pairs][32 heads][S][2] (max in log2 units, sum)
-  uint64_t* counters;       // [pairs][2]: attention arrivals, merge parts done (zero between calls); null:
-                            // the merge runs as a launch of its own
+  uint64_t* counters;       // [pairs][cstride]: attention arrivals, merge parts done in the first two words
+                            // (zero between calls); null: the merge runs as a launch of its own
+  int cstride;              // words between pairs' counters: one 128-byte line per pair when they fit
   int nattn;                // attention workgroups (pairs x S); higher blockIdx.x are merge workgroups
 };
 
@@ -211,7 +212,7 @@ __device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
     uint64_t c = 0;
     int it = 0;
     for (; it < kSpinMax; ++it) {
-      c = __hip_atomic_load(&a.counters[2 * pair], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      c = __hip_atomic_load(&a.counters[a.cstride * pair], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if ((int)(c & 255u) >= S) break;
       __builtin_amdgcn_s_sleep(2);
     }
@@ -287,11 +288,11 @@ __device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
   }
   // every merge workgroup of the pair has seen all S arrivals once the last one gets here
   if (tid == 0) {
-    const uint64_t d = __hip_atomic_fetch_add(&a.counters[2 * pair + 1], uint64_t(1), __ATOMIC_RELAXED,
+    const uint64_t d = __hip_atomic_fetch_add(&a.counters[a.cstride * pair + 1], uint64_t(1), __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
     if (d == kMergeParts - 1) {
-      __hip_atomic_store(&a.counters[2 * pair], uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.counters[2 * pair + 1], uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.counters[a.cstride * pair], uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.counters[a.cstride * pair + 1], uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0)
-    __hip_atomic_fetch_add(&a.counters[2 * pair], uint64_t(1) | (uint64_t(1) << (8 + 4 * xcc_id())),
+    __hip_atomic_fetch_add(&a.counters[a.cstride * pair], uint64_t(1) | (uint64_t(1) << (8 + 4 * xcc_id())),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -745,6 +746,9 @@ hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, c
     char* b = static_cast<char*>(ws);
     if (p.xcd) {
       a.counters = reinterpret_cast<uint64_t*>(b);
+      // each pair's counters on a line of their own when the pairs allow it (the arrivals and polls of
+      // different pairs then do not queue on one line), else packed down to 16 bytes
+      a.cstride = std::max(2, std::min(16, (int)(kAttnCounterBytes / 8) / p.pairs));
       nmerge = kMergeParts * p.pairs;
     }
     a.ws_o = reinterpret_cast<_Float16*>(b + kAttnCounterBytes);
