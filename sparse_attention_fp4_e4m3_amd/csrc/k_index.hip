@@ -48,6 +48,7 @@ constexpr int kD1 = 4096, kD2 = 2048, kD3 = 256;
 constexpr int kS1 = 19, kS2 = 8;
 constexpr int kScanSlots = 768;  // resident scan workgroups on 256 CUs (3 each)
 constexpr int kMaxHeads = 32;
+constexpr int kQPrepared = -1;  // query "dtype" of a Reindex scan reading the prepared fp32 block
 
 // One wave scores 64 keys at a time (one key per lane).  The keys' rows are
 // loaded with fully coalesced 16-byte pieces, staged in the wave's own LDS
@@ -332,8 +333,9 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
   // prepared block, already in that order; Reindex: the caller's [head][64] queries, bf16 widened): every
   // lane reads a quad's H x 4 values as same-address (broadcast) LDS loads, which the compiler issues
   // ahead of their use.  Full over bf16 / fp32 keys, whose key rows already come from LDS, keeps scalar
-  // loads of the prepared block (measured: LDS queries there halve its rate).
-  constexpr bool kLdsQ = REINDEX || T::kMx;
+  // loads of the prepared block (measured: LDS queries there halve its rate), and so does Reindex over
+  // such keys when a prepared block exists (QDT = kQPrepared: the prefill rescoring).
+  constexpr bool kLdsQ = (REINDEX && QDT != kQPrepared) || T::kMx;
   for (int i = threadIdx.x; kLdsQ && i < H * kIdxDim; i += kThreads) {
     float v;
     if constexpr (REINDEX) {
@@ -1605,7 +1607,11 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
     if (record && ev.start) (void)hipEventRecord(ev.start, s);
     const bool qbf = q_dtype == CSA2_BF16;
-    if (k_dtype == CSA2_MXFP4) {
+    // the prefill rescoring (Reindex over the candidate lists) reads the block k_prep laid out
+    const bool prepared = !full && shared && prep_done;
+    if (prepared && k_dtype == CSA2_BF16) dispatch_heads<CSA2_BF16, true, false, kQPrepared>(H, sa, L.qf, grid, s);
+    else if (prepared && k_dtype == CSA2_F32) dispatch_heads<CSA2_F32, true, false, kQPrepared>(H, sa, L.qf, grid, s);
+    else if (k_dtype == CSA2_MXFP4) {
       if (!full && qbf) dispatch_heads<CSA2_MXFP4, true, false, CSA2_BF16>(H, sa, idx_q, grid, s);
       else if (!full) dispatch_heads<CSA2_MXFP4, true, false, CSA2_F32>(H, sa, idx_q, grid, s);
       else if (pool_on) dispatch_heads<CSA2_MXFP4, false, true, CSA2_F32>(H, sa, L.qf, grid, s);
