@@ -301,11 +301,14 @@ __device__ __forceinline__ void flush_packed(uint32_t* __restrict__ g, const uin
 // caller's queries as they are (qsrc: [row][head][64] of dtype QDT), so it needs
 // no preparation kernel, and builds no histogram (its selection counts the
 // pool's scores itself).
+// One workgroup scores the slots [tile0 * 256, (tile0 + ntl) * 256) of row r (clipped to the row):
+// wave w takes the 64-key tiles w, w + 4, ...  Returns early (the whole workgroup) when the range
+// holds no slot.
 template <int KDT, int HC, bool REINDEX, bool POOL, int QDT>
-__global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* __restrict__ qsrc) {
+__device__ __forceinline__ void score_rows(const ScoreArgs& a, const void* __restrict__ qsrc, uint8_t* smem, int r,
+                                           int64_t tile0, int ntl) {
   using T = KeyTile<KDT>;
   constexpr int NACC = HC > 0 ? HC : kMaxHeads;
-  extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint8_t* tile = smem + wv * T::kWaveBytes;                                       // this wave's rows
   uint32_t* h1 = reinterpret_cast<uint32_t*>(smem + kWavesPerWG * T::kWaveBytes);  // kD1/2 packed
@@ -314,15 +317,14 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
   float* sq = reinterpret_cast<float*>(REINDEX ? h1 : hb + (POOL ? kD1 / 2 : 0));
 
   const int H = HC > 0 ? HC : a.H;
-  const int r = blockIdx.y, trange = blockIdx.x;
   if (a.row_mask && !a.row_mask[r]) return;
   const int vis = clampv(a.row_visible[r], a.max_visible);
   int plen = 0;
   if (REINDEX) plen = a.pool_len ? clampv(a.pool_len[r], a.pool_stride) : a.pool_stride;
   const int n = REINDEX ? plen : vis;  // slots scored: Reindex, the pool's valid length
-  const int64_t base0 = (int64_t)trange * a.tiles_per_wg * kWGKeys;
+  const int64_t base0 = tile0 * kWGKeys;
   if (base0 >= n) return;
-  const int ntiles = (int)std::min<int64_t>(a.tiles_per_wg, ceil_div(n - base0, kWGKeys));
+  const int ntiles = (int)std::min<int64_t>(ntl, ceil_div(n - base0, kWGKeys));
   if (!REINDEX) {
     for (int b = threadIdx.x; b < kD1 / 2; b += kThreads) {
       h1[b] = 0u;
@@ -518,6 +520,43 @@ __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* 
   __syncthreads();
   flush_packed(a.hist_s + (int64_t)r * kD1, h1);
   if (POOL) flush_packed(a.hist_b + (int64_t)r * kD1, hb);
+}
+
+template <int KDT, int HC, bool REINDEX, bool POOL, int QDT>
+__global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* __restrict__ qsrc) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  score_rows<KDT, HC, REINDEX, POOL, QDT>(a, qsrc, smem, (int)blockIdx.y, (int64_t)blockIdx.x * a.tiles_per_wg,
+                                           a.tiles_per_wg);
+}
+
+// Full over rows of different lengths: the grid's workgroups share the batch's 256-entry tiles
+// evenly (about 1/gridDim.x of them each, in row order), so short rows leave no workgroup idle.
+// Each workgroup takes the row lengths (at most 256 rows, one per thread), their tile prefix sums,
+// and scores its range row segment by row segment, flushing each row's histograms.
+template <int KDT, int HC, bool POOL>
+__global__ __launch_bounds__(kThreads, 3) void k_scan_even(ScoreArgs a, const void* __restrict__ qsrc, int R) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ uint32_t xs[8];
+  const int i = threadIdx.x;
+  const uint32_t tl = i < R ? (uint32_t)ceil_div(clampv(a.row_visible[i], a.max_visible), kWGKeys) : 0u;
+  uint32_t total;
+  const uint32_t ex = block_excl_sum<kThreads>(tl, xs, &total);
+  uint32_t cur = (uint32_t)((uint64_t)total * blockIdx.x / gridDim.x);
+  const uint32_t end = (uint32_t)((uint64_t)total * (blockIdx.x + 1) / gridDim.x);
+  while (cur < end) {
+    if (tl > 0u && ex <= cur && cur < ex + tl) {  // the row holding tile `cur`
+      xs[4] = (uint32_t)i;
+      xs[5] = ex;
+      xs[6] = ex + tl;
+    }
+    __syncthreads();
+    const int r = (int)xs[4];
+    const uint32_t lo = xs[5], seg = min(end, xs[6]);
+    __syncthreads();
+    score_rows<KDT, HC, false, POOL, CSA2_F32>(a, qsrc, smem, r, (int64_t)(cur - lo), (int)(seg - cur));
+    __syncthreads();  // (the histogram flush has read the LDS counters before the next segment zeroes them)
+    cur = seg;
+  }
 }
 
 struct Series {
@@ -1527,11 +1566,25 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
   return L;
 }
 
+// even_rows > 0: the Full scan with the batch's tiles shared evenly (k_scan_even over that many rows)
 template <int KDT, int HC, bool REINDEX, bool POOL, int QDT>
-void launch_score(const ScoreArgs& sa, const void* qsrc, dim3 grid, hipStream_t s) {
+void launch_score(const ScoreArgs& sa, const void* qsrc, dim3 grid, hipStream_t s, int even_rows) {
   using T = KeyTile<KDT>;
   const size_t lds = (size_t)kWavesPerWG * T::kWaveBytes + (REINDEX ? 0 : (size_t)kD1 / 2 * 4 * (POOL ? 2 : 1)) +
                      ((REINDEX || T::kMx) ? (size_t)(HC > 0 ? HC : kMaxHeads) * kIdxDim * 4 : 0);
+  if constexpr (!REINDEX && QDT == CSA2_F32) {
+    if (even_rows > 0) {
+      auto kern = k_scan_even<KDT, HC, POOL>;
+      static bool configured = false;
+      if (!configured) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+        configured = true;
+      }
+      hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, sa, qsrc, even_rows);
+      return;
+    }
+  }
   auto kern = k_score<KDT, HC, REINDEX, POOL, QDT>;
   static bool configured = false;
   if (!configured) {
@@ -1543,10 +1596,10 @@ void launch_score(const ScoreArgs& sa, const void* qsrc, dim3 grid, hipStream_t 
 }
 
 template <int KDT, bool REINDEX, bool POOL, int QDT>
-void dispatch_heads(int H, const ScoreArgs& sa, const void* qsrc, dim3 grid, hipStream_t s) {
-  if (H == 8) launch_score<KDT, 8, REINDEX, POOL, QDT>(sa, qsrc, grid, s);
-  else if (H == 4) launch_score<KDT, 4, REINDEX, POOL, QDT>(sa, qsrc, grid, s);
-  else launch_score<KDT, 0, REINDEX, POOL, QDT>(sa, qsrc, grid, s);
+void dispatch_heads(int H, const ScoreArgs& sa, const void* qsrc, dim3 grid, hipStream_t s, int even_rows = 0) {
+  if (H == 8) launch_score<KDT, 8, REINDEX, POOL, QDT>(sa, qsrc, grid, s, even_rows);
+  else if (H == 4) launch_score<KDT, 4, REINDEX, POOL, QDT>(sa, qsrc, grid, s, even_rows);
+  else launch_score<KDT, 0, REINDEX, POOL, QDT>(sa, qsrc, grid, s, even_rows);
 }
 
 }  // namespace
@@ -1603,7 +1656,11 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     const int64_t tiles = ceil_div(n, (int64_t)kWGKeys);
     sa.tiles_per_wg =
         (int)std::min<int64_t>(255, ceil_div(tiles, std::max<int64_t>(1, ceil_div((int64_t)kScanSlots, R))));
-    const dim3 grid((unsigned)ceil_div(tiles, (int64_t)sa.tiles_per_wg), (unsigned)R);
+    dim3 grid((unsigned)ceil_div(tiles, (int64_t)sa.tiles_per_wg), (unsigned)R);
+    // Full decode batches of up to 256 rows: the tiles shared evenly over the grid (rows of different
+    // lengths leave no workgroup idle); at most 255 tiles per workgroup (its packed histogram counters)
+    const int even = (full && !shared && !row_mask && R <= kThreads) ? R : 0;
+    if (even) grid = dim3((unsigned)std::max<int64_t>(kScanSlots, ceil_div((int64_t)R * tiles, 255)), 1u);
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
     if (record && ev.start) (void)hipEventRecord(ev.start, s);
     const bool qbf = q_dtype == CSA2_BF16;
@@ -1614,18 +1671,18 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     else if (k_dtype == CSA2_MXFP4) {
       if (!full && qbf) dispatch_heads<CSA2_MXFP4, true, false, CSA2_BF16>(H, sa, idx_q, grid, s);
       else if (!full) dispatch_heads<CSA2_MXFP4, true, false, CSA2_F32>(H, sa, idx_q, grid, s);
-      else if (pool_on) dispatch_heads<CSA2_MXFP4, false, true, CSA2_F32>(H, sa, L.qf, grid, s);
-      else dispatch_heads<CSA2_MXFP4, false, false, CSA2_F32>(H, sa, L.qf, grid, s);
+      else if (pool_on) dispatch_heads<CSA2_MXFP4, false, true, CSA2_F32>(H, sa, L.qf, grid, s, even);
+      else dispatch_heads<CSA2_MXFP4, false, false, CSA2_F32>(H, sa, L.qf, grid, s, even);
     } else if (k_dtype == CSA2_BF16) {
       if (!full && qbf) dispatch_heads<CSA2_BF16, true, false, CSA2_BF16>(H, sa, idx_q, grid, s);
       else if (!full) dispatch_heads<CSA2_BF16, true, false, CSA2_F32>(H, sa, idx_q, grid, s);
-      else if (pool_on) dispatch_heads<CSA2_BF16, false, true, CSA2_F32>(H, sa, L.qf, grid, s);
-      else dispatch_heads<CSA2_BF16, false, false, CSA2_F32>(H, sa, L.qf, grid, s);
+      else if (pool_on) dispatch_heads<CSA2_BF16, false, true, CSA2_F32>(H, sa, L.qf, grid, s, even);
+      else dispatch_heads<CSA2_BF16, false, false, CSA2_F32>(H, sa, L.qf, grid, s, even);
     } else {
       if (!full && qbf) dispatch_heads<CSA2_F32, true, false, CSA2_BF16>(H, sa, idx_q, grid, s);
       else if (!full) dispatch_heads<CSA2_F32, true, false, CSA2_F32>(H, sa, idx_q, grid, s);
-      else if (pool_on) dispatch_heads<CSA2_F32, false, true, CSA2_F32>(H, sa, L.qf, grid, s);
-      else dispatch_heads<CSA2_F32, false, false, CSA2_F32>(H, sa, L.qf, grid, s);
+      else if (pool_on) dispatch_heads<CSA2_F32, false, true, CSA2_F32>(H, sa, L.qf, grid, s, even);
+      else dispatch_heads<CSA2_F32, false, false, CSA2_F32>(H, sa, L.qf, grid, s, even);
     }
     if (record && ev.stop) (void)hipEventRecord(ev.stop, s);
   }
