@@ -714,7 +714,9 @@ def main():
                 "unit": "TFLOP/s", "frac": dk["TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
                 "traffic": traffic_from_profiles(wname, "k_index.hip")}
     else:
-        roof = {"kernel": "k_scan_full" if dominant == "index_scan" else "k_score_pool", "bound": "hbm",
+        # the Full scan: k_scan_even (decode batches of up to 256 rows share the tiles evenly), else k_score
+        scan_name = "k_scan_even" if w.rows <= 256 else "k_score (Full)"
+        roof = {"kernel": scan_name if dominant == "index_scan" else "k_score (Reindex)", "bound": "hbm",
                 "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["hbm_frac"],
                 "traffic": traffic_from_profiles(wname, "k_index.hip")}
 
