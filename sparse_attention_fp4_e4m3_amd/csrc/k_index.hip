@@ -48,6 +48,7 @@ constexpr int kD1 = 4096, kD2 = 2048, kD3 = 256;
 constexpr int kS1 = 19, kS2 = 8;
 constexpr int kScanSlots = 768;  // resident scan workgroups on 256 CUs (3 each)
 constexpr int kMaxHeads = 32;
+constexpr int kListRows = 64;  // grid rows of a pass over a device-side row list
 constexpr int kQPrepared = -1;  // query "dtype" of a Reindex scan reading the prepared fp32 block
 
 // One wave scores 64 keys at a time (one key per lane).  The keys' rows are
@@ -268,7 +269,8 @@ struct ScoreArgs {
   uint32_t* hist_s;           // [R][kD1]
   uint32_t* hist_b;           // [R][kD1]
   int tiles_per_wg;
-  const uint32_t* row_mask;   // [R] nonzero = score this row; null = every row
+  const uint32_t* row_list;   // non-null: grid row i scores rows row_list[i], row_list[i + gridDim.y], ...
+  const uint32_t* row_count;  //   (of *row_count listed rows)
   int shared_start;           // every row reads the segment at row_start[0]
 };
 
@@ -317,7 +319,6 @@ __device__ __forceinline__ void score_rows(const ScoreArgs& a, const void* __res
   float* sq = reinterpret_cast<float*>(REINDEX ? h1 : hb + (POOL ? kD1 / 2 : 0));
 
   const int H = HC > 0 ? HC : a.H;
-  if (a.row_mask && !a.row_mask[r]) return;
   const int vis = clampv(a.row_visible[r], a.max_visible);
   int plen = 0;
   if (REINDEX) plen = a.pool_len ? clampv(a.pool_len[r], a.pool_stride) : a.pool_stride;
@@ -525,8 +526,12 @@ __device__ __forceinline__ void score_rows(const ScoreArgs& a, const void* __res
 template <int KDT, int HC, bool REINDEX, bool POOL, int QDT>
 __global__ __launch_bounds__(kThreads, 3) void k_score(ScoreArgs a, const void* __restrict__ qsrc) {
   extern __shared__ __align__(16) uint8_t smem[];
-  score_rows<KDT, HC, REINDEX, POOL, QDT>(a, qsrc, smem, (int)blockIdx.y, (int64_t)blockIdx.x * a.tiles_per_wg,
-                                           a.tiles_per_wg);
+  int r = (int)blockIdx.y;
+  if (a.row_list) {  // grid row i scores the i-th listed row, if there is one
+    if (blockIdx.y >= *a.row_count) return;
+    r = (int)a.row_list[blockIdx.y];
+  }
+  score_rows<KDT, HC, REINDEX, POOL, QDT>(a, qsrc, smem, r, (int64_t)blockIdx.x * a.tiles_per_wg, a.tiles_per_wg);
 }
 
 // Full over rows of different lengths: the grid's workgroups share the batch's 256-entry tiles
@@ -584,7 +589,8 @@ struct SelArgs {
   int32_t* out_pool_len; // [R]
   int pool_size;
   const int32_t* pool_len;   // Reindex: valid slots per row (null = pool_stride)
-  const uint32_t* row_mask;  // [R] nonzero = select for this row; null = every row
+  const uint32_t* row_list;  // non-null: grid row i selects for rows row_list[i], row_list[i + grid rows], ...
+  const uint32_t* row_count; //   (of *row_count listed rows)
   int by_len;                // Reindex: split each row by its valid slots, not its capacity
 };
 
@@ -928,11 +934,7 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
 // Full mode: each wave compacts its slice of kSub elements, keeping those
 // whose first digit is at least the threshold bin (all valid ones when the
 // row holds fewer than K).
-__global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
-  __shared__ uint32_t red[32];
-  const int series = blockIdx.z, r = blockIdx.y;
-  if (series >= a.nseries) return;
-  if (a.row_mask && !a.row_mask[r]) return;
+__device__ __forceinline__ void collect_row(const SelArgs& a, int series, int r, uint32_t* red) {
   const Series& S = a.s[series];
   const int n = series_len(a, series, r);
   const int64_t wg_base = (int64_t)blockIdx.x * 4 * kSub;
@@ -978,6 +980,24 @@ __global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
   if (lane == 0) S.counts[(int64_t)r * S.nsub + sub] = cnt;
 }
 
+// LIST: the rows of a device-side list (a grid of at most kListRows rows, looping over the list),
+// else grid row r collects for row r
+template <bool LIST>
+__global__ __launch_bounds__(kThreads) void k_collect(SelArgs a) {
+  __shared__ uint32_t red[32];
+  const int series = blockIdx.z;
+  if (series >= a.nseries) return;
+  if constexpr (!LIST) {
+    collect_row(a, series, (int)blockIdx.y, red);
+  } else {
+    const uint32_t nl = *a.row_count;
+    for (uint32_t li = blockIdx.y; li < nl; li += gridDim.y) {
+      collect_row(a, series, (int)a.row_list[li], red);
+      __syncthreads();  // (red reused by the next listed row)
+    }
+  }
+}
+
 constexpr size_t kFinLdsWords = kFinThreads + kD2 + 1028 + 32 + 2 * (size_t)kFinCap;
 
 __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
@@ -989,10 +1009,17 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(SelArgs a) {
   uint32_t* lkey = red + 32;                  // kFinCap
   int32_t* lpos = reinterpret_cast<int32_t*>(lkey + kFinCap);
   if ((int)blockIdx.y >= a.nseries) return;
-  if (a.row_mask && !a.row_mask[blockIdx.x]) return;
   // one instantiation per series (entries, blocks), so neither carries the other's branches
-  if (blockIdx.y == 0) finalize_row<kFinThreads, 0>(a, blockIdx.x, hist, hist2, pre, red, lkey, lpos);
-  else finalize_row<kFinThreads, 1>(a, blockIdx.x, hist, hist2, pre, red, lkey, lpos);
+  auto one = [&](int r) {
+    if (blockIdx.y == 0) finalize_row<kFinThreads, 0>(a, r, hist, hist2, pre, red, lkey, lpos);
+    else finalize_row<kFinThreads, 1>(a, r, hist, hist2, pre, red, lkey, lpos);
+  };
+  int r = (int)blockIdx.x;
+  if (a.row_list) {  // workgroup i selects for the i-th listed row, if there is one
+    if (blockIdx.x >= *a.row_count) return;
+    r = (int)a.row_list[blockIdx.x];
+  }
+  one(r);
 }
 
 // ------------------------------------------------------------ prefill: approximate MFMA passes
@@ -1054,7 +1081,8 @@ struct PfArgs {
   int nwords;
   int32_t* cand;              // [R][kPfCap] candidate positions, ascending
   int32_t* ccnt;              // [R] candidates (0 on overflow)
-  uint32_t* over;             // [R] 1 = overflow: exact fallback
+  uint32_t* over_list;        // [R] the rows whose candidates overflow (exact fallback), in no particular order
+  uint32_t* nover;            // their count (zeroed by the call's first kernels)
   uint32_t* hist2;            // [R][kD1] the failed rows' histograms (zeroed by k_pf_certify)
   uint32_t* xhist;            // [R][kD1] the exact path's first-digit histograms (zeroed for overflow rows)
 };
@@ -1467,7 +1495,7 @@ __global__ __launch_bounds__(256) void k_pf_compact(PfArgs a) {
   const bool overflow = total > (uint32_t)kPfCap;
   if (threadIdx.x == 0) {
     a.ccnt[r] = overflow ? 0 : (int32_t)total;
-    a.over[r] = overflow ? 1u : 0u;
+    if (overflow) a.over_list[atomicAdd(a.nover, 1u)] = (uint32_t)r;
   }
   if (overflow) {  // this row takes the exact full scan, whose first-digit histogram starts at zero
     u32x4* h = reinterpret_cast<u32x4*>(a.xhist + (int64_t)r * kD1);
@@ -1512,7 +1540,8 @@ struct Layout {
   int nwords;
   int32_t* cand;
   int32_t* ccnt;
-  uint32_t* over;
+  uint32_t* over_list;
+  uint32_t* nover;
   float* cscore;   // [R][kPfCap] exact scores of the candidates
   size_t bytes;
 };
@@ -1559,7 +1588,8 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
     L.bits = c.take<uint32_t>((size_t)R * L.nwords);
     L.cand = c.take<int32_t>((size_t)R * kPfCap);
     L.ccnt = c.take<int32_t>((size_t)R);
-    L.over = c.take<uint32_t>((size_t)R);
+    L.over_list = c.take<uint32_t>((size_t)R);
+    L.nover = c.take<uint32_t>(1);
     L.cscore = c.take<float>((size_t)R * kPfCap);
   }
   L.bytes = c.off;
@@ -1613,14 +1643,19 @@ int topk_max_visible() { return 1024 * kSub; }
 namespace {
 
 // the exact path: scan (Full: every visible entry; Reindex: the pool), then
-// the exact selection; row_mask restricts it to flagged rows
+// the exact selection; a row list restricts it to the listed rows
 void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H, const void* idx_k,
                const uint8_t* idx_ks, int k_dtype,
                const int64_t* row_start, const int32_t* row_visible, int max_visible, const int32_t* pool,
                const int32_t* pool_len, int pool_stride, int top_k, int32_t* out_idx, int pool_size,
-               int32_t* out_pool, int32_t* out_pool_len, const uint32_t* row_mask, float* scores,
-               int64_t score_stride, bool prep_done, bool record, const void* idx_q, hipStream_t s) {
+               int32_t* out_pool, int32_t* out_pool_len, float* scores,
+               int64_t score_stride, bool prep_done, bool record, const void* idx_q, hipStream_t s,
+               const uint32_t* row_list = nullptr, const uint32_t* row_count = nullptr) {
   const bool full = mode == CSA2_FULL;
+  // a row list (rows known only on the device, usually none): the scan and the selection keep a grid
+  // row per possible row (workgroups past the list's length exit at once); the collection, whose grid is
+  // widest, takes at most kListRows grid rows that loop over the list
+  const int Rg = row_list ? std::min(R, kListRows) : R;
   const bool pool_on = full && pool_size > 0;
   if (!prep_done && full) {  // (Reindex reads the queries as given and counts in its selection)
     const int64_t nq = (int64_t)R * H * kIdxDim;
@@ -1648,7 +1683,8 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     // rescoring (Reindex over candidate lists) leaves the first one to its Full fallback
     sa.hist_s = full ? L.hist : L.hist + (size_t)R * kD1;
     sa.hist_b = L.hist + (size_t)R * kD1;
-    sa.row_mask = row_mask;
+    sa.row_list = row_list;
+    sa.row_count = row_count;
     sa.shared_start = shared ? 1 : 0;
     // Full: about three workgroups per CU over the whole batch (each scans
     // tiles_per_wg x 256 consecutive entries); Reindex: 256 pool slots each
@@ -1659,7 +1695,7 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
     dim3 grid((unsigned)ceil_div(tiles, (int64_t)sa.tiles_per_wg), (unsigned)R);
     // Full decode batches of up to 256 rows: the tiles shared evenly over the grid (rows of different
     // lengths leave no workgroup idle); at most 255 tiles per workgroup (its packed histogram counters)
-    const int even = (full && !shared && !row_mask && R <= kThreads) ? R : 0;
+    const int even = (full && !shared && !row_list && R <= kThreads) ? R : 0;
     if (even) grid = dim3((unsigned)std::max<int64_t>(kScanSlots, ceil_div((int64_t)R * tiles, 255)), 1u);
     auto& ev = profile_events(full ? CSA2_KERNEL_INDEX_SCAN : CSA2_KERNEL_REINDEX_SCORE);
     if (record && ev.start) (void)hipEventRecord(ev.start, s);
@@ -1695,7 +1731,8 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
   a.pool = pool;
   a.pool_len = pool_len;
   a.by_len = shared ? 1 : 0;  // the prefill candidate lists are mostly empty
-  a.row_mask = row_mask;
+  a.row_list = row_list;
+  a.row_count = row_count;
   a.out_idx = out_idx;
   a.out_pool = out_pool;
   a.out_pool_len = out_pool_len;
@@ -1709,7 +1746,12 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
                     pool_size / kBlock};
   if (full) {
     const int gx = (int)ceil_div(std::max(L.nsub, pool_on ? L.nbsub : 1), 4);
-    hipLaunchKernelGGL(k_collect, dim3((unsigned)gx, (unsigned)R, (unsigned)a.nseries), dim3(kThreads), 0, s, a);
+    if (row_list)
+      hipLaunchKernelGGL(k_collect<true>, dim3((unsigned)gx, (unsigned)Rg, (unsigned)a.nseries), dim3(kThreads), 0, s,
+                         a);
+    else
+      hipLaunchKernelGGL(k_collect<false>, dim3((unsigned)gx, (unsigned)R, (unsigned)a.nseries), dim3(kThreads), 0, s,
+                         a);
   }
   const size_t lds = kFinLdsWords * 4;
   static bool configured = false;
@@ -1761,7 +1803,7 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   Layout L = layout(ws, mode, R, H, max_visible, pool_stride, pool_size);
   if (!topk_uses_prefill_path(mode, q_dtype, k_dtype, H, pool_size)) {
     run_exact(L, emode, shared, R, q_dtype, H, idx_k, idx_ks, k_dtype, row_start, row_visible, max_visible, pool, pool_len,
-              pool_stride, top_k, out_idx, pool_size, out_pool, out_pool_len, nullptr, L.scores, L.n_pad, false, true,
+              pool_stride, top_k, out_idx, pool_size, out_pool, out_pool_len, L.scores, L.n_pad, false, true,
               idx_q, s);
     return hipGetLastError();
   }
@@ -1789,7 +1831,8 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   p.nwords = L.nwords;
   p.cand = L.cand;
   p.ccnt = L.ccnt;
-  p.over = L.over;
+  p.over_list = L.over_list;
+  p.nover = L.nover;
   p.hist2 = L.phist2;
   p.xhist = L.hist;
   {
@@ -1803,7 +1846,7 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
                        0, s, L.phist, (int64_t)R * kD1, L.nhi, (int64_t)R, L.nhi, (int64_t)0, L.kmax);
     hipLaunchKernelGGL(k_zero, dim3((unsigned)ceil_div((int64_t)R, 256)), dim3(256), 0, s,
                        reinterpret_cast<uint32_t*>(L.qn), (int64_t)R, L.failed, (int64_t)0, L.failed, (int64_t)0,
-                       nullptr);
+                       L.nover);
   }
   const int64_t nn = std::max<int64_t>((int64_t)max_visible * (k_dtype == CSA2_MXFP4 ? 1 : 8), (int64_t)R * H);
   hipLaunchKernelGGL(k_pf_norms, dim3((unsigned)std::min<int64_t>(1024, ceil_div(nn, 256))), dim3(256), 0, s, p, H);
@@ -1845,10 +1888,11 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   hipLaunchKernelGGL(k_pf_compact, dim3((unsigned)R), dim3(256), 0, s, p);
   // exact scores of the candidates and the exact selection among them (Reindex over the candidate lists)
   run_exact(L, CSA2_REINDEX, true, R, q_dtype, H, idx_k, idx_ks, k_dtype, row_start, row_visible, max_visible, L.cand,
-            L.ccnt, kPfCap, top_k, out_idx, 0, nullptr, nullptr, nullptr, L.cscore, kPfCap, true, true, idx_q, s);
+            L.ccnt, kPfCap, top_k, out_idx, 0, nullptr, nullptr, L.cscore, kPfCap, true, true, idx_q, s);
   // rows whose candidates overflowed: the exact full scan and selection, for those rows only
   run_exact(L, CSA2_FULL, true, R, q_dtype, H, idx_k, idx_ks, k_dtype, row_start, row_visible, max_visible, nullptr,
-            nullptr, 0, top_k, out_idx, 0, nullptr, nullptr, L.over, L.scores, L.n_pad, true, false, idx_q, s);
+            nullptr, 0, top_k, out_idx, 0, nullptr, nullptr, L.scores, L.n_pad, true, false, idx_q, s,
+            L.over_list, L.nover);
   return hipGetLastError();
 }
 
