@@ -1109,6 +1109,15 @@ struct PfArgs {
 // max(x, +0) as one integer max: negative floats (sign bit set, -0 included) compare below 0
 __device__ __forceinline__ float relu0(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// v + (bit `lane` of the wave mask m): one add with the mask as its carry-in, where a compare, a
+// select and an add would otherwise build and add a 0/1 value
+__device__ __forceinline__ uint32_t add_lane_bit(uint32_t v, unsigned long long m) {
+  uint32_t r;
+  unsigned long long co;
+  asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(co) : "v"(v), "s"(m));
+  return r;
+}
+
 // norms: one thread per key of the shared segment, then one per (row, head) query
 // Key norms (MXFP4: one thread per key; bf16: eight lanes per key, 16 coalesced bytes each, summed
 // across the eight lanes; the order of the sum does not matter for the bound: 64 terms of rounding
@@ -1221,7 +1230,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
   constexpr int TG = H / 4;             // M tiles per group of four rows
   constexpr int NG = kPfRows / 4;       // row groups
   extern __shared__ __align__(16) uint32_t pl[];  // MODE 0: kPfRows x kD1/2 packed counters
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index as a uniform value, so that the step positions derived from it are too
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n16 = lane & 15, g = lane >> 4;
   const int r0 = blockIdx.x * kPfRows;
   const int64_t seg = a.row_start[0];
@@ -1261,6 +1271,11 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
     }
   }
   // this lane's output row in row group rg: 4rg + g; key lane n16 of each 16-key tile
+  // the smallest visible end of the workgroup's rows: steps wholly below it need no per-key bound test
+  int vmin = klim;
+#pragma unroll
+  for (int i = 0; i < kPfRows; ++i)
+    if (r0 + i < a.R) vmin = min(vmin, clampv(a.row_visible[r0 + i], a.max_visible));
   int vis[NG], rowo[NG];
   uint32_t* wrow[NG];  // MODE 1: this row's bitmap (stored by lane n16 == 0), null past the last row
   float lo[NG], cq[NG], hi[NG];
@@ -1333,20 +1348,22 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
       }
     }
   };
-  // the products of one step: every (row group, key tile, head tile) accumulator
-  // first, so the epilogue reads results issued well before it
+  // the products of one row group in one step: its (key tile, head tile) accumulators
+  auto products_rg = [&](int rg, const Step& st, floatx4 (&acc)[2][TG]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        floatx4 c = floatx4{0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rg][t][0], __builtin_bit_cast(bf16x8, st.b[tt][0]), c, 0, 0, 0);
+        acc[tt][t] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rg][t][1], __builtin_bit_cast(bf16x8, st.b[tt][1]), c, 0, 0, 0);
+      }
+  };
+  // every accumulator of a step first, so the epilogue reads results issued well before it
   auto products = [&](const Step& st, floatx4 (&acc)[NG][2][TG]) {
 #pragma unroll
-    for (int rg = 0; rg < NG; ++rg)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int t = 0; t < TG; ++t) {
-          floatx4 c = floatx4{0.f, 0.f, 0.f, 0.f};
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rg][t][0], __builtin_bit_cast(bf16x8, st.b[tt][0]), c, 0, 0, 0);
-          acc[rg][tt][t] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rg][t][1], __builtin_bit_cast(bf16x8, st.b[tt][1]), c, 0, 0, 0);
-        }
+    for (int rg = 0; rg < NG; ++rg) products_rg(rg, st, acc[rg]);
   };
   // approximate score of (row 4rg + g, key lane of a tile): ReLU per head, summed over the row's heads
   auto score = [&](const floatx4 (&acc)[TG]) {
@@ -1368,30 +1385,55 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
   auto body = [&](int p, Step& cur, Step& ahead) {
     load_step(min(p + 8, nsteps - 1), ahead);  // clamped: always in bounds
     const int j0 = kbeg + 32 * p * sample;
-    floatx4 acc[NG][2][TG];
     widen(cur);
-    products(cur, acc);
+    if (MODE == 0) {
+      floatx4 acc[NG][2][TG];
+      products(cur, acc);
 #pragma unroll
-    for (int rg = 0; rg < NG; ++rg) {
-      if (MODE == 0) {
+      for (int rg = 0; rg < NG; ++rg)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const float sc = score(acc[rg][tt]);
           if (j0 + 16 * tt + n16 < vis[rg]) hist_add(pl + (rowo[rg] - r0) * (kD1 / 2), __float_as_uint(sc) >> kS1);
         }
-      } else {
-        unsigned long long m[2];
+    } else {
+      // ballots built straight from the compares (the int-predicate __ballot would turn each compare
+      // into a 0/1 value and compare that again); the per-key bound test only in steps that reach a
+      // row's visible end (a uniform branch: j0 and vmin are wave-uniform)
+      // Row group rg's products are issued beside the epilogue of row group rg - 1 (independent
+      // work for the matrix and vector units of one wave), and the bitmap words are stored at the
+      // end of the step, so the step is one block the scheduler can interleave.
+      auto marks = [&](auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        floatx4 acc[NG][2][TG];
+        uint32_t word[NG];
+        auto epilogue = [&](int rg) {
+          unsigned long long m[2];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const float sc = score(acc[rg][tt]);
-          const bool ok = j0 + 16 * tt + n16 < vis[rg];
-          m[tt] = __ballot(ok && __builtin_fmaf(cq[rg], cur.kn[tt], sc) >= lo[rg]);
-          nh[rg] += (ok && sc >= hi[rg]) ? 1u : 0u;
+          for (int tt = 0; tt < 2; ++tt) {
+            const float sc = score(acc[rg][tt]);
+            const bool ok = FULL || j0 + 16 * tt + n16 < vis[rg];
+            m[tt] = __builtin_amdgcn_ballot_w64(ok && __builtin_fmaf(cq[rg], cur.kn[tt], sc) >= lo[rg]);
+            nh[rg] = add_lane_bit(nh[rg], __builtin_amdgcn_ballot_w64(ok && sc >= hi[rg]));
+          }
+          // bitmap word of row g: its 16 keys of each tile (lanes 16g .. 16g+15)
+          word[rg] = ((uint32_t)(m[0] >> (16 * g)) & 0xFFFFu) | ((uint32_t)(m[1] >> (16 * g)) << 16);
+        };
+        products_rg(0, cur, acc[0]);
+#pragma unroll
+        for (int rg = 1; rg < NG; ++rg) {
+          products_rg(rg, cur, acc[rg]);
+          epilogue(rg - 1);
         }
-        // bitmap word of row g: its 16 keys of each tile (lanes 16g .. 16g+15)
-        const uint32_t word = ((uint32_t)(m[0] >> (16 * g)) & 0xFFFFu) | ((uint32_t)(m[1] >> (16 * g)) << 16);
-        if (n16 == 0 && wrow[rg]) wrow[rg][j0 / 32] = word;
-      }
+        epilogue(NG - 1);
+        if (n16 == 0) {
+#pragma unroll
+          for (int rg = 0; rg < NG; ++rg)
+            if (wrow[rg]) wrow[rg][j0 / 32] = word[rg];
+        }
+      };
+      if (j0 + 32 <= vmin) marks(std::true_type{});
+      else marks(std::false_type{});
     }
   };
   // whole rounds of three steps (no conditional step in the loop body, so the
