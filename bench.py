@@ -486,6 +486,69 @@ class HipEvent:
 
 # ------------------------------------------------------------------ main
 
+def attn_row_sweep(rows_list, steps, warmup):
+    """The decode attention call alone at the 128K chain's shape (64 bf16 query heads of 512, top-2048
+    over 131,072 cached FP4 entries per row, each row its own segment) for several row counts: one JSON
+    line with microseconds per launch (a HIP graph of `steps` back-to-back launches, warm caches) and the
+    launch's algorithmic bytes and flops against the HBM and fp16 MFMA peaks.  Cache bytes are random
+    codes and finite scales: only the timing is of interest here."""
+    import torch
+
+    from sparse_attention_fp4_e4m3_amd import csa2
+
+    device = torch.device("cuda:0")
+    ctx, Hq, K = 131072, 64, 2048
+    per_row = K * 288 + K * 4 + Hq * 512 * 2 + Hq * 512 * 4
+    out = []
+    rmax = max(rows_list)
+    gen_t = torch.Generator(device=device)
+    gen_t.manual_seed(7)
+    codes = torch.randint(0, 256, (rmax * ctx, 256), dtype=torch.uint8, device=device, generator=gen_t)
+    scales = torch.randint(0x28, 0x50, (rmax * ctx, 32), dtype=torch.uint8, device=device, generator=gen_t)
+    for R in rows_list:
+        q = (torch.randn(R, Hq, 512, device=device, generator=gen_t)).to(torch.bfloat16)
+        idx = torch.stack([torch.randperm(ctx, device=device, generator=gen_t)[:K] for _ in range(R)]).to(torch.int32)
+        idx, _ = torch.sort(idx, dim=1)
+        starts = torch.arange(R, dtype=torch.int64, device=device) * ctx
+        vis = torch.full((R,), ctx, dtype=torch.int32, device=device)
+        o = torch.empty(R, Hq, 512, dtype=torch.float32, device=device)
+        ws = torch.zeros(max(256, csa2.sparse_attn_workspace_size(R, Hq, csa2.BF16, K)), dtype=torch.uint8,
+                         device=device)
+
+        def call():
+            csa2.sparse_attn(q, codes, scales, starts, idx, o, 1.0 / 512 ** 0.5, row_visible=vis, workspace=ws)
+
+        for _ in range(max(1, warmup)):
+            call()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(steps):
+                    call()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(5):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / steps)
+        nbytes, flops = R * per_row, 4.0 * R * Hq * K * 512
+        out.append({"rows": R, "us_per_launch": best, "bytes": nbytes, "GBps": nbytes / best * 1e-3,
+                    "hbm_frac": nbytes / best * 1e-3 / 8000.0, "TFLOPs": flops / best * 1e-6,
+                    "mfma_frac": flops / best * 1e-6 / 2500.0})
+        log("attention alone, %d rows: %.2f us per launch, %.3f of HBM" % (R, best, out[-1]["hbm_frac"]))
+        del q, idx, o, ws, g
+    print(json.dumps({"attn_rows_sweep": out, "shape": {"ctx_per_row": ctx, "q_heads": Hq, "top_k": K,
+                                                         "q_dtype": "bf16", "kv": "fp4 e2m1 + e4m3 per 16"},
+                      "timing": "hip graph of %d back-to-back launches, best of 5 replays, warm caches" % steps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -504,11 +567,17 @@ def main():
                     help="per-kernel timing events: created without a system fence, or torch's default")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--attn-rows", default="",
+                    help="comma-separated row counts: time the decode attention call alone at the 128K chain's "
+                         "shape for each (one JSON line), instead of a workload step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU per process and box; --gpus %d is not supported "
               "(multi-GPU sharding is a design note only)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.attn_rows:
+        attn_row_sweep([int(x) for x in args.attn_rows.split(",")], max(1, min(args.steps, 50)), args.warmup)
+        return
 
     import torch
 
