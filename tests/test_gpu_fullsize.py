@@ -115,7 +115,7 @@ def _chain_fullsize(name, sample, swa=False, mxfp4=False, select_all=False):
 
 
 def test_decode_full_32x_32k_64k():
-    _chain_fullsize("c2", sample=[0, 17, 31])
+    _chain_fullsize("c2", sample=[0, 17, 31], select_all=True)
 
 
 def test_chain_128k_batch16():
@@ -131,7 +131,7 @@ def test_chain_128k_batch16_mxfp4_indexer_keys():
 
 
 def test_chain_128k_verification_5_draft_rows():
-    _chain_fullsize("c3v", sample=[3])
+    _chain_fullsize("c3v", sample=[3], select_all=True)
 
 
 def test_long_decode_1m_batch4():
