@@ -592,6 +592,13 @@ struct SelArgs {
   const uint32_t* row_list;  // non-null: grid row i selects for rows row_list[i], row_list[i + grid rows], ...
   const uint32_t* row_count; //   (of *row_count listed rows)
   int by_len;                // Reindex: split each row by its valid slots, not its capacity
+  // the prefill rescoring's certification (null: none): a row whose exact selection does not prove the
+  // sampled bound cert_thi[r] is appended to cert_list (count *cert_count) with its first-digit histogram
+  // cert_xhist[r] zeroed, for the exact fallback that follows
+  const float* cert_thi;
+  uint32_t* cert_list;
+  uint32_t* cert_count;
+  uint32_t* cert_xhist;
 };
 
 __device__ __forceinline__ int series_len(const SelArgs& a, int series, int r) {
@@ -669,6 +676,29 @@ __device__ __forceinline__ uint32_t fin_gather(const Series& S, int r, bool full
     cnt += (uint32_t)__popcll(m);
   }
   return cnt;
+}
+
+// The prefill rescoring's certification of the sampled bound thi, taken on the exact scores: if at
+// least K candidates have an exact score of at least thi, the K-th largest exact score over all
+// entries is at least thi, so every entry of the exact top-K (ties included) has A + eps >= thi - eps_max
+// and is a candidate.  That holds when the K-th largest exact candidate score T reaches thi (scores are
+// non-negative, so their bits order like the values), or, with fewer than K candidates, when every
+// visible entry is one.  A row that fails joins the exact fallback's list, its first-digit histogram
+// zeroed here (before that scan); rows whose candidates overflowed (count -1) are on the list already.
+template <int NT>
+__device__ __forceinline__ void certify_row(const SelArgs& a, int r, int n, int vis, bool all, uint32_t T,
+                                            uint32_t* flag) {
+  if (threadIdx.x == 0) {
+    bool ok = true;
+    if (a.pool_len[r] >= 0 && vis > 0) ok = all ? n >= vis : T >= __float_as_uint(a.cert_thi[r]);
+    if (!ok) a.cert_list[atomicAdd(a.cert_count, 1u)] = (uint32_t)r;
+    *flag = ok ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*flag == 0u) {
+    u32x4* h = reinterpret_cast<u32x4*>(a.cert_xhist + (int64_t)r * kD1);
+    for (int i = threadIdx.x; i < kD1 / 4; i += NT) h[i] = u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
 // Exact selection for one (row, series) by one workgroup of NT threads.
@@ -794,6 +824,8 @@ __device__ __forceinline__ void finalize_row(const SelArgs& a, int r, uint32_t* 
       need = K;  // ties at T to take, in candidate order
     }
     const uint32_t T = prefix;  // the full 31-bit key of the K-th largest
+    // (the prefill rescoring: pre[] is unused by Reindex rows, its word 1026 carries the verdict)
+    if (a.cert_thi) certify_row<NT>(a, r, n, vis, all, T, pre + 1026);
 
     // ---- ordered compaction over each wave's run, 64 candidates at a time
     auto is_gt = [&](uint32_t key) { return !(key >> 31) && (all || key > T); };
@@ -1055,13 +1087,15 @@ __global__ __launch_bounds__(kFinSmallThreads) __attribute__((amdgpu_waves_per_e
 // any fp32 summation order with round-to-nearest or truncation.  By
 // Cauchy-Schwarz sum_c |q_c k_c| <= |q_h| |k|, so
 //   |A - E| <= eps_j = c |k_j| sum_h |q_h|,   c = 2 (gamma_64 + gamma_7 (1 + gamma_64)),
-// taken here with further safety factors.  If t_A is the K-th largest A,
-// at least K entries have E >= t_A - eps_max, so every entry of the exact
-// top-K (ties included) has A_j + eps_j >= t_A - eps_max >= lo(b) - eps_max,
-// where lo(b) is the lower edge of the histogram bin holding t_A.  Those
-// candidates are then rescored exactly and selected exactly, so the result is
-// the exact top-K.  A row whose candidates overflow the list falls back to
-// the exact full scan.
+// taken here with further safety factors.  The bound lo(b), the lower edge
+// of the histogram bin that holds a sampled order statistic of A, marks as
+// candidates the entries with A_j + eps_j >= lo(b) - eps_max; they are
+// rescored exactly and selected exactly.  The bound is proven afterwards, on
+// the exact scores: if at least K candidates have E >= lo(b), every entry of
+// the exact top-K (ties included) has E_j >= lo(b), so A_j + eps_j >= lo(b)
+// and it is a candidate: the result is the exact top-K.  A row that fails that
+// test, or whose candidates overflow the list, falls back to the exact full
+// scan.
 
 // query rows per workgroup of the approximate passes: each key a wave loads feeds
 // every row of its workgroup (16 rows for up to 8 heads; 8 keep 16 heads in registers)
@@ -1088,35 +1122,23 @@ struct PfArgs {
   float* knorm;               // [max_visible] |k_j| bound
   uint32_t* kmax;             // [1] max |k_j| (float bits)
   float* qn;                  // [R] sum_h |q_h| bound
-  uint32_t* hist;             // [R][kD1] first-digit histograms of A (of a sample, or of every entry)
-  float* plo;                 // [R] candidate bound lo(b) - eps_max (-inf: every valid entry)
-  float* thi;                 // [R] sampled bound lo(b) that the candidate pass certifies
-  uint32_t* nhi;              // [R] entries with A >= thi (certification count)
-  uint32_t* failed;           // [R] 1 = the sampled bound was not certified: full histogram pass
-  const uint32_t* mask;       // [R] rows to process (null = all)
+  uint32_t* hist;             // [R][kD1] first-digit histograms of A over a sample of the keys
+  float* plo;                 // [R] candidate bound lo(b) - eps_max (+inf: no candidates, the exact fallback)
+  float* thi;                 // [R] sampled bound lo(b) that the exact selection certifies
   int sample;                 // MODE 0: every sample-th 32-key step
   uint32_t target;            // entries the threshold bin must cover (K, or more for a sample)
   uint32_t* bits;             // [R][nwords] candidate bitmap
   int nwords;
   int32_t* cand;              // [R][kPfCap] candidate positions, ascending
-  int32_t* ccnt;              // [R] candidates (0 on overflow)
-  uint32_t* over_list;        // [R] the rows whose candidates overflow (exact fallback), in no particular order
+  int32_t* ccnt;              // [R] candidates (-1 on overflow)
+  uint32_t* over_list;        // [R] the rows for the exact fallback (candidates overflow, or the bound is not
+                              // certified), in no particular order
   uint32_t* nover;            // their count (zeroed by the call's first kernels)
-  uint32_t* hist2;            // [R][kD1] the failed rows' histograms (zeroed by k_pf_certify)
-  uint32_t* xhist;            // [R][kD1] the exact path's first-digit histograms (zeroed for overflow rows)
+  uint32_t* xhist;            // [R][kD1] the exact path's first-digit histograms (zeroed for listed rows)
 };
 
 // max(x, +0) as one integer max: negative floats (sign bit set, -0 included) compare below 0
 __device__ __forceinline__ float relu0(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-// v + (bit `lane` of the wave mask m): one add with the mask as its carry-in, where a compare, a
-// select and an add would otherwise build and add a 0/1 value
-__device__ __forceinline__ uint32_t add_lane_bit(uint32_t v, unsigned long long m) {
-  uint32_t r;
-  unsigned long long co;
-  asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(co) : "v"(v), "s"(m));
-  return r;
-}
 
 // norms: one thread per key of the shared segment, then one per (row, head) query
 // Key norms (MXFP4: one thread per key; bf16: eight lanes per key, 16 coalesced bytes each, summed
@@ -1243,12 +1265,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
   const int kbeg = MODE == 0 ? 0 : (int)blockIdx.y * kPfRange;
   const int klim = MODE == 0 ? kend : min(kend, kbeg + kPfRange);
   if (kbeg >= klim) return;
-  if (a.mask) {
-    bool any = false;
-#pragma unroll
-    for (int i = 0; i < kPfRows; ++i) any |= (r0 + i < a.R) && a.mask[r0 + i] != 0u;
-    if (!any) return;
-  }
 
   if (MODE == 0) {
     for (int i = threadIdx.x; i < kPfRows * kD1 / 2; i += 256) pl[i] = 0u;
@@ -1278,8 +1294,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
     if (r0 + i < a.R) vmin = min(vmin, clampv(a.row_visible[r0 + i], a.max_visible));
   int vis[NG], rowo[NG];
   uint32_t* wrow[NG];  // MODE 1: this row's bitmap (stored by lane n16 == 0), null past the last row
-  float lo[NG], cq[NG], hi[NG];
-  uint32_t nh[NG];
+  float lo[NG], cq[NG];
 #pragma unroll
   for (int rg = 0; rg < NG; ++rg) {
     const int row = r0 + 4 * rg + g;
@@ -1288,11 +1303,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
     vis[rg] = row < a.R ? min(clampv(a.row_visible[row], a.max_visible), klim) : 0;
     lo[rg] = 0.0f;
     cq[rg] = 0.0f;
-    hi[rg] = INFINITY;
-    nh[rg] = 0u;
     if (MODE == 1 && row < a.R) {
       lo[rg] = a.plo[row];
-      hi[rg] = a.thi[row];
       cq[rg] = a.qn[row] * pf_err(H);
     }
   }
@@ -1414,7 +1426,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
             const float sc = score(acc[rg][tt]);
             const bool ok = FULL || j0 + 16 * tt + n16 < vis[rg];
             m[tt] = __builtin_amdgcn_ballot_w64(ok && __builtin_fmaf(cq[rg], cur.kn[tt], sc) >= lo[rg]);
-            nh[rg] = add_lane_bit(nh[rg], __builtin_amdgcn_ballot_w64(ok && sc >= hi[rg]));
           }
           // bitmap word of row g: its 16 keys of each tile (lanes 16g .. 16g+15)
           word[rg] = ((uint32_t)(m[0] >> (16 * g)) & 0xFFFFu) | ((uint32_t)(m[1] >> (16 * g)) << 16);
@@ -1446,18 +1457,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
   }
   if (p0 < nsteps) body(p0, sA, sC);
   if (p0 + 4 < nsteps) body(p0 + 4, sB, sA);
-  if (MODE == 1) {
-    // counts of the entries reaching thi: sum over the 16 lanes of each row
-#pragma unroll
-    for (int rg = 0; rg < NG; ++rg) {
-      uint32_t c = nh[rg];
-      c += __shfl_xor(c, 1, 64);
-      c += __shfl_xor(c, 2, 64);
-      c += __shfl_xor(c, 4, 64);
-      c += __shfl_xor(c, 8, 64);
-      if (n16 == 0 && rowo[rg] < a.R && c) atomicAdd(a.nhi + rowo[rg], c);
-    }
-  }
   if (MODE == 0) {
     __syncthreads();
     for (int i = threadIdx.x; i < kPfRows * (kD1 / 2); i += 256) {
@@ -1472,41 +1471,24 @@ __global__ __launch_bounds__(256, 2) void k_pf_pass(PfArgs a) {
   }
 }
 
-// per row: the bin holding the target-th largest approximate score -> candidate bound.
-// From a sample (sampled = 1) the bound is provisional: the candidate pass
-// counts the entries with A >= thi and k_pf_certify checks that at least K
-// do; a row whose sample is too small is left failed at once.
-__global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a, int H, int sampled) {
+// per row: the bin holding the target-th largest sampled approximate score -> candidate bound.  A row
+// whose sample is too small to place it gets no candidates (+inf): its exact selection then fails the
+// certification and it takes the exact fallback.
+__global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a, int H) {
   __shared__ uint32_t red[32];
   const int r = blockIdx.x;
-  if (a.mask && !a.mask[r]) return;
   uint32_t above, total;
   const int b = find_bin<256, kD1>(a.hist + (int64_t)r * kD1, a.target, &above, &total, red);
   if (threadIdx.x == 0) {
     if (b < 0) {
-      // sample: too few entries to place the bound -> no candidates now, certification fails;
-      // every entry: fewer than K valid entries, all of them are candidates
-      a.plo[r] = sampled ? INFINITY : -INFINITY;
-      a.thi[r] = sampled ? INFINITY : -INFINITY;
+      a.plo[r] = INFINITY;
+      a.thi[r] = INFINITY;
     } else {
       const float edge = __uint_as_float((uint32_t)b << kS1);
       const float emax = a.qn[r] * pf_err(H) * __uint_as_float(*a.kmax);
       a.plo[r] = (edge - emax) - 1e-6f * edge;  // nudged down: rounding of the subtraction
       a.thi[r] = edge;
     }
-  }
-}
-
-// per row: the provisional bound holds if at least K entries reach it; a row that fails gets its
-// second approximate histogram zeroed here, before the pass that fills it
-__global__ __launch_bounds__(256) void k_pf_certify(PfArgs a) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= a.R) return;
-  const bool fail = a.nhi[r] < (uint32_t)a.K;
-  a.failed[r] = fail ? 1u : 0u;
-  if (fail) {
-    u32x4* h = reinterpret_cast<u32x4*>(a.hist2 + (int64_t)r * kD1);
-    for (int i = 0; i < kD1 / 4; ++i) h[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -1555,7 +1537,7 @@ __global__ __launch_bounds__(256) void k_pf_compact(PfArgs a) {
   }
   const bool overflow = total > (uint32_t)kPfCap;
   if (threadIdx.x == 0) {
-    a.ccnt[r] = overflow ? 0 : (int32_t)total;
+    a.ccnt[r] = overflow ? -1 : (int32_t)total;
     if (overflow) a.over_list[atomicAdd(a.nover, 1u)] = (uint32_t)r;
   }
   if (overflow) {  // this row takes the exact full scan, whose first-digit histogram starts at zero
@@ -1594,9 +1576,6 @@ struct Layout {
   uint32_t* phist;
   float* plo;
   float* thi;
-  uint32_t* nhi;
-  uint32_t* failed;
-  uint32_t* phist2;
   uint32_t* bits;
   int nwords;
   int32_t* cand;
@@ -1643,9 +1622,6 @@ Layout layout(void* base, int mode, int R, int H, int max_visible, int pool_stri
     L.phist = c.take<uint32_t>((size_t)R * kD1);
     L.plo = c.take<float>((size_t)R);
     L.thi = c.take<float>((size_t)R);
-    L.nhi = c.take<uint32_t>((size_t)R);
-    L.failed = c.take<uint32_t>((size_t)R);
-    L.phist2 = c.take<uint32_t>((size_t)R * kD1);
     L.bits = c.take<uint32_t>((size_t)R * L.nwords);
     L.cand = c.take<int32_t>((size_t)R * kPfCap);
     L.ccnt = c.take<int32_t>((size_t)R);
@@ -1705,13 +1681,22 @@ namespace {
 
 // the exact path: scan (Full: every visible entry; Reindex: the pool), then
 // the exact selection; a row list restricts it to the listed rows
+// the prefill rescoring's certification: bounds, the fallback list and its count, the exact histograms
+struct Cert {
+  const float* thi;
+  uint32_t* list;
+  uint32_t* count;
+  uint32_t* xhist;
+};
+
 void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H, const void* idx_k,
                const uint8_t* idx_ks, int k_dtype,
                const int64_t* row_start, const int32_t* row_visible, int max_visible, const int32_t* pool,
                const int32_t* pool_len, int pool_stride, int top_k, int32_t* out_idx, int pool_size,
                int32_t* out_pool, int32_t* out_pool_len, float* scores,
                int64_t score_stride, bool prep_done, bool record, const void* idx_q, hipStream_t s,
-               const uint32_t* row_list = nullptr, const uint32_t* row_count = nullptr) {
+               const uint32_t* row_list = nullptr, const uint32_t* row_count = nullptr,
+               const Cert* cert = nullptr) {
   const bool full = mode == CSA2_FULL;
   // a row list (rows known only on the device, usually none): the scan and the selection keep a grid
   // row per possible row (workgroups past the list's length exit at once); the collection, whose grid is
@@ -1792,6 +1777,12 @@ void run_exact(const Layout& L, int mode, bool shared, int R, int q_dtype, int H
   a.pool = pool;
   a.pool_len = pool_len;
   a.by_len = shared ? 1 : 0;  // the prefill candidate lists are mostly empty
+  if (cert) {
+    a.cert_thi = cert->thi;
+    a.cert_list = cert->list;
+    a.cert_count = cert->count;
+    a.cert_xhist = cert->xhist;
+  }
   a.row_list = row_list;
   a.row_count = row_count;
   a.out_idx = out_idx;
@@ -1895,8 +1886,6 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   p.hist = L.phist;
   p.plo = L.plo;
   p.thi = L.thi;
-  p.nhi = L.nhi;
-  p.failed = L.failed;
   p.sample = 1;
   p.target = (uint32_t)top_k;
   p.bits = L.bits;
@@ -1905,19 +1894,18 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   p.ccnt = L.ccnt;
   p.over_list = L.over_list;
   p.nover = L.nover;
-  p.hist2 = L.phist2;
   p.xhist = L.hist;
   {
-    // the queries for the exact path (fallback rows); the approximate histogram, the certification
-    // counts and the key-norm maximum zeroed; the exact path's histograms of rows that overflow are
-    // zeroed by k_pf_compact, the second approximate histogram of rows that fail by k_pf_certify
+    // the queries for the exact path (fallback rows); the approximate histogram, the key-norm maximum,
+    // the query norms and the fallback list's count zeroed; the exact path's histograms of listed rows
+    // are zeroed by the kernel that lists them (k_pf_compact, the rescoring's selection)
     const int64_t nq = (int64_t)R * H * kIdxDim;
     hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<int64_t>(2048, ceil_div(nq, 256))), dim3(256), 0, s, idx_q,
                        q_dtype, R, H, L.qf, L.hist, (int64_t)0);
     hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>(2048, ceil_div((int64_t)R * kD1, 256))), dim3(256),
-                       0, s, L.phist, (int64_t)R * kD1, L.nhi, (int64_t)R, L.nhi, (int64_t)0, L.kmax);
+                       0, s, L.phist, (int64_t)R * kD1, L.phist, (int64_t)0, L.phist, (int64_t)0, L.kmax);
     hipLaunchKernelGGL(k_zero, dim3((unsigned)ceil_div((int64_t)R, 256)), dim3(256), 0, s,
-                       reinterpret_cast<uint32_t*>(L.qn), (int64_t)R, L.failed, (int64_t)0, L.failed, (int64_t)0,
+                       reinterpret_cast<uint32_t*>(L.qn), (int64_t)R, L.nover, (int64_t)0, L.nover, (int64_t)0,
                        L.nover);
   }
   const int64_t nn = std::max<int64_t>((int64_t)max_visible * (k_dtype == CSA2_MXFP4 ? 1 : 8), (int64_t)R * H);
@@ -1939,29 +1927,21 @@ hipError_t launch_index_topk(int mode, int R, const void* idx_q, int q_dtype, in
   PfArgs ps = p;
   ps.hist = L.phist;
   ps.sample = kPfSample;
-  ps.mask = nullptr;
   ps.target = (uint32_t)ceil_div((int64_t)top_k * 3, 2 * kPfSample);
   pass(0, ps);
-  hipLaunchKernelGGL(k_pf_thresh, dim3((unsigned)R), dim3(256), 0, s, ps, H, 1);
-  // 2. the candidate pass over every key, counting the entries that certify the bound
+  hipLaunchKernelGGL(k_pf_thresh, dim3((unsigned)R), dim3(256), 0, s, ps, H);
+  // 2. the candidate pass over every key
   pass(1, ps);
-  hipLaunchKernelGGL(k_pf_certify, dim3((unsigned)ceil_div(R, 256)), dim3(256), 0, s, ps);
-  // 3. rows whose bound failed: the full histogram, the exact bin bound, the candidate pass again
-  //    (every workgroup without such a row returns at once)
-  PfArgs pf = p;
-  pf.hist = L.phist2;
-  pf.sample = 1;
-  pf.mask = L.failed;
-  pf.target = (uint32_t)top_k;
-  pass(0, pf);
-  hipLaunchKernelGGL(k_pf_thresh, dim3((unsigned)R), dim3(256), 0, s, pf, H, 0);
-  pass(1, pf);
   if (ev.stop) (void)hipEventRecord(ev.stop, s);
   hipLaunchKernelGGL(k_pf_compact, dim3((unsigned)R), dim3(256), 0, s, p);
-  // exact scores of the candidates and the exact selection among them (Reindex over the candidate lists)
+  // exact scores of the candidates and the exact selection among them (Reindex over the candidate lists),
+  // which also certifies each row's bound on the exact scores and lists the rows that fail
+  const Cert cert{L.thi, L.over_list, L.nover, L.hist};
   run_exact(L, CSA2_REINDEX, true, R, q_dtype, H, idx_k, idx_ks, k_dtype, row_start, row_visible, max_visible, L.cand,
-            L.ccnt, kPfCap, top_k, out_idx, 0, nullptr, nullptr, L.cscore, kPfCap, true, true, idx_q, s);
-  // rows whose candidates overflowed: the exact full scan and selection, for those rows only
+            L.ccnt, kPfCap, top_k, out_idx, 0, nullptr, nullptr, L.cscore, kPfCap, true, true, idx_q, s, nullptr,
+            nullptr, &cert);
+  // listed rows (candidates overflowed, or the bound not certified): the exact full scan and selection,
+  // for those rows only
   run_exact(L, CSA2_FULL, true, R, q_dtype, H, idx_k, idx_ks, k_dtype, row_start, row_visible, max_visible, nullptr,
             nullptr, 0, top_k, out_idx, 0, nullptr, nullptr, L.scores, L.n_pad, true, false, idx_q, s,
             L.over_list, L.nover);

@@ -101,7 +101,8 @@ def test_shared_all_zero_scores():
 
 def test_shared_unrepresentative_sample():
     """Keys of large norm exactly at the positions the provisional bound samples: the sampled
-    bound is too high, its certification fails, and the rows take the full-histogram pass."""
+    bound is too high, the exact selection among the candidates does not certify it, and the rows
+    take the exact fallback scan."""
     P0, T, K, H = 30000, 40, 512, 8
     rng = np.random.default_rng(6)
     n = P0 + T
