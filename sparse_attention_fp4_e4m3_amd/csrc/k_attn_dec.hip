@@ -584,7 +584,8 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // ---- split partial: the lane's 32 normalized outputs in fp16, in accumulator order: piece p = 2t + j
   // of every lane of the wave is one contiguous KiB (each store instruction writes whole lines)
   const size_t pbase = (size_t)pair * S + split;
-  u32x4* po = reinterpret_cast<u32x4*>(a.ws_o) + (pbase * 8 + w) * 256 + lane;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(a.ws_o, 0, 0x7FFFFFFF, 0x00020000);
+  const uint32_t pofs = (uint32_t)(((pbase * 8 + w) * 256 + lane) * 16);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -596,9 +597,10 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         pk[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[t][i] * inv[i])) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[t][i + 1] * inv[i + 1])) << 16);
       }
-      // streaming stores: the partials are read once, by the merge, and a kernel ending with 8 MB of
-      // them dirty in L2 would first write them back
-      __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]}, po + 64 * (2 * t + j));
+      // device-scope stores (written through to memory, the line kept in this XCD's L2): the merge reads
+      // them back from L2, and the kernel does not end with 8 MB of them dirty in L2
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{pk[0], pk[1], pk[2], pk[3]}, rw,
+                                             (int)(pofs + 1024u * (uint32_t)(2 * t + j)), 0, 16);
     }
   if (w == 0 && lane < 32)
     *reinterpret_cast<float2*>(a.ws_ml + (((size_t)pair * kHG + lane) * S + split) * 2) = make_float2(m_run, l_run);
