@@ -957,6 +957,7 @@ struct SmemWide {
   float red_sum[kWaves][64];
   float alpha[64];
   float lfin[64];
+  int moved;            // 1: some head's reference moved in this step (written before its second barrier)
   uint8_t fresh[kDim];  // the row's newest window token, when the call writes it
 };
 
@@ -1101,6 +1102,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
         if (w == 0) sm.alpha[h] = alpha[ht];
       }
     }
+    if (w == 0) {
+      // whether any head's reference moved this step (wave 0's lanes hold every head)
+      bool mv = false;
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) mv |= alpha[ht] != 1.0f;
+      const bool any = __ballot(mv) != 0ull;
+      if (lane == 0) sm.moved = any ? 1 : 0;
+    }
     lds_barrier();  // B2: probabilities, sums, alpha and staged codes visible
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -1110,24 +1119,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
       for (int ww = 1; ww < kWaves; ++ww) add += sm.red_sum[ww][h];
       lrun[ht] = lrun[ht] * alpha[ht] + add;
     }
-    if (st > 0) {
-      float al[NHT][4];
-      bool moved = false;
+    // the outputs rescaled only in a step where some head's reference moved (one LDS word read)
+    if (st > 0 && sm.moved) {
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          al[ht][i] = sm.alpha[16 * ht + 4 * q4 + i];
-          moved |= al[ht][i] != 1.0f;
+          const float al = sm.alpha[16 * ht + 4 * q4 + i];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) O[ht][t][i] *= al;
         }
-      if (__ballot(moved)) {
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) O[ht][t][i] *= al[ht][i];
-      }
     }
 
     // ---- PV over the step's 128 keys, 32 per K-step: this lane's keys key0 .. key0+7
