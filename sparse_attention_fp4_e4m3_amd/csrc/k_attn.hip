@@ -1088,12 +1088,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
       alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
       mref[ht] = mnew;
       _Float16 pv[4];
-      float sum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
-        sum += (float)pv[i];
-      }
+      for (int i = 0; i < 4; ++i) pv[i] = (_Float16)__builtin_amdgcn_exp2f(S[ht][i] - muse);
+      // the rounded probabilities summed two per instruction in fp32 (v_dot2 with ones)
+      float sum = __builtin_amdgcn_fdot2(half2v{pv[0], pv[1]}, half2v{1.0f16, 1.0f16}, 0.0f, false);
+      sum = __builtin_amdgcn_fdot2(half2v{pv[2], pv[3]}, half2v{1.0f16, 1.0f16}, sum, false);
       *reinterpret_cast<u32x2*>(&sm.p[h * kPStride + 16 * w + 4 * q4]) =
           u32x2{h2_bits(half2v{pv[0], pv[1]}), h2_bits(half2v{pv[2], pv[3]})};
       sum = rows_sum(sum);

@@ -443,11 +443,20 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const uint32_t vm = (uint32_t)__ballot(vcur);  // bit k: key k of this wave (lanes 0..31)
     float z[16];
     float mx = -INFINITY;
+    // the logits, masked per key only when some key of the wave is invalid (a uniform branch)
+    if (vm == 0xFFFFFFFFu) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * h2 + (i & 3);
-      z[i] = ((vm >> key) & 1u) ? St[i] * c2h : -INFINITY;
-      mx = fmaxf(mx, z[i]);
+      for (int i = 0; i < 16; ++i) {
+        z[i] = St[i] * c2h;
+        mx = fmaxf(mx, z[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i >> 2) + 4 * h2 + (i & 3);
+        z[i] = ((vm >> key) & 1u) ? St[i] * c2h : -INFINITY;
+        mx = fmaxf(mx, z[i]);
+      }
     }
     mx = half_max(mx);
     if (lane < 32) sm.red_max[w][lane] = mx;
@@ -465,8 +474,7 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     for (int i = 0; i < 16; i += 2) {
       const _Float16 p0 = (_Float16)__builtin_amdgcn_exp2f(z[i] - m_use);
       const _Float16 p1 = (_Float16)__builtin_amdgcn_exp2f(z[i + 1] - m_use);
-      sum += (float)p0;
-      sum += (float)p1;
+      sum = __builtin_amdgcn_fdot2(half2v{p0, p1}, half2v{1.0f16, 1.0f16}, sum, false);  // p0 + p1 + sum in fp32
       pw[i >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, p0) | ((uint32_t)__builtin_bit_cast(uint16_t, p1) << 16);
     }
 #pragma unroll
