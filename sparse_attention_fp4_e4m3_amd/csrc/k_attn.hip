@@ -965,6 +965,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   SmemWide& sm = *reinterpret_cast<SmemWide*>(smem_raw);
   constexpr int NHT = 4, HG = 64;
+  static_assert(kWaves == 8, "the cross-wave reductions give each of the 4 lane groups two waves");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
@@ -1080,9 +1081,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
-      float mstep = sm.red_max[0][h];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) mstep = fmaxf(mstep, sm.red_max[ww][h]);
+      // lane group q4 takes waves 2q4 and 2q4+1, the four groups then meet across lanes
+      const float mstep = rows_max(fmaxf(sm.red_max[2 * q4][h], sm.red_max[2 * q4 + 1][h]));
       const float mnew = (mstep > mref[ht] + kLazy) ? mstep : mref[ht];
       const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
       alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
@@ -1113,9 +1113,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
-      float add = sm.red_sum[0][h];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) add += sm.red_sum[ww][h];
+      const float add = rows_sum(sm.red_sum[2 * q4][h] + sm.red_sum[2 * q4 + 1][h]);  // same order in every lane
       lrun[ht] = lrun[ht] * alpha[ht] + add;
     }
     // the outputs rescaled only in a step where some head's reference moved (one LDS word read)
@@ -1224,9 +1222,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
-      float mstep = sm.red_max[0][h];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) mstep = fmaxf(mstep, sm.red_max[ww][h]);
+      // lane group q4 takes waves 2q4 and 2q4+1, the four groups then meet across lanes
+      const float mstep = rows_max(fmaxf(sm.red_max[2 * q4][h], sm.red_max[2 * q4 + 1][h]));
       const float mnew = (mstep > mref[ht] + kLazy) ? mstep : mref[ht];
       const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
       alpha[ht] = (mnew == mref[ht]) ? 1.0f : __builtin_amdgcn_exp2f(mref[ht] - muse);
@@ -1250,9 +1247,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_attn_wide(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = 16 * ht + n16;
-      float add = sm.red_sum[0][h];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) add += sm.red_sum[ww][h];
+      const float add = rows_sum(sm.red_sum[2 * q4][h] + sm.red_sum[2 * q4 + 1][h]);  // same order in every lane
       lrun[ht] = lrun[ht] * alpha[ht] + add;
     }
     {
