@@ -752,8 +752,13 @@ def main():
         del kern["reindex_score"]  # a chain without Reindex layers
     if args.swa:
         # the window: 128 entries x 512 B per row; QK^T and PV over them for every head
-        kern["swa_attention"] = {"avg_us": per_kernel_us["swa_attention"], "bytes": w.rows * 128 * 512,
-                                 "flops": 4.0 * w.rows * w.Hq * 128 * 512}
+        win_bytes, win_flops = w.rows * 128 * 512, 4.0 * w.rows * w.Hq * 128 * 512
+        if per_kernel_us["swa_attention"] is None:
+            # the 64-head plan joins the window to the selection as one more step of the attention launch
+            kern["attention"]["bytes"] += win_bytes
+            kern["attention"]["flops"] += win_flops
+        else:
+            kern["swa_attention"] = {"avg_us": per_kernel_us["swa_attention"], "bytes": win_bytes, "flops": win_flops}
         if w.is_prefill:
             kern["quantize_fp8"] = {"avg_us": per_kernel_us["quantize_fp8"], "bytes": w.prefill_tokens * (512 * 4 + 512)}
     for k, v in kern.items():
