@@ -218,13 +218,17 @@ int32_t csa2_index_topk_mxfp4(int32_t mode, int32_t n_rows,
  *
  * q            [n_rows, n_heads, 512] of q_dtype (CSA2_F32 or CSA2_BF16);
  *              16-byte aligned.  The products run in fp16 on the matrix
- *              cores.  bf16 queries: decode launches (bf16, no window,
- *              n_heads a multiple of 32, n_rows * n_heads / 32 <= 256, and
- *              not n_rows * n_heads / 64 >= 256) first scale each head by
+ *              cores.  bf16 queries: decode launches (bf16, n_heads a
+ *              multiple of 32, n_rows * n_heads / 32 <= 256, and not
+ *              n_rows * n_heads / 64 >= 256; with a window, also
+ *              top_k > 256 and n_rows * n_heads / 32 a multiple of 8 below
+ *              256) first scale each head by
  *              the power of two that puts its largest |q| in [2^14, 2^15)
  *              (undone in the logit scale), so every finite value at least
- *              2^-28 of its head's largest is used exactly; other launches
- *              use a bf16 value exactly when 2^-14 <= |q| < 65520 (the fp16
+ *              2^-28 of its head's largest is used exactly over the selected
+ *              entries; other launches, and a window's entries
+ *              (csa2_sparse_attn_swa), use a bf16 value exactly when
+ *              2^-14 <= |q| < 65520 (the fp16
  *              normal range): smaller values lose low bits (below 2^-24 they
  *              count as 0) and larger ones overflow.  fp32 queries are split
  *              into two fp16 halves (about 22 significant bits in the fp16

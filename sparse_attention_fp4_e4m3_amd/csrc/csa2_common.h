@@ -62,12 +62,17 @@ constexpr size_t kAttnCounterBytes = 4096;
 // window = true: one more partial slot per (row, head) for the local window
 size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window);
 
-// decode attention with 32-head workgroups (bf16 queries, no window) and the merge of its key splits
+// decode attention with 32-head workgroups (bf16 queries) and the merge of its key splits; a local
+// window joins when that merge runs inside the launch, as a partial the window kernel writes first
+// (normalized fp32 [R][Hq][2][512], slot 1, with its (max, sum) [R][Hq][2]) in the last
+// attn_dec_window_bytes of the workspace
 bool attn_dec_applies(int R, int Hq, int q_dtype, int top_k, bool window);
-size_t attn_dec_workspace_bytes(int R, int Hq, int top_k);
+size_t attn_dec_window_bytes(int R, int Hq);
+size_t attn_dec_workspace_bytes(int R, int Hq, int top_k, bool window);
 hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, const uint8_t* scales,
                            const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
-                           float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
+                           float softmax_scale, void* out, int out_dtype, float* lse, const float* win_o,
+                           const float* win_m, const float* win_l, void* ws, hipStream_t s);
 
 // top_k may be 0 when a window is given (win != nullptr): the window alone is attended
 hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const uint8_t* codes, const uint8_t* scales,

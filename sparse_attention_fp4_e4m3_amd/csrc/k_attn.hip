@@ -1744,7 +1744,7 @@ int attn_slots(int R, int Hq, int q_dtype, int top_k, bool window) {
 }  // namespace
 
 size_t attn_workspace_bytes(int R, int Hq, int q_dtype, int top_k, bool window) {
-  if (attn_dec_applies(R, Hq, q_dtype, top_k, window)) return attn_dec_workspace_bytes(R, Hq, top_k);
+  if (attn_dec_applies(R, Hq, q_dtype, top_k, window)) return attn_dec_workspace_bytes(R, Hq, top_k, window);
   const int slots = attn_slots(R, Hq, q_dtype, top_k, window);
   if (slots <= 1) return 0;
   const size_t n = (size_t)R * Hq * slots;
@@ -1758,10 +1758,11 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
                               float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s) {
   if (R == 0) return hipSuccess;
   const bool window = win != nullptr;
-  if (attn_dec_applies(R, Hq, q_dtype, top_k, window))
+  const bool dec = attn_dec_applies(R, Hq, q_dtype, top_k, window);
+  if (dec && !window)
     return launch_attn_dec(R, q, Hq, codes, scales, row_start, idx, top_k, row_visible, softmax_scale, out, out_dtype,
-                           lse, ws, s);
-  const Plan p = top_k > 0 ? plan(R, Hq, q_dtype, top_k) : Plan{};
+                           lse, nullptr, nullptr, nullptr, ws, s);
+  const Plan p = top_k > 0 && !dec ? plan(R, Hq, q_dtype, top_k) : Plan{};
   AttnArgs a{};
   a.q = q;
   a.Hq = Hq;
@@ -1784,6 +1785,24 @@ hipError_t launch_sparse_attn(int R, const void* q, int q_dtype, int Hq, const u
   a.new_x_dtype = new_x_dtype;
   a.new_x_stride = new_x_stride;
   a.new_rows = new_rows;
+  if (dec) {
+    // the window first, as a partial (slot 1 of two) that the decode kernel's merge takes as one more term
+    const size_t n = (size_t)R * Hq * 2;
+    char* b = static_cast<char*>(ws) + attn_dec_workspace_bytes(R, Hq, top_k, false);
+    a.slots = 2;
+    a.ws_o = reinterpret_cast<float*>(b);
+    b += (n * kDim * 4 + 255) & ~size_t(255);
+    a.ws_m = reinterpret_cast<float*>(b);
+    b += (n * 4 + 255) & ~size_t(255);
+    a.ws_l = reinterpret_cast<float*>(b);
+    auto& ew = profile_events(CSA2_KERNEL_SWA_ATTN);
+    if (ew.start) (void)hipEventRecord(ew.start, s);
+    const hipError_t e = go_swa<1, false, CSA2_BF16>(R, Hq / 16, a, s);
+    if (ew.stop) (void)hipEventRecord(ew.stop, s);
+    if (e != hipSuccess) return e;
+    return launch_attn_dec(R, q, Hq, codes, scales, row_start, idx, top_k, row_visible, softmax_scale, out, out_dtype,
+                           lse, a.ws_o, a.ws_m, a.ws_l, ws, s);
+  }
   if (a.slots > 1) {
     const size_t n = (size_t)R * Hq * a.slots;
     char* b = static_cast<char*>(ws) + kAttnCounterBytes;

@@ -33,9 +33,13 @@
 //    keys' scales (staged as fp16, transposed, by the QK lanes).
 //  Every FP4 element is dequantized once for QK^T and once for PV.
 // Split-K: each (row, head group) has S workgroups; each writes its
-// normalized fp16 partial straight from its accumulators (streaming stores,
+// normalized fp16 partial straight from its accumulators (device-scope stores,
 // no transpose) and its (max, sum) per head, and k_dec_combine merges the S
 // partials in fixed split order, so results are deterministic.
+// A row's local window ("The Paper" in the talk write-up: the selected
+// entries and the recent window share one softmax) joins as one more
+// partial: the window kernel writes it (normalized fp32, with its (max, sum))
+// before this launch, and the in-launch merge weighs it after the splits.
 #include <algorithm>
 
 #include "csa2_common.h"
@@ -74,6 +78,10 @@ struct DecArgs {
   void* out;
   int out_dtype;
   float* lse;
+  const float* win_o;       // the local window's partial, written before this launch, or null:
+                            // normalized fp32 [R][Hq][2][512] (slot 1), its (max, sum) in win_m, win_l [R][Hq][2]
+  const float* win_m;
+  const float* win_l;
   int splits;               // S
   int kps;                  // keys per split (multiple of kChunk)
   int xcd_map;              // 1: the S splits of a (row, head group) share blockIdx.x % 8
@@ -101,6 +109,7 @@ struct __align__(16) SmemDec {
   float alpha[kHG];
   float ifin[kHG];
   __align__(16) float om[16][kMaxSplits];  // merge workgroups: weights of the splits of their 16 heads
+  float omw[16];                           // and of the window's partial
   int flag;
 };
 
@@ -238,9 +247,24 @@ __device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
     const uint32_t off = (uint32_t)((((((size_t)pair * S + (s2 < S ? s2 : 0)) * 8 + w) * 4 + pc) * 64 + lane) * 16);
     v[s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off, 0, 16);
   }
-  // weights of the splits of each head, in fixed split order
+  // the window's partial (an earlier launch wrote it): this thread's 8 outputs, its heads' (max, sum)
+  float wo[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wm = -INFINITY, wl = 0.0f;
+  if (a.win_o) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t hh = (int64_t)r * a.Hq + h0 + 16 * jj + 8 * (e >> 2) + 4 * h2 + (e & 3);
+      wo[e] = a.win_o[(hh * 2 + 1) * kDim + 64 * w + 32 * tt + l32];
+    }
+    if (tid < 16) {
+      const int64_t hh = (int64_t)r * a.Hq + h0 + 16 * jj + tid;
+      wm = a.win_m[hh * 2 + 1];
+      wl = a.win_l[hh * 2 + 1];
+    }
+  }
+  // weights of the splits of each head, in fixed split order, then the window's
   if (tid < 16) {
-    float M = -INFINITY;
+    float M = wm;
 #pragma unroll
     for (int s2 = 0; s2 < kMaxSplits; ++s2)
       if (s2 < S) M = fmaxf(M, __uint_as_float(ml[s2][0]));
@@ -252,9 +276,12 @@ __device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
                    : 0.0f;
       L += wg[s2];
     }
+    const float ww = M != -INFINITY ? __builtin_amdgcn_exp2f(wm - M) * wl : 0.0f;  // 0 without a window
+    L += ww;
     const float iL = L > 0.0f ? 1.0f / L : 0.0f;
     *reinterpret_cast<floatx4*>(&sm.om[tid][0]) = floatx4{wg[0] * iL, wg[1] * iL, wg[2] * iL, wg[3] * iL};
     *reinterpret_cast<floatx4*>(&sm.om[tid][4]) = floatx4{wg[4] * iL, wg[5] * iL, wg[6] * iL, wg[7] * iL};
+    sm.omw[tid] = ww * iL;
     if (a.lse && tt == 0)
       a.lse[(int64_t)r * a.Hq + h0 + 16 * jj + tid] = !ok ? __builtin_nanf("") : L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
   }
@@ -276,6 +303,10 @@ __device__ __forceinline__ void merge_part(const DecArgs& a, SmemDec& sm) {
       acc[2 * k] += wv[2 * k][s2 >> 2][s2 & 3] * h_lo(v[s2][k]);
       acc[2 * k + 1] += wv[2 * k + 1][s2 >> 2][s2 & 3] * h_hi(v[s2][k]);
     }
+  }
+  if (a.win_o) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += sm.omw[8 * (e >> 2) + 4 * h2 + (e & 3)] * wo[e];
   }
   const int64_t ob = ((int64_t)r * a.Hq + h0 + 16 * jj) * kDim + 64 * w + 32 * tt + l32;
   const float bad = __builtin_nanf("");
@@ -714,24 +745,36 @@ DecPlan dec_plan(int R, int Hq, int top_k) {
 }  // namespace
 
 bool attn_dec_applies(int R, int Hq, int q_dtype, int top_k, bool window) {
-  if (window || q_dtype != CSA2_BF16 || Hq % kHG != 0 || top_k < 1) return false;
+  if (q_dtype != CSA2_BF16 || Hq % kHG != 0 || top_k < 1) return false;
   const int64_t pairs = (int64_t)R * (Hq / kHG);
   // rows x 64-head groups that fill the chip take the 64-head prefill kernel
   if ((Hq / 16) % 4 == 0 && (int64_t)R * (Hq / 64) >= 256) return false;
-  return pairs <= kMaxPairs;
+  if (pairs > kMaxPairs) return false;
+  if (!window) return true;
+  // a window joins as one more term of the in-launch merge, so only plans that merge in the launch take it
+  const DecPlan p = dec_plan(R, Hq, top_k);
+  return p.splits > 1 && p.xcd;
 }
 
-size_t attn_dec_workspace_bytes(int R, int Hq, int top_k) {
+size_t attn_dec_window_bytes(int R, int Hq) {
+  const size_t n = (size_t)R * Hq * 2;
+  return round_up(n * kDim * 4, 256) + 2 * round_up(n * 4, 256);
+}
+
+size_t attn_dec_workspace_bytes(int R, int Hq, int top_k, bool window) {
   const DecPlan p = dec_plan(R, Hq, top_k);
   if (p.splits <= 1) return 0;
   const size_t n = (size_t)p.pairs * p.splits;
-  return kAttnCounterBytes + round_up(n * kHG * 512 * 2, 256) + round_up(n * kHG * 8, 256);
+  return kAttnCounterBytes + round_up(n * kHG * 512 * 2, 256) + round_up(n * kHG * 8, 256) +
+         (window ? attn_dec_window_bytes(R, Hq) : 0);
 }
 
 hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, const uint8_t* scales,
                            const int64_t* row_start, const int32_t* idx, int top_k, const int32_t* row_visible,
-                           float softmax_scale, void* out, int out_dtype, float* lse, void* ws, hipStream_t s) {
+                           float softmax_scale, void* out, int out_dtype, float* lse, const float* win_o,
+                           const float* win_m, const float* win_l, void* ws, hipStream_t s) {
   const DecPlan p = dec_plan(R, Hq, top_k);
+  if (win_o && !(p.splits > 1 && p.xcd)) return hipErrorInvalidValue;  // only the in-launch merge takes a window
   DecArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.Hq = Hq;
@@ -745,6 +788,9 @@ hipError_t launch_attn_dec(int R, const void* q, int Hq, const uint8_t* codes, c
   a.out = out;
   a.out_dtype = out_dtype;
   a.lse = lse;
+  a.win_o = win_o;
+  a.win_m = win_m;
+  a.win_l = win_l;
   a.splits = p.splits;
   a.kps = p.kps;
   a.xcd_map = p.xcd ? 1 : 0;
