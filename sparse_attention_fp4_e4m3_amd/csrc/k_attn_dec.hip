@@ -492,9 +492,9 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     mx = half_max(mx);
     if (lane < 32) sm.red_max[w][lane] = mx;
     lds_barrier();
-    float mc = sm.red_max[0][l32];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) mc = fmaxf(mc, sm.red_max[k][l32]);
+    // half h2 of the wave takes waves 4h2 .. 4h2+3, the two halves then meet across lanes
+    const float mc = half_max(fmaxf(fmaxf(sm.red_max[4 * h2][l32], sm.red_max[4 * h2 + 1][l32]),
+                                    fmaxf(sm.red_max[4 * h2 + 2][l32], sm.red_max[4 * h2 + 3][l32])));
     const float m_new = fmaxf(m_run, mc);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while nothing has been seen
@@ -515,9 +515,8 @@ __global__ __launch_bounds__(kT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     if (lane < 32) sm.red_sum[w][lane] = sum;
     if (w == 0 && lane < 32) sm.alpha[lane] = alpha;
     lds_barrier();
-    float ls = sm.red_sum[0][l32];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) ls += sm.red_sum[k][l32];
+    const float ls = half_sum((sm.red_sum[4 * h2][l32] + sm.red_sum[4 * h2 + 1][l32]) +
+                              (sm.red_sum[4 * h2 + 2][l32] + sm.red_sum[4 * h2 + 3][l32]));  // same bits in both halves
     l_run = l_run * alpha + ls;
 
     // ---- PV: O[head][channel] for channels [64w, 64w+64), two 32-channel tiles
