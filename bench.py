@@ -348,6 +348,7 @@ def cpu_baseline(w, lens, sample_rows, reps, swa=False, mxfp4=False):
 
     rows = list(range(min(sample_rows, w.B)))
     V = w.verify
+    reps = max(1, reps // V)  # V query rows per sequence multiply the work of a step: keep the sample's CPU time bounded
     log("cpu baseline: preparing oracle cache for %d sequences" % len(rows))
     caches = {}
     for b in rows:
